@@ -1,0 +1,161 @@
+"""Pins for the oracle's verify attention (stage 3), LM head (stage 4a) and
+the padded-vs-ragged equivalence."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.attention import verify_attention, attention_row
+from oracle.lm_head import lm_head_logits, lm_head_pred
+from ragged_verification_amd import synth
+
+
+def _np(t):
+    return None if t is None else t.to(torch.float64).cpu().numpy()
+
+
+def _paged_case(seed, Hq=4, Hkv=2, D=8, Dv=None, latent=False, P=4):
+    rng = np.random.default_rng(seed)
+    B = 3
+    ctx = rng.integers(0, 9, size=B)
+    gamma = 3
+    pages = (ctx + gamma + P - 1) // P
+    n_pages = int(pages.sum())
+    perm = rng.permutation(n_pages)
+    pt = np.full((B, int(pages.max())), -1)
+    o = 0
+    for i in range(B):
+        pt[i, :pages[i]] = perm[o:o + pages[i]]
+        o += pages[i]
+    Dv = D if Dv is None else Dv
+    k_cache = rng.standard_normal((n_pages, P, Hkv, D))
+    v_cache = None if latent else rng.standard_normal((n_pages, P, Hkv, Dv))
+    w = rng.integers(1, gamma + 1, size=B)
+    cu, M, M_pad, row_req, row_pos, tok, slot = oracle.pack(
+        w, np.zeros(B), np.zeros((B, gamma - 1)), ctx, pt, P, ())
+    q = rng.standard_normal((M, Hq, D))
+    return dict(k=k_cache, v=v_cache, pt=pt, P=P, ctx=ctx, w=w, M=M, row_req=row_req,
+                row_pos=row_pos, slot=slot, q=q, Hq=Hq, Hkv=Hkv, D=D, Dv=Dv)
+
+
+@pytest.mark.parametrize("latent", [False, True])
+def test_attention_matches_torch_sdpa(latent):
+    """Against torch's scaled_dot_product_attention (CPU, fp64), keys gathered
+    position by position from the slot list, GQA heads expanded."""
+    c = _paged_case(1, Hq=6, Hkv=1 if latent else 3, D=10, Dv=7 if latent else None,
+                    latent=latent)
+    scale = 0.37
+    o, lse = verify_attention(c["q"], c["k"], c["v"], c["pt"], c["P"], c["row_req"],
+                              c["row_pos"], c["M"], scale, Dv=c["Dv"])
+    group = c["Hq"] // c["Hkv"]
+    kflat = c["k"].reshape(-1, c["Hkv"], c["D"])
+    for r in range(c["M"]):
+        i, p = int(c["row_req"][r]), int(c["row_pos"][r])
+        slots = [int(c["pt"][i][pos // c["P"]]) * c["P"] + pos % c["P"] for pos in range(p + 1)]
+        K = torch.tensor(kflat[slots])                     # [L, Hkv, D]
+        if latent:
+            Vv = K[:, :, :c["Dv"]]
+        else:
+            Vv = torch.tensor(c["v"].reshape(-1, c["Hkv"], c["Dv"])[slots])
+        Kh = K.repeat_interleave(group, dim=1).permute(1, 0, 2)[None]   # [1,Hq,L,D]
+        Vh = Vv.repeat_interleave(group, dim=1).permute(1, 0, 2)[None]
+        qh = torch.tensor(c["q"][r])[None, :, None, :]                # [1,Hq,1,D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qh, Kh, Vh, scale=scale)
+        np.testing.assert_allclose(o[r], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+        s = scale * torch.einsum("hd,hld->hl", torch.tensor(c["q"][r]), Kh[0])
+        np.testing.assert_allclose(lse[r], torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((4, 16))
+    keys = rng.standard_normal((1, 2, 16))
+    vals = rng.standard_normal((1, 2, 5))
+    o, lse = attention_row(q, keys, vals, 0.25)
+    # a single visible key: the output is that key's value, exactly
+    assert np.array_equal(o[:2], np.repeat(vals[:, 0], 2, axis=0))
+    assert np.array_equal(o[2:], np.repeat(vals[:, 1], 2, axis=0))
+    # identical keys: uniform weights, output is the mean value
+    keys = np.repeat(rng.standard_normal((1, 1, 16)), 9, axis=0)
+    vals = rng.standard_normal((9, 1, 5))
+    o, lse = attention_row(q, keys, vals, 0.5)
+    np.testing.assert_allclose(o, np.repeat(vals.mean(0), 4, axis=0), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, 0.5 * keys[0, 0] @ q.T + np.log(9), rtol=1e-13)
+    # one key aligned with the query and huge: its value wins
+    keys = rng.standard_normal((6, 1, 16))
+    keys[3, 0] = 60.0 * q[0] / np.linalg.norm(q[0])
+    o, _ = attention_row(q[:1], keys, vals[:6], 1.0)
+    np.testing.assert_allclose(o[0], vals[3, 0], atol=1e-12)
+
+
+def test_attention_padding_rows_are_zero():
+    c = _paged_case(3)
+    row_req = np.concatenate([c["row_req"], [-1, -1]])
+    row_pos = np.concatenate([c["row_pos"], [-1, -1]])
+    q = np.concatenate([c["q"], np.ones((2, c["Hq"], c["D"]))])
+    o, lse = verify_attention(q, c["k"], c["v"], c["pt"], c["P"], row_req, row_pos,
+                              c["M"] + 2, 0.3)
+    assert np.all(o[c["M"]:] == 0) and np.all(np.isneginf(lse[c["M"]:]))
+
+
+def test_lm_head_planted_targets_and_identity():
+    wl = synth.workload("tiny_f32")
+    d = synth.make_inputs(wl)
+    B, gamma = d["B"], d["gamma"]
+    x = _np(d["hidden_block"]).reshape(B * gamma, -1)
+    z = lm_head_logits(x, _np(d["W"]), chunk=100)
+    pred = lm_head_pred(z)
+    assert np.array_equal(pred, d["targets"].reshape(-1).numpy())
+    # identity projection: logits are the hidden values themselves
+    H = 12
+    X = np.random.default_rng(0).standard_normal((5, H))
+    z = lm_head_logits(X, np.eye(H))
+    assert np.array_equal(z, X)
+    assert np.array_equal(lm_head_pred(z), np.argmax(X, axis=1))
+
+
+def test_lm_head_ties_pick_lowest_index():
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((30, 8))
+    W[17] = W[4]
+    x = 50 * W[4][None] / np.linalg.norm(W[4])
+    z = lm_head_logits(x, W)
+    assert z[0, 4] == z[0, 17]
+    assert lm_head_pred(z)[0] == 4
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "gqa_bf16", "mla_bf16"])
+def test_static_ragged_equals_dense_padded(name):
+    """Static mode packs full blocks; it must reproduce a masked fixed-shape
+    padded verify row for row (attention output, predictions, accepts)."""
+    if name == "tiny_f32":
+        wl = synth.workload(name)
+        B = None
+    elif name == "gqa_bf16":
+        wl = synth.workload(name, V=300, H=64, Hq=8, Hkv=2, ctx=("uniform", 5, 40))
+        B = 3
+    else:
+        wl = synth.workload(name, V=300, H=64, Hq=4, ctx=("uniform", 5, 70))
+        B = 2
+    d = synth.make_inputs(wl, B=B)
+    B, gamma = d["B"], d["gamma"]
+    bias, alpha, theta = d["cost_bias"], d["cost_alpha"].numpy(), d["cost_theta"].numpy()
+    wc, wv, _, _ = oracle.schedule(d["conf"].numpy(), gamma, oracle.STATIC, bias, alpha, theta)
+    cu, M, M_pad, row_req, row_pos, tok, slot = oracle.pack(
+        wv, d["anchor"].numpy(), d["drafts"].numpy(), d["ctx"].numpy(),
+        d["page_table"].numpy(), d["page_size"], ())
+    qb = _np(d["q_block"])
+    q = qb.reshape(B * gamma, wl.Hq, wl.Dqk)
+    o, _ = verify_attention(q, _np(d["k_cache"]), _np(d["v_cache"]), d["page_table"].numpy(),
+                            d["page_size"], row_req, row_pos, M_pad, d["sm_scale"], Dv=wl.Dv)
+    x = _np(d["hidden_block"]).reshape(B * gamma, -1)
+    pred = lm_head_pred(lm_head_logits(x, _np(d["W"])))
+    acc, bonus, ceil = oracle.accept_greedy(pred, cu, wc, wv, d["drafts"].numpy())
+    od, pd, ad, bd = oracle.dense_padded_verify(
+        qb, _np(d["k_cache"]), _np(d["v_cache"]), d["page_table"].numpy(), d["page_size"],
+        d["ctx"].numpy(), d["sm_scale"], _np(d["hidden_block"]), _np(d["W"]),
+        d["drafts"].numpy(), Dv=wl.Dv)
+    np.testing.assert_allclose(o.reshape(B, gamma, wl.Hq, wl.Dv), od, rtol=1e-10, atol=1e-12)
+    assert np.array_equal(pred.reshape(B, gamma), pd)
+    assert np.array_equal(acc, ad) and np.array_equal(bonus, bd)
