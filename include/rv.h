@@ -1,0 +1,329 @@
+/*
+ * rv.h -- C ABI of the ragged, confidence-driven verify step (librv.so).
+ *
+ * The step is the verify half of DSpark speculative decoding as described on
+ * the page "DSpark in SGLang: Speculative Decoding with Confidence-Driven,
+ * Variable-Length Verification" (papercache.org summary of the LMSYS blog,
+ * below: the DSpark-in-SGLang page).  Five calls, run in this order on one
+ * stream:
+ *
+ *   rv_schedule        per-request verify windows from draft confidences
+ *   rv_pack            front-pack the windows into a cu_seqlens buffer
+ *   rv_verify_attn     varlen causal attention of packed rows, paged KV
+ *   rv_lm_head_accept  target LM head, argmax / min(1,p/q) accept
+ *   rv_compact_scatter write committed tokens and KV slots back
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array pointers are DEVICE memory owned by the caller unless a field
+ *   says "host".  Arrays are dense, row-major, with the shapes given per field.
+ *   Integers are int32, confidences/uniforms float32, cost tables float64.
+ * - Block layout: each request has a block of `gamma` positions; position 0 is
+ *   the anchor (the last committed token, whose KV is written but not yet
+ *   committed) and positions 1..gamma-1 hold drafts d_1..d_{gamma-1}.  A window
+ *   w in [1, gamma] counts packed rows.  Row k of request i sits at sequence
+ *   position ctx[i] + k and its prediction checks draft d_{k+1}.
+ * - Every call only enqueues work on `stream` (a hipStream_t, NULL = default
+ *   stream) and returns; nothing is synchronised and nothing is allocated.
+ *   Scratch memory comes from `workspace` (size from rv_workspace_size); the
+ *   first 256 bytes of a workspace hold a sticky device status word.
+ *   Distinct workspaces make concurrent calls independent.
+ * - Host-checkable problems (NULL pointers, sizes out of range, unsupported
+ *   shapes, workspace too small) return a negative rv_status before anything
+ *   is enqueued.  Data problems found on the device (confidence outside [0,1],
+ *   window outside [1,gamma], page or token index out of range, packed total
+ *   above the largest tier, history overflow, non-positive step time) set the
+ *   sticky device status (first error wins, read with rv_device_status); the
+ *   kernels then keep every access in bounds and give the offending request a
+ *   defined result, as stated per call.
+ * - Nothing in the library aborts the process.
+ */
+#ifndef RV_H_
+#define RV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes (host return values) ---------------------------------- */
+#define RV_OK 0
+#define RV_ERR_INVALID_ARG (-1)   /* NULL pointer or size out of range */
+#define RV_ERR_UNSUPPORTED (-2)   /* shape/dtype combination not built */
+#define RV_ERR_TIER (-3)          /* tier list not ascending, or too long */
+#define RV_ERR_WORKSPACE (-4)     /* workspace NULL or smaller than needed */
+#define RV_ERR_HIP (-5)           /* a HIP runtime call failed */
+typedef int32_t rv_status;
+
+/* ---- sticky device status codes (rv_device_status) ---------------------- */
+#define RV_DEV_OK 0
+#define RV_DEV_BAD_CONF 1         /* confidence NaN or outside [0, 1] */
+#define RV_DEV_BAD_COST 2         /* step time not positive (or NaN) */
+#define RV_DEV_BAD_WINDOW 3       /* window outside [1, gamma] */
+#define RV_DEV_TIER_OVERFLOW 4    /* packed total above the largest tier */
+#define RV_DEV_BAD_PAGE 5         /* page-table entry outside [0, num_pages) */
+#define RV_DEV_BAD_TOKEN 6        /* token id outside [0, V) */
+#define RV_DEV_HIST_OVERFLOW 7    /* history or req_to_token row too short */
+
+/* ---- enums ---------------------------------------------------------------- */
+/* Verify modes, DSpark-in-SGLang page, section A2 (verify modes) and A3
+ * (no-trim): static verifies and commits full blocks; compact verifies and
+ * commits the scheduled windows; cap-accept verifies full blocks and commits up
+ * to the scheduled window; no-trim is compact without a cost table (full
+ * windows, ragged path). */
+#define RV_STATIC 0
+#define RV_COMPACT 1
+#define RV_CAP_ACCEPT 2
+#define RV_NO_TRIM 3
+
+/* Acceptance rules: greedy (drafts kept up to the first disagreement with
+ * the target argmax) and rejection sampling (keep x with probability
+ * min(1, p(x)/q(x))); lshu.cn DSpark explainer, sections 1.2, 2.3, 3.3. */
+#define RV_GREEDY 0
+#define RV_REJECTION 1
+
+/* Element types of the floating-point payloads. */
+#define RV_F32 0
+#define RV_BF16 1
+
+/* Limits of this build. */
+#define RV_MAX_GAMMA 16
+#define RV_MAX_TIERS 16
+#define RV_MAX_SCHED_CANDIDATES 4096   /* B * (gamma - 1), compact/cap-accept */
+#define RV_MAX_ROWS 8192               /* B * gamma */
+
+/* ---- sizing ------------------------------------------------------------- */
+/* Upper bounds of the problem a workspace must serve.  Any field may be 0 when
+ * the corresponding call is never made with that workspace (e.g. H = V = 0 if
+ * rv_lm_head_accept is not used). */
+typedef struct {
+  int32_t B;          /* requests */
+  int32_t gamma;      /* block width (anchor + drafts) */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* KV heads (1 for the latent layout) */
+  int32_t Dqk;        /* query/key head dim */
+  int32_t Dv;         /* value head dim */
+  int32_t V;          /* vocabulary size */
+  int32_t dtype;      /* RV_F32 or RV_BF16 */
+} rv_dims;
+
+/* Library version string (static storage). */
+const char* rv_version(void);
+
+/* Bytes of workspace the five calls need for problems bounded by *dims.
+ * Host-only, pure.  Returns RV_ERR_INVALID_ARG on NULL or negative fields. */
+rv_status rv_workspace_size(const rv_dims* dims, size_t* bytes);
+
+/* Copies the sticky device status of `workspace` to *code (host) after
+ * synchronising `stream`.  Returns RV_ERR_HIP if the copy fails. */
+rv_status rv_device_status(const void* workspace, int32_t* code, void* stream);
+
+/* Enqueues a reset of the sticky device status to RV_DEV_OK (a kernel, not a
+ * memset, so the call may sit inside a captured graph). */
+rv_status rv_clear_status(void* workspace, void* stream);
+
+/* ---- stage 1: confidence scheduler -------------------------------------- */
+/* DSpark-in-SGLang page: section A2 (the confidence head scores each draft;
+ * the product of scores over the block is its survival probability; the
+ * scheduler turns survival into per-request verify budgets), section 速读 and
+ * A2 "cost-table profiling" (T(bs,K) = bias + alpha(bs) + theta(M), M = bs+K;
+ * the argmax trades expected accepted tokens against marginal cost).
+ *
+ * Computes S[i,k] = prod_{j<=k} conf[i,j] left to right in fp64, ranks all
+ * (i,k), k>=1, by (S desc, i asc, k asc), and for K = 0..B*(gamma-1) evaluates
+ * R(K) = (B*2^40 + sum_{first K} floor(S*2^40)) / ((bias + alpha[B]) +
+ * theta[B+K]) with int64 sums and one fp64 divide; K* is the first maximiser
+ * and w_i = 1 + #{ranked-first-K* candidates of request i}.  static / no-trim:
+ * w = gamma.  Outputs are bit-identical to a sequential evaluation. */
+typedef struct {
+  const float* conf;         /* [B][gamma-1] draft confidences in [0,1] */
+  int32_t B;                 /* 1..RV_MAX_ROWS/gamma */
+  int32_t gamma;             /* 2..RV_MAX_GAMMA */
+  int32_t mode;              /* RV_STATIC / RV_COMPACT / RV_CAP_ACCEPT / RV_NO_TRIM */
+  int32_t alpha_len;         /* entries of cost_alpha, must exceed B */
+  int32_t theta_len;         /* entries of cost_theta, must exceed B*gamma */
+  int32_t _pad0;
+  double cost_bias;          /* host value, ms */
+  const double* cost_alpha;  /* [alpha_len] alpha(bs), ms */
+  const double* cost_theta;  /* [theta_len] theta(M), ms */
+  int32_t* w_commit;         /* out [B] rows whose verdicts may be committed */
+  int32_t* w_verify;         /* out [B] rows packed and verified */
+  int32_t* k_star;           /* out [1] extra verify tokens K* */
+  double* e_star;            /* out [1] expected committed tokens at K* */
+  void* workspace;
+  size_t workspace_bytes;
+} rv_schedule_args;
+/* Device errors: BAD_CONF (that confidence counts as 0), BAD_COST (windows
+ * fall back to 1). */
+rv_status rv_schedule(const rv_schedule_args* a, void* stream);
+
+/* ---- stage 2: ragged front-packing -------------------------------------- */
+/* DSpark-in-SGLang page, section A2 "ragged verify over a full CUDA graph"
+ * and Fig. 2: windows are front-packed into one compact cu_seqlens-style
+ * buffer with no per-request padding, and only the total is rounded up to the
+ * nearest captured tier.
+ *
+ * cu = exclusive scan of w_verify (cu[B] = M); M_pad = smallest tier >= M (M
+ * when n_tiers == 0).  For row r = cu[i] + k: row_req = i, row_pos = ctx[i]+k,
+ * tok = anchor[i] (k == 0) or drafts[i][k-1], slot = page_table[i][pos/P]*P +
+ * pos%P.  Rows [M, M_pad) get -1 in all four arrays; rows >= M_pad are not
+ * written. */
+typedef struct {
+  const int32_t* w_verify;   /* [B] windows from rv_schedule */
+  const int32_t* anchor;     /* [B] anchor token per request */
+  const int32_t* drafts;     /* [B][gamma-1] */
+  const int32_t* ctx;        /* [B] committed tokens before the anchor */
+  const int32_t* page_table; /* [B][max_pages] KV page per page_size positions */
+  int32_t B, gamma;
+  int32_t max_pages;         /* row stride of page_table */
+  int32_t page_size;         /* positions per page, >= 1 */
+  int32_t num_pages;         /* pages in the KV cache (bounds check) */
+  int32_t n_tiers;           /* 0..RV_MAX_TIERS */
+  const int32_t* tiers;      /* HOST [n_tiers], strictly ascending, > 0 */
+  int32_t rows_cap;          /* rows of the four row arrays, >= B*gamma */
+  int32_t _pad0;
+  int32_t* cu;               /* out [B+1] */
+  int32_t* mm;               /* out [2] = {M, M_pad} */
+  int32_t* row_req;          /* out [rows_cap] */
+  int32_t* row_pos;          /* out [rows_cap] */
+  int32_t* tok;              /* out [rows_cap] */
+  int32_t* slot;             /* out [rows_cap] */
+  void* workspace;
+  size_t workspace_bytes;
+} rv_pack_args;
+/* Device errors: BAD_WINDOW (window clamped to [1,gamma]), TIER_OVERFLOW
+ * (M_pad = M, still within rows_cap), BAD_PAGE (slot = -1). */
+rv_status rv_pack(const rv_pack_args* a, void* stream);
+
+/* ---- stage 3: verify attention ------------------------------------------ */
+/* DSpark-in-SGLang page, section A2: the packed buffer uses a cu_seqlens-style
+ * variable-length layout so compact verify reuses the backend's varlen
+ * attention (native sparse-MLA on DeepSeek-V4); each backend rebuilds its
+ * varlen metadata for the packed layout.
+ *
+ * For every real row r (request i, row k, position p = ctx[i]+k) and query
+ * head h (KV head g = h / (Hq/Hkv)): o[r,h] = softmax_j(sm_scale * q[r,h] .
+ * K[i,j,g]) V[i,j,g] over keys j = 0..p read through the page table;
+ * lse[r,h] = natural log of the softmax normaliser.  Latent layout
+ * (v_cache == NULL, Hkv == 1): V[i,j] = first Dv entries of K[i,j].  Rows
+ * [M, M_pad) get o = 0, lse = -inf; rows >= M_pad are not written.
+ *
+ * Built shapes: dtype RV_BF16 with (Dqk,Dv) = (576,512) latent, Hq % 64 == 0;
+ * or (128,128) with Hq/Hkv in {1,2,4,8,16}; dtype RV_F32 with Dqk = Dv <= 128
+ * (any group).  bf16 accumulates in fp32. */
+typedef struct {
+  const void* q;             /* [rows_cap][Hq][Dqk] packed queries, dtype */
+  const void* k_cache;       /* [num_pages][page_size][Hkv][Dqk], dtype */
+  const void* v_cache;       /* [num_pages][page_size][Hkv][Dv] or NULL (latent) */
+  const int32_t* page_table; /* [B][max_pages] */
+  const int32_t* ctx;        /* [B] */
+  const int32_t* cu;         /* [B+1] from rv_pack */
+  const int32_t* mm;         /* [2] {M, M_pad} from rv_pack */
+  int32_t B, gamma;          /* requests; block width (bounds every window) */
+  int32_t rows_cap, max_pages, page_size, num_pages;
+  int32_t Hq, Hkv, Dqk, Dv, dtype;
+  float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(Dqk)) */
+  void* o;                   /* out [rows_cap][Hq][Dv], dtype */
+  float* lse;                /* out [rows_cap][Hq] or NULL */
+  void* workspace;
+  size_t workspace_bytes;
+} rv_attn_args;
+/* Device errors: BAD_PAGE (the key is read from page 0 instead). */
+rv_status rv_verify_attn(const rv_attn_args* a, void* stream);
+
+/* ---- stage 4: LM head + accept ------------------------------------------ */
+/* Target LM head over the packed rows (z = W h, fp32 accumulation) and the
+ * acceptance rule (lshu.cn DSpark explainer: section 1.2 greedy first-mismatch,
+ * sections 2.3/3.3 min(1,p/q)); cap-accept ceiling (DSpark-in-SGLang page,
+ * section A2 "verify modes" and "observability").
+ *
+ * pred[r] = lowest index of the maximal logit of real row r; -1 for rows
+ * [M, M_pad).  Per request i (rows cu[i]..cu[i]+w_verify[i]-1):
+ *  greedy:    ceiling = leading j with drafts[i][j-1] == pred[cu[i]+j-1];
+ *  rejection: p = softmax(z) (T=1), accept draft j iff
+ *             u[i][j-1] * q_rows[i][j-1][d_j] < p_{row j-1}(d_j), stop at the
+ *             first reject;
+ *  accept = min(ceiling, w_commit[i]-1);
+ *  bonus (greedy) = pred at row accept; bonus (rejection) = inverse-CDF draw
+ *  with u_bonus[i] from max(0, p_{row c} - q_{c+1}) after a reject at draft
+ *  c+1 <= w_commit-1, else from p at row w_commit-1 (smallest v whose running
+ *  mass exceeds u_bonus * total). */
+typedef struct {
+  const void* hidden;        /* [rows_cap][H] packed final hidden states, dtype */
+  const void* W;             /* [V][H] LM-head weight, dtype */
+  const int32_t* mm;         /* [2] {M, M_pad} */
+  const int32_t* cu;         /* [B+1] */
+  const int32_t* w_commit;   /* [B] */
+  const int32_t* w_verify;   /* [B] */
+  const int32_t* drafts;     /* [B][gamma-1] */
+  const float* q_rows;       /* [B][gamma-1][V] draft distributions (rejection) */
+  const float* u;            /* [B][gamma-1] uniforms (rejection) */
+  const float* u_bonus;      /* [B] uniforms (rejection) */
+  int32_t B, gamma, rows_cap, H, V, dtype, rule;
+  int32_t _pad0;
+  int32_t* pred;             /* out [rows_cap] */
+  int32_t* accept;           /* out [B] accepted drafts */
+  int32_t* bonus;            /* out [B] bonus token */
+  int32_t* ceiling;          /* out [B] accepts over all verified rows */
+  float* logits;             /* out [rows_cap][V] fp32 (required for
+                                rejection, optional for greedy, real rows) */
+  void* workspace;
+  size_t workspace_bytes;
+} rv_lm_args;
+/* Device errors: BAD_TOKEN for a draft outside [0,V) (it never matches;
+ * under rejection it is rejected), BAD_WINDOW. */
+rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
+
+/* ---- stage 5: compact scatter ------------------------------------------- */
+/* DSpark-in-SGLang page, section A2 "performance and zero-overhead
+ * scheduling": a fused compact-scatter kernel writes the accepted results
+ * back; the page table stays on the device.
+ *
+ * commit_cu = exclusive scan of accept+1.  Request i commits tokens
+ * d_1..d_a, bonus at commit_tok[commit_cu[i]..] and the KV slots of rows
+ * 0..a at commit_slot[...]; req_to_token[i][ctx[i]+k] = slot of row k
+ * (k <= a); hist[i][hist_len[i]+k] = committed token k and hist_len += a+1
+ * (when hist != NULL); ctx[i] += a+1; anchor[i] = bonus.  Slots of rows
+ * a+1..w_verify-1 are listed in free_slots (in request order), their count in
+ * *free_count. */
+typedef struct {
+  const int32_t* cu;         /* [B+1] */
+  const int32_t* w_verify;   /* [B] */
+  const int32_t* accept;     /* [B] */
+  const int32_t* bonus;      /* [B] */
+  const int32_t* drafts;     /* [B][gamma-1] */
+  const int32_t* slot;       /* [rows_cap] from rv_pack */
+  int32_t B, gamma;
+  int32_t r2t_stride;        /* row length of req_to_token */
+  int32_t hist_stride;       /* row length of hist (ignored if hist NULL) */
+  int32_t* ctx;              /* in/out [B] */
+  int32_t* anchor;           /* in/out [B] */
+  int32_t* req_to_token;     /* in/out [B][r2t_stride] */
+  int32_t* hist;             /* in/out [B][hist_stride] or NULL */
+  int32_t* hist_len;         /* in/out [B] or NULL */
+  int32_t* commit_cu;        /* out [B+1] */
+  int32_t* commit_tok;       /* out [B*gamma] */
+  int32_t* commit_slot;      /* out [B*gamma] */
+  int32_t* free_slots;       /* out [B*gamma] */
+  int32_t* free_count;       /* out [1] */
+  void* workspace;
+  size_t workspace_bytes;
+} rv_scatter_args;
+/* Device errors: HIST_OVERFLOW (the request's req_to_token / hist writes are
+ * skipped; counters still advance), BAD_WINDOW (accept clamped). */
+rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream);
+
+/* ---- ABI self-description ----------------------------------------------- */
+/* Fills out[0] = sizeof(struct), out[1..] = offsetof of each field in
+ * declaration order, for struct `which` (0 schedule, 1 pack, 2 attn, 3 lm,
+ * 4 scatter, 5 dims).  Returns the number of values written, or -1 if `cap`
+ * is too small or `which` unknown.  Host-only; lets a binding verify its
+ * struct mirror. */
+int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RV_H_ */

@@ -1,0 +1,775 @@
+// Stage 3: varlen causal verify attention over a paged KV cache.
+//
+// DSpark-in-SGLang page, section A2 "ragged verify over a full CUDA graph":
+// the packed buffer is a cu_seqlens-style variable-length batch, so verify
+// reuses ordinary varlen causal attention (native sparse-MLA on DeepSeek-V4);
+// each backend rebuilds its varlen metadata from the packed layout.
+//
+// Design (gfx950):
+//  * A plan kernel (one workgroup) rebuilds that metadata on the device from
+//    cu[] and ctx[]: it cuts every request into q-tiles (up to 16 query
+//    vectors per wave that share one KV head) and, when the batch alone cannot
+//    fill the chip, splits the key range into chunks (split-KV).  Work items are
+//    ordered request-major so the tiles that read the same KV chunk run
+//    together and share it through L2.
+//  * The main kernel streams each item's keys through LDS in 32-key tiles read
+//    via the page table (register prefetch of the next tile overlaps the MFMA
+//    work of the current one), computes S^T = K Q^T and O^T += V^T P^T with
+//    bf16 16x16x32 MFMAs (fp32 accumulation) and keeps an online base-2
+//    softmax per query vector.  In the S^T orientation each lane owns one
+//    query vector, so the row max needs two cross-lane steps and P^T feeds the
+//    PV MFMA straight from registers; V is stored transposed in LDS.
+//  * The latent (MLA-style) layout reads one 576-wide row per key and uses its
+//    first 512 entries as the value.
+//  * Split items write fp32 partials (O, running max, normaliser) that a
+//    combine kernel merges.
+//  * fp32 inputs take a plain vector kernel.
+
+#include <float.h>
+
+#include "rv_common.h"
+
+namespace rv {
+namespace {
+
+constexpr int kNK = 32;            // keys per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct AttnShape {
+  int Hq, Hkv, G;        // G = Hq / Hkv
+  int QT;                // query vectors per tile (16 per wave)
+  int NH;                // heads per tile
+  int RT;                // rows per tile
+  int n_hb;              // head blocks per KV head = G / NH
+  int tpr_max;           // tiles per request at most
+};
+
+struct PlanParams {
+  const int32_t* cu;
+  const int32_t* ctx;
+  const int32_t* mm;
+  int4* req_info;        // per request: {n_splits, item_off, part_off, tiles}
+  int4* items;           // {request, tile, split, 0}
+  int32_t* hdr;          // [0] n_items, [1] chunk, [2] part slots used
+  int B, gamma, item_cap, part_cap, target;
+  AttnShape sh;
+};
+
+__device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---- plan: device-side varlen metadata -------------------------------------
+__global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
+  __shared__ long long red[1024];
+  __shared__ int scan_a[1024], scan_b[1024];
+  __shared__ int s_chunk;
+  const int t = threadIdx.x;
+  const int B = p.B;
+  const AttnShape& sh = p.sh;
+
+  // total work: sum over tiles of keys visible to the tile's last row
+  long long work = 0;
+  for (int i = t; i < B; i += 1024) {
+    const int w = p.cu[i + 1] - p.cu[i];
+    const int L = p.ctx[i] + w;
+    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
+    work += (long long)tiles * L;
+  }
+  red[t] = work;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (t < off) red[t] += red[t + off];
+    __syncthreads();
+  }
+  if (t == 0) {
+    long long c = (red[0] + p.target - 1) / p.target;
+    c = (c + kNK - 1) / kNK * kNK;
+    if (c < kMinChunk) c = kMinChunk;
+    if (c > (1 << 30)) c = 1 << 30;
+    s_chunk = (int)c;
+  }
+  __syncthreads();
+
+  // grow the chunk until items and partial slots fit their buffers
+  for (int iter = 0; iter < 32; ++iter) {
+    const int C = s_chunk;
+    int n_items = 0, n_parts = 0;
+    for (int i = t; i < B; i += 1024) {
+      const int w = p.cu[i + 1] - p.cu[i];
+      const int L = p.ctx[i] + w;
+      const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
+      const int ns = L > 0 ? ceil_div(L, C) : 1;
+      n_items += ns * tiles;
+      n_parts += ns > 1 ? ns * tiles : 0;
+    }
+    scan_a[t] = n_items;
+    scan_b[t] = n_parts;
+    __syncthreads();
+    for (int off = 512; off > 0; off >>= 1) {
+      if (t < off) { scan_a[t] += scan_a[t + off]; scan_b[t] += scan_b[t + off]; }
+      __syncthreads();
+    }
+    const bool fits = scan_a[0] <= p.item_cap && scan_b[0] <= p.part_cap;
+    __syncthreads();
+    if (fits || s_chunk >= (1 << 29)) break;
+    if (t == 0) s_chunk = s_chunk * 2;
+    __syncthreads();
+  }
+  const int C = s_chunk;
+
+  // per-request offsets (requests strided over threads, two-level scan)
+  const int seg = ceil_div(B, 1024);
+  const int i0 = t * seg;
+  int my_items = 0, my_parts = 0;
+  for (int s = 0; s < seg; ++s) {
+    const int i = i0 + s;
+    if (i >= B) break;
+    const int w = p.cu[i + 1] - p.cu[i];
+    const int L = p.ctx[i] + w;
+    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
+    const int ns = L > 0 ? ceil_div(L, C) : 1;
+    my_items += ns * tiles;
+    my_parts += ns > 1 ? ns * tiles : 0;
+  }
+  scan_a[t] = my_items;
+  scan_b[t] = my_parts;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int a = t >= off ? scan_a[t - off] : 0;
+    const int b = t >= off ? scan_b[t - off] : 0;
+    __syncthreads();
+    scan_a[t] += a;
+    scan_b[t] += b;
+    __syncthreads();
+  }
+  int item_off = scan_a[t] - my_items;
+  int part_off = scan_b[t] - my_parts;
+  for (int s = 0; s < seg; ++s) {
+    const int i = i0 + s;
+    if (i >= B) break;
+    const int w = p.cu[i + 1] - p.cu[i];
+    const int L = p.ctx[i] + w;
+    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
+    const int ns = L > 0 ? ceil_div(L, C) : 1;
+    p.req_info[i] = make_int4(ns, item_off, ns > 1 ? part_off : -1, tiles);
+    for (int sp = 0; sp < ns; ++sp)
+      for (int tl = 0; tl < tiles; ++tl) p.items[item_off + sp * tiles + tl] = make_int4(i, tl, sp, 0);
+    item_off += ns * tiles;
+    part_off += ns > 1 ? ns * tiles : 0;
+  }
+  if (t == 1023) {
+    p.hdr[0] = scan_a[1023];
+    p.hdr[1] = C;
+    p.hdr[2] = scan_b[1023];
+  }
+}
+
+// ---- main bf16 MFMA kernel ---------------------------------------------------
+struct MainParams {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;        // nullptr for the latent layout
+  const int32_t* page_table;
+  const int32_t* ctx;
+  const int32_t* cu;
+  const int4* req_info;
+  const int4* items;
+  const int32_t* hdr;
+  bf16_t* o;
+  float* lse;
+  float* part_o;          // [part_cap][QT][DV]
+  float* part_ml;         // [part_cap][QT][2]
+  int32_t* status;
+  int max_pages, page_size, num_pages, Hq, Hkv, G, NH, RT, n_hb, part_cap;
+  float scale_log2;       // sm_scale * log2(e)
+};
+
+template <int DQK, int DV, int NW, bool LATENT>
+struct AttnCfg {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kQT = 16 * NW;
+  static constexpr int kKStride = DQK + 8;      // bf16 per K row in LDS
+  static constexpr int kVStride = kNK + 8;      // bf16 per V^T row in LDS
+  static constexpr int kKChunks = kNK * DQK / 8;   // 16-byte chunks per K tile
+  static constexpr int kVChunks = LATENT ? 0 : kNK * DV / 8;
+  static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
+  static constexpr int kVPer = (kVChunks + kThreads - 1) / kThreads;
+  static constexpr int kLdsBytes = (kNK * kKStride + DV * kVStride) * 2;
+};
+
+template <int DQK, int DV, int NW, bool LATENT>
+__global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
+  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* Vt = Ks + kNK * Cfg::kKStride;
+
+  // XCD-aware order: hardware places workgroup b on XCD b % 8; give each XCD
+  // a contiguous run of items so tiles sharing a KV chunk share its L2.
+  const int n_items = p.hdr[0];
+  const int per_xcd = (n_items + 7) / 8;
+  const int k_local = blockIdx.x / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + k_local;
+  if (k_local >= per_xcd || item >= n_items) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int n16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int4 rec = p.items[item];
+  const int i = rec.x, tile = rec.y, sp = rec.z;
+  const int4 info = p.req_info[i];
+  const int ns = info.x;
+  const int row_start = p.cu[i];
+  const int w = p.cu[i + 1] - row_start;
+  const int c = p.ctx[i];
+  const int rb = tile / (p.Hkv * p.n_hb);
+  const int rem = tile % (p.Hkv * p.n_hb);
+  const int g = rem / p.n_hb;
+  const int hb = rem % p.n_hb;
+  const int row0 = rb * p.RT;
+  const int rows_here = min(p.RT, w - row0);
+  const int L_tile = c + row0 + rows_here;
+  // chunk bounds: uniform split of the request's key range
+  const int chunk = p.hdr[1];
+  const int kv_begin = sp * chunk;
+  const int kv_end = min(kv_begin + chunk, L_tile);
+
+  // this lane's query vector
+  const int qv = wid * 16 + n16;
+  const int q_row_local = qv / p.NH;
+  const int head = g * p.G + hb * p.NH + (qv % p.NH);
+  const bool q_valid = q_row_local < rows_here;
+  const int q_row = row_start + row0 + q_row_local;
+  const int limit = c + row0 + q_row_local;   // last visible key position
+
+  // Q fragments (B operand of S^T = K Q^T)
+  u32x4_t qf[DQK / 32];
+#pragma unroll
+  for (int ks = 0; ks < DQK / 32; ++ks) {
+    if (q_valid) {
+      const bf16_t* src = p.q + ((size_t)q_row * p.Hq + head) * DQK + ks * 32 + grp * 8;
+      qf[ks] = *reinterpret_cast<const u32x4_t*>(src);
+    } else {
+      qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  f32x4_t oacc[DV / 16];
+#pragma unroll
+  for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  const int P = p.page_size;
+  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
+
+  // register prefetch buffers for one KV tile
+  u32x4_t kbuf[Cfg::kKPer];
+  u32x4_t vbuf[Cfg::kVPer > 0 ? Cfg::kVPer : 1];
+
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < Cfg::kKPer; ++e) {
+      const int ch = tid + e * Cfg::kThreads;
+      u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
+      if (ch < Cfg::kKChunks) {
+        const int kk = ch / (DQK / 8);
+        const int part = ch % (DQK / 8);
+        const int j = t0 + kk;
+        if (j < kv_end) {
+          int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
+          if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+          const size_t tok = (size_t)pg * P + (j % P);
+          val = *reinterpret_cast<const u32x4_t*>(p.k + (tok * p.Hkv + g) * DQK + part * 8);
+        }
+      }
+      kbuf[e] = val;
+    }
+    if constexpr (!LATENT) {
+#pragma unroll
+      for (int e = 0; e < Cfg::kVPer; ++e) {
+        const int ch = tid + e * Cfg::kThreads;
+        u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
+        if (ch < Cfg::kVChunks) {
+          const int kk = ch / (DV / 8);
+          const int part = ch % (DV / 8);
+          const int j = t0 + kk;
+          if (j < kv_end) {
+            int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
+            if (pg < 0 || pg >= p.num_pages) pg = 0;
+            const size_t tok = (size_t)pg * P + (j % P);
+            val = *reinterpret_cast<const u32x4_t*>(p.v + (tok * p.Hkv + g) * DV + part * 8);
+          }
+        }
+        vbuf[e] = val;
+      }
+    }
+  };
+
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int e = 0; e < Cfg::kKPer; ++e) {
+      const int ch = tid + e * Cfg::kThreads;
+      if (ch < Cfg::kKChunks) {
+        const int kk = ch / (DQK / 8);
+        const int part = ch % (DQK / 8);
+        *reinterpret_cast<u32x4_t*>(Ks + kk * Cfg::kKStride + part * 8) = kbuf[e];
+        if constexpr (LATENT) {
+          if (part * 8 < DV) {
+            const bf16_t* hv = reinterpret_cast<const bf16_t*>(&kbuf[e]);
+#pragma unroll
+            for (int x = 0; x < 8; ++x) Vt[(part * 8 + x) * Cfg::kVStride + kk] = hv[x];
+          }
+        }
+      }
+    }
+    if constexpr (!LATENT) {
+#pragma unroll
+      for (int e = 0; e < Cfg::kVPer; ++e) {
+        const int ch = tid + e * Cfg::kThreads;
+        if (ch < Cfg::kVChunks) {
+          const int kk = ch / (DV / 8);
+          const int part = ch % (DV / 8);
+          const bf16_t* hv = reinterpret_cast<const bf16_t*>(&vbuf[e]);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) Vt[(part * 8 + x) * Cfg::kVStride + kk] = hv[x];
+        }
+      }
+    }
+  };
+
+  if (kv_begin < kv_end) load_tile(kv_begin);
+  for (int t0 = kv_begin; t0 < kv_end; t0 += kNK) {
+    store_tile();
+    __syncthreads();
+    if (t0 + kNK < kv_end) load_tile(t0 + kNK);
+
+    // S^T (keys x query vectors): lane holds keys 16*mb + 4*grp + j of query n16
+    f32x4_t sacc[kNK / 16];
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb) {
+      sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DQK / 32; ++ks) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+            Ks + (mb * 16 + n16) * Cfg::kKStride + ks * 32 + grp * 8);
+        sacc[mb] = mfma16(a, qf[ks], sacc[mb]);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kpos = t0 + mb * 16 + grp * 4 + j;
+        float s = sacc[mb][j] * p.scale_log2;
+        if (!q_valid || kpos >= kv_end || kpos > limit) s = -INFINITY;
+        sacc[mb][j] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // no branch around the MFMAs: a fully masked query gets alpha = p = 0
+    const float m_new = fmaxf(m_run, tmax);
+    {
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < kNK / 16; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float s = sacc[mb][j];
+          const float pr = (s == -INFINITY) ? 0.f : exp2f(s - m_new);
+          sacc[mb][j] = pr;
+          psum += pr;
+        }
+      }
+      l_part = l_part * alpha + psum;
+      m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] *= alpha;
+      // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
+      u32x4_t pb;
+      pb[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
+      pb[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
+      pb[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
+      pb[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
+#pragma unroll
+      for (int mb = 0; mb < DV / 16; ++mb) {
+        const bf16_t* vrow = Vt + (mb * 16 + n16) * Cfg::kVStride;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + grp * 4);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + grp * 4);
+        const u32x4_t a = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        oacc[mb] = mfma16(a, pb, oacc[mb]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // normaliser over the four lane groups that share a query vector
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!q_valid) return;
+
+  if (ns == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16_t* dst = p.o + ((size_t)q_row * p.Hq + head) * DV;
+#pragma unroll
+    for (int mb = 0; mb < DV / 16; ++mb) {
+      uint2 pk;
+      pk.x = pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv);
+      pk.y = pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv);
+      *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
+    }
+    if (p.lse && grp == 0)
+      p.lse[(size_t)q_row * p.Hq + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const int slot = info.z + sp * info.w + tile;
+    if (slot < 0 || slot >= p.part_cap) return;   // the plan keeps slots below the cap
+    float* po = p.part_o + ((size_t)slot * Cfg::kQT + qv) * DV;
+#pragma unroll
+    for (int mb = 0; mb < DV / 16; ++mb)
+      *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[mb];
+    if (grp == 0) {
+      float* pml = p.part_ml + ((size_t)slot * Cfg::kQT + qv) * 2;
+      pml[0] = m_run;
+      pml[1] = l_tot;
+    }
+  }
+}
+
+// ---- combine split partials ----------------------------------------------------
+struct CombineParams {
+  const int32_t* cu;
+  const int4* req_info;
+  const float* part_o;
+  const float* part_ml;
+  bf16_t* o;
+  float* lse;
+  int Hq, Hkv, G, NH, RT, n_hb, QT, DV, tpr_max, part_cap;
+};
+
+__global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
+  const int i = blockIdx.x / p.tpr_max;
+  const int tile = blockIdx.x % p.tpr_max;
+  const int4 info = p.req_info[i];
+  const int ns = info.x;
+  if (ns <= 1 || tile >= info.w) return;
+  if (info.z < 0 || info.z + (ns - 1) * info.w + tile >= p.part_cap) return;
+  const int row_start = p.cu[i];
+  const int w = p.cu[i + 1] - row_start;
+  const int rb = tile / (p.Hkv * p.n_hb);
+  const int rem = tile % (p.Hkv * p.n_hb);
+  const int g = rem / p.n_hb;
+  const int hb = rem % p.n_hb;
+  const int row0 = rb * p.RT;
+  const int rows_here = min(p.RT, w - row0);
+  for (int idx = threadIdx.x; idx < p.QT * p.DV; idx += blockDim.x) {
+    const int qv = idx / p.DV;
+    const int d = idx % p.DV;
+    const int rl = qv / p.NH;
+    if (rl >= rows_here) continue;
+    const int head = g * p.G + hb * p.NH + (qv % p.NH);
+    const int row = row_start + row0 + rl;
+    float m = -INFINITY;
+    for (int s = 0; s < ns; ++s) {
+      const int slot = info.z + s * info.w + tile;
+      m = fmaxf(m, p.part_ml[((size_t)slot * p.QT + qv) * 2]);
+    }
+    float acc = 0.f, l = 0.f;
+    if (m != -INFINITY) {
+      for (int s = 0; s < ns; ++s) {
+        const int slot = info.z + s * info.w + tile;
+        const float ms = p.part_ml[((size_t)slot * p.QT + qv) * 2];
+        if (ms == -INFINITY) continue;
+        const float wgt = exp2f(ms - m);
+        l += wgt * p.part_ml[((size_t)slot * p.QT + qv) * 2 + 1];
+        acc += wgt * p.part_o[((size_t)slot * p.QT + qv) * p.DV + d];
+      }
+    }
+    p.o[((size_t)row * p.Hq + head) * p.DV + d] = f32_to_bf16(l > 0.f ? acc / l : 0.f);
+    if (d == 0 && p.lse)
+      p.lse[(size_t)row * p.Hq + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---- padding rows [M, M_pad): o = 0, lse = -inf --------------------------------
+__global__ __launch_bounds__(256) void k_attn_pad(const int32_t* mm, void* o, float* lse,
+                                                  int Hq, int Dv, int elem_bytes, int rows_cap) {
+  const int M = mm[0], Mpad = mm[1];
+  const int row = M + blockIdx.x;
+  if (row < 0 || row >= Mpad || row >= rows_cap) return;
+  const size_t n = (size_t)Hq * Dv * elem_bytes / 4;   // whole 32-bit words
+  uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(o) + (size_t)row * Hq * Dv * elem_bytes);
+  for (size_t k = threadIdx.x; k < n; k += blockDim.x) dst[k] = 0u;
+  if (lse)
+    for (int h = threadIdx.x; h < Hq; h += blockDim.x) lse[(size_t)row * Hq + h] = -INFINITY;
+}
+
+// ---- fp32 path: one workgroup per (row, head) --------------------------------
+struct F32Params {
+  const float* q;
+  const float* k;
+  const float* v;
+  const int32_t* page_table;
+  const int32_t* ctx;
+  const int32_t* cu;
+  const int32_t* mm;
+  float* o;
+  float* lse;
+  int32_t* status;
+  int B, max_pages, page_size, num_pages, Hq, Hkv, D, Dv;
+  float sm_scale;
+};
+
+__global__ __launch_bounds__(128) void k_attn_f32(F32Params p) {
+  __shared__ float sc[128];
+  __shared__ float red[128];
+  const int row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  if (row >= p.mm[0]) return;   // padding rows are written by k_attn_pad
+  int lo = 0, hi = p.B - 1;     // request containing this row
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (p.cu[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  const int i = lo;
+  const int pos = p.ctx[i] + (row - p.cu[i]);
+  const int g = h / (p.Hq / p.Hkv);
+  const float* qv = p.q + ((size_t)row * p.Hq + h) * p.D;
+  const int P = p.page_size;
+  float m = -INFINITY, l = 0.f, acc = 0.f;   // thread tid owns output dim tid
+  for (int j0 = 0; j0 <= pos; j0 += 128) {
+    const int j = j0 + tid;
+    float s = -INFINITY;
+    if (j <= pos) {
+      int pg = (j / P < p.max_pages) ? p.page_table[(size_t)i * p.max_pages + j / P] : -1;
+      if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+      const float* kr = p.k + (((size_t)pg * P + j % P) * p.Hkv + g) * p.D;
+      float dot = 0.f;
+      for (int d = 0; d < p.D; ++d) dot += qv[d] * kr[d];
+      s = dot * p.sm_scale;
+    }
+    sc[tid] = s;
+    red[tid] = s;
+    __syncthreads();
+    for (int off = 64; off > 0; off >>= 1) {
+      if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+      __syncthreads();
+    }
+    const float m_new = fmaxf(m, red[0]);
+    const float alpha = (m == -INFINITY) ? 0.f : expf(m - m_new);
+    __syncthreads();
+    const int n = min(128, pos + 1 - j0);
+    float psum = 0.f, vacc = 0.f;
+    for (int jj = 0; jj < n; ++jj) {
+      const float pr = expf(sc[jj] - m_new);
+      psum += pr;
+      if (tid < p.Dv) {
+        const int jk = j0 + jj;
+        int pg = (jk / P < p.max_pages) ? p.page_table[(size_t)i * p.max_pages + jk / P] : -1;
+        if (pg < 0 || pg >= p.num_pages) pg = 0;
+        const float* vr = (p.v ? p.v : p.k) + (((size_t)pg * P + jk % P) * p.Hkv + g) * (p.v ? p.Dv : p.D);
+        vacc += pr * vr[tid];
+      }
+    }
+    l = l * alpha + psum;
+    acc = acc * alpha + vacc;
+    m = m_new;
+    __syncthreads();
+  }
+  if (tid < p.Dv) p.o[((size_t)row * p.Hq + h) * p.Dv + tid] = acc / l;
+  if (tid == 0 && p.lse) p.lse[(size_t)row * p.Hq + h] = m + logf(l);
+}
+
+// ---- host side -----------------------------------------------------------------
+bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnShape* sh, int* nw) {
+  if (Hkv <= 0 || Hq % Hkv != 0) return false;
+  const int G = Hq / Hkv;
+  if (latent) {
+    if (!(Dqk == 576 && Dv == 512 && Hkv == 1 && Hq % 64 == 0)) return false;
+    *nw = 4;   // 64 query vectors per tile: Q fragments and O^T fit 512 registers
+  } else {
+    if (!(Dqk == 128 && Dv == 128)) return false;
+    if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return false;
+    *nw = (G * gamma <= 32) ? 2 : 4;
+  }
+  const int QT = 16 * *nw;
+  sh->Hq = Hq;
+  sh->Hkv = Hkv;
+  sh->G = G;
+  sh->QT = QT;
+  sh->NH = G < QT ? G : QT;
+  sh->RT = QT / sh->NH;
+  sh->n_hb = G / sh->NH;
+  sh->tpr_max = ((gamma + sh->RT - 1) / sh->RT) * Hkv * sh->n_hb;
+  return true;
+}
+
+struct AttnScratch {
+  size_t hdr, req_info, items, part_ml, part_o, total;
+  int item_cap;
+};
+
+AttnScratch attn_layout(int B, const AttnShape& sh, int Dv) {
+  AttnScratch L;
+  L.item_cap = kTargetItems + B * sh.tpr_max;
+  size_t off = 0;
+  L.hdr = off; off = align_up(off + 256, 256);
+  L.req_info = off; off = align_up(off + sizeof(int4) * (size_t)B, 256);
+  L.items = off; off = align_up(off + sizeof(int4) * (size_t)L.item_cap, 256);
+  L.part_ml = off; off = align_up(off + sizeof(float) * 2 * (size_t)kPartSlots * sh.QT, 256);
+  L.part_o = off; off = align_up(off + sizeof(float) * (size_t)kPartSlots * sh.QT * Dv, 256);
+  L.total = off;
+  return L;
+}
+
+template <int DQK, int DV, int NW, bool LATENT>
+hipError_t launch_main(const MainParams& mp, int grid, hipStream_t s) {
+  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
+  auto kern = k_attn_mfma<DQK, DV, NW, LATENT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::kThreads), Cfg::kLdsBytes, s, mp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent) {
+  if (dtype == RV_F32) return Dqk <= 128 && Dv <= 128 && Dqk > 0 && Dv > 0 && Hkv > 0 && Hq % Hkv == 0 &&
+                              (!latent || Dv <= Dqk);
+  AttnShape sh;
+  int nw;
+  return pick_shape(Hq, Hkv, Dqk, Dv, 2, latent, &sh, &nw);
+}
+
+size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, int dtype) {
+  if (dtype == RV_F32 || B <= 0) return 0;
+  AttnShape sh;
+  int nw;
+  const bool latent = (Dqk == 576);
+  if (!pick_shape(Hq, Hkv, Dqk, Dv, gamma, latent, &sh, &nw)) return 0;
+  return attn_layout(B, sh, Dv).total;
+}
+
+hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
+  const bool latent = (a.v_cache == nullptr);
+  char* ws = static_cast<char*>(a.workspace);
+  int32_t* status = status_ptr(a.workspace);
+  hipError_t e;
+
+  hipLaunchKernelGGL(k_attn_pad, dim3(a.rows_cap), dim3(256), 0, s, a.mm, a.o, a.lse, a.Hq, a.Dv,
+                     a.dtype == RV_F32 ? 4 : 2, a.rows_cap);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  if (a.dtype == RV_F32) {
+    F32Params f;
+    f.q = static_cast<const float*>(a.q);
+    f.k = static_cast<const float*>(a.k_cache);
+    f.v = static_cast<const float*>(a.v_cache);
+    f.page_table = a.page_table;
+    f.ctx = a.ctx;
+    f.cu = a.cu;
+    f.mm = a.mm;
+    f.o = static_cast<float*>(a.o);
+    f.lse = a.lse;
+    f.status = status;
+    f.B = a.B;
+    f.max_pages = a.max_pages;
+    f.page_size = a.page_size;
+    f.num_pages = a.num_pages;
+    f.Hq = a.Hq;
+    f.Hkv = a.Hkv;
+    f.D = a.Dqk;
+    f.Dv = a.Dv;
+    f.sm_scale = a.sm_scale;
+    hipLaunchKernelGGL(k_attn_f32, dim3(a.rows_cap, a.Hq), dim3(128), 0, s, f);
+    return hipGetLastError();
+  }
+
+  AttnShape sh;
+  int nw = 0;
+  if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw)) return hipErrorInvalidValue;
+  const AttnScratch L = attn_layout(a.B, sh, a.Dv);
+  char* base = ws + kStatusBytes;
+
+  PlanParams pp;
+  pp.cu = a.cu;
+  pp.ctx = a.ctx;
+  pp.mm = a.mm;
+  pp.req_info = reinterpret_cast<int4*>(base + L.req_info);
+  pp.items = reinterpret_cast<int4*>(base + L.items);
+  pp.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
+  pp.B = a.B;
+  pp.gamma = a.gamma;
+  pp.item_cap = L.item_cap;
+  pp.part_cap = kPartSlots;
+  pp.target = kTargetItems;
+  pp.sh = sh;
+  hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(1024), 0, s, pp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  MainParams mp;
+  mp.q = static_cast<const bf16_t*>(a.q);
+  mp.k = static_cast<const bf16_t*>(a.k_cache);
+  mp.v = static_cast<const bf16_t*>(a.v_cache);
+  mp.page_table = a.page_table;
+  mp.ctx = a.ctx;
+  mp.cu = a.cu;
+  mp.req_info = pp.req_info;
+  mp.items = pp.items;
+  mp.hdr = pp.hdr;
+  mp.o = static_cast<bf16_t*>(a.o);
+  mp.lse = a.lse;
+  mp.part_o = reinterpret_cast<float*>(base + L.part_o);
+  mp.part_ml = reinterpret_cast<float*>(base + L.part_ml);
+  mp.status = status;
+  mp.max_pages = a.max_pages;
+  mp.page_size = a.page_size;
+  mp.num_pages = a.num_pages;
+  mp.Hq = a.Hq;
+  mp.Hkv = a.Hkv;
+  mp.G = sh.G;
+  mp.NH = sh.NH;
+  mp.RT = sh.RT;
+  mp.n_hb = sh.n_hb;
+  mp.part_cap = kPartSlots;
+  mp.scale_log2 = a.sm_scale * kLog2e;
+  const int grid = L.item_cap;
+
+  if (latent) {
+    e = launch_main<576, 512, 4, true>(mp, grid, s);
+  } else {
+    e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, grid, s) : launch_main<128, 128, 4, false>(mp, grid, s);
+  }
+  if (e != hipSuccess) return e;
+
+  CombineParams cp;
+  cp.cu = a.cu;
+  cp.req_info = pp.req_info;
+  cp.part_o = mp.part_o;
+  cp.part_ml = mp.part_ml;
+  cp.o = mp.o;
+  cp.lse = a.lse;
+  cp.Hq = a.Hq;
+  cp.Hkv = a.Hkv;
+  cp.G = sh.G;
+  cp.NH = sh.NH;
+  cp.RT = sh.RT;
+  cp.n_hb = sh.n_hb;
+  cp.QT = sh.QT;
+  cp.DV = a.Dv;
+  cp.tpr_max = sh.tpr_max;
+  cp.part_cap = kPartSlots;
+  hipLaunchKernelGGL(k_attn_combine, dim3(a.B * sh.tpr_max), dim3(256), 0, s, cp);
+  return hipGetLastError();
+}
+
+}  // namespace rv

@@ -1,0 +1,229 @@
+// librv C ABI: argument validation, workspace sizing, launches.
+//
+// Every entry point checks what the host can check before anything is
+// enqueued and returns a negative rv_status on failure; see include/rv.h for
+// the contract of each call.
+
+#include <math.h>
+#include <stddef.h>
+
+#include "rv_common.h"
+
+namespace rv {
+namespace {
+
+__global__ void k_clear_status(int32_t* status) {
+  if (threadIdx.x == 0) status[0] = 0;
+}
+
+bool ws_ok(const void* ws, size_t bytes, size_t need) { return ws != nullptr && bytes >= need; }
+
+bool block_ok(int B, int gamma) {
+  return B >= 1 && gamma >= 2 && gamma <= RV_MAX_GAMMA && (long long)B * gamma <= RV_MAX_ROWS;
+}
+
+rv_status hip_status(hipError_t e) { return e == hipSuccess ? RV_OK : RV_ERR_HIP; }
+
+}  // namespace
+
+hipError_t launch_clear_status(void* ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status_ptr(ws));
+  return hipGetLastError();
+}
+
+}  // namespace rv
+
+using namespace rv;
+
+extern "C" {
+
+const char* rv_version(void) { return "librv 0.1.0 gfx950 (ragged confidence-driven verify)"; }
+
+rv_status rv_workspace_size(const rv_dims* d, size_t* bytes) {
+  if (!d || !bytes) return RV_ERR_INVALID_ARG;
+  if (d->B < 0 || d->gamma < 0 || d->Hq < 0 || d->Hkv < 0 || d->Dqk < 0 || d->Dv < 0 || d->V < 0)
+    return RV_ERR_INVALID_ARG;
+  size_t need = 0;
+  if (d->B > 0 && d->gamma > 0 && d->Hq > 0 && d->Hkv > 0 && d->Dqk > 0 && d->Dv > 0)
+    need = attn_scratch_bytes(d->B, d->gamma, d->Hq, d->Hkv, d->Dqk, d->Dv, d->dtype);
+  if (d->B > 0 && d->gamma > 0 && d->V > 0) {
+    const size_t lm = lm_scratch_bytes(d->B, d->gamma, d->V);
+    if (lm > need) need = lm;
+  }
+  *bytes = (size_t)kStatusBytes + need;
+  return RV_OK;
+}
+
+rv_status rv_device_status(const void* workspace, int32_t* code, void* stream) {
+  if (!workspace || !code) return RV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(code, workspace, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return RV_ERR_HIP;
+  return hip_status(hipStreamSynchronize(s));
+}
+
+rv_status rv_clear_status(void* workspace, void* stream) {
+  if (!workspace) return RV_ERR_INVALID_ARG;
+  return hip_status(launch_clear_status(workspace, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_schedule(const rv_schedule_args* a, void* stream) {
+  if (!a || !a->conf || !a->cost_alpha || !a->cost_theta || !a->w_commit || !a->w_verify ||
+      !a->k_star || !a->e_star)
+    return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if (a->mode < RV_STATIC || a->mode > RV_NO_TRIM) return RV_ERR_INVALID_ARG;
+  if ((a->mode == RV_COMPACT || a->mode == RV_CAP_ACCEPT) &&
+      (long long)a->B * (a->gamma - 1) > RV_MAX_SCHED_CANDIDATES)
+    return RV_ERR_UNSUPPORTED;
+  if (a->alpha_len <= a->B || (long long)a->theta_len <= (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (!isfinite(a->cost_bias)) return RV_ERR_INVALID_ARG;
+  if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_schedule(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_pack(const rv_pack_args* a, void* stream) {
+  if (!a || !a->w_verify || !a->anchor || !a->drafts || !a->ctx || !a->page_table || !a->cu ||
+      !a->mm || !a->row_req || !a->row_pos || !a->tok || !a->slot)
+    return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if (a->page_size < 1 || a->max_pages < 1 || a->num_pages < 1) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (a->n_tiers < 0 || a->n_tiers > RV_MAX_TIERS) return RV_ERR_TIER;
+  if (a->n_tiers > 0) {
+    if (!a->tiers) return RV_ERR_TIER;
+    for (int k = 0; k < a->n_tiers; ++k) {
+      if (a->tiers[k] < 1 || (k > 0 && a->tiers[k] <= a->tiers[k - 1])) return RV_ERR_TIER;
+    }
+    if (a->tiers[a->n_tiers - 1] > a->rows_cap) return RV_ERR_TIER;
+  }
+  if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_pack(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
+  if (!a || !a->q || !a->k_cache || !a->page_table || !a->ctx || !a->cu || !a->mm || !a->o)
+    return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (a->page_size < 1 || a->max_pages < 1 || a->num_pages < 1) return RV_ERR_INVALID_ARG;
+  if (a->Hq < 1 || a->Hkv < 1 || a->Dqk < 1 || a->Dv < 1 || a->Hq % a->Hkv != 0) return RV_ERR_INVALID_ARG;
+  if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
+  if (!isfinite(a->sm_scale)) return RV_ERR_INVALID_ARG;
+  const bool latent = (a->v_cache == nullptr);
+  if (latent && (a->Hkv != 1 || a->Dv > a->Dqk)) return RV_ERR_UNSUPPORTED;
+  if (!attn_shape_supported(a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype, latent)) return RV_ERR_UNSUPPORTED;
+  const size_t need = kStatusBytes + attn_scratch_bytes(a->B, a->gamma, a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype);
+  if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_attn(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream) {
+  if (!a || !a->hidden || !a->W || !a->mm || !a->cu || !a->w_commit || !a->w_verify || !a->drafts ||
+      !a->pred || !a->accept || !a->bonus || !a->ceiling)
+    return RV_ERR_INVALID_ARG;
+  if (a->rule != RV_GREEDY && a->rule != RV_REJECTION) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_REJECTION && (!a->q_rows || !a->u || !a->u_bonus || !a->logits)) return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (a->H < 1 || a->V < 1) return RV_ERR_INVALID_ARG;
+  if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
+  if (a->dtype == RV_BF16 && a->H % 64 != 0) return RV_ERR_UNSUPPORTED;
+  const size_t need = kStatusBytes + lm_scratch_bytes(a->B, a->gamma, a->V);
+  if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_lm(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream) {
+  if (!a || !a->cu || !a->w_verify || !a->accept || !a->bonus || !a->drafts || !a->slot || !a->ctx ||
+      !a->anchor || !a->req_to_token || !a->commit_cu || !a->commit_tok || !a->commit_slot ||
+      !a->free_slots || !a->free_count)
+    return RV_ERR_INVALID_ARG;
+  if ((a->hist == nullptr) != (a->hist_len == nullptr)) return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if (a->r2t_stride < 1 || (a->hist && a->hist_stride < 1)) return RV_ERR_INVALID_ARG;
+  if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_scatter(*a, static_cast<hipStream_t>(stream)));
+}
+
+#define RV_OFF(S, f) (int64_t) offsetof(S, f)
+
+int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap) {
+  int64_t v[48];
+  int n = 0;
+  switch (which) {
+    case 0: {
+      typedef rv_schedule_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, conf), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, mode),
+                     RV_OFF(S, alpha_len), RV_OFF(S, theta_len), RV_OFF(S, _pad0), RV_OFF(S, cost_bias),
+                     RV_OFF(S, cost_alpha), RV_OFF(S, cost_theta), RV_OFF(S, w_commit), RV_OFF(S, w_verify),
+                     RV_OFF(S, k_star), RV_OFF(S, e_star), RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 1: {
+      typedef rv_pack_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, w_verify), RV_OFF(S, anchor), RV_OFF(S, drafts), RV_OFF(S, ctx),
+                     RV_OFF(S, page_table), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, max_pages),
+                     RV_OFF(S, page_size), RV_OFF(S, num_pages), RV_OFF(S, n_tiers), RV_OFF(S, tiers),
+                     RV_OFF(S, rows_cap), RV_OFF(S, _pad0), RV_OFF(S, cu), RV_OFF(S, mm), RV_OFF(S, row_req),
+                     RV_OFF(S, row_pos), RV_OFF(S, tok), RV_OFF(S, slot), RV_OFF(S, workspace),
+                     RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 2: {
+      typedef rv_attn_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, q), RV_OFF(S, k_cache), RV_OFF(S, v_cache), RV_OFF(S, page_table),
+                     RV_OFF(S, ctx), RV_OFF(S, cu), RV_OFF(S, mm), RV_OFF(S, B), RV_OFF(S, gamma),
+                     RV_OFF(S, rows_cap), RV_OFF(S, max_pages), RV_OFF(S, page_size), RV_OFF(S, num_pages),
+                     RV_OFF(S, Hq), RV_OFF(S, Hkv), RV_OFF(S, Dqk), RV_OFF(S, Dv), RV_OFF(S, dtype),
+                     RV_OFF(S, sm_scale), RV_OFF(S, o), RV_OFF(S, lse), RV_OFF(S, workspace),
+                     RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 3: {
+      typedef rv_lm_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, hidden), RV_OFF(S, W), RV_OFF(S, mm), RV_OFF(S, cu),
+                     RV_OFF(S, w_commit), RV_OFF(S, w_verify), RV_OFF(S, drafts), RV_OFF(S, q_rows),
+                     RV_OFF(S, u), RV_OFF(S, u_bonus), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, rows_cap),
+                     RV_OFF(S, H), RV_OFF(S, V), RV_OFF(S, dtype), RV_OFF(S, rule), RV_OFF(S, _pad0),
+                     RV_OFF(S, pred), RV_OFF(S, accept), RV_OFF(S, bonus), RV_OFF(S, ceiling),
+                     RV_OFF(S, logits), RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 4: {
+      typedef rv_scatter_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, cu), RV_OFF(S, w_verify), RV_OFF(S, accept), RV_OFF(S, bonus),
+                     RV_OFF(S, drafts), RV_OFF(S, slot), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, r2t_stride),
+                     RV_OFF(S, hist_stride), RV_OFF(S, ctx), RV_OFF(S, anchor), RV_OFF(S, req_to_token),
+                     RV_OFF(S, hist), RV_OFF(S, hist_len), RV_OFF(S, commit_cu), RV_OFF(S, commit_tok),
+                     RV_OFF(S, commit_slot), RV_OFF(S, free_slots), RV_OFF(S, free_count),
+                     RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 5: {
+      typedef rv_dims S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, Hq), RV_OFF(S, Hkv),
+                     RV_OFF(S, Dqk), RV_OFF(S, Dv), RV_OFF(S, V), RV_OFF(S, dtype)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    default:
+      return -1;
+  }
+  if (!out || cap < n) return -1;
+  for (int k = 0; k < n; ++k) out[k] = v[k];
+  return n;
+}
+
+}  // extern "C"

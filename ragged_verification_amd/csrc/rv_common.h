@@ -1,0 +1,78 @@
+// Internal helpers shared by the librv kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rv.h"
+
+namespace rv {
+
+constexpr int kStatusBytes = 256;        // status word + padding at workspace start
+constexpr int kTargetItems = 1024;       // attention work items aimed for per launch
+constexpr int kPartSlots = 1024;         // split-KV partial tiles held in workspace
+constexpr int kMinChunk = 256;           // smallest split-KV chunk (keys)
+
+// ---- sticky device status: first error wins --------------------------------
+__device__ inline void set_status(int32_t* status, int32_t code) {
+  if (status) atomicCAS(status, 0, code);
+}
+
+// ---- bf16 <-> f32 ------------------------------------------------------------
+typedef uint16_t bf16_t;
+
+__device__ inline float bf16_to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// round to nearest even; NaN kept quiet
+__device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// ---- MFMA operand types (gfx950 bf16 MFMAs take 8 bf16 per lane) ------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// D(16x16, fp32) += A(16x32) * B(32x16).  Lane l: A row l%16, B column l%16,
+// both holding k = 8*(l/16) .. 8*(l/16)+7; D column l%16, rows 4*(l/16)+j.
+__device__ inline f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D(32x32, fp32) += A(32x16) * B(16x32).  Lane l: A row l%32, B column l%32,
+// both holding k = 8*(l/32) .. +7; D column l%32, rows 8*(j/4) + 4*(l/32) + j%4.
+__device__ inline f32x16_t mfma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__host__ __device__ inline int32_t* status_ptr(void* ws) { return reinterpret_cast<int32_t*>(ws); }
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- launchers (defined next to their kernels) -------------------------------
+struct SchedLaunch;
+hipError_t launch_schedule(const rv_schedule_args& a, hipStream_t s);
+hipError_t launch_pack(const rv_pack_args& a, hipStream_t s);
+hipError_t launch_attn(const rv_attn_args& a, hipStream_t s);
+hipError_t launch_lm(const rv_lm_args& a, hipStream_t s);
+hipError_t launch_scatter(const rv_scatter_args& a, hipStream_t s);
+hipError_t launch_clear_status(void* ws, hipStream_t s);
+
+// host-side sizing helpers shared by the API layer and the launchers
+size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, int dtype);
+size_t lm_scratch_bytes(int B, int gamma, int V);
+bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent);
+
+}  // namespace rv

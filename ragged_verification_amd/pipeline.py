@@ -1,0 +1,148 @@
+"""One verify step through the five C-ABI calls, with its device buffers.
+
+``VerifyStep`` owns the buffers of a workload on the GPU (torch allocates
+them; the HIP library computes everything) and runs
+
+    rv_schedule -> rv_pack -> [payload staging] -> rv_verify_attn
+    -> rv_lm_head_accept -> rv_compact_scatter
+
+Payload staging gathers the block-major query / hidden-state payloads into
+the packed row order.  In a serving stack the target model's layers produce
+packed rows directly; here it stands in for them and is kept outside the
+five-stage timing.  ``restore()`` resets the state the scatter mutates (ctx,
+anchor, req_to_token, history) so repeated steps see identical inputs.
+"""
+
+import torch
+
+from . import rv
+
+
+class VerifyStep:
+    def __init__(self, inp, mode="compact", with_logits=False, rows_cap=None, r2t_extra=64,
+                 hist_cap=64, stream=None):
+        wl = inp["workload"]
+        self.inp, self.wl = inp, wl
+        self.mode = mode
+        dev = inp["conf"].device
+        if dev.type != "cuda":
+            raise ValueError("VerifyStep needs inputs on the GPU")
+        B, gamma = inp["B"], inp["gamma"]
+        self.B, self.gamma = B, gamma
+        tiers = list(inp["tiers"])
+        self.tiers = tiers
+        self.rows_cap = rows_cap or max([B * gamma] + tiers)
+        i32 = dict(dtype=torch.int32, device=dev)
+        R = self.rows_cap
+        self.rule = rv.RV_REJECTION if wl.rule == "rejection" else rv.RV_GREEDY
+        self.dtype = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+
+        # stage 1
+        self.w_commit = torch.zeros(B, **i32)
+        self.w_verify = torch.zeros(B, **i32)
+        self.k_star = torch.zeros(1, **i32)
+        self.e_star = torch.zeros(1, dtype=torch.float64, device=dev)
+        # stage 2
+        self.cu = torch.zeros(B + 1, **i32)
+        self.mm = torch.zeros(2, **i32)
+        self.row_req = torch.full((R,), -1, **i32)
+        self.row_pos = torch.full((R,), -1, **i32)
+        self.tok = torch.full((R,), -1, **i32)
+        self.slot = torch.full((R,), -1, **i32)
+        # stage 3
+        self.q = torch.zeros((R, wl.Hq, wl.Dqk), dtype=self.dtype, device=dev)
+        self.o = torch.zeros((R, wl.Hq, wl.Dv), dtype=self.dtype, device=dev)
+        self.lse = torch.zeros((R, wl.Hq), dtype=torch.float32, device=dev)
+        # stage 4
+        self.hidden = torch.zeros((R, wl.H), dtype=self.dtype, device=dev)
+        self.pred = torch.zeros(R, **i32)
+        self.accept = torch.zeros(B, **i32)
+        self.bonus = torch.zeros(B, **i32)
+        self.ceiling = torch.zeros(B, **i32)
+        need_logits = with_logits or self.rule == rv.RV_REJECTION
+        self.logits = torch.zeros((R, wl.V), dtype=torch.float32, device=dev) if need_logits else None
+        # stage 5 state (mutated in place) and its pristine copies
+        self.ctx0 = inp["ctx"].clone()
+        self.anchor0 = inp["anchor"].clone()
+        self.ctx = self.ctx0.clone()
+        self.anchor = self.anchor0.clone()
+        r2t_len = int(self.ctx0.max()) + gamma + r2t_extra
+        self.req_to_token0 = torch.full((B, r2t_len), -1, **i32)
+        self.req_to_token = self.req_to_token0.clone()
+        self.hist0 = torch.full((B, hist_cap), -1, **i32)
+        self.hist_len0 = torch.zeros(B, **i32)
+        self.hist = self.hist0.clone()
+        self.hist_len = self.hist_len0.clone()
+        self.commit_cu = torch.zeros(B + 1, **i32)
+        self.commit_tok = torch.zeros(B * gamma, **i32)
+        self.commit_slot = torch.zeros(B * gamma, **i32)
+        self.free_slots = torch.zeros(B * gamma, **i32)
+        self.free_count = torch.zeros(1, **i32)
+
+        ws = rv.rv_workspace_size(B, gamma, wl.Hq, wl.Hkv, wl.Dqk, wl.Dv, wl.V,
+                                  rv.RV_F32 if wl.dtype == "f32" else rv.RV_BF16)
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)
+        self.q_flat = inp["q_block"].reshape(B * gamma, wl.Hq, wl.Dqk)
+        self.h_flat = inp["hidden_block"].reshape(B * gamma, wl.H)
+        self.stream = stream
+
+    # ---- stages ------------------------------------------------------------------
+    def schedule(self):
+        i = self.inp
+        rv.rv_schedule(i["conf"], self.gamma, self.mode, i["cost_bias"], i["cost_alpha"], i["cost_theta"],
+                       self.w_commit, self.w_verify, self.k_star, self.e_star, self.workspace, self.stream)
+
+    def pack(self):
+        i = self.inp
+        rv.rv_pack(self.w_verify, self.anchor, i["drafts"], self.ctx, i["page_table"], i["page_size"],
+                   i["num_pages"], self.tiers, self.cu, self.mm, self.row_req, self.row_pos, self.tok,
+                   self.slot, self.workspace, self.stream)
+
+    def stage_payload(self):
+        """Gather block-major payload rows into packed order (harness work)."""
+        req = self.row_req.long()
+        valid = req >= 0
+        k = self.row_pos.long() - self.ctx[req.clamp(min=0)].long()
+        src = torch.where(valid, req.clamp(min=0) * self.gamma + k.clamp(0, self.gamma - 1),
+                          torch.zeros_like(req))
+        torch.index_select(self.q_flat, 0, src, out=self.q)
+        torch.index_select(self.h_flat, 0, src, out=self.hidden)
+
+    def attn(self):
+        i = self.inp
+        rv.rv_verify_attn(self.q, i["k_cache"], i["v_cache"], i["page_table"], i["page_size"], i["num_pages"],
+                          self.ctx, self.cu, self.mm, self.gamma, i["sm_scale"], self.o, self.lse,
+                          self.workspace, self.stream)
+
+    def lm(self):
+        i = self.inp
+        rv.rv_lm_head_accept(self.hidden, i["W"], self.mm, self.cu, self.w_commit, self.w_verify, i["drafts"],
+                             self.rule, self.pred, self.accept, self.bonus, self.ceiling, self.workspace,
+                             logits=self.logits, q_rows=i.get("q_rows"), u=i.get("u"), u_bonus=i.get("u_bonus"),
+                             stream=self.stream)
+
+    def scatter(self):
+        i = self.inp
+        rv.rv_compact_scatter(self.cu, self.w_verify, self.accept, self.bonus, i["drafts"], self.slot, self.ctx,
+                              self.anchor, self.req_to_token, self.commit_cu, self.commit_tok, self.commit_slot,
+                              self.free_slots, self.free_count, self.workspace, hist=self.hist,
+                              hist_len=self.hist_len, stream=self.stream)
+
+    def restore(self):
+        self.ctx.copy_(self.ctx0)
+        self.anchor.copy_(self.anchor0)
+        self.req_to_token.copy_(self.req_to_token0)
+        self.hist.copy_(self.hist0)
+        self.hist_len.copy_(self.hist_len0)
+
+    def run(self):
+        """All five stages plus staging, in order, on the current stream."""
+        self.schedule()
+        self.pack()
+        self.stage_payload()
+        self.attn()
+        self.lm()
+        self.scatter()
+
+    def status(self):
+        return rv.rv_device_status(self.workspace, self.stream)

@@ -1,0 +1,273 @@
+"""Thin ctypes binding of librv (include/rv.h): argument marshalling only.
+
+Each ``rv_*`` function here has the name and arguments of the C entry point;
+tensors are passed as device pointers (``data_ptr``), the stream is torch's
+current HIP stream unless one is given.  All arithmetic happens in the HIP
+kernels; torch only provides device memory and streams.  If the shared
+library is missing, ``load()`` raises: there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librv.so")
+
+RV_OK, RV_ERR_INVALID_ARG, RV_ERR_UNSUPPORTED, RV_ERR_TIER, RV_ERR_WORKSPACE, RV_ERR_HIP = 0, -1, -2, -3, -4, -5
+STATUS_NAMES = {0: "RV_OK", -1: "RV_ERR_INVALID_ARG", -2: "RV_ERR_UNSUPPORTED", -3: "RV_ERR_TIER",
+                -4: "RV_ERR_WORKSPACE", -5: "RV_ERR_HIP"}
+DEV_NAMES = {0: "RV_DEV_OK", 1: "RV_DEV_BAD_CONF", 2: "RV_DEV_BAD_COST", 3: "RV_DEV_BAD_WINDOW",
+             4: "RV_DEV_TIER_OVERFLOW", 5: "RV_DEV_BAD_PAGE", 6: "RV_DEV_BAD_TOKEN",
+             7: "RV_DEV_HIST_OVERFLOW"}
+RV_STATIC, RV_COMPACT, RV_CAP_ACCEPT, RV_NO_TRIM = 0, 1, 2, 3
+MODES = {"static": RV_STATIC, "compact": RV_COMPACT, "cap_accept": RV_CAP_ACCEPT, "no_trim": RV_NO_TRIM}
+RV_GREEDY, RV_REJECTION = 0, 1
+RV_F32, RV_BF16 = 0, 1
+RV_MAX_GAMMA, RV_MAX_TIERS, RV_MAX_ROWS = 16, 16, 8192
+
+_vp, _i32, _f32, _f64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("B", _i32), ("gamma", _i32), ("Hq", _i32), ("Hkv", _i32), ("Dqk", _i32),
+                ("Dv", _i32), ("V", _i32), ("dtype", _i32)]
+
+
+class ScheduleArgs(ctypes.Structure):
+    _fields_ = [("conf", _vp), ("B", _i32), ("gamma", _i32), ("mode", _i32), ("alpha_len", _i32),
+                ("theta_len", _i32), ("_pad0", _i32), ("cost_bias", _f64), ("cost_alpha", _vp),
+                ("cost_theta", _vp), ("w_commit", _vp), ("w_verify", _vp), ("k_star", _vp),
+                ("e_star", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class PackArgs(ctypes.Structure):
+    _fields_ = [("w_verify", _vp), ("anchor", _vp), ("drafts", _vp), ("ctx", _vp), ("page_table", _vp),
+                ("B", _i32), ("gamma", _i32), ("max_pages", _i32), ("page_size", _i32),
+                ("num_pages", _i32), ("n_tiers", _i32), ("tiers", _vp), ("rows_cap", _i32),
+                ("_pad0", _i32), ("cu", _vp), ("mm", _vp), ("row_req", _vp), ("row_pos", _vp),
+                ("tok", _vp), ("slot", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("q", _vp), ("k_cache", _vp), ("v_cache", _vp), ("page_table", _vp), ("ctx", _vp),
+                ("cu", _vp), ("mm", _vp), ("B", _i32), ("gamma", _i32), ("rows_cap", _i32),
+                ("max_pages", _i32), ("page_size", _i32), ("num_pages", _i32), ("Hq", _i32),
+                ("Hkv", _i32), ("Dqk", _i32), ("Dv", _i32), ("dtype", _i32), ("sm_scale", _f32),
+                ("o", _vp), ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+class LmArgs(ctypes.Structure):
+    _fields_ = [("hidden", _vp), ("W", _vp), ("mm", _vp), ("cu", _vp), ("w_commit", _vp),
+                ("w_verify", _vp), ("drafts", _vp), ("q_rows", _vp), ("u", _vp), ("u_bonus", _vp),
+                ("B", _i32), ("gamma", _i32), ("rows_cap", _i32), ("H", _i32), ("V", _i32),
+                ("dtype", _i32), ("rule", _i32), ("_pad0", _i32), ("pred", _vp), ("accept", _vp),
+                ("bonus", _vp), ("ceiling", _vp), ("logits", _vp), ("workspace", _vp),
+                ("workspace_bytes", _sz)]
+
+
+class ScatterArgs(ctypes.Structure):
+    _fields_ = [("cu", _vp), ("w_verify", _vp), ("accept", _vp), ("bonus", _vp), ("drafts", _vp),
+                ("slot", _vp), ("B", _i32), ("gamma", _i32), ("r2t_stride", _i32),
+                ("hist_stride", _i32), ("ctx", _vp), ("anchor", _vp), ("req_to_token", _vp),
+                ("hist", _vp), ("hist_len", _vp), ("commit_cu", _vp), ("commit_tok", _vp),
+                ("commit_slot", _vp), ("free_slots", _vp), ("free_count", _vp), ("workspace", _vp),
+                ("workspace_bytes", _sz)]
+
+
+STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims]
+EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
+           "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout"]
+
+_LIB = None
+
+
+class RVError(RuntimeError):
+    def __init__(self, call, code):
+        super().__init__(f"{call} returned {STATUS_NAMES.get(code, code)}")
+        self.code = code
+
+
+def load(path=LIB_PATH):
+    """Load librv.so and check that the ctypes structs match the C layout."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m ragged_verification_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.rv_version.restype = ctypes.c_char_p
+    lib.rv_version.argtypes = []
+    lib.rv_workspace_size.restype = _i32
+    lib.rv_workspace_size.argtypes = [ctypes.POINTER(Dims), ctypes.POINTER(_sz)]
+    lib.rv_device_status.restype = _i32
+    lib.rv_device_status.argtypes = [_vp, ctypes.POINTER(_i32), _vp]
+    lib.rv_clear_status.restype = _i32
+    lib.rv_clear_status.argtypes = [_vp, _vp]
+    for name, st in (("rv_schedule", ScheduleArgs), ("rv_pack", PackArgs), ("rv_verify_attn", AttnArgs),
+                     ("rv_lm_head_accept", LmArgs), ("rv_compact_scatter", ScatterArgs)):
+        fn = getattr(lib, name)
+        fn.restype = _i32
+        fn.argtypes = [ctypes.POINTER(st), _vp]
+    lib.rv_abi_layout.restype = _i32
+    lib.rv_abi_layout.argtypes = [_i32, ctypes.POINTER(ctypes.c_int64), _i32]
+    for which, st in enumerate(STRUCTS):
+        c_layout = abi_layout(lib, which)
+        py_layout = [ctypes.sizeof(st)] + [getattr(st, f[0]).offset for f in st._fields_]
+        if c_layout != py_layout:
+            raise RuntimeError(f"struct {st.__name__} layout mismatch: C {c_layout} vs ctypes {py_layout}")
+    _LIB = lib
+    return lib
+
+
+def abi_layout(lib, which):
+    buf = (ctypes.c_int64 * 64)()
+    n = lib.rv_abi_layout(which, buf, 64)
+    if n < 0:
+        raise RuntimeError(f"rv_abi_layout({which}) failed")
+    return list(buf[:n])
+
+
+# ---- marshalling helpers ------------------------------------------------------
+def _ptr(t, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be device memory (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(call, code):
+    if code != RV_OK:
+        raise RVError(call, code)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return RV_F32
+    if t.dtype == torch.bfloat16:
+        return RV_BF16
+    raise TypeError(f"unsupported payload dtype {t.dtype}")
+
+
+# ---- entry points ---------------------------------------------------------------
+def rv_version():
+    return load().rv_version().decode()
+
+
+def rv_workspace_size(B, gamma, Hq=0, Hkv=0, Dqk=0, Dv=0, V=0, dtype=RV_BF16):
+    d = Dims(B, gamma, Hq, Hkv, Dqk, Dv, V, dtype)
+    out = _sz(0)
+    _check("rv_workspace_size", load().rv_workspace_size(ctypes.byref(d), ctypes.byref(out)))
+    return out.value
+
+
+def rv_device_status(workspace, stream=None):
+    code = _i32(0)
+    _check("rv_device_status", load().rv_device_status(_ptr(workspace, name="workspace"),
+                                                       ctypes.byref(code), _stream(stream)))
+    return code.value
+
+
+def rv_clear_status(workspace, stream=None):
+    _check("rv_clear_status", load().rv_clear_status(_ptr(workspace, name="workspace"), _stream(stream)))
+
+
+def rv_schedule(conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, w_verify, k_star,
+                e_star, workspace, stream=None):
+    B = conf.shape[0]
+    a = ScheduleArgs(conf=_ptr(conf, torch.float32, "conf"), B=B, gamma=gamma,
+                     mode=MODES[mode] if isinstance(mode, str) else mode,
+                     alpha_len=cost_alpha.numel(), theta_len=cost_theta.numel(), cost_bias=float(cost_bias),
+                     cost_alpha=_ptr(cost_alpha, torch.float64, "cost_alpha"),
+                     cost_theta=_ptr(cost_theta, torch.float64, "cost_theta"),
+                     w_commit=_ptr(w_commit, torch.int32, "w_commit"),
+                     w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+                     k_star=_ptr(k_star, torch.int32, "k_star"), e_star=_ptr(e_star, torch.float64, "e_star"),
+                     workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_schedule", load().rv_schedule(ctypes.byref(a), _stream(stream)))
+
+
+def rv_pack(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
+            row_pos, tok, slot, workspace, stream=None):
+    B, g1 = drafts.shape
+    tiers = list(tiers or ())
+    tarr = (ctypes.c_int32 * max(1, len(tiers)))(*tiers)
+    a = PackArgs(w_verify=_ptr(w_verify, torch.int32, "w_verify"), anchor=_ptr(anchor, torch.int32, "anchor"),
+                 drafts=_ptr(drafts, torch.int32, "drafts"), ctx=_ptr(ctx, torch.int32, "ctx"),
+                 page_table=_ptr(page_table, torch.int32, "page_table"), B=B, gamma=g1 + 1,
+                 max_pages=page_table.shape[1], page_size=page_size, num_pages=num_pages,
+                 n_tiers=len(tiers), tiers=ctypes.cast(tarr, ctypes.c_void_p) if tiers else None,
+                 rows_cap=row_req.numel(), cu=_ptr(cu, torch.int32, "cu"), mm=_ptr(mm, torch.int32, "mm"),
+                 row_req=_ptr(row_req, torch.int32, "row_req"), row_pos=_ptr(row_pos, torch.int32, "row_pos"),
+                 tok=_ptr(tok, torch.int32, "tok"), slot=_ptr(slot, torch.int32, "slot"),
+                 workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_pack", load().rv_pack(ctypes.byref(a), _stream(stream)))
+
+
+def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+                   o, lse, workspace, stream=None):
+    rows_cap, Hq, Dqk = q.shape
+    Hkv = k_cache.shape[2]
+    Dv = o.shape[2]
+    dt = _dtype_code(q)
+    a = AttnArgs(q=_ptr(q, q.dtype, "q"), k_cache=_ptr(k_cache, q.dtype, "k_cache"),
+                 v_cache=_ptr(v_cache, q.dtype, "v_cache"), page_table=_ptr(page_table, torch.int32, "page_table"),
+                 ctx=_ptr(ctx, torch.int32, "ctx"), cu=_ptr(cu, torch.int32, "cu"), mm=_ptr(mm, torch.int32, "mm"),
+                 B=ctx.numel(), gamma=gamma, rows_cap=rows_cap, max_pages=page_table.shape[1],
+                 page_size=page_size, num_pages=num_pages, Hq=Hq, Hkv=Hkv, Dqk=Dqk, Dv=Dv, dtype=dt,
+                 sm_scale=float(sm_scale), o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
+                 workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
+
+
+def rv_lm_head_accept(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
+                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None):
+    rows_cap, H = hidden.shape
+    V = W.shape[0]
+    B, g1 = drafts.shape
+    a = LmArgs(hidden=_ptr(hidden, hidden.dtype, "hidden"), W=_ptr(W, hidden.dtype, "W"),
+               mm=_ptr(mm, torch.int32, "mm"), cu=_ptr(cu, torch.int32, "cu"),
+               w_commit=_ptr(w_commit, torch.int32, "w_commit"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+               drafts=_ptr(drafts, torch.int32, "drafts"), q_rows=_ptr(q_rows, torch.float32, "q_rows"),
+               u=_ptr(u, torch.float32, "u"), u_bonus=_ptr(u_bonus, torch.float32, "u_bonus"),
+               B=B, gamma=g1 + 1, rows_cap=rows_cap, H=H, V=V, dtype=_dtype_code(hidden), rule=rule,
+               pred=_ptr(pred, torch.int32, "pred"), accept=_ptr(accept, torch.int32, "accept"),
+               bonus=_ptr(bonus, torch.int32, "bonus"), ceiling=_ptr(ceiling, torch.int32, "ceiling"),
+               logits=_ptr(logits, torch.float32, "logits"),
+               workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_lm_head_accept", load().rv_lm_head_accept(ctypes.byref(a), _stream(stream)))
+
+
+def rv_compact_scatter(cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, req_to_token, commit_cu,
+                       commit_tok, commit_slot, free_slots, free_count, workspace, hist=None, hist_len=None,
+                       stream=None):
+    B, g1 = drafts.shape
+    a = ScatterArgs(cu=_ptr(cu, torch.int32, "cu"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+                    accept=_ptr(accept, torch.int32, "accept"), bonus=_ptr(bonus, torch.int32, "bonus"),
+                    drafts=_ptr(drafts, torch.int32, "drafts"), slot=_ptr(slot, torch.int32, "slot"),
+                    B=B, gamma=g1 + 1, r2t_stride=req_to_token.shape[1],
+                    hist_stride=hist.shape[1] if hist is not None else 0,
+                    ctx=_ptr(ctx, torch.int32, "ctx"), anchor=_ptr(anchor, torch.int32, "anchor"),
+                    req_to_token=_ptr(req_to_token, torch.int32, "req_to_token"),
+                    hist=_ptr(hist, torch.int32, "hist"), hist_len=_ptr(hist_len, torch.int32, "hist_len"),
+                    commit_cu=_ptr(commit_cu, torch.int32, "commit_cu"),
+                    commit_tok=_ptr(commit_tok, torch.int32, "commit_tok"),
+                    commit_slot=_ptr(commit_slot, torch.int32, "commit_slot"),
+                    free_slots=_ptr(free_slots, torch.int32, "free_slots"),
+                    free_count=_ptr(free_count, torch.int32, "free_count"),
+                    workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_compact_scatter", load().rv_compact_scatter(ctypes.byref(a), _stream(stream)))

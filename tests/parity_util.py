@@ -1,0 +1,158 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the CPU oracle on the same seeded inputs.
+
+Expected values always come from the oracle (or from what the generator
+planted); nothing computed on the GPU is fed to the oracle.
+"""
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import oracle
+from ragged_verification_amd import synth
+from ragged_verification_amd.pipeline import VerifyStep
+
+MODE_CODES = {"static": oracle.STATIC, "compact": oracle.COMPACT, "cap_accept": oracle.CAP_ACCEPT,
+              "no_trim": oracle.NO_TRIM}
+
+# tolerances: bf16 attention output max-abs 2e-2; LM-head logits relative
+# (row inf-norm) 1e-2; fp32 paths 1e-4 / 1e-5
+ATTN_TOL = {"bf16": 2e-2, "f32": 1e-4}
+LOGIT_TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+def log(msg):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def make_inputs(name, B=None, device="cuda", gen_on_gpu=False, **overrides):
+    wl = synth.workload(name, **overrides)
+    t0 = time.time()
+    if gen_on_gpu:
+        inp = synth.make_inputs(wl, device=device, B=B)
+    else:
+        inp = synth.make_inputs(wl, device="cpu", B=B)
+        inp = {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    log(f"inputs {name} B={inp['B']} built in {time.time() - t0:.1f}s")
+    return inp
+
+
+def np64(t):
+    return None if t is None else t.detach().to(torch.float64).cpu().numpy()
+
+
+def npi(t):
+    return t.detach().cpu().numpy().astype(np.int64)
+
+
+def run_gpu(inp, mode, with_logits=False):
+    step = VerifyStep(inp, mode=mode, with_logits=with_logits)
+    step.run()
+    torch.cuda.synchronize()
+    return step
+
+
+def oracle_schedule_pack(inp, mode):
+    conf = inp["conf"].cpu().numpy()
+    gamma = inp["gamma"]
+    wc, wv, k_star, e_star = oracle.schedule(conf, gamma, MODE_CODES[mode], inp["cost_bias"],
+                                             inp["cost_alpha"].cpu().numpy(), inp["cost_theta"].cpu().numpy())
+    cu, M, M_pad, row_req, row_pos, tok, slot = oracle.pack(
+        wv, npi(inp["anchor"]), npi(inp["drafts"]), npi(inp["ctx"]), npi(inp["page_table"]),
+        inp["page_size"], inp["tiers"])
+    return dict(w_commit=wc, w_verify=wv, k_star=k_star, e_star=e_star, cu=cu, M=M, M_pad=M_pad,
+                row_req=row_req, row_pos=row_pos, tok=tok, slot=slot)
+
+
+def check_schedule_pack(step, ref):
+    assert np.array_equal(npi(step.w_commit), ref["w_commit"])
+    assert np.array_equal(npi(step.w_verify), ref["w_verify"])
+    assert int(step.k_star.item()) == ref["k_star"]
+    assert float(step.e_star.item()) == ref["e_star"]          # bitwise
+    assert np.array_equal(npi(step.cu), ref["cu"])
+    assert npi(step.mm).tolist() == [ref["M"], ref["M_pad"]]
+    n = ref["M_pad"]
+    for f in ("row_req", "row_pos", "tok", "slot"):
+        assert np.array_equal(npi(getattr(step, f))[:n], ref[f]), f
+
+
+def packed_block_index(ref, gamma):
+    """Block-major row index (i*gamma + k) of every real packed row."""
+    M = ref["M"]
+    i = ref["row_req"][:M]
+    k = np.arange(M) - ref["cu"][i]
+    return i * gamma + k
+
+
+def mini_cache(inp, requests):
+    """Host copy of only the KV pages of ``requests``, with a renumbered page
+    table (so full-size checks need not copy the whole cache)."""
+    pt = npi(inp["page_table"])
+    pages = sorted({int(p) for r in requests for p in pt[r] if p >= 0})
+    remap = {p: j for j, p in enumerate(pages)}
+    idx = torch.tensor(pages, dtype=torch.long, device=inp["k_cache"].device)
+    k = np64(inp["k_cache"].index_select(0, idx))
+    v = None if inp["v_cache"] is None else np64(inp["v_cache"].index_select(0, idx))
+    pt2 = np.full_like(pt, -1)
+    for r in requests:
+        pt2[r] = [remap[int(p)] if p >= 0 else -1 for p in pt[r]]
+    return k, v, pt2
+
+
+def oracle_attention_rows(inp, ref, rows):
+    wl = inp["workload"]
+    gamma = inp["gamma"]
+    reqs = sorted({int(ref["row_req"][r]) for r in rows})
+    k, v, pt2 = mini_cache(inp, reqs)
+    bidx = packed_block_index(ref, gamma)
+    qb = inp["q_block"].reshape(-1, wl.Hq, wl.Dqk)
+    out = {}
+    for r in rows:
+        q = np64(qb[int(bidx[r])])[None]
+        o, lse = oracle.verify_attention(q, k, v, pt2, inp["page_size"], ref["row_req"][r:r + 1],
+                                         ref["row_pos"][r:r + 1], 1, inp["sm_scale"], Dv=wl.Dv)
+        out[r] = (o[0], lse[0])
+    return out
+
+
+def check_attention(step, inp, ref, rows, dtype):
+    want = oracle_attention_rows(inp, ref, rows)
+    o = step.o.float().cpu().numpy()
+    lse = step.lse.cpu().numpy()
+    worst = 0.0
+    for r, (o_ref, lse_ref) in want.items():
+        err = np.max(np.abs(o[r] - o_ref))
+        worst = max(worst, err)
+        assert err <= ATTN_TOL[dtype], (r, err)
+        np.testing.assert_allclose(lse[r], lse_ref, rtol=1e-3, atol=1e-3)
+    M, M_pad = ref["M"], ref["M_pad"]
+    if M_pad > M:
+        assert np.all(o[M:M_pad] == 0) and np.all(np.isneginf(lse[M:M_pad]))
+    return worst
+
+
+def oracle_logits_rows(inp, ref, rows):
+    wl = inp["workload"]
+    bidx = packed_block_index(ref, inp["gamma"])
+    hb = inp["hidden_block"].reshape(-1, wl.H)
+    x = np64(hb[torch.tensor(bidx[rows], dtype=torch.long, device=hb.device)])
+    W = inp["W"]
+    z = np.empty((len(rows), wl.V))
+    chunk = 16384
+    for v0 in range(0, wl.V, chunk):
+        Wc = W[v0:v0 + chunk].to(torch.float64).cpu().numpy()
+        z[:, v0:v0 + chunk] = oracle.lm_head_logits(x, Wc, chunk=chunk)
+    return z
+
+
+def check_pred_gap(z, frac=1e-3):
+    """Precondition of a bit-exact argmax: the top-2 gap of every compared
+    row is at least ``frac`` of the row's largest |logit|."""
+    part = np.partition(z, -2, axis=1)
+    gap = part[:, -1] - part[:, -2]
+    scale = np.max(np.abs(z), axis=1)
+    assert np.all(gap >= frac * scale), "argmax decision too close to call: inputs violate the guard"

@@ -1,0 +1,137 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, its structs match the binding, and host-side validation rejects bad
+arguments before anything is enqueued."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from ragged_verification_amd import rv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rv.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:rv_status|const char\*|int32_t)\s+(rv_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rv.LIB_PATH):
+        pytest.fail("librv.so is not built (run __graft_entry__.build())")
+    return rv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_functions()
+    assert set(names) == set(rv.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match(lib):
+    for which, st in enumerate(rv.STRUCTS):
+        c_layout = rv.abi_layout(lib, which)
+        assert c_layout[0] == ctypes.sizeof(st)
+        assert c_layout[1:] == [getattr(st, f[0]).offset for f in st._fields_]
+    assert lib.rv_abi_layout(99, None, 0) == -1
+
+
+def test_version_and_workspace(lib):
+    assert "gfx950" in rv.rv_version()
+    small = rv.rv_workspace_size(4, 4, V=512, dtype=rv.RV_F32)
+    assert small >= 256
+    big = rv.rv_workspace_size(256, 8, 128, 1, 576, 512, 129280, rv.RV_BF16)
+    assert big > small
+    d = rv.Dims(-1, 4, 0, 0, 0, 0, 0, 0)
+    out = ctypes.c_size_t(0)
+    assert lib.rv_workspace_size(ctypes.byref(d), ctypes.byref(out)) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_workspace_size(None, ctypes.byref(out)) == rv.RV_ERR_INVALID_ARG
+
+
+def _fake(n=1):
+    # host addresses that are never dereferenced: validation fails first
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_schedule_validation(lib):
+    a = rv.ScheduleArgs()
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_schedule(None, None) == rv.RV_ERR_INVALID_ARG
+    for f in ("conf", "cost_alpha", "cost_theta", "w_commit", "w_verify", "k_star", "e_star"):
+        setattr(a, f, _fake())
+    a.B, a.gamma, a.mode, a.alpha_len, a.theta_len, a.cost_bias = 4, 4, rv.RV_COMPACT, 5, 17, 1.0
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
+    a.gamma = 1
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.gamma = 17
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.gamma, a.theta_len = 4, 16   # theta must cover M = B*gamma
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.theta_len, a.mode = 17, 7
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.mode, a.B, a.gamma, a.alpha_len, a.theta_len = rv.RV_COMPACT, 1000, 8, 1001, 8001
+    assert lib.rv_schedule(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED  # > 4096 candidates
+
+
+def test_pack_validation(lib):
+    a = rv.PackArgs()
+    for f in ("w_verify", "anchor", "drafts", "ctx", "page_table", "cu", "mm", "row_req", "row_pos",
+              "tok", "slot"):
+        setattr(a, f, _fake())
+    a.B, a.gamma, a.max_pages, a.page_size, a.num_pages, a.rows_cap = 4, 4, 1, 16, 4, 16
+    assert lib.rv_pack(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
+    a.rows_cap = 15   # below B*gamma
+    assert lib.rv_pack(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.rows_cap = 16
+    tiers = (ctypes.c_int32 * 3)(8, 8, 16)   # not strictly ascending
+    a.n_tiers, a.tiers = 3, ctypes.cast(tiers, ctypes.c_void_p)
+    assert lib.rv_pack(ctypes.byref(a), None) == rv.RV_ERR_TIER
+    tiers2 = (ctypes.c_int32 * 2)(8, 32)     # largest tier above rows_cap
+    a.n_tiers, a.tiers = 2, ctypes.cast(tiers2, ctypes.c_void_p)
+    assert lib.rv_pack(ctypes.byref(a), None) == rv.RV_ERR_TIER
+    a.n_tiers = 17
+    assert lib.rv_pack(ctypes.byref(a), None) == rv.RV_ERR_TIER
+
+
+def test_attn_validation(lib):
+    a = rv.AttnArgs()
+    for f in ("q", "k_cache", "v_cache", "page_table", "ctx", "cu", "mm", "o"):
+        setattr(a, f, _fake())
+    a.B, a.gamma, a.rows_cap, a.max_pages, a.page_size, a.num_pages = 2, 8, 16, 4, 16, 8
+    a.Hq, a.Hkv, a.Dqk, a.Dv, a.dtype, a.sm_scale = 32, 8, 128, 128, rv.RV_BF16, 0.088
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
+    a.Dqk = a.Dv = 96            # no bf16 kernel for this head dim
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.Dqk = a.Dv = 128
+    a.Hq = 30                    # not a multiple of Hkv
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.Hq, a.v_cache, a.Hkv = 32, None, 8   # latent layout needs one KV head
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.sm_scale = float("nan")
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+
+
+def test_lm_and_scatter_validation(lib):
+    a = rv.LmArgs()
+    for f in ("hidden", "W", "mm", "cu", "w_commit", "w_verify", "drafts", "pred", "accept", "bonus",
+              "ceiling"):
+        setattr(a, f, _fake())
+    a.B, a.gamma, a.rows_cap, a.H, a.V, a.dtype, a.rule = 2, 4, 8, 128, 1000, rv.RV_BF16, rv.RV_GREEDY
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
+    a.H = 100                    # bf16 GEMM needs H % 64 == 0
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.H, a.rule = 128, rv.RV_REJECTION   # rejection needs q_rows, u, u_bonus, logits
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    s = rv.ScatterArgs()
+    for f in ("cu", "w_verify", "accept", "bonus", "drafts", "slot", "ctx", "anchor", "req_to_token",
+              "commit_cu", "commit_tok", "commit_slot", "free_slots", "free_count"):
+        setattr(s, f, _fake())
+    s.B, s.gamma, s.r2t_stride = 2, 4, 64
+    assert lib.rv_compact_scatter(ctypes.byref(s), None) == rv.RV_ERR_WORKSPACE
+    s.hist = _fake()             # hist without hist_len
+    assert lib.rv_compact_scatter(ctypes.byref(s), None) == rv.RV_ERR_INVALID_ARG

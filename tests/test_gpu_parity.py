@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer outputs (windows, K*, E*, cu_seqlens, tiers, row metadata, argmax,
+accept lengths, bonus tokens, scatter indices) must match bit for bit;
+attention output within 2e-2 max-abs (bf16) / 1e-4 (fp32), LM-head logits
+within 1e-2 relative to the row's largest logit (bf16) / 1e-5 (fp32).
+Reduced-size cases compare every element; full-size cases run the bench's
+launch configuration and compare sampled rows plus properties that hold at
+any size.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity_util as pu
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_full(inp, ref, mode):
+    """Oracle stages 3-5 on every real row (small cases only)."""
+    wl = inp["workload"]
+    gamma = inp["gamma"]
+    M = ref["M"]
+    bidx = pu.packed_block_index(ref, gamma)
+    q = pu.np64(inp["q_block"].reshape(-1, wl.Hq, wl.Dqk))[bidx]
+    o, lse = oracle.verify_attention(q, pu.np64(inp["k_cache"]), pu.np64(inp["v_cache"]),
+                                     pu.npi(inp["page_table"]), inp["page_size"], ref["row_req"],
+                                     ref["row_pos"], ref["M_pad"], inp["sm_scale"], Dv=wl.Dv)
+    x = pu.np64(inp["hidden_block"].reshape(-1, wl.H))[bidx]
+    z = oracle.lm_head_logits(x, pu.np64(inp["W"]))
+    pred = oracle.lm_head_pred(z)
+    drafts = pu.npi(inp["drafts"])
+    diag = {}
+    if wl.rule == "greedy":
+        acc, bonus, ceil = oracle.accept_greedy(pred, ref["cu"], ref["w_commit"], ref["w_verify"], drafts)
+    else:
+        acc, bonus, ceil = oracle.accept_rejection(z, ref["cu"], ref["w_commit"], ref["w_verify"], drafts,
+                                                   pu.np64(inp["q_rows"]), pu.np64(inp["u"]),
+                                                   pu.np64(inp["u_bonus"]), diag=diag)
+    B = inp["B"]
+    r2t = np.full((B, int(pu.npi(inp["ctx"]).max()) + gamma + 64), -1)
+    hist = np.full((B, 64), -1)
+    sc = oracle.compact_scatter(ref["cu"], ref["w_verify"], acc, bonus, drafts, ref["slot"], pu.npi(inp["ctx"]),
+                                pu.npi(inp["anchor"]), r2t, hist, np.zeros(B, dtype=np.int64))
+    return dict(o=o, lse=lse, z=z, pred=pred, accept=acc, bonus=bonus, ceiling=ceil, scatter=sc, diag=diag)
+
+
+def _check_bonus(step_bonus, ref_bonus, diag, z_rows_ok=True, thresh=1e-6):
+    """Rejection bonus draws compare exactly unless the oracle's target lies
+    within ``thresh`` (relative) of a CDF boundary, where fp32 and fp64 may
+    legitimately pick adjacent tokens."""
+    for i, (g, r) in enumerate(zip(step_bonus, ref_bonus)):
+        if diag and diag["bonus_margin"][i] < thresh:
+            assert abs(int(g) - int(r)) <= 64, (i, g, r)   # a neighbouring token
+        else:
+            assert int(g) == int(r), (i, g, r)
+
+
+def _check_scatter(step, sc, B):
+    n = int(sc["commit_cu"][-1])
+    assert np.array_equal(pu.npi(step.commit_cu), sc["commit_cu"])
+    assert np.array_equal(pu.npi(step.commit_tok)[:n], sc["commit_tok"])
+    assert np.array_equal(pu.npi(step.commit_slot)[:n], sc["commit_slot"])
+    nf = int(step.free_count.item())
+    assert nf == len(sc["free_slots"])
+    assert np.array_equal(pu.npi(step.free_slots)[:nf], sc["free_slots"])
+    assert np.array_equal(pu.npi(step.ctx), sc["ctx"])
+    assert np.array_equal(pu.npi(step.anchor), sc["anchor"])
+    assert np.array_equal(pu.npi(step.req_to_token), sc["req_to_token"])
+    assert np.array_equal(pu.npi(step.hist), sc["hist"])
+    assert np.array_equal(pu.npi(step.hist_len), sc["hist_len"])
+
+
+def _full_parity(inp, mode, dtype):
+    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode}")
+    ref = pu.oracle_schedule_pack(inp, mode)
+    step = pu.run_gpu(inp, mode, with_logits=True)
+    assert step.status() == 0
+    pu.check_schedule_pack(step, ref)
+    want = _oracle_full(inp, ref, mode)
+    M, M_pad = ref["M"], ref["M_pad"]
+    o = step.o.float().cpu().numpy()
+    err = np.max(np.abs(o[:M] - want["o"][:M]))
+    assert err <= pu.ATTN_TOL[dtype], err
+    assert np.all(o[M:M_pad] == 0)
+    lse = step.lse.cpu().numpy()
+    np.testing.assert_allclose(lse[:M], want["lse"][:M], rtol=1e-3, atol=1e-3)
+    z = step.logits.cpu().numpy()[:M]
+    rel = np.max(np.abs(z - want["z"]), axis=1) / np.max(np.abs(want["z"]), axis=1)
+    assert np.all(rel <= pu.LOGIT_TOL[dtype]), rel.max()
+    pu.check_pred_gap(want["z"]) if inp["workload"].rule == "greedy" else None
+    pred = pu.npi(step.pred)
+    if inp["workload"].rule == "greedy":
+        assert np.array_equal(pred[:M], want["pred"])
+    assert np.all(pred[M:M_pad] == -1)
+    assert np.array_equal(pu.npi(step.accept), want["accept"])
+    assert np.array_equal(pu.npi(step.ceiling), want["ceiling"])
+    if inp["workload"].rule == "greedy":
+        assert np.array_equal(pu.npi(step.bonus), want["bonus"])
+        _check_scatter(step, want["scatter"], inp["B"])
+    else:
+        for m in want["diag"]["decision_margin"]:
+            assert all(x >= 1e-4 for x in m), "accept decision too close to call"
+        _check_bonus(pu.npi(step.bonus), want["bonus"], want["diag"])
+    pu.log(f"ok attn max err {err:.3g}, logits rel {rel.max():.3g}, M={M}, M_pad={M_pad}")
+    return step, ref, want
+
+
+@pytest.mark.parametrize("mode", ["static", "compact", "cap_accept"])
+def test_tiny_f32(mode):
+    inp = pu.make_inputs("tiny_f32")
+    _full_parity(inp, mode, "f32")
+
+
+@pytest.mark.parametrize("mode", ["compact", "static"])
+def test_gqa_reduced(mode):
+    inp = pu.make_inputs("gqa_bf16", B=6, V=1000, H=256, ctx=("uniform", 40, 900))
+    _full_parity(inp, mode, "bf16")
+
+
+@pytest.mark.parametrize("mode", ["compact", "static"])
+def test_mla_reduced(mode):
+    inp = pu.make_inputs("mla_bf16", B=3, V=1000, H=512, ctx=("uniform", 60, 700))
+    _full_parity(inp, mode, "bf16")
+
+
+@pytest.mark.parametrize("mode", ["compact", "cap_accept"])
+def test_rejection_reduced(mode):
+    inp = pu.make_inputs("rejection_bf16", B=6, V=3000, H=256, ctx=("lognormal", 200, 1.0, 600))
+    _full_parity(inp, mode, "bf16")
+
+
+def test_gqa_group8_and_split_kv():
+    """Eight query heads per KV head (64 query vectors per tile) and one long
+    request so the key range is split and merged."""
+    inp = pu.make_inputs("gqa_bf16", B=2, Hq=64, V=700, H=128, ctx=("uniform", 2500, 3000))
+    _full_parity(inp, "compact", "bf16")
+
+
+def test_sweep_classes_cap_accept_equals_compact():
+    inp = pu.make_inputs("sweep_gqa", B=24, V=800, H=128, ctx=("uniform", 30, 300))
+    s_c, ref_c, want_c = _full_parity(inp, "compact", "bf16")
+    c_tok = pu.npi(s_c.commit_tok).copy()
+    c_cu = pu.npi(s_c.commit_cu).copy()
+    c_slot = pu.npi(s_c.commit_slot).copy()
+    s_a, ref_a, want_a = _full_parity(inp, "cap_accept", "bf16")
+    assert np.array_equal(pu.npi(s_a.commit_cu), c_cu)
+    n = int(c_cu[-1])
+    assert np.array_equal(pu.npi(s_a.commit_tok)[:n], c_tok[:n])
+    assert np.array_equal(pu.npi(s_a.commit_slot)[:n], c_slot[:n])
+    assert np.all(pu.npi(s_a.ceiling) >= pu.npi(s_a.accept))
+
+
+def test_static_rows_equal_compact_rows():
+    """By causality a compact row equals the static row of the same block
+    position (attention output and prediction)."""
+    inp = pu.make_inputs("mla_bf16", B=4, V=600, H=256, ctx=("uniform", 100, 400))
+    st = pu.run_gpu(inp, "static")
+    so, sp = st.o.float().cpu().numpy(), pu.npi(st.pred)
+    co_step = pu.run_gpu(inp, "compact")
+    co, cp = co_step.o.float().cpu().numpy(), pu.npi(co_step.pred)
+    cu = pu.npi(co_step.cu)
+    g = inp["gamma"]
+    for i in range(inp["B"]):
+        for k in range(cu[i + 1] - cu[i]):
+            assert np.max(np.abs(co[cu[i] + k] - so[i * g + k])) <= 2e-2
+            assert cp[cu[i] + k] == sp[i * g + k]
+
+
+def test_edge_cases():
+    """One request, anchor-only windows (huge theta), zero context (the only
+    visible key is the anchor's own), block width 2."""
+    inp = pu.make_inputs("tiny_f32", B=1, gamma=2, ctx=("uniform", 0, 0))
+    _full_parity(inp, "compact", "f32")
+    inp = pu.make_inputs("gqa_bf16", B=3, V=300, H=64, ctx=("uniform", 0, 5))
+    inp["cost_theta"] = inp["cost_theta"] * 1e6
+    step, ref, _ = _full_parity(inp, "compact", "bf16")
+    assert np.all(pu.npi(step.w_verify) == 1)
+
+
+def test_device_status_errors():
+    """Bad data found on the device raises the sticky status and keeps every
+    access in bounds."""
+    from ragged_verification_amd import rv
+    inp = pu.make_inputs("tiny_f32")
+    step = pu.run_gpu(inp, "compact")
+    assert step.status() == 0
+    bad = dict(inp)
+    bad["conf"] = inp["conf"].clone()
+    bad["conf"][0, 0] = 1.5
+    s2 = pu.run_gpu(bad, "compact")
+    assert s2.status() == 1                      # BAD_CONF
+    rv.rv_clear_status(s2.workspace)
+    assert s2.status() == 0
+    bad = dict(inp)
+    bad["tiers"] = (4,)                          # M > 4 always here: overflow
+    s3 = pu.run_gpu(bad, "static")
+    assert s3.status() == 4
+    assert pu.npi(s3.mm).tolist() == [16, 16]
+    bad = dict(inp)
+    bad["page_table"] = inp["page_table"].clone()
+    bad["page_table"][1, 0] = 10_000             # out of range page id
+    s4 = pu.run_gpu(bad, "static")
+    assert s4.status() == 5
+
+
+def test_deterministic_replay():
+    inp = pu.make_inputs("mla_bf16", B=3, V=500, H=128, ctx=("uniform", 300, 900))
+    a = pu.run_gpu(inp, "compact", with_logits=True)
+    o1, z1 = a.o.clone(), a.logits.clone()
+    a.restore()
+    a.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.o, o1) and torch.equal(a.logits, z1)
