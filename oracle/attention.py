@@ -43,14 +43,14 @@ def attention_row(q_row, keys, values, sm_scale):
     group = Hq // Hkv
     o = np.zeros((Hq, values.shape[2]), dtype=np.float64)
     lse = np.zeros(Hq, dtype=np.float64)
-    for h in range(Hq):
-        g = h // group
-        s = sm_scale * (keys[:, g, :] @ q_row[h])
-        m = np.max(s)
+    for g in range(Hkv):
+        heads = slice(g * group, (g + 1) * group)   # query heads sharing KV head g
+        s = sm_scale * (q_row[heads] @ keys[:, g, :].T)        # [group, L]
+        m = np.max(s, axis=1, keepdims=True)
         e = np.exp(s - m)
-        denom = np.sum(e)
-        o[h] = (e @ values[:, g, :]) / denom
-        lse[h] = m + np.log(denom)
+        denom = np.sum(e, axis=1)
+        o[heads] = (e @ values[:, g, :]) / denom[:, None]
+        lse[heads] = m[:, 0] + np.log(denom)
     return o, lse
 
 
