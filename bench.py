@@ -42,23 +42,31 @@ def log(msg):
 
 
 class StageTimer:
-    """HIP events on torch's current stream (the stream every call uses)."""
+    """HIP events on torch's current stream (the stream every call uses);
+    read back once after the timed region has been synchronised."""
 
     def __init__(self, names):
         self.names = names
-        self.ev = {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for n in names}
+        self.pairs = {n: [] for n in names}
         self.acc = {n: 0.0 for n in names}
 
     def start(self, n):
-        self.ev[n][0].record()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[n].append([e, None])
 
     def stop(self, n):
-        self.ev[n][1].record()
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[n][-1][1] = e
 
     def collect(self):
+        pass
+
+    def finish(self):
+        torch.cuda.synchronize()
         for n in self.names:
-            self.acc[n] += self.ev[n][0].elapsed_time(self.ev[n][1])
+            self.acc[n] = sum(a.elapsed_time(b) for a, b in self.pairs[n])
 
 
 STAGES = ["schedule", "pack", "attn", "lm_accept", "scatter"]
@@ -127,6 +135,7 @@ def measure(step, steps, warmup):
     run_steps(step, steps, timer)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    timer.finish()
     assert step.status() == 0, f"device status {rv.DEV_NAMES.get(step.status())}"
     per = {k: v / steps for k, v in timer.acc.items()}
     five = sum(per[s] for s in STAGES)
