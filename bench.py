@@ -294,7 +294,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(inp, None)
-    print(json.dumps(line), flush=True)
+    print(json.dumps(line, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)
 
 
 if __name__ == "__main__":
