@@ -146,7 +146,7 @@ def measure(step, steps, warmup):
                 committed=committed)
 
 
-def cpu_baseline(inp, step, n_req=2):
+def cpu_baseline(inp, step, n_req=24):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     schedule and pack for the whole batch, then attention, LM head, accept and
     scatter for the rows of ``n_req`` requests."""

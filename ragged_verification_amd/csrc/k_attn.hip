@@ -18,7 +18,9 @@
 //    bf16 16x16x32 MFMAs (fp32 accumulation) and keeps an online base-2
 //    softmax per query vector.  In the S^T orientation each lane owns one
 //    query vector, so the row max needs two cross-lane steps and P^T feeds the
-//    PV MFMA straight from registers; V is stored transposed in LDS.
+//    PV MFMA straight from registers; the V^T operand comes from the
+//    row-major value tile through gfx950's transposing LDS reads, so the
+//    latent layout keeps a single copy of each key row in LDS.
 //  * The latent (MLA-style) layout reads one 576-wide row per key and uses its
 //    first 512 entries as the value.
 //  * Split items write fp32 partials (O, running max, normaliser) that a
@@ -188,21 +190,36 @@ template <int DQK, int DV, int NW, bool LATENT>
 struct AttnCfg {
   static constexpr int kThreads = 64 * NW;
   static constexpr int kQT = 16 * NW;
-  static constexpr int kKStride = DQK + 8;      // bf16 per K row in LDS
-  static constexpr int kVStride = kNK + 8;      // bf16 per V^T row in LDS
+  static constexpr int kKStride = DQK + 8;      // bf16 per K row in LDS (16-byte pad)
+  static constexpr int kVStride = DV + 8;       // bf16 per V row (separate V only)
   static constexpr int kKChunks = kNK * DQK / 8;   // 16-byte chunks per K tile
   static constexpr int kVChunks = LATENT ? 0 : kNK * DV / 8;
   static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
   static constexpr int kVPer = (kVChunks + kThreads - 1) / kThreads;
-  static constexpr int kLdsBytes = (kNK * kKStride + DV * kVStride) * 2;
+  static constexpr int kLdsBytes = (kNK * kKStride + (LATENT ? 0 : kNK * kVStride)) * 2;
 };
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// gfx950 transposing LDS read: within each 16-lane group, lane 4s+e receives
+// element e of the 4-element blocks addressed by lanes s, 4+s, 8+s, 12+s.
+// With lane r of the group addressing row (key0 + r/4), columns c0 + 4*(r%4)
+// of a row-major tile, lane m receives column c0 + m of rows key0..key0+3:
+// the k-contiguous MFMA operand fragment of a [keys x dims] tile.
+__device__ inline uint2 lds_read_tr16(const bf16_t* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 template <int DQK, int DV, int NW, bool LATENT>
 __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
   using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* Vt = Ks + kNK * Cfg::kKStride;
+  // the value rows: the latent layout reuses the key rows' first DV entries
+  bf16_t* Vs = LATENT ? Ks : Ks + kNK * Cfg::kKStride;
+  constexpr int kVs = LATENT ? Cfg::kKStride : Cfg::kVStride;
 
   // XCD-aware order: hardware places workgroup b on XCD b % 8; give each XCD
   // a contiguous run of items so tiles sharing a KV chunk share its L2.
@@ -317,13 +334,6 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
         const int kk = ch / (DQK / 8);
         const int part = ch % (DQK / 8);
         *reinterpret_cast<u32x4_t*>(Ks + kk * Cfg::kKStride + part * 8) = kbuf[e];
-        if constexpr (LATENT) {
-          if (part * 8 < DV) {
-            const bf16_t* hv = reinterpret_cast<const bf16_t*>(&kbuf[e]);
-#pragma unroll
-            for (int x = 0; x < 8; ++x) Vt[(part * 8 + x) * Cfg::kVStride + kk] = hv[x];
-          }
-        }
       }
     }
     if constexpr (!LATENT) {
@@ -333,9 +343,7 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
         if (ch < Cfg::kVChunks) {
           const int kk = ch / (DV / 8);
           const int part = ch % (DV / 8);
-          const bf16_t* hv = reinterpret_cast<const bf16_t*>(&vbuf[e]);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) Vt[(part * 8 + x) * Cfg::kVStride + kk] = hv[x];
+          *reinterpret_cast<u32x4_t*>(Vs + kk * Cfg::kVStride + part * 8) = vbuf[e];
         }
       }
     }
@@ -398,11 +406,14 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
       pb[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
       pb[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
       pb[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
+      // V^T fragments straight from the row-major value tile: k-slots
+      // 8*grp..+3 <- keys 4*grp..+3, k-slots 8*grp+4..+7 <- keys 16+4*grp..+3
+      const bf16_t* v_lo = Vs + (grp * 4 + (n16 >> 2)) * kVs + 4 * (n16 & 3);
+      const bf16_t* v_hi = v_lo + 16 * kVs;
 #pragma unroll
       for (int mb = 0; mb < DV / 16; ++mb) {
-        const bf16_t* vrow = Vt + (mb * 16 + n16) * Cfg::kVStride;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + grp * 4);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16 + grp * 4);
+        const uint2 lo = lds_read_tr16(v_lo + mb * 16);
+        const uint2 hi = lds_read_tr16(v_hi + mb * 16);
         const u32x4_t a = u32x4_t{lo.x, lo.y, hi.x, hi.y};
         oacc[mb] = mfma16(a, pb, oacc[mb]);
       }
