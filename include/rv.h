@@ -210,7 +210,8 @@ rv_status rv_pack(const rv_pack_args* a, void* stream);
  * (v_cache == NULL, Hkv == 1): V[i,j] = first Dv entries of K[i,j].  Rows
  * [M, M_pad) get o = 0, lse = -inf; rows >= M_pad are not written.
  *
- * Built shapes: dtype RV_BF16 with (Dqk,Dv) = (576,512) latent, Hq % 64 == 0;
+ * Built shapes: dtype RV_BF16 with (Dqk,Dv) = (576,512) latent, Hq % 64 == 0,
+ * max_pages <= 2047;
  * or (128,128) with Hq/Hkv in {1,2,4,8,16}; dtype RV_F32 with Dqk = Dv <= 128
  * (any group).  bf16 accumulates in fp32. */
 typedef struct {

@@ -453,6 +453,288 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
   }
 }
 
+// ---- latent (MLA-style) bf16 kernel: LDS DMA ring ---------------------------------
+//
+// One workgroup = four waves against one latent KV head; each wave owns QB
+// blocks of 16 query vectors (QB = 1: 64 query vectors per workgroup, e.g.
+// half of a 128-head row).  Keys arrive through direct global->LDS DMA
+// (global_load_lds_dwordx4) into a ring of kMlaStages 32-key stages issued
+// kMlaStages-1 tiles ahead, so no registers stage the data and the latency of
+// the next tiles hides behind the MFMA work of the current one.  The DMA is
+// issued from inline assembly because the compiler would otherwise wait for
+// every outstanding DMA before each LDS read; the kernel tracks the
+// vector-memory counter itself (loads complete in issue order).
+//
+// LDS layout of a stage: 32 rows of 1152 bytes (576 bf16, no padding) whose
+// 16-byte chunks are XOR-swizzled within aligned groups of eight
+// (physical = logical ^ ((row >> 1) & 7)) so that fragment reads of sixteen
+// consecutive rows hit distinct banks.  The request's page-table entries for
+// the item's key range sit in an LDS window.  The softmax reference max moves
+// lazily (only when a tile's max exceeds it by more than 2^8), so the O
+// accumulators are rescaled only on such jumps.
+
+constexpr int kMlaD = 576, kMlaDv = 512;
+constexpr int kMlaRowBytes = kMlaD * 2;                    // 1152
+constexpr int kMlaStageBytes = kNK * kMlaRowBytes;         // 36864
+constexpr int kMlaStages = 3;
+constexpr int kPageWin = 2048;
+constexpr int kMlaChunksPerRow = kMlaD / 8;                // 72
+constexpr int kMlaDmaPerWave = kNK * kMlaChunksPerRow / 256;  // 9 per wave per tile
+constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kPageWin * 4;
+constexpr int kMlaQB = 1;                                  // 16-vector blocks per wave
+constexpr int kMlaQT = 4 * 16 * kMlaQB;                    // query vectors per tile
+
+__device__ inline void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ inline int swz(int row) { return (row >> 1) & 7; }
+
+template <int QB>
+__global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int* pwin = reinterpret_cast<int*>(smem + kMlaStages * kMlaStageBytes);
+
+  const int n_items = p.hdr[0];
+  const int per_xcd = (n_items + 7) / 8;
+  const int k_local = blockIdx.x / 8;
+  const int item = (blockIdx.x % 8) * per_xcd + k_local;
+  if (k_local >= per_xcd || item >= n_items) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = tid >> 6;
+  const int n16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int4 rec = p.items[item];
+  const int i = rec.x, tile = rec.y, sp = rec.z;
+  const int4 info = p.req_info[i];
+  const int ns = info.x;
+  const int row_start = p.cu[i];
+  const int w = p.cu[i + 1] - row_start;
+  const int c = p.ctx[i];
+  const int rb = tile / p.n_hb;          // one KV head
+  const int hb = tile % p.n_hb;
+  const int row0 = rb * p.RT;
+  const int rows_here = min(p.RT, w - row0);
+  const int L_tile = c + row0 + rows_here;
+  const int chunk = p.hdr[1];
+  const int kv_begin = sp * chunk;
+  const int kv_end = min(kv_begin + chunk, L_tile);
+  const int P = p.page_size;
+
+  // page-table window for keys [kv_begin, kv_end)
+  const int pg0 = kv_begin / P;
+  int npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
+  if (npg > kPageWin) {                 // context longer than the page table allows
+    if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
+    npg = kPageWin;
+  }
+  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
+  for (int x = tid; x < npg; x += 256) {
+    int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
+    if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+    pwin[x] = pg;
+  }
+
+  // query fragments (B operand of S^T = K Q^T)
+  int q_row[QB], head[QB], limit[QB];
+  bool q_valid[QB];
+  u32x4_t qf[QB][kMlaD / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qv = (wid * QB + qb) * 16 + n16;
+    const int rl = qv / p.NH;
+    head[qb] = hb * p.NH + (qv % p.NH);
+    q_valid[qb] = rl < rows_here;
+    q_row[qb] = row_start + row0 + (q_valid[qb] ? rl : 0);
+    limit[qb] = c + row0 + rl;
+    const bf16_t* qsrc = p.q + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaD + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < kMlaD / 32; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
+  }
+  wait_vm<0>();
+  __syncthreads();   // page window visible
+
+  f32x4_t oacc[QB][kMlaDv / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[QB], l_part[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_part[qb] = 0.f; }
+
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+  const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
+
+  // DMA of one 32-key tile into stage `st`: wave wid issues chunks
+  // (wid*9 + e)*64 + lane, e = 0..8; chunk c lands at row c/72, physical
+  // position c%72 and holds logical chunk (c%72) ^ swz(row)
+  auto issue = [&](int t, int st) {
+    const int t0 = kv_begin + t * kNK;
+#pragma unroll
+    for (int e = 0; e < kMlaDmaPerWave; ++e) {
+      const int cidx = (wid * kMlaDmaPerWave + e) * 64 + lane;
+      const int row = cidx / kMlaChunksPerRow;
+      const int phys = cidx % kMlaChunksPerRow;
+      const int logical = phys ^ swz(row);
+      const int j = min(t0 + row, kv_end - 1);   // keys past the end: a valid row, masked later
+      const int pg = pwin[min(j / P - pg0, npg - 1)];
+      const bf16_t* g = p.k + ((size_t)pg * P + (j % P)) * kMlaD + logical * 8;
+      const uint32_t lds = __builtin_amdgcn_readfirstlane(
+          smem_base + st * kMlaStageBytes + (wid * kMlaDmaPerWave + e) * 1024);
+      dma16(g, lds);
+    }
+  };
+
+  // per-lane LDS byte offsets of the fragment reads (swizzle precomputed)
+  // QK: A rows 16*mb + n16, logical chunk 4*ks + grp; pattern repeats every 2 ks
+  int qk_off[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int r = mb * 16 + n16;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) qk_off[mb][kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ swz(r)) * 16;
+  }
+  // PV (transposing reads): rows kb + n16/4 (kb = 4*grp or 16 + 4*grp), elements
+  // 16*mb + 4*(n16 & 3): logical chunk 2*mb + ((n16 & 3) >> 1), half (n16 & 1);
+  // the pattern repeats every 4 mb (one aligned group of 8 chunks = 128 bytes)
+  int pv_off[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = h * 16 + grp * 4 + (n16 >> 2);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int lc = 2 * mm + ((n16 & 3) >> 1);
+      pv_off[h][mm] = r * kMlaRowBytes + (lc ^ swz(r)) * 16 + (n16 & 1) * 8;
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < kMlaStages - 1; ++t)
+    if (t < n_tiles) issue(t, t);
+
+  for (int t = 0; t < n_tiles; ++t) {
+    // tile t must have landed; tiles up to t + kMlaStages - 2 may stay in flight
+    if (t + 1 < n_tiles) wait_vm<kMlaDmaPerWave * (kMlaStages - 2)>(); else wait_vm<0>();
+    __syncthreads();
+    if (t + kMlaStages - 1 < n_tiles) issue(t + kMlaStages - 1, (t + kMlaStages - 1) % kMlaStages);
+
+    const unsigned char* stg = smem + (t % kMlaStages) * kMlaStageBytes;
+    const int t0 = kv_begin + t * kNK;
+
+    f32x4_t sacc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) sacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kMlaD / 32; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(stg + qk_off[mb][ks & 1] + (ks >> 1) * 128);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma16(a, qf[qb][ks], sacc[qb][mb]);
+      }
+    }
+
+    u32x4_t pb[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kpos = t0 + mb * 16 + grp * 4 + j;
+          float sc = sacc[qb][mb][j] * p.scale_log2;
+          if (!q_valid[qb] || kpos >= kv_end || kpos > limit[qb]) sc = -INFINITY;
+          sacc[qb][mb][j] = sc;
+          tmax = fmaxf(tmax, sc);
+        }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (tmax > m_run[qb] + 8.f) {   // lazy rescale (rare after the first tile)
+        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : exp2f(m_run[qb] - tmax);
+        l_part[qb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] *= alpha;
+        m_run[qb] = tmax;
+      }
+      const float m_ref = m_run[qb];
+      float psum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sc = sacc[qb][mb][j];
+          const float pr = (sc == -INFINITY) ? 0.f : exp2f(sc - m_ref);
+          sacc[qb][mb][j] = pr;
+          psum += pr;
+        }
+      }
+      l_part[qb] += psum;
+      // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
+      pb[qb][0] = pack_bf16x2(sacc[qb][0][0], sacc[qb][0][1]);
+      pb[qb][1] = pack_bf16x2(sacc[qb][0][2], sacc[qb][0][3]);
+      pb[qb][2] = pack_bf16x2(sacc[qb][1][0], sacc[qb][1][1]);
+      pb[qb][3] = pack_bf16x2(sacc[qb][1][2], sacc[qb][1][3]);
+    }
+
+    // O^T += V^T P^T with V^T fragments from transposing reads of the key rows
+#pragma unroll
+    for (int mb = 0; mb < kMlaDv / 16; ++mb) {
+      const uint2 lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(stg + pv_off[0][mb & 3] + (mb >> 2) * 128));
+      const uint2 hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(stg + pv_off[1][mb & 3] + (mb >> 2) * 128));
+      const u32x4_t a = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][mb] = mfma16(a, pb[qb], oacc[qb][mb]);
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float l_tot = l_part[qb] + __shfl_xor(l_part[qb], 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    if (!q_valid[qb]) continue;
+    const int qv = (wid * QB + qb) * 16 + n16;
+    if (ns == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16_t* dst = p.o + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaDv;
+#pragma unroll
+      for (int mb = 0; mb < kMlaDv / 16; ++mb) {
+        uint2 pk;
+        pk.x = pack_bf16x2(oacc[qb][mb][0] * inv, oacc[qb][mb][1] * inv);
+        pk.y = pack_bf16x2(oacc[qb][mb][2] * inv, oacc[qb][mb][3] * inv);
+        *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
+      }
+      if (p.lse && grp == 0)
+        p.lse[(size_t)q_row[qb] * p.Hq + head[qb]] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+    } else {
+      const int slot = info.z + sp * info.w + tile;
+      if (slot < 0 || slot >= p.part_cap) continue;
+      float* po = p.part_o + ((size_t)slot * kMlaQT + qv) * kMlaDv;
+#pragma unroll
+      for (int mb = 0; mb < kMlaDv / 16; ++mb)
+        *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[qb][mb];
+      if (grp == 0) {
+        float* pml = p.part_ml + ((size_t)slot * kMlaQT + qv) * 2;
+        pml[0] = m_run[qb];
+        pml[1] = l_tot;
+      }
+    }
+  }
+}
+
 // ---- combine split partials ----------------------------------------------------
 struct CombineParams {
   const int32_t* cu;
@@ -604,13 +886,13 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
   const int G = Hq / Hkv;
   if (latent) {
     if (!(Dqk == 576 && Dv == 512 && Hkv == 1 && Hq % 64 == 0)) return false;
-    *nw = 4;   // 64 query vectors per tile: Q fragments and O^T fit 512 registers
+    *nw = 4 * kMlaQB;   // DMA-ring kernel: 4 waves x 16*kMlaQB query vectors per tile
   } else {
     if (!(Dqk == 128 && Dv == 128)) return false;
     if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return false;
     *nw = (G * gamma <= 32) ? 2 : 4;
   }
-  const int QT = 16 * *nw;
+  const int QT = 16 * *nw;   // query vectors per tile
   sh->Hq = Hq;
   sh->Hkv = Hkv;
   sh->G = G;
@@ -652,6 +934,10 @@ hipError_t launch_main(const MainParams& mp, int grid, hipStream_t s) {
 }
 
 }  // namespace
+
+int attn_max_pages_limit(int dtype, bool latent) {
+  return (dtype == RV_BF16 && latent) ? kPageWin - 1 : (1 << 30);
+}
 
 bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent) {
   if (dtype == RV_F32) return Dqk <= 128 && Dv <= 128 && Dqk > 0 && Dv > 0 && Hkv > 0 && Hq % Hkv == 0 &&
@@ -756,7 +1042,11 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   const int grid = L.item_cap;
 
   if (latent) {
-    e = launch_main<576, 512, 4, true>(mp, grid, s);
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_mla<kMlaQB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_mla<kMlaQB>, dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    e = hipGetLastError();
   } else {
     e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, grid, s) : launch_main<128, 128, 4, false>(mp, grid, s);
   }

@@ -113,6 +113,7 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
   const bool latent = (a->v_cache == nullptr);
   if (latent && (a->Hkv != 1 || a->Dv > a->Dqk)) return RV_ERR_UNSUPPORTED;
   if (!attn_shape_supported(a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype, latent)) return RV_ERR_UNSUPPORTED;
+  if (a->max_pages > attn_max_pages_limit(a->dtype, latent)) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + attn_scratch_bytes(a->B, a->gamma, a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
   return hip_status(launch_attn(*a, static_cast<hipStream_t>(stream)));

@@ -74,5 +74,6 @@ hipError_t launch_clear_status(void* ws, hipStream_t s);
 size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, int dtype);
 size_t lm_scratch_bytes(int B, int gamma, int V);
 bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent);
+int attn_max_pages_limit(int dtype, bool latent);
 
 }  // namespace rv
