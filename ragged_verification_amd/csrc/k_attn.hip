@@ -183,6 +183,7 @@ struct MainParams {
   float* part_ml;         // [part_cap][QT][2]
   int32_t* status;
   int max_pages, page_size, num_pages, Hq, Hkv, G, NH, RT, n_hb, part_cap;
+  int log2P;              // log2(page_size) when it is a power of two, else -1
   float scale_log2;       // sm_scale * log2(e)
 };
 
@@ -209,6 +210,15 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // the k-contiguous MFMA operand fragment of a [keys x dims] tile.
 __device__ inline uint2 lds_read_tr16(const bf16_t* p) {
   s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// reads at raw 32-bit LDS byte addresses (constant parts fold into the
+// instruction's offset field)
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+__device__ inline u32x4_t lds_b128(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
+__device__ inline uint2 lds_tr16(uint32_t addr) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)addr);
   return __builtin_bit_cast(uint2, v);
 }
 
@@ -484,8 +494,21 @@ constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kPageWin * 4;
 constexpr int kMlaQB = 1;                                  // 16-vector blocks per wave
 constexpr int kMlaQT = 4 * 16 * kMlaQB;                    // query vectors per tile
 
+// DMA of 16 bytes per lane: global (64-bit address) -> LDS at m0 + 16*lane
 __device__ inline void dma16(const void* g, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+// same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset
+__device__ inline void dma16_s(uint32_t off, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ inline const void* uniform_ptr(const void* x) {
+  const uint64_t v = reinterpret_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 // s_waitcnt with only the vector-memory count limited (gfx9 encoding)
@@ -496,7 +519,14 @@ __device__ inline void wait_vm() {
 
 __device__ inline int swz(int row) { return (row >> 1) & 7; }
 
-template <int QB>
+__device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};   // v_cvt_pk_bf16_f32 (RNE)
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// FAST: page size is a power of two >= 32, so a 32-key tile lies in one page
+template <int QB, bool FAST>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   int* pwin = reinterpret_cast<int*>(smem + kMlaStages * kMlaStageBytes);
@@ -509,7 +539,7 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -545,7 +575,7 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   }
 
   // query fragments (B operand of S^T = K Q^T)
-  int q_row[QB], head[QB], limit[QB];
+  int q_row[QB], head[QB], lim[QB];
   bool q_valid[QB];
   u32x4_t qf[QB][kMlaD / 32];
 #pragma unroll
@@ -555,43 +585,61 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
     head[qb] = hb * p.NH + (qv % p.NH);
     q_valid[qb] = rl < rows_here;
     q_row[qb] = row_start + row0 + (q_valid[qb] ? rl : 0);
-    limit[qb] = c + row0 + rl;
+    lim[qb] = min(c + row0 + rl, kv_end - 1);   // last key this vector may see here
     const bf16_t* qsrc = p.q + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < kMlaD / 32; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
   }
+  // tiles ending at or before this key need no mask for any valid vector
+  const int full_lim = min(c + row0, kv_end - 1);
   wait_vm<0>();
   __syncthreads();   // page window visible
 
   f32x4_t oacc[QB][kMlaDv / 16];
+  float m_run[QB], l_part[QB], m_seen[QB];
+  bool over[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[QB], l_part[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; l_part[qb] = 0.f; }
+  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; m_seen[qb] = -INFINITY; }
 
-  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
   const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)smem + wid * kMlaDmaPerWave * 1024);
 
-  // DMA of one 32-key tile into stage `st`: wave wid issues chunks
-  // (wid*9 + e)*64 + lane, e = 0..8; chunk c lands at row c/72, physical
-  // position c%72 and holds logical chunk (c%72) ^ swz(row)
+  // this lane's DMA chunks (tile independent): wave wid issues chunks
+  // (wid*9 + e)*64 + lane; chunk c lands at row c/72, physical position c%72
+  // and holds logical chunk (c%72) ^ swz(row)
+  int drow[kMlaDmaPerWave];
+  uint32_t dlog[kMlaDmaPerWave];
+#pragma unroll
+  for (int e = 0; e < kMlaDmaPerWave; ++e) {
+    const int cidx = (wid * kMlaDmaPerWave + e) * 64 + lane;
+    drow[e] = cidx / kMlaChunksPerRow;
+    dlog[e] = (uint32_t)(((cidx % kMlaChunksPerRow) ^ swz(drow[e])) * 16);
+  }
+  const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
+
   auto issue = [&](int t, int st) {
     const int t0 = kv_begin + t * kNK;
+    const uint32_t lds0 = wave_lds + st * kMlaStageBytes;
+    if constexpr (FAST) {
+      const int pg = __builtin_amdgcn_readfirstlane(pwin[(t0 >> p.log2P) - pg0]);
+      const void* base = uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
+                                     (size_t)pg * P * kMlaRowBytes);
 #pragma unroll
-    for (int e = 0; e < kMlaDmaPerWave; ++e) {
-      const int cidx = (wid * kMlaDmaPerWave + e) * 64 + lane;
-      const int row = cidx / kMlaChunksPerRow;
-      const int phys = cidx % kMlaChunksPerRow;
-      const int logical = phys ^ swz(row);
-      const int j = min(t0 + row, kv_end - 1);   // keys past the end: a valid row, masked later
-      const int pg = pwin[min(j / P - pg0, npg - 1)];
-      const bf16_t* g = p.k + ((size_t)pg * P + (j % P)) * kMlaD + logical * 8;
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(
-          smem_base + st * kMlaStageBytes + (wid * kMlaDmaPerWave + e) * 1024);
-      dma16(g, lds);
+      for (int e = 0; e < kMlaDmaPerWave; ++e) {
+        const int j = min(t0 + drow[e], last);
+        dma16_s((uint32_t)(j & (P - 1)) * kMlaRowBytes + dlog[e], base, lds0 + e * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kMlaDmaPerWave; ++e) {
+        const int j = min(t0 + drow[e], last);
+        const int pg = pwin[min(j / P - pg0, npg - 1)];
+        const unsigned char* g = reinterpret_cast<const unsigned char*>(p.k) +
+                                 ((size_t)pg * P + (j % P)) * kMlaRowBytes + dlog[e];
+        dma16(g, lds0 + e * 1024);
+      }
     }
   };
 
@@ -618,88 +666,138 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
     }
   }
 
+  // Softmax reference: the first tile's max fixes each vector's reference
+  // m_ref; later probabilities may exceed 1 by up to 2^kSlack, which fp32
+  // accumulation and bf16 P absorb.  A tile exceeding that marks the vector;
+  // the workgroup then reruns the item once with the true maximum as the
+  // reference.  The O accumulators are therefore only ever zeroed and
+  // MFMA-accumulated, never rescaled in registers.
+  constexpr float kSlack = 32.f;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    l_part[qb] = 0.f;
+    over[qb] = false;
+    if (pass == 1) m_run[qb] = m_seen[qb];
+  }
 #pragma unroll
   for (int t = 0; t < kMlaStages - 1; ++t)
     if (t < n_tiles) issue(t, t);
 
+  int st_cur = 0;                    // stage of tile t
   for (int t = 0; t < n_tiles; ++t) {
     // tile t must have landed; tiles up to t + kMlaStages - 2 may stay in flight
     if (t + 1 < n_tiles) wait_vm<kMlaDmaPerWave * (kMlaStages - 2)>(); else wait_vm<0>();
     __syncthreads();
     if (t + kMlaStages - 1 < n_tiles) issue(t + kMlaStages - 1, (t + kMlaStages - 1) % kMlaStages);
 
-    const unsigned char* stg = smem + (t % kMlaStages) * kMlaStageBytes;
+    // stage base (wave uniform) plus the per-lane offsets: 12 addresses per
+    // tile; the remaining constants fold into the LDS instructions' offsets
+    const uint32_t stg = __builtin_amdgcn_readfirstlane(smem_lds + st_cur * kMlaStageBytes);
+    st_cur = (st_cur == kMlaStages - 1) ? 0 : st_cur + 1;
+    uint32_t aq[2][2], av[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) aq[mb][kk] = stg + qk_off[mb][kk];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) av[h][mm] = stg + pv_off[h][mm];
     const int t0 = kv_begin + t * kNK;
+    const bool full = (t0 + kNK - 1 <= full_lim);   // wave uniform
 
+    // S^T = K Q^T; K fragments are read two steps ahead of their MFMAs
+    // (scheduling barriers keep that order) so LDS latency overlaps MFMA work
     f32x4_t sacc[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) sacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    constexpr int kKs = kMlaD / 32;
+    u32x4_t fa[3][2];
 #pragma unroll
-    for (int ks = 0; ks < kMlaD / 32; ++ks) {
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(stg + qk_off[mb][ks & 1] + (ks >> 1) * 128);
+      for (int mb = 0; mb < 2; ++mb) fa[ks][mb] = lds_b128(aq[mb][ks & 1] + (ks >> 1) * 128);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma16(a, qf[qb][ks], sacc[qb][mb]);
+    for (int ks = 0; ks < kKs; ++ks) {
+      if (ks + 2 < kKs) {
+        const int kn = ks + 2;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) fa[kn % 3][mb] = lds_b128(aq[mb][kn & 1] + (kn >> 1) * 128);
       }
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma16(fa[ks % 3][mb], qf[qb][ks], sacc[qb][mb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     u32x4_t pb[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float tmax = -INFINITY;
+      float sv[8];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int kpos = t0 + mb * 16 + grp * 4 + j;
-          float sc = sacc[qb][mb][j] * p.scale_log2;
-          if (!q_valid[qb] || kpos >= kv_end || kpos > limit[qb]) sc = -INFINITY;
-          sacc[qb][mb][j] = sc;
-          tmax = fmaxf(tmax, sc);
-        }
+        for (int j = 0; j < 4; ++j) sv[mb * 4 + j] = sacc[qb][mb][j] * p.scale_log2;
+      if (!full) {   // tail tile: keys past this vector's limit get probability 0
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (t0 + mb * 16 + grp * 4 + j > lim[qb]) sv[mb * 4 + j] = -INFINITY;
       }
+      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      if (tmax > m_run[qb] + 8.f) {   // lazy rescale (rare after the first tile)
-        const float alpha = (m_run[qb] == -INFINITY) ? 0.f : exp2f(m_run[qb] - tmax);
-        l_part[qb] *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] *= alpha;
-        m_run[qb] = tmax;
-      }
-      const float m_ref = m_run[qb];
+      m_seen[qb] = fmaxf(m_seen[qb], tmax);
+      if (m_run[qb] == -INFINITY) m_run[qb] = tmax;          // first tile with a visible key
+      over[qb] = over[qb] || (tmax > m_run[qb] + kSlack);
+      const float m_ref = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
+      float pr[8];
       float psum = 0.f;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float sc = sacc[qb][mb][j];
-          const float pr = (sc == -INFINITY) ? 0.f : exp2f(sc - m_ref);
-          sacc[qb][mb][j] = pr;
-          psum += pr;
-        }
+      for (int x = 0; x < 8; ++x) {
+        pr[x] = __builtin_amdgcn_exp2f(sv[x] - m_ref);   // exp2(-inf) = 0
+        psum += pr[x];
       }
       l_part[qb] += psum;
       // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
-      pb[qb][0] = pack_bf16x2(sacc[qb][0][0], sacc[qb][0][1]);
-      pb[qb][1] = pack_bf16x2(sacc[qb][0][2], sacc[qb][0][3]);
-      pb[qb][2] = pack_bf16x2(sacc[qb][1][0], sacc[qb][1][1]);
-      pb[qb][3] = pack_bf16x2(sacc[qb][1][2], sacc[qb][1][3]);
+      pb[qb][0] = cvt_bf16x2(pr[0], pr[1]);
+      pb[qb][1] = cvt_bf16x2(pr[2], pr[3]);
+      pb[qb][2] = cvt_bf16x2(pr[4], pr[5]);
+      pb[qb][3] = cvt_bf16x2(pr[6], pr[7]);
     }
 
-    // O^T += V^T P^T with V^T fragments from transposing reads of the key rows
+    // O^T += V^T P^T with V^T fragments from transposing reads of the key
+    // rows, read three blocks ahead of their MFMAs
+    constexpr int kMb = kMlaDv / 16;
+    u32x4_t va[4];
+    auto rd_v = [&](int mb) {
+      const uint2 lo = lds_tr16(av[0][mb & 3] + (mb >> 2) * 128);
+      const uint2 hi = lds_tr16(av[1][mb & 3] + (mb >> 2) * 128);
+      return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    };
 #pragma unroll
-    for (int mb = 0; mb < kMlaDv / 16; ++mb) {
-      const uint2 lo = lds_read_tr16(reinterpret_cast<const bf16_t*>(stg + pv_off[0][mb & 3] + (mb >> 2) * 128));
-      const uint2 hi = lds_read_tr16(reinterpret_cast<const bf16_t*>(stg + pv_off[1][mb & 3] + (mb >> 2) * 128));
-      const u32x4_t a = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    for (int mb = 0; mb < 3; ++mb) va[mb] = rd_v(mb);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][mb] = mfma16(a, pb[qb], oacc[qb][mb]);
+    for (int mb = 0; mb < kMb; ++mb) {
+      if (mb + 3 < kMb) va[(mb + 3) & 3] = rd_v(mb + 3);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][mb] = mfma16(va[mb & 3], pb[qb], oacc[qb][mb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  int any_over = 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) any_over |= over[qb] ? 1 : 0;
+  if (!__syncthreads_or(any_over)) break;
+  }   // pass
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -713,8 +811,8 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
 #pragma unroll
       for (int mb = 0; mb < kMlaDv / 16; ++mb) {
         uint2 pk;
-        pk.x = pack_bf16x2(oacc[qb][mb][0] * inv, oacc[qb][mb][1] * inv);
-        pk.y = pack_bf16x2(oacc[qb][mb][2] * inv, oacc[qb][mb][3] * inv);
+        pk.x = cvt_bf16x2(oacc[qb][mb][0] * inv, oacc[qb][mb][1] * inv);
+        pk.y = cvt_bf16x2(oacc[qb][mb][2] * inv, oacc[qb][mb][3] * inv);
         *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
       }
       if (p.lse && grp == 0)
@@ -1038,14 +1136,23 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   mp.RT = sh.RT;
   mp.n_hb = sh.n_hb;
   mp.part_cap = kPartSlots;
+  mp.log2P = -1;
+  if ((a.page_size & (a.page_size - 1)) == 0) {
+    int l2 = 0;
+    while ((1 << l2) < a.page_size) ++l2;
+    mp.log2P = l2;
+  }
   mp.scale_log2 = a.sm_scale * kLog2e;
   const int grid = L.item_cap;
 
   if (latent) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_attn_mla<kMlaQB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
+    const bool fast = mp.log2P >= 5;   // power-of-two pages of at least 32 keys
+    const void* kern = fast ? reinterpret_cast<const void*>(k_attn_mla<kMlaQB, true>)
+                            : reinterpret_cast<const void*>(k_attn_mla<kMlaQB, false>);
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_mla<kMlaQB>, dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    if (fast) hipLaunchKernelGGL((k_attn_mla<kMlaQB, true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    else hipLaunchKernelGGL((k_attn_mla<kMlaQB, false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
     e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, grid, s) : launch_main<128, 128, 4, false>(mp, grid, s);

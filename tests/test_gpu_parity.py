@@ -222,3 +222,21 @@ def test_mla_two_rows_per_tile_and_long_split():
     range is split into chunks and merged."""
     inp = pu.make_inputs("mla_bf16", B=2, Hq=64, V=500, H=256, ctx=("uniform", 3000, 5000))
     _full_parity(inp, "compact", "bf16")
+
+
+def test_mla_late_score_jump_reruns_exactly():
+    """A key late in the context whose score exceeds every earlier one by far
+    more than the kernel's fixed softmax reference allows: the workgroup must
+    rerun the item with the true maximum and still match the oracle."""
+    inp = pu.make_inputs("mla_bf16", B=2, V=400, H=128, ctx=("uniform", 600, 900))
+    pt = inp["page_table"].cpu()
+    P = inp["page_size"]
+    c0 = int(inp["ctx"][0])
+    pos = c0 - 40                         # well after the first 32-key tile
+    page = int(pt[0, pos // P])
+    q0 = inp["q_block"][0, 0, 5].float()  # request 0, block row 0, head 5
+    inp["k_cache"][page, pos % P, 0] = (2.0 * q0).to(inp["k_cache"].dtype)
+    step, ref, want = _full_parity(inp, "compact", "bf16")
+    # the planted key dominates head 5 of request 0's first row
+    lse = step.lse.cpu().numpy()
+    assert lse[0, 5] > 40.0
