@@ -153,6 +153,8 @@ def _confidences(wl, B, g, device):
         classes = wl.conf[1:]
         c = torch.empty(shape, dtype=torch.float64, device=device)
         for j, (a, b) in enumerate(classes):
+            if j >= B:
+                break
             idx = torch.arange(j, B, len(classes), device=device)
             if len(idx):
                 c[idx] = _beta(a, b, (len(idx), wl.gamma - 1), g, device)
