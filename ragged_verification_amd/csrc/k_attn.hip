@@ -465,23 +465,24 @@ __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
 
 // ---- latent (MLA-style) bf16 kernel: LDS DMA ring ---------------------------------
 //
-// One workgroup = four waves against one latent KV head; each wave owns QB
-// blocks of 16 query vectors (QB = 1: 64 query vectors per workgroup, e.g.
-// half of a 128-head row).  Keys arrive through direct global->LDS DMA
-// (global_load_lds_dwordx4) into a ring of kMlaStages 32-key stages issued
-// kMlaStages-1 tiles ahead, so no registers stage the data and the latency of
-// the next tiles hides behind the MFMA work of the current one.  The DMA is
-// issued from inline assembly because the compiler would otherwise wait for
-// every outstanding DMA before each LDS read; the kernel tracks the
-// vector-memory counter itself (loads complete in issue order).
+// One workgroup = four waves against one latent KV head and 64 query vectors
+// (e.g. half of a 128-head row).  Keys arrive through direct global->LDS DMA
+// (global_load_lds_dwordx4) into a ring of kMlaStages 32-key stages issued two
+// tiles ahead, so no registers stage the data and the latency of the next
+// tiles hides behind the MFMA work of the current one.  The DMA is issued from
+// inline assembly because the compiler would otherwise wait for every
+// outstanding DMA before each LDS read; the kernel tracks the vector-memory
+// counter itself (loads complete in issue order).
 //
 // LDS layout of a stage: 32 rows of 1152 bytes (576 bf16, no padding) whose
 // 16-byte chunks are XOR-swizzled within aligned groups of eight
 // (physical = logical ^ ((row >> 1) & 7)) so that fragment reads of sixteen
 // consecutive rows hit distinct banks.  The request's page-table entries for
-// the item's key range sit in an LDS window.  The softmax reference max moves
-// lazily (only when a tile's max exceeds it by more than 2^8), so the O
-// accumulators are rescaled only on such jumps.
+// the item's key range sit in an LDS window.  The softmax reference of each
+// query vector is fixed by the first tile; if the visible scores of the item
+// end up far above (overflow risk) or far below (underflow risk) it, the item
+// runs once more with the true maximum, so the O accumulators are never
+// rescaled.
 
 constexpr int kMlaD = 576, kMlaDv = 512;
 constexpr int kMlaRowBytes = kMlaD * 2;                    // 1152
@@ -490,9 +491,7 @@ constexpr int kMlaStages = 3;
 constexpr int kPageWin = 2048;
 constexpr int kMlaChunksPerRow = kMlaD / 8;                // 72
 constexpr int kMlaDmaPerWave = kNK * kMlaChunksPerRow / 256;  // 9 per wave per tile
-constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kPageWin * 4;
-constexpr int kMlaQB = 1;                                  // 16-vector blocks per wave
-constexpr int kMlaQT = 4 * 16 * kMlaQB;                    // query vectors per tile
+constexpr int kMlaQT = 64;                                 // query vectors per tile (2 wave pairs x 32)
 
 // DMA of 16 bytes per lane: global (64-bit address) -> LDS at m0 + 16*lane
 __device__ inline void dma16(const void* g, uint32_t lds_addr) {
@@ -525,11 +524,42 @@ __device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// FAST: page size is a power of two >= 32, so a 32-key tile lies in one page
-template <int QB, bool FAST>
+// FAST: page size is a power of two >= 32, so a 32-key tile lies in one page.
+//
+// Work split inside a workgroup (4 waves, 64 query vectors): waves 2p and
+// 2p+1 form pair p and share query vectors 32p..32p+31 (two 16-wide blocks).
+// Wave h of the pair scores keys [16h, 16h+16) of every 32-key tile over all
+// 576 head dims and turns them into probabilities; the two waves swap those
+// bf16 probabilities through LDS, and each then accumulates all 32 keys into
+// its own half of the output columns, [256h, 256h+256).  Every K and V^T
+// fragment read from LDS feeds two MFMAs, no partial scores cross waves and
+// no wave repeats another's softmax.
+//
+// Software pipeline, one barrier per 32-key tile: iteration t scores tile t+1
+// (QK), then accumulates tile t (PV) while the new scores become
+// probabilities, and publishes them; the barrier of iteration t+1 makes them
+// visible to the partner.  The DMA of tile t+2 is issued right after the
+// barrier into the stage that tile t-1 used.
+constexpr int kMlaXBytes = 2 * 4 * 2 * 64 * 8;     // probabilities [buffer][wave][block][lane], 8 B each
+constexpr int kMlaRedBytes = 2 * 4 * 2 * 16 * 4;   // column max and sum [wave][block][16]
+constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kMlaXBytes + kMlaRedBytes + kPageWin * 4;
+
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+__device__ inline uint2 lds_b64(uint32_t addr) {
+  return __builtin_bit_cast(uint2, *(const lds_u32x2_t*)(size_t)addr);
+}
+__device__ inline void lds_st_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
+  *(lds_u32x2_t*)(size_t)addr = u32x2_t{lo, hi};
+}
+
+template <bool FAST>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  int* pwin = reinterpret_cast<int*>(smem + kMlaStages * kMlaStageBytes);
+  constexpr int kRing = kMlaStages * kMlaStageBytes;
+  float* red_m = reinterpret_cast<float*>(smem + kRing + kMlaXBytes);
+  float* red_l = red_m + 4 * 2 * 16;
+  int* pwin = reinterpret_cast<int*>(smem + kRing + kMlaXBytes + kMlaRedBytes);
 
   const int n_items = p.hdr[0];
   const int per_xcd = (n_items + 7) / 8;
@@ -540,6 +570,8 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wid >> 1;
+  const int half = wid & 1;
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -574,13 +606,13 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
     pwin[x] = pg;
   }
 
-  // query fragments (B operand of S^T = K Q^T)
-  int q_row[QB], head[QB], lim[QB];
-  bool q_valid[QB];
-  u32x4_t qf[QB][kMlaD / 32];
+  // query fragments: both 16-vector blocks of the pair, all 576 dims
+  int q_row[2], head[2], lim[2];
+  bool q_valid[2];
+  u32x4_t qf[2][18];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qv = (wid * QB + qb) * 16 + n16;
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qv = pair * 32 + qb * 16 + n16;
     const int rl = qv / p.NH;
     head[qb] = hb * p.NH + (qv % p.NH);
     q_valid[qb] = rl < rows_here;
@@ -588,35 +620,22 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
     lim[qb] = min(c + row0 + rl, kv_end - 1);   // last key this vector may see here
     const bf16_t* qsrc = p.q + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaD + grp * 8;
 #pragma unroll
-    for (int ks = 0; ks < kMlaD / 32; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
+    for (int ks = 0; ks < 18; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
   }
   // tiles ending at or before this key need no mask for any valid vector
   const int full_lim = min(c + row0, kv_end - 1);
   wait_vm<0>();
   __syncthreads();   // page window visible
 
-  f32x4_t oacc[QB][kMlaDv / 16];
-  float m_run[QB], l_part[QB], m_seen[QB];
-  bool over[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) { m_run[qb] = -INFINITY; m_seen[qb] = -INFINITY; }
-
   const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
-  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)smem + wid * kMlaDmaPerWave * 1024);
+  const uint32_t xbase = smem_lds + kRing;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wid * kMlaDmaPerWave * 1024);
 
-  // this lane's DMA chunks (tile independent): wave wid issues chunks
-  // (wid*9 + e)*64 + lane; chunk c lands at row c/72, physical position c%72
-  // and holds logical chunk (c%72) ^ swz(row)
-  int drow[kMlaDmaPerWave];
-  uint32_t dlog[kMlaDmaPerWave];
-#pragma unroll
-  for (int e = 0; e < kMlaDmaPerWave; ++e) {
-    const int cidx = (wid * kMlaDmaPerWave + e) * 64 + lane;
-    drow[e] = cidx / kMlaChunksPerRow;
-    dlog[e] = (uint32_t)(((cidx % kMlaChunksPerRow) ^ swz(drow[e])) * 16);
-  }
+  // DMA chunks: wave wid issues chunks (wid*9 + e)*64 + lane of a tile; chunk
+  // c lands at row c/72, physical position c%72 and holds logical chunk
+  // (c%72) ^ swz(row)
+  const int cbase = wid * kMlaDmaPerWave * 64 + lane;
   const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
 
   auto issue = [&](int t, int st) {
@@ -628,205 +647,268 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
                                      (size_t)pg * P * kMlaRowBytes);
 #pragma unroll
       for (int e = 0; e < kMlaDmaPerWave; ++e) {
-        const int j = min(t0 + drow[e], last);
-        dma16_s((uint32_t)(j & (P - 1)) * kMlaRowBytes + dlog[e], base, lds0 + e * 1024);
+        const int cidx = cbase + e * 64;
+        const int row = cidx / kMlaChunksPerRow;
+        const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
+        const int j = min(t0 + row, last);
+        dma16_s((uint32_t)(j & (P - 1)) * kMlaRowBytes + lg, base, lds0 + e * 1024);
       }
     } else {
 #pragma unroll
       for (int e = 0; e < kMlaDmaPerWave; ++e) {
-        const int j = min(t0 + drow[e], last);
+        const int cidx = cbase + e * 64;
+        const int row = cidx / kMlaChunksPerRow;
+        const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
+        const int j = min(t0 + row, last);
         const int pg = pwin[min(j / P - pg0, npg - 1)];
         const unsigned char* g = reinterpret_cast<const unsigned char*>(p.k) +
-                                 ((size_t)pg * P + (j % P)) * kMlaRowBytes + dlog[e];
+                                 ((size_t)pg * P + (j % P)) * kMlaRowBytes + lg;
         dma16(g, lds0 + e * 1024);
       }
     }
   };
 
   // per-lane LDS byte offsets of the fragment reads (swizzle precomputed)
-  // QK: A rows 16*mb + n16, logical chunk 4*ks + grp; pattern repeats every 2 ks
-  int qk_off[2][2];
+  // QK: A rows 16*half + n16 (this wave's keys), logical chunk 4*ks + grp; the
+  // swizzle only touches the low three chunk bits, so the pattern repeats every 2 ks
+  int qk_off[2];
+  {
+    const int r = half * 16 + n16;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int r = mb * 16 + n16;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) qk_off[mb][kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ swz(r)) * 16;
+    for (int kk = 0; kk < 2; ++kk) qk_off[kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ swz(r)) * 16;
   }
   // PV (transposing reads): rows kb + n16/4 (kb = 4*grp or 16 + 4*grp), elements
-  // 16*mb + 4*(n16 & 3): logical chunk 2*mb + ((n16 & 3) >> 1), half (n16 & 1);
+  // 256*half + 16*mb + 4*(n16 & 3): logical chunk 32*half + 2*mb + ((n16 & 3) >> 1);
   // the pattern repeats every 4 mb (one aligned group of 8 chunks = 128 bytes)
   int pv_off[2][4];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int r = h * 16 + grp * 4 + (n16 >> 2);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = hh * 16 + grp * 4 + (n16 >> 2);
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
-      const int lc = 2 * mm + ((n16 & 3) >> 1);
-      pv_off[h][mm] = r * kMlaRowBytes + (lc ^ swz(r)) * 16 + (n16 & 1) * 8;
+      const int lc = 32 * half + 2 * mm + ((n16 & 3) >> 1);
+      pv_off[hh][mm] = r * kMlaRowBytes + (lc ^ swz(r)) * 16 + (n16 & 1) * 8;
     }
   }
+  // probability exchange: buffer b, wave wv, block qb, 8 bytes per lane
+  auto xaddr = [&](int b, int wv, int qb) {
+    return xbase + (uint32_t)((((b * 4 + wv) * 2 + qb) * 64 + lane) * 8);
+  };
 
-  // Softmax reference: the first tile's max fixes each vector's reference
-  // m_ref; later probabilities may exceed 1 by up to 2^kSlack, which fp32
-  // accumulation and bf16 P absorb.  A tile exceeding that marks the vector;
-  // the workgroup then reruns the item once with the true maximum as the
-  // reference.  The O accumulators are therefore only ever zeroed and
-  // MFMA-accumulated, never rescaled in registers.
-  constexpr float kSlack = 32.f;
+  // S^T of this wave's 16 keys x 32 vectors for the tile in stage `stg`
+  auto qk_tile = [&](uint32_t stg, f32x4_t (&sc)[2]) {
+    sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const uint32_t a0 = stg + qk_off[0], a1 = stg + qk_off[1];
+    u32x4_t fa[4];
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) fa[ks] = lds_b128(((ks & 1) ? a1 : a0) + (ks >> 1) * 128);
+#pragma unroll
+    for (int ks = 0; ks < 18; ++ks) {
+      if (ks + 3 < 18) {
+        const int kn = ks + 3;
+        fa[kn & 3] = lds_b128(((kn & 1) ? a1 : a0) + (kn >> 1) * 128);
+      }
+      sc[0] = mfma16(fa[ks & 3], qf[0][ks], sc[0]);
+      sc[1] = mfma16(fa[ks & 3], qf[1][ks], sc[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // own keys of this lane within a tile: 16*half + 4*grp + j; their
+  // probabilities fill k-slots 8*grp + 4*half + j of the PV B operand
+  const int key_lane = half * 16 + grp * 4;
+  f32x4_t oacc[2][16];
+  float m_ref[2] = {0.f, 0.f}, l_part[2], m_seen[2];
+  float l_all[2] = {0.f, 0.f};
+
+  // Softmax reference: each query vector's reference m_ref is the max of the
+  // first tile's scaled scores (whole tile, both waves, mask ignored).
+  // Probabilities are exp2(score - m_ref), so the O accumulators are never
+  // rescaled.  After a pass the true max of the visible scores is known; if it
+  // lies more than 2^32 above the reference (overflow risk) or more than 2^64
+  // below it (underflow risk) the item runs once more with the true max.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-    for (int mb = 0; mb < kMlaDv / 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    l_part[qb] = 0.f;
-    over[qb] = false;
-    if (pass == 1) m_run[qb] = m_seen[qb];
-  }
-#pragma unroll
-  for (int t = 0; t < kMlaStages - 1; ++t)
-    if (t < n_tiles) issue(t, t);
-
-  int st_cur = 0;                    // stage of tile t
-  for (int t = 0; t < n_tiles; ++t) {
-    // tile t must have landed; tiles up to t + kMlaStages - 2 may stay in flight
-    if (t + 1 < n_tiles) wait_vm<kMlaDmaPerWave * (kMlaStages - 2)>(); else wait_vm<0>();
-    __syncthreads();
-    if (t + kMlaStages - 1 < n_tiles) issue(t + kMlaStages - 1, (t + kMlaStages - 1) % kMlaStages);
-
-    // stage base (wave uniform) plus the per-lane offsets: 12 addresses per
-    // tile; the remaining constants fold into the LDS instructions' offsets
-    const uint32_t stg = __builtin_amdgcn_readfirstlane(smem_lds + st_cur * kMlaStageBytes);
-    st_cur = (st_cur == kMlaStages - 1) ? 0 : st_cur + 1;
-    uint32_t aq[2][2], av[2][4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) aq[mb][kk] = stg + qk_off[mb][kk];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) av[h][mm] = stg + pv_off[h][mm];
-    const int t0 = kv_begin + t * kNK;
-    const bool full = (t0 + kNK - 1 <= full_lim);   // wave uniform
-
-    // S^T = K Q^T; K fragments are read two steps ahead of their MFMAs
-    // (scheduling barriers keep that order) so LDS latency overlaps MFMA work
-    f32x4_t sacc[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    constexpr int kKs = kMlaD / 32;
-    u32x4_t fa[3][2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) fa[ks][mb] = lds_b128(aq[mb][ks & 1] + (ks >> 1) * 128);
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      if (ks + 2 < kKs) {
-        const int kn = ks + 2;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) fa[kn % 3][mb] = lds_b128(aq[mb][kn & 1] + (kn >> 1) * 128);
-      }
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][mb] = mfma16(fa[ks % 3][mb], qf[qb][ks], sacc[qb][mb]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int mb = 0; mb < 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      l_part[qb] = 0.f;
+      m_seen[qb] = -INFINITY;
     }
+    uint32_t po[2][2];   // this wave's probabilities of the tile being accumulated
 
-    u32x4_t pb[QB];
+    // scaled scores -> probabilities, one 16-vector block (4 keys per lane)
+    auto soft = [&](const f32x4_t& sc, int qb, int t0, bool full, uint32_t (&out)[2]) {
+      float v[4];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float sv[8];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sv[mb * 4 + j] = sacc[qb][mb][j] * p.scale_log2;
+      for (int j = 0; j < 4; ++j) v[j] = sc[j] * p.scale_log2;
       if (!full) {   // tail tile: keys past this vector's limit get probability 0
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (t0 + mb * 16 + grp * 4 + j > lim[qb]) sv[mb * 4 + j] = -INFINITY;
+        for (int j = 0; j < 4; ++j)
+          if (t0 + key_lane + j > lim[qb]) v[j] = -INFINITY;
       }
-      float tmax = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      m_seen[qb] = fmaxf(m_seen[qb], tmax);
-      if (m_run[qb] == -INFINITY) m_run[qb] = tmax;          // first tile with a visible key
-      over[qb] = over[qb] || (tmax > m_run[qb] + kSlack);
-      const float m_ref = (m_run[qb] == -INFINITY) ? 0.f : m_run[qb];
-      float pr[8];
-      float psum = 0.f;
+      m_seen[qb] = fmaxf(m_seen[qb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+      float e[4];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        pr[x] = __builtin_amdgcn_exp2f(sv[x] - m_ref);   // exp2(-inf) = 0
-        psum += pr[x];
+      for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_exp2f(v[j] - m_ref[qb]);   // exp2(-inf) = 0
+      l_part[qb] += (e[0] + e[1]) + (e[2] + e[3]);
+      out[0] = cvt_bf16x2(e[0], e[1]);
+      out[1] = cvt_bf16x2(e[2], e[3]);
+    };
+
+    if (n_tiles > 0) {
+      // prologue: tiles 0 and 1 in flight, probabilities of tile 0 published
+      issue(0, 0);
+      if (n_tiles > 1) issue(1, 1);
+      if (n_tiles > 1) wait_vm<kMlaDmaPerWave>(); else wait_vm<0>();
+      __syncthreads();
+      f32x4_t sc[2];
+      qk_tile(smem_lds, sc);
+      if (pass == 0) {
+        float mx[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          mx[qb] = fmaxf(fmaxf(sc[qb][0], sc[qb][1]), fmaxf(sc[qb][2], sc[qb][3])) * p.scale_log2;
+          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 16));
+          mx[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32));
+          if (grp == 0) red_m[(wid * 2 + qb) * 16 + n16] = mx[qb];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) m_ref[qb] = fmaxf(mx[qb], red_m[((wid ^ 1) * 2 + qb) * 16 + n16]);
       }
-      l_part[qb] += psum;
-      // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
-      pb[qb][0] = cvt_bf16x2(pr[0], pr[1]);
-      pb[qb][1] = cvt_bf16x2(pr[2], pr[3]);
-      pb[qb][2] = cvt_bf16x2(pr[4], pr[5]);
-      pb[qb][3] = cvt_bf16x2(pr[6], pr[7]);
+      const bool full0 = (kv_begin + kNK - 1 <= full_lim);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        soft(sc[qb], qb, kv_begin, full0, po[qb]);
+        lds_st_b64(xaddr(0, wid, qb), po[qb][0], po[qb][1]);
+      }
     }
 
-    // O^T += V^T P^T with V^T fragments from transposing reads of the key
-    // rows, read three blocks ahead of their MFMAs
-    constexpr int kMb = kMlaDv / 16;
-    u32x4_t va[4];
-    auto rd_v = [&](int mb) {
-      const uint2 lo = lds_tr16(av[0][mb & 3] + (mb >> 2) * 128);
-      const uint2 hi = lds_tr16(av[1][mb & 3] + (mb >> 2) * 128);
-      return u32x4_t{lo.x, lo.y, hi.x, hi.y};
-    };
+    int st_cur = 0;                    // stage of tile t
+    for (int t = 0; t < n_tiles; ++t) {
+      // tile t+1 (next QK) must have landed; it is the only DMA in flight
+      wait_vm<0>();
+      __syncthreads();
+      if (t + 2 < n_tiles) issue(t + 2, (t + 2) % kMlaStages);
+
+      // the partner's probabilities of tile t
+      uint2 pp[2];
 #pragma unroll
-    for (int mb = 0; mb < 3; ++mb) va[mb] = rd_v(mb);
+      for (int qb = 0; qb < 2; ++qb) pp[qb] = lds_b64(xaddr(t & 1, wid ^ 1, qb));
+
+      const uint32_t stg = smem_lds + st_cur * kMlaStageBytes;
+      st_cur = (st_cur == kMlaStages - 1) ? 0 : st_cur + 1;
+      const uint32_t stg_next = smem_lds + st_cur * kMlaStageBytes;
+      const bool more = t + 1 < n_tiles;   // uniform
+      const int t0n = kv_begin + (t + 1) * kNK;
+      const bool full_n = (t0n + kNK - 1 <= full_lim);
+
+      f32x4_t sc[2];
+      if (more) qk_tile(stg_next, sc);
+
+      u32x4_t pb[2];
 #pragma unroll
-    for (int mb = 0; mb < kMb; ++mb) {
-      if (mb + 3 < kMb) va[(mb + 3) & 3] = rd_v(mb + 3);
+      for (int qb = 0; qb < 2; ++qb)
+        pb[qb] = half ? u32x4_t{pp[qb].x, pp[qb].y, po[qb][0], po[qb][1]}
+                      : u32x4_t{po[qb][0], po[qb][1], pp[qb].x, pp[qb].y};
+
+      // O^T[256 half columns] += V^T P^T; each transposed V fragment feeds both
+      // blocks.  The next tile's softmax is spread over the first iterations so
+      // that its VALU work runs under the MFMAs.
+      uint32_t pn[2][2];
+      {
+        uint32_t av[2][4];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][mb] = mfma16(va[mb & 3], pb[qb], oacc[qb][mb]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int mm = 0; mm < 4; ++mm) av[hh][mm] = stg + pv_off[hh][mm];
+        u32x4_t va[4];
+        auto rd_v = [&](int mb) {
+          const uint2 lo = lds_tr16(av[0][mb & 3] + (mb >> 2) * 128);
+          const uint2 hi = lds_tr16(av[1][mb & 3] + (mb >> 2) * 128);
+          return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        };
+#pragma unroll
+        for (int mb = 0; mb < 3; ++mb) va[mb] = rd_v(mb);
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb) {
+          if (mb + 3 < 16) va[(mb + 3) & 3] = rd_v(mb + 3);
+          oacc[0][mb] = mfma16(va[mb & 3], pb[0], oacc[0][mb]);
+          oacc[1][mb] = mfma16(va[mb & 3], pb[1], oacc[1][mb]);
+          if (more && (mb == 2 || mb == 6)) soft(sc[mb >> 2], mb >> 2, t0n, full_n, pn[mb >> 2]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          po[qb][0] = pn[qb][0];
+          po[qb][1] = pn[qb][1];
+          lds_st_b64(xaddr((t + 1) & 1, wid, qb), pn[qb][0], pn[qb][1]);
+        }
+      }
     }
-  }
-  int any_over = 0;
+
+    // column max of the visible scores and column sums, over the lane groups
+    // and then over the pair
+    float mcol[2], lcol[2];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) any_over |= over[qb] ? 1 : 0;
-  if (!__syncthreads_or(any_over)) break;
+    for (int qb = 0; qb < 2; ++qb) {
+      mcol[qb] = fmaxf(m_seen[qb], __shfl_xor(m_seen[qb], 16));
+      mcol[qb] = fmaxf(mcol[qb], __shfl_xor(mcol[qb], 32));
+      lcol[qb] = l_part[qb] + __shfl_xor(l_part[qb], 16);
+      lcol[qb] += __shfl_xor(lcol[qb], 32);
+      if (grp == 0) {
+        red_m[(wid * 2 + qb) * 16 + n16] = mcol[qb];
+        red_l[(wid * 2 + qb) * 16 + n16] = lcol[qb];
+      }
+    }
+    __syncthreads();
+    int need = 0;
+    float m_all[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      m_all[qb] = fmaxf(mcol[qb], red_m[((wid ^ 1) * 2 + qb) * 16 + n16]);
+      l_all[qb] = lcol[qb] + red_l[((wid ^ 1) * 2 + qb) * 16 + n16];
+      if (pass == 0 && q_valid[qb] && m_all[qb] > -INFINITY &&
+          (m_all[qb] > m_ref[qb] + 32.f || m_all[qb] < m_ref[qb] - 64.f))
+        need = 1;
+    }
+    if (!__syncthreads_or(need)) break;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      if (m_all[qb] > -INFINITY) m_ref[qb] = m_all[qb];
   }   // pass
 
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float l_tot = l_part[qb] + __shfl_xor(l_part[qb], 16);
-    l_tot += __shfl_xor(l_tot, 32);
+  for (int qb = 0; qb < 2; ++qb) {
     if (!q_valid[qb]) continue;
-    const int qv = (wid * QB + qb) * 16 + n16;
+    const float l_tot = l_all[qb];
+    const int qv = pair * 32 + qb * 16 + n16;
     if (ns == 1) {
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16_t* dst = p.o + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaDv;
+      bf16_t* dst = p.o + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaDv + half * 256;
 #pragma unroll
-      for (int mb = 0; mb < kMlaDv / 16; ++mb) {
+      for (int mb = 0; mb < 16; ++mb) {
         uint2 pk;
         pk.x = cvt_bf16x2(oacc[qb][mb][0] * inv, oacc[qb][mb][1] * inv);
         pk.y = cvt_bf16x2(oacc[qb][mb][2] * inv, oacc[qb][mb][3] * inv);
         *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
       }
-      if (p.lse && grp == 0)
-        p.lse[(size_t)q_row[qb] * p.Hq + head[qb]] = l_tot > 0.f ? (m_run[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
+      if (p.lse && grp == 0 && half == 0)
+        p.lse[(size_t)q_row[qb] * p.Hq + head[qb]] = l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
       const int slot = info.z + sp * info.w + tile;
       if (slot < 0 || slot >= p.part_cap) continue;
-      float* po = p.part_o + ((size_t)slot * kMlaQT + qv) * kMlaDv;
+      float* po_ = p.part_o + ((size_t)slot * kMlaQT + qv) * kMlaDv + half * 256;
 #pragma unroll
-      for (int mb = 0; mb < kMlaDv / 16; ++mb)
-        *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[qb][mb];
-      if (grp == 0) {
+      for (int mb = 0; mb < 16; ++mb)
+        *reinterpret_cast<f32x4_t*>(po_ + mb * 16 + grp * 4) = oacc[qb][mb];
+      if (grp == 0 && half == 0) {
         float* pml = p.part_ml + ((size_t)slot * kMlaQT + qv) * 2;
-        pml[0] = m_run[qb];
+        pml[0] = l_tot > 0.f ? m_ref[qb] : -INFINITY;
         pml[1] = l_tot;
       }
     }
@@ -984,7 +1066,7 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
   const int G = Hq / Hkv;
   if (latent) {
     if (!(Dqk == 576 && Dv == 512 && Hkv == 1 && Hq % 64 == 0)) return false;
-    *nw = 4 * kMlaQB;   // DMA-ring kernel: 4 waves x 16*kMlaQB query vectors per tile
+    *nw = kMlaQT / 16;   // DMA-ring kernel: 64 query vectors per tile
   } else {
     if (!(Dqk == 128 && Dv == 128)) return false;
     if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return false;
@@ -1147,12 +1229,12 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
 
   if (latent) {
     const bool fast = mp.log2P >= 5;   // power-of-two pages of at least 32 keys
-    const void* kern = fast ? reinterpret_cast<const void*>(k_attn_mla<kMlaQB, true>)
-                            : reinterpret_cast<const void*>(k_attn_mla<kMlaQB, false>);
+    const void* kern = fast ? reinterpret_cast<const void*>(k_attn_mla<true>)
+                            : reinterpret_cast<const void*>(k_attn_mla<false>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
     if (e != hipSuccess) return e;
-    if (fast) hipLaunchKernelGGL((k_attn_mla<kMlaQB, true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
-    else hipLaunchKernelGGL((k_attn_mla<kMlaQB, false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    if (fast) hipLaunchKernelGGL((k_attn_mla<true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
     e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, grid, s) : launch_main<128, 128, 4, false>(mp, grid, s);
