@@ -204,6 +204,20 @@ def cpu_baseline(inp, step, n_req=24):
             "seconds": dt}
 
 
+def copy_calibration(mib):
+    """A plain device copy of known size (reads and writes ``mib`` MiB per
+    launch): profiled under the same counters as the verify kernels, it gives
+    the factor between FETCH_SIZE / WRITE_SIZE and bytes actually moved."""
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 2, "copy_calibration_bytes_written": n * 2,
+                      "launches": 5}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +226,8 @@ def main():
     ap.add_argument("--workload", default="mla_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain elementwise copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -220,6 +236,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     rv.load()
     wl = synth.workload(args.workload)
     t0 = time.time()

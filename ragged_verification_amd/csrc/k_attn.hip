@@ -29,6 +29,9 @@
 
 #include <float.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "rv_common.h"
 
 namespace rv {
@@ -47,13 +50,19 @@ struct AttnShape {
   int tpr_max;           // tiles per request at most
 };
 
+// Work header written by the plan: [0] items, [1] chunk, [2] partial slots
+// used, [8 + x] / [16 + x] start and length of XCD x's item list, [24 + x]
+// that list's take counter (zeroed by the plan, advanced by the workers).
+constexpr int kHdrXOff = 8, kHdrXLen = 16, kHdrCtr = 24;
+
 struct PlanParams {
   const int32_t* cu;
   const int32_t* ctx;
   const int32_t* mm;
-  int4* req_info;        // per request: {n_splits, item_off, part_off, tiles}
-  int4* items;           // {request, tile, split, 0}
-  int32_t* hdr;          // [0] n_items, [1] chunk, [2] part slots used
+  int4* req_info;        // per request: {n_splits, first group, part_off, tiles}
+  int4* items;           // {request, tile, split, 0}, grouped by XCD list
+  int2* grp;             // scratch: {request, split} of each group by rank
+  int32_t* hdr;
   int B, gamma, item_cap, part_cap, target;
   AttnShape sh;
 };
@@ -119,10 +128,17 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
   }
   const int C = s_chunk;
 
-  // per-request offsets (requests strided over threads, two-level scan)
+  // A group is the set of tiles of one request that read one key chunk; its
+  // tiles run on one XCD, one after another in that XCD's list, so the chunk
+  // is fetched into that XCD's L2 once.  Groups are ranked longest chunk
+  // first (counting sort over 64 length buckets) and dealt to the 8 lists in
+  // snake order (ranks 8c..8c+7 go to XCDs 0..7 for even c, 7..0 for odd c),
+  // which balances the lists and starts the longest items first.
+  __shared__ int hist[64];
+  if (t < 64) hist[t] = 0;
   const int seg = ceil_div(B, 1024);
   const int i0 = t * seg;
-  int my_items = 0, my_parts = 0;
+  int my_groups = 0, my_parts = 0;
   for (int s = 0; s < seg; ++s) {
     const int i = i0 + s;
     if (i >= B) break;
@@ -130,10 +146,10 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
     const int L = p.ctx[i] + w;
     const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
     const int ns = L > 0 ? ceil_div(L, C) : 1;
-    my_items += ns * tiles;
+    my_groups += ns;
     my_parts += ns > 1 ? ns * tiles : 0;
   }
-  scan_a[t] = my_items;
+  scan_a[t] = my_groups;
   scan_b[t] = my_parts;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -144,8 +160,29 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
     scan_b[t] += b;
     __syncthreads();
   }
-  int item_off = scan_a[t] - my_items;
+  const int n_groups = scan_a[1023];
+  const int n_parts = scan_b[1023];
+  int grp_off = scan_a[t] - my_groups;
   int part_off = scan_b[t] - my_parts;
+  // bucket of a chunk of `len` keys: 0 for a full chunk, up to 63 for the shortest
+  auto bucket = [&](int len) { return (int)(((long long)(C - len) * 64) / C); };
+  for (int s = 0; s < seg; ++s) {
+    const int i = i0 + s;
+    if (i >= B) break;
+    const int L = p.ctx[i] + p.cu[i + 1] - p.cu[i];
+    const int ns = L > 0 ? ceil_div(L, C) : 1;
+    for (int sp = 0; sp < ns; ++sp) atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int b = 0; b < 64; ++b) {
+      const int n = hist[b];
+      hist[b] = run;
+      run += n;
+    }
+  }
+  __syncthreads();
   for (int s = 0; s < seg; ++s) {
     const int i = i0 + s;
     if (i >= B) break;
@@ -153,16 +190,77 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
     const int L = p.ctx[i] + w;
     const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
     const int ns = L > 0 ? ceil_div(L, C) : 1;
-    p.req_info[i] = make_int4(ns, item_off, ns > 1 ? part_off : -1, tiles);
-    for (int sp = 0; sp < ns; ++sp)
-      for (int tl = 0; tl < tiles; ++tl) p.items[item_off + sp * tiles + tl] = make_int4(i, tl, sp, 0);
-    item_off += ns * tiles;
+    p.req_info[i] = make_int4(ns, grp_off, ns > 1 ? part_off : -1, tiles);
+    for (int sp = 0; sp < ns; ++sp) {
+      const int rank = atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
+      p.grp[rank] = make_int2(i, sp);
+    }
+    grp_off += ns;
     part_off += ns > 1 ? ns * tiles : 0;
   }
-  if (t == 1023) {
-    p.hdr[0] = scan_a[1023];
+  __syncthreads();   // the ranked groups are visible to the whole workgroup
+
+  // items per (cycle, XCD) slot, scanned along the cycles of each XCD
+  __shared__ int xs[1024][8];
+  const int nc = ceil_div(n_groups, 8);
+  const int segc = ceil_div(nc, 1024);
+  auto rank_of = [](int c, int x) { return 8 * c + ((c & 1) ? 7 - x : x); };
+  auto tiles_of = [&](int i) { return ceil_div(p.cu[i + 1] - p.cu[i], sh.RT) * sh.Hkv * sh.n_hb; };
+  int cnt[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) cnt[x] = 0;
+  for (int cc = 0; cc < segc; ++cc) {
+    const int c = t * segc + cc;
+    if (c >= nc) break;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int r = rank_of(c, x);
+      if (r < n_groups) cnt[x] += tiles_of(p.grp[r].x);
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 8; ++x) xs[t][x] = cnt[x];
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int a[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) a[x] = t >= off ? xs[t - off][x] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) xs[t][x] += a[x];
+    __syncthreads();
+  }
+  int xoff[8], pos[8];
+  int total = 0;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    xoff[x] = total;
+    total += xs[1023][x];
+    pos[x] = xoff[x] + xs[t][x] - cnt[x];
+  }
+  for (int cc = 0; cc < segc; ++cc) {
+    const int c = t * segc + cc;
+    if (c >= nc) break;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int r = rank_of(c, x);
+      if (r >= n_groups) continue;
+      const int2 g = p.grp[r];
+      const int tiles = tiles_of(g.x);
+      for (int tl = 0; tl < tiles; ++tl) p.items[pos[x] + tl] = make_int4(g.x, tl, g.y, 0);
+      pos[x] += tiles;
+    }
+  }
+  if (t == 0) {
+    p.hdr[0] = total;
     p.hdr[1] = C;
-    p.hdr[2] = scan_b[1023];
+    p.hdr[2] = n_parts;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      p.hdr[kHdrXOff + x] = xoff[x];
+      p.hdr[kHdrXLen + x] = xs[1023][x];
+      p.hdr[kHdrCtr + x] = 0;
+    }
   }
 }
 
@@ -177,6 +275,7 @@ struct MainParams {
   const int4* req_info;
   const int4* items;
   const int32_t* hdr;
+  int32_t* ctr;           // hdr + kHdrCtr: per-XCD take counters
   bf16_t* o;
   float* lse;
   float* part_o;          // [part_cap][QT][DV]
@@ -222,22 +321,50 @@ __device__ inline uint2 lds_tr16(uint32_t addr) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Persistent workers: the hardware places workgroup b on XCD b % 8.  A
+// workgroup takes the next item of its XCD's list (longest first) and, once
+// that list is empty, of the other lists; it returns -1 when all are empty,
+// so every workgroup ends after at most one failed take per list.
+__device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done) {
+  __syncthreads();   // every thread has read the previous item
+  if (threadIdx.x == 0) {
+    const int x = blockIdx.x & 7;
+    int it = -1;
+    for (int probe = 0; probe < 8 && it < 0; ++probe) {
+      const int y = (x + probe) & 7;
+      if (done & (1u << y)) continue;
+      const int k = atomicAdd(p.ctr + y, 1);
+      if (k < p.hdr[kHdrXLen + y]) it = p.hdr[kHdrXOff + y] + k;
+      else done |= 1u << y;
+    }
+    *s_item = it;
+  }
+  __syncthreads();
+  return *s_item;
+}
+
+template <int DQK, int DV, int NW, bool LATENT>
+__device__ __forceinline__ void attn_mfma_item(const MainParams& p, int item, unsigned char* smem);
+
 template <int DQK, int DV, int NW, bool LATENT>
 __global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
-  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_item;
+  unsigned done = 0;
+  for (;;) {
+    const int item = next_item(p, &s_item, done);
+    if (item < 0) break;
+    attn_mfma_item<DQK, DV, NW, LATENT>(p, item, smem);
+  }
+}
+
+template <int DQK, int DV, int NW, bool LATENT>
+__device__ __forceinline__ void attn_mfma_item(const MainParams& p, int item, unsigned char* smem) {
+  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
   bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
   // the value rows: the latent layout reuses the key rows' first DV entries
   bf16_t* Vs = LATENT ? Ks : Ks + kNK * Cfg::kKStride;
   constexpr int kVs = LATENT ? Cfg::kKStride : Cfg::kVStride;
-
-  // XCD-aware order: hardware places workgroup b on XCD b % 8; give each XCD
-  // a contiguous run of items so tiles sharing a KV chunk share its L2.
-  const int n_items = p.hdr[0];
-  const int per_xcd = (n_items + 7) / 8;
-  const int k_local = blockIdx.x / 8;
-  const int item = (blockIdx.x % 8) * per_xcd + k_local;
-  if (k_local >= per_xcd || item >= n_items) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -554,18 +681,26 @@ __device__ inline void lds_st_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
 }
 
 template <bool FAST>
+__device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, unsigned char* smem);
+
+template <bool FAST>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_item;
+  unsigned done = 0;
+  for (;;) {
+    const int item = next_item(p, &s_item, done);
+    if (item < 0) break;
+    attn_mla_item<FAST>(p, item, smem);
+  }
+}
+
+template <bool FAST>
+__device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, unsigned char* smem) {
   constexpr int kRing = kMlaStages * kMlaStageBytes;
   float* red_m = reinterpret_cast<float*>(smem + kRing + kMlaXBytes);
   float* red_l = red_m + 4 * 2 * 16;
   int* pwin = reinterpret_cast<int*>(smem + kRing + kMlaXBytes + kMlaRedBytes);
-
-  const int n_items = p.hdr[0];
-  const int per_xcd = (n_items + 7) / 8;
-  const int k_local = blockIdx.x / 8;
-  const int item = (blockIdx.x % 8) * per_xcd + k_local;
-  if (k_local >= per_xcd || item >= n_items) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1085,7 +1220,7 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
 }
 
 struct AttnScratch {
-  size_t hdr, req_info, items, part_ml, part_o, total;
+  size_t hdr, req_info, items, grp, part_ml, part_o, total;
   int item_cap;
 };
 
@@ -1096,19 +1231,48 @@ AttnScratch attn_layout(int B, const AttnShape& sh, int Dv) {
   L.hdr = off; off = align_up(off + 256, 256);
   L.req_info = off; off = align_up(off + sizeof(int4) * (size_t)B, 256);
   L.items = off; off = align_up(off + sizeof(int4) * (size_t)L.item_cap, 256);
+  L.grp = off; off = align_up(off + sizeof(int2) * (size_t)L.item_cap, 256);
   L.part_ml = off; off = align_up(off + sizeof(float) * 2 * (size_t)kPartSlots * sh.QT, 256);
   L.part_o = off; off = align_up(off + sizeof(float) * (size_t)kPartSlots * sh.QT * Dv, 256);
   L.total = off;
   return L;
 }
 
+// Workgroups that fit on the device at once (the persistent grid), rounded up
+// to whole rounds of the 8 XCDs; cached per device and kernel.
+hipError_t persistent_grid(const void* kern, int threads, int lds, int* grid) {
+  struct Entry { const void* kern; int dev, grid; };
+  static std::mutex mu;
+  static Entry cache[32];
+  static int n_cache = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (int j = 0; j < n_cache; ++j)
+      if (cache[j].kern == kern && cache[j].dev == dev) { *grid = cache[j].grid; return hipSuccess; }
+  }
+  int cus = 0, occ = 0;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kern, threads, lds)) != hipSuccess) return e;
+  const int g = ((std::max(cus, 1) * std::max(occ, 1) + 7) / 8) * 8;
+  std::lock_guard<std::mutex> lk(mu);
+  if (n_cache < 32) cache[n_cache++] = Entry{kern, dev, g};
+  *grid = g;
+  return hipSuccess;
+}
+
 template <int DQK, int DV, int NW, bool LATENT>
-hipError_t launch_main(const MainParams& mp, int grid, hipStream_t s) {
+hipError_t launch_main(const MainParams& mp, hipStream_t s) {
   using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
   auto kern = k_attn_mfma<DQK, DV, NW, LATENT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
   if (e != hipSuccess) return e;
+  int grid = 0;
+  if ((e = persistent_grid(reinterpret_cast<const void*>(kern), Cfg::kThreads, Cfg::kLdsBytes, &grid)) != hipSuccess)
+    return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::kThreads), Cfg::kLdsBytes, s, mp);
   return hipGetLastError();
 }
@@ -1184,6 +1348,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.req_info = reinterpret_cast<int4*>(base + L.req_info);
   pp.items = reinterpret_cast<int4*>(base + L.items);
   pp.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
+  pp.grp = reinterpret_cast<int2*>(base + L.grp);
   pp.B = a.B;
   pp.gamma = a.gamma;
   pp.item_cap = L.item_cap;
@@ -1225,7 +1390,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     mp.log2P = l2;
   }
   mp.scale_log2 = a.sm_scale * kLog2e;
-  const int grid = L.item_cap;
+  mp.ctr = pp.hdr + kHdrCtr;
 
   if (latent) {
     const bool fast = mp.log2P >= 5;   // power-of-two pages of at least 32 keys
@@ -1233,11 +1398,13 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
                             : reinterpret_cast<const void*>(k_attn_mla<false>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
     if (e != hipSuccess) return e;
+    int grid = 0;
+    if ((e = persistent_grid(kern, 256, kMlaLdsBytes, &grid)) != hipSuccess) return e;
     if (fast) hipLaunchKernelGGL((k_attn_mla<true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
-    e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, grid, s) : launch_main<128, 128, 4, false>(mp, grid, s);
+    e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, s) : launch_main<128, 128, 4, false>(mp, s);
   }
   if (e != hipSuccess) return e;
 

@@ -218,8 +218,8 @@ def test_deterministic_replay():
 
 
 def test_mla_two_rows_per_tile_and_long_split():
-    """64 latent heads (a tile spans two rows) and one long request whose key
-    range is split into chunks and merged."""
+    """64 latent heads (one head block per row) and one long request whose
+    key range is split into chunks and merged."""
     inp = pu.make_inputs("mla_bf16", B=2, Hq=64, V=500, H=256, ctx=("uniform", 3000, 5000))
     _full_parity(inp, "compact", "bf16")
 
