@@ -653,21 +653,22 @@ __device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
 
 // FAST: page size is a power of two >= 32, so a 32-key tile lies in one page.
 //
-// Work split inside a workgroup (4 waves, 64 query vectors): waves 2p and
-// 2p+1 form pair p and share query vectors 32p..32p+31 (two 16-wide blocks).
-// Wave h of the pair scores keys [16h, 16h+16) of every 32-key tile over all
-// 576 head dims and turns them into probabilities; the two waves swap those
-// bf16 probabilities through LDS, and each then accumulates all 32 keys into
-// its own half of the output columns, [256h, 256h+256).  Every K and V^T
-// fragment read from LDS feeds two MFMAs, no partial scores cross waves and
-// no wave repeats another's softmax.
+// Work split inside a workgroup (4 waves, 64 query vectors in four 16-wide
+// blocks): waves 2p and 2p+1 form pair p, which owns blocks 2p and 2p+1.
+// Wave h of the pair scores keys [16h, 16h+16) of every 32-key tile for its
+// pair's 32 vectors over all 576 head dims and turns them into bf16
+// probabilities, which every wave then reads from LDS.  Wave w accumulates
+// all 32 keys for all 64 vectors into its quarter of the output columns,
+// [128w, 128w+128).  Every K fragment read from LDS feeds two MFMAs and every
+// transposed V fragment four; no partial scores cross waves and no wave
+// repeats another's softmax.
 //
 // Software pipeline, one barrier per 32-key tile: iteration t scores tile t+1
 // (QK), then accumulates tile t (PV) while the new scores become
 // probabilities, and publishes them; the barrier of iteration t+1 makes them
 // visible to the partner.  The DMA of tile t+2 is issued right after the
 // barrier into the stage that tile t-1 used.
-constexpr int kMlaXBytes = 2 * 4 * 2 * 64 * 8;     // probabilities [buffer][wave][block][lane], 8 B each
+constexpr int kMlaXBytes = 2 * 4 * 64 * 16;       // probabilities [buffer][block][lane], 16 B each
 constexpr int kMlaRedBytes = 2 * 4 * 2 * 16 * 4;   // column max and sum [wave][block][16]
 constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kMlaXBytes + kMlaRedBytes + kPageWin * 4;
 
@@ -813,7 +814,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     for (int kk = 0; kk < 2; ++kk) qk_off[kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ swz(r)) * 16;
   }
   // PV (transposing reads): rows kb + n16/4 (kb = 4*grp or 16 + 4*grp), elements
-  // 256*half + 16*mb + 4*(n16 & 3): logical chunk 32*half + 2*mb + ((n16 & 3) >> 1);
+  // 128*wid + 16*mb + 4*(n16 & 3): logical chunk 16*wid + 2*mb + ((n16 & 3) >> 1);
   // the pattern repeats every 4 mb (one aligned group of 8 chunks = 128 bytes)
   int pv_off[2][4];
 #pragma unroll
@@ -821,14 +822,14 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     const int r = hh * 16 + grp * 4 + (n16 >> 2);
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
-      const int lc = 32 * half + 2 * mm + ((n16 & 3) >> 1);
+      const int lc = 16 * wid + 2 * mm + ((n16 & 3) >> 1);
       pv_off[hh][mm] = r * kMlaRowBytes + (lc ^ swz(r)) * 16 + (n16 & 1) * 8;
     }
   }
-  // probability exchange: buffer b, wave wv, block qb, 8 bytes per lane
-  auto xaddr = [&](int b, int wv, int qb) {
-    return xbase + (uint32_t)((((b * 4 + wv) * 2 + qb) * 64 + lane) * 8);
-  };
+  // probability exchange: buffer b, block B (0..3), 16 bytes per lane = the
+  // PV B operand of that block; the wave scoring keys [16h, 16h+16) fills
+  // bytes [8h, 8h+8)
+  auto xaddr = [&](int b, int blk) { return xbase + (uint32_t)(((b * 4 + blk) * 64 + lane) * 16); };
 
   // S^T of this wave's 16 keys x 32 vectors for the tile in stage `stg`
   auto qk_tile = [&](uint32_t stg, f32x4_t (&sc)[2]) {
@@ -853,7 +854,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   // own keys of this lane within a tile: 16*half + 4*grp + j; their
   // probabilities fill k-slots 8*grp + 4*half + j of the PV B operand
   const int key_lane = half * 16 + grp * 4;
-  f32x4_t oacc[2][16];
+  f32x4_t oacc[4][8];   // [block][16-column group of this wave's quarter]
   float m_ref[2] = {0.f, 0.f}, l_part[2], m_seen[2];
   float l_all[2] = {0.f, 0.f};
 
@@ -865,13 +866,14 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   // below it (underflow risk) the item runs once more with the true max.
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) oacc[qb][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < 8; ++mb) oacc[blk][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       l_part[qb] = 0.f;
       m_seen[qb] = -INFINITY;
     }
-    uint32_t po[2][2];   // this wave's probabilities of the tile being accumulated
 
     // scaled scores -> probabilities, one 16-vector block (4 keys per lane)
     auto soft = [&](const f32x4_t& sc, int qb, int t0, bool full, uint32_t (&out)[2]) {
@@ -916,8 +918,9 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       const bool full0 = (kv_begin + kNK - 1 <= full_lim);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        soft(sc[qb], qb, kv_begin, full0, po[qb]);
-        lds_st_b64(xaddr(0, wid, qb), po[qb][0], po[qb][1]);
+        uint32_t po[2];
+        soft(sc[qb], qb, kv_begin, full0, po);
+        lds_st_b64(xaddr(0, 2 * pair + qb) + half * 8, po[0], po[1]);
       }
     }
 
@@ -928,10 +931,10 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       __syncthreads();
       if (t + 2 < n_tiles) issue(t + 2, (t + 2) % kMlaStages);
 
-      // the partner's probabilities of tile t
-      uint2 pp[2];
+      // the probabilities of tile t, all four blocks
+      u32x4_t pb[4];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) pp[qb] = lds_b64(xaddr(t & 1, wid ^ 1, qb));
+      for (int blk = 0; blk < 4; ++blk) pb[blk] = lds_b128(xaddr(t & 1, blk));
 
       const uint32_t stg = smem_lds + st_cur * kMlaStageBytes;
       st_cur = (st_cur == kMlaStages - 1) ? 0 : st_cur + 1;
@@ -943,15 +946,9 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       f32x4_t sc[2];
       if (more) qk_tile(stg_next, sc);
 
-      u32x4_t pb[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        pb[qb] = half ? u32x4_t{pp[qb].x, pp[qb].y, po[qb][0], po[qb][1]}
-                      : u32x4_t{po[qb][0], po[qb][1], pp[qb].x, pp[qb].y};
-
-      // O^T[256 half columns] += V^T P^T; each transposed V fragment feeds both
-      // blocks.  The next tile's softmax is spread over the first iterations so
-      // that its VALU work runs under the MFMAs.
+      // O^T[this wave's 128 columns] += V^T P^T; each transposed V fragment
+      // feeds all four blocks.  The next tile's softmax runs between MFMAs so
+      // that its VALU work overlaps them.
       uint32_t pn[2][2];
       {
         uint32_t av[2][4];
@@ -968,21 +965,18 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 #pragma unroll
         for (int mb = 0; mb < 3; ++mb) va[mb] = rd_v(mb);
 #pragma unroll
-        for (int mb = 0; mb < 16; ++mb) {
-          if (mb + 3 < 16) va[(mb + 3) & 3] = rd_v(mb + 3);
-          oacc[0][mb] = mfma16(va[mb & 3], pb[0], oacc[0][mb]);
-          oacc[1][mb] = mfma16(va[mb & 3], pb[1], oacc[1][mb]);
-          if (more && (mb == 2 || mb == 6)) soft(sc[mb >> 2], mb >> 2, t0n, full_n, pn[mb >> 2]);
+        for (int mb = 0; mb < 8; ++mb) {
+          if (mb + 3 < 8) va[(mb + 3) & 3] = rd_v(mb + 3);
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) oacc[blk][mb] = mfma16(va[mb & 3], pb[blk], oacc[blk][mb]);
+          if (more && (mb == 1 || mb == 4)) soft(sc[mb >> 2], mb >> 2, t0n, full_n, pn[mb >> 2]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (more) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          po[qb][0] = pn[qb][0];
-          po[qb][1] = pn[qb][1];
-          lds_st_b64(xaddr((t + 1) & 1, wid, qb), pn[qb][0], pn[qb][1]);
-        }
+        for (int qb = 0; qb < 2; ++qb)
+          lds_st_b64(xaddr((t + 1) & 1, 2 * pair + qb) + half * 8, pn[qb][0], pn[qb][1]);
       }
     }
 
@@ -1017,35 +1011,52 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       if (m_all[qb] > -INFINITY) m_ref[qb] = m_all[qb];
   }   // pass
 
+  // the scoring pair's statistics (lse, partial max and sum) for its own
+  // blocks; the sums of the other pair's blocks come from its column sums
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    if (!q_valid[qb]) continue;
+    if (!q_valid[qb] || grp != 0 || half != 0) continue;
     const float l_tot = l_all[qb];
     const int qv = pair * 32 + qb * 16 + n16;
     if (ns == 1) {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16_t* dst = p.o + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaDv + half * 256;
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        uint2 pk;
-        pk.x = cvt_bf16x2(oacc[qb][mb][0] * inv, oacc[qb][mb][1] * inv);
-        pk.y = cvt_bf16x2(oacc[qb][mb][2] * inv, oacc[qb][mb][3] * inv);
-        *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
-      }
-      if (p.lse && grp == 0 && half == 0)
+      if (p.lse)
         p.lse[(size_t)q_row[qb] * p.Hq + head[qb]] = l_tot > 0.f ? (m_ref[qb] + log2f(l_tot)) * kLn2 : -INFINITY;
     } else {
       const int slot = info.z + sp * info.w + tile;
-      if (slot < 0 || slot >= p.part_cap) continue;
-      float* po_ = p.part_o + ((size_t)slot * kMlaQT + qv) * kMlaDv + half * 256;
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb)
-        *reinterpret_cast<f32x4_t*>(po_ + mb * 16 + grp * 4) = oacc[qb][mb];
-      if (grp == 0 && half == 0) {
+      if (slot >= 0 && slot < p.part_cap) {
         float* pml = p.part_ml + ((size_t)slot * kMlaQT + qv) * 2;
         pml[0] = l_tot > 0.f ? m_ref[qb] : -INFINITY;
         pml[1] = l_tot;
       }
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int qv = blk * 16 + n16;
+    const int rl = qv / p.NH;
+    if (rl >= rows_here) continue;
+    const int row = row_start + row0 + rl;
+    const int hd = hb * p.NH + (qv % p.NH);
+    // column sum: the two scoring waves of the block's pair, in a fixed order
+    const int pw = (blk >> 1) * 2;
+    const float l_tot = red_l[(pw * 2 + (blk & 1)) * 16 + n16] + red_l[((pw + 1) * 2 + (blk & 1)) * 16 + n16];
+    if (ns == 1) {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16_t* dst = p.o + ((size_t)row * p.Hq + hd) * kMlaDv + wid * 128;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        uint2 pk;
+        pk.x = cvt_bf16x2(oacc[blk][mb][0] * inv, oacc[blk][mb][1] * inv);
+        pk.y = cvt_bf16x2(oacc[blk][mb][2] * inv, oacc[blk][mb][3] * inv);
+        *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
+      }
+    } else {
+      const int slot = info.z + sp * info.w + tile;
+      if (slot < 0 || slot >= p.part_cap) continue;
+      float* po_ = p.part_o + ((size_t)slot * kMlaQT + qv) * kMlaDv + wid * 128;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        *reinterpret_cast<f32x4_t*>(po_ + mb * 16 + grp * 4) = oacc[blk][mb];
     }
   }
 }
