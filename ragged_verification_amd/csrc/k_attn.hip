@@ -774,21 +774,42 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   const int cbase = wid * kMlaDmaPerWave * 64 + lane;
   const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
 
+  // FAST: this lane's source byte offsets relative to a tile's first row.  A
+  // tile lies in one page, so a DMA is a uniform base plus these offsets;
+  // rows past the item's last key are clamped to that key's final 16 bytes
+  // (finite data; those keys are masked).
+  uint32_t dma_off[kMlaDmaPerWave];
+#pragma unroll
+  for (int e = 0; e < kMlaDmaPerWave; ++e) {
+    const int cidx = cbase + e * 64;
+    const int row = cidx / kMlaChunksPerRow;
+    dma_off[e] = (uint32_t)(row * kMlaRowBytes + ((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
+  }
+  struct DmaTile {
+    const void* base;   // the tile's first row
+    uint32_t lim;       // largest source offset (last valid row's final chunk)
+    uint32_t lds0;      // this wave's destination in the stage
+  };
+  auto dma_tile = [&](int t, int st, int pg) {
+    const int t0 = kv_begin + t * kNK;
+    DmaTile d;
+    d.base = uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
+                         ((size_t)pg * P + (t0 & (P - 1))) * kMlaRowBytes);
+    d.lim = (uint32_t)(min(last - t0, kNK - 1) * kMlaRowBytes + kMlaRowBytes - 16);
+    d.lds0 = wave_lds + st * kMlaStageBytes;
+    return d;
+  };
+  auto dma_one = [&](const DmaTile& d, int e) { dma16_s(min(dma_off[e], d.lim), d.base, d.lds0 + e * 1024); };
+  // FAST: window index of tile t's page
+  auto page_at = [&](int t) { return pwin[((kv_begin + t * kNK) >> p.log2P) - pg0]; };
+
   auto issue = [&](int t, int st) {
     const int t0 = kv_begin + t * kNK;
     const uint32_t lds0 = wave_lds + st * kMlaStageBytes;
     if constexpr (FAST) {
-      const int pg = __builtin_amdgcn_readfirstlane(pwin[(t0 >> p.log2P) - pg0]);
-      const void* base = uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
-                                     (size_t)pg * P * kMlaRowBytes);
+      const DmaTile d = dma_tile(t, st, __builtin_amdgcn_readfirstlane(page_at(t)));
 #pragma unroll
-      for (int e = 0; e < kMlaDmaPerWave; ++e) {
-        const int cidx = cbase + e * 64;
-        const int row = cidx / kMlaChunksPerRow;
-        const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
-        const int j = min(t0 + row, last);
-        dma16_s((uint32_t)(j & (P - 1)) * kMlaRowBytes + lg, base, lds0 + e * 1024);
-      }
+      for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(d, e);
     } else {
 #pragma unroll
       for (int e = 0; e < kMlaDmaPerWave; ++e) {
@@ -832,7 +853,8 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   auto xaddr = [&](int b, int blk) { return xbase + (uint32_t)(((b * 4 + blk) * 64 + lane) * 16); };
 
   // S^T of this wave's 16 keys x 32 vectors for the tile in stage `stg`
-  auto qk_tile = [&](uint32_t stg, f32x4_t (&sc)[2]) {
+  // `between(ks)` runs after step ks's MFMAs (used to spread a tile's DMA)
+  auto qk_tile = [&](uint32_t stg, f32x4_t (&sc)[2], auto&& between) {
     sc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     sc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const uint32_t a0 = stg + qk_off[0], a1 = stg + qk_off[1];
@@ -847,9 +869,11 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       }
       sc[0] = mfma16(fa[ks & 3], qf[0][ks], sc[0]);
       sc[1] = mfma16(fa[ks & 3], qf[1][ks], sc[1]);
+      between(ks);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto no_op = [](int) {};
 
   // own keys of this lane within a tile: 16*half + 4*grp + j; their
   // probabilities fill k-slots 8*grp + 4*half + j of the PV B operand
@@ -901,7 +925,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       if (n_tiles > 1) wait_vm<kMlaDmaPerWave>(); else wait_vm<0>();
       __syncthreads();
       f32x4_t sc[2];
-      qk_tile(smem_lds, sc);
+      qk_tile(smem_lds, sc, no_op);
       if (pass == 0) {
         float mx[2];
 #pragma unroll
@@ -924,12 +948,25 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       }
     }
 
+    // FAST: page of the tile the next iteration fetches, read one iteration ahead
+    int pg_pref = 0;
+    if constexpr (FAST)
+      if (n_tiles > 0) pg_pref = page_at(min(2, n_tiles - 1));
     int st_cur = 0;                    // stage of tile t
     for (int t = 0; t < n_tiles; ++t) {
       // tile t+1 (next QK) must have landed; it is the only DMA in flight
       wait_vm<0>();
       __syncthreads();
-      if (t + 2 < n_tiles) issue(t + 2, (t + 2) % kMlaStages);
+      // DMA of tile t+2 into the stage tile t-1 used.  FAST spreads it over
+      // the QK steps below; near the end it refetches the last tile into that
+      // (dead) stage, which keeps the QK loop free of branches.
+      DmaTile dnext{};
+      if constexpr (FAST) {
+        dnext = dma_tile(min(t + 2, n_tiles - 1), (t + 2) % kMlaStages, __builtin_amdgcn_readfirstlane(pg_pref));
+        pg_pref = page_at(min(t + 3, n_tiles - 1));
+      } else {
+        if (t + 2 < n_tiles) issue(t + 2, (t + 2) % kMlaStages);
+      }
 
       // the probabilities of tile t, all four blocks
       u32x4_t pb[4];
@@ -944,7 +981,16 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       const bool full_n = (t0n + kNK - 1 <= full_lim);
 
       f32x4_t sc[2];
-      if (more) qk_tile(stg_next, sc);
+      auto spread_dma = [&](int ks) {
+        if constexpr (FAST)
+          if ((ks & 1) == 0) dma_one(dnext, ks >> 1);
+      };
+      if (more) {
+        qk_tile(stg_next, sc, spread_dma);
+      } else if constexpr (FAST) {
+#pragma unroll
+        for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(dnext, e);
+      }
 
       // O^T[this wave's 128 columns] += V^T P^T; each transposed V fragment
       // feeds all four blocks.  The next tile's softmax runs between MFMAs so
@@ -980,6 +1026,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       }
     }
 
+    wait_vm<0>();   // no DMA in flight past the pass
     // column max of the visible scores and column sums, over the lane groups
     // and then over the pair
     float mcol[2], lcol[2];
