@@ -1119,9 +1119,23 @@ struct CombineParams {
   int Hq, Hkv, G, NH, RT, n_hb, QT, DV, tpr_max, part_cap;
 };
 
+// One workgroup per (request, tile with split keys, group of 8 query
+// vectors).  The partials' maxima and sums give each vector its combined max
+// m and sum l; each split's weight 2^(m_s - m) / l goes to LDS (in rounds of
+// kCombRound splits) and every output element is the weighted sum of its
+// partials, read as float4 runs.
+constexpr int kCombVec = 8;       // query vectors per workgroup
+constexpr int kCombRound = 512;   // split weights held in LDS at once
+
+template <int DV>
 __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
-  const int i = blockIdx.x / p.tpr_max;
-  const int tile = blockIdx.x % p.tpr_max;
+  __shared__ float s_red[256];
+  __shared__ float s_w[kCombRound][kCombVec];
+  constexpr int kPer = kCombVec * DV / 4 / 256;   // float4 runs per thread
+  const int groups = p.QT / kCombVec;
+  const int i = blockIdx.x / (p.tpr_max * groups);
+  const int tile = (blockIdx.x / groups) % p.tpr_max;
+  const int v0 = (blockIdx.x % groups) * kCombVec;
   const int4 info = p.req_info[i];
   const int ns = info.x;
   if (ns <= 1 || tile >= info.w) return;
@@ -1134,32 +1148,75 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
   const int hb = rem % p.n_hb;
   const int row0 = rb * p.RT;
   const int rows_here = min(p.RT, w - row0);
-  for (int idx = threadIdx.x; idx < p.QT * p.DV; idx += blockDim.x) {
-    const int qv = idx / p.DV;
-    const int d = idx % p.DV;
-    const int rl = qv / p.NH;
-    if (rl >= rows_here) continue;
-    const int head = g * p.G + hb * p.NH + (qv % p.NH);
-    const int row = row_start + row0 + rl;
-    float m = -INFINITY;
-    for (int s = 0; s < ns; ++s) {
-      const int slot = info.z + s * info.w + tile;
-      m = fmaxf(m, p.part_ml[((size_t)slot * p.QT + qv) * 2]);
+  const int t = threadIdx.x;
+  const int vl = t % kCombVec, ss = t / kCombVec;   // 32 split lanes per vector
+  constexpr int kLanes = 256 / kCombVec;
+  const int qv = v0 + vl;
+  auto slot = [&](int s_) { return (size_t)(info.z + s_ * info.w + tile); };
+  auto ml = [&](int s_) { return p.part_ml + (slot(s_) * p.QT + qv) * 2; };
+
+  // combined max and sum (empty partials carry max -inf and sum 0)
+  float m = -INFINITY;
+  for (int s_ = ss; s_ < ns; s_ += kLanes) m = fmaxf(m, ml(s_)[0]);
+  s_red[t] = m;
+  __syncthreads();
+  m = s_red[vl];
+  for (int k = 1; k < kLanes; ++k) m = fmaxf(m, s_red[vl + k * kCombVec]);
+  __syncthreads();
+  float l = 0.f;
+  if (m != -INFINITY)
+    for (int s_ = ss; s_ < ns; s_ += kLanes) {
+      const float ms = ml(s_)[0];
+      if (ms != -INFINITY) l += exp2f(ms - m) * ml(s_)[1];
     }
-    float acc = 0.f, l = 0.f;
-    if (m != -INFINITY) {
-      for (int s = 0; s < ns; ++s) {
-        const int slot = info.z + s * info.w + tile;
-        const float ms = p.part_ml[((size_t)slot * p.QT + qv) * 2];
-        if (ms == -INFINITY) continue;
-        const float wgt = exp2f(ms - m);
-        l += wgt * p.part_ml[((size_t)slot * p.QT + qv) * 2 + 1];
-        acc += wgt * p.part_o[((size_t)slot * p.QT + qv) * p.DV + d];
+  s_red[t] = l;
+  __syncthreads();
+  l = 0.f;
+  for (int k = 0; k < kLanes; ++k) l += s_red[vl + k * kCombVec];
+  const int rl = qv / p.NH;
+  if (ss == 0 && rl < rows_here && p.lse) {
+    const int head = g * p.G + hb * p.NH + (qv % p.NH);
+    p.lse[(size_t)(row_start + row0 + rl) * p.Hq + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+
+  // this thread's float4 runs: element e = 4 * (t + 256 k) of the group
+  float4 acc[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r0 = 0; r0 < ns; r0 += kCombRound) {
+    const int nr = min(kCombRound, ns - r0);
+    for (int s_ = ss; s_ < nr; s_ += kLanes) {
+      const float ms = ml(r0 + s_)[0];
+      s_w[s_][vl] = (l > 0.f && ms != -INFINITY) ? exp2f(ms - m) / l : 0.f;
+    }
+    __syncthreads();
+    for (int s_ = 0; s_ < nr; ++s_) {
+      const float4* src = reinterpret_cast<const float4*>(p.part_o + (slot(r0 + s_) * p.QT + v0) * DV);
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int e = 4 * (t + 256 * k);
+        const float wt = s_w[s_][e / DV];
+        const float4 x = src[t + 256 * k];
+        acc[k].x += wt * x.x;
+        acc[k].y += wt * x.y;
+        acc[k].z += wt * x.z;
+        acc[k].w += wt * x.w;
       }
     }
-    p.o[((size_t)row * p.Hq + head) * p.DV + d] = f32_to_bf16(l > 0.f ? acc / l : 0.f);
-    if (d == 0 && p.lse)
-      p.lse[(size_t)row * p.Hq + head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int e = 4 * (t + 256 * k);
+    const int v = v0 + e / DV;
+    const int rv_ = v / p.NH;
+    if (rv_ >= rows_here) continue;
+    const int head = g * p.G + hb * p.NH + (v % p.NH);
+    bf16_t* dst = p.o + ((size_t)(row_start + row0 + rv_) * p.Hq + head) * DV + (e % DV);
+    uint2 pk;
+    pk.x = pack_bf16x2(acc[k].x, acc[k].y);
+    pk.y = pack_bf16x2(acc[k].z, acc[k].w);
+    *reinterpret_cast<uint2*>(dst) = pk;
   }
 }
 
@@ -1483,7 +1540,9 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   cp.DV = a.Dv;
   cp.tpr_max = sh.tpr_max;
   cp.part_cap = kPartSlots;
-  hipLaunchKernelGGL(k_attn_combine, dim3(a.B * sh.tpr_max), dim3(256), 0, s, cp);
+  const dim3 cgrid(a.B * sh.tpr_max * (sh.QT / kCombVec));
+  if (a.Dv == 512) hipLaunchKernelGGL(k_attn_combine<512>, cgrid, dim3(256), 0, s, cp);
+  else hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, cp);
   return hipGetLastError();
 }
 
