@@ -314,8 +314,6 @@ __device__ inline uint2 lds_read_tr16(const bf16_t* p) {
 
 // reads at raw 32-bit LDS byte addresses (constant parts fold into the
 // instruction's offset field)
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-__device__ inline u32x4_t lds_b128(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
 __device__ inline uint2 lds_tr16(uint32_t addr) {
   s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)addr);
   return __builtin_bit_cast(uint2, v);
@@ -619,29 +617,6 @@ constexpr int kPageWin = 2048;
 constexpr int kMlaChunksPerRow = kMlaD / 8;                // 72
 constexpr int kMlaDmaPerWave = kNK * kMlaChunksPerRow / 256;  // 9 per wave per tile
 constexpr int kMlaQT = 64;                                 // query vectors per tile (2 wave pairs x 32)
-
-// DMA of 16 bytes per lane: global (64-bit address) -> LDS at m0 + 16*lane
-__device__ inline void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
-}
-// same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset
-__device__ inline void dma16_s(uint32_t off, const void* base, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-__device__ inline const void* uniform_ptr(const void* x) {
-  const uint64_t v = reinterpret_cast<uint64_t>(x);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// s_waitcnt with only the vector-memory count limited (gfx9 encoding)
-template <int N>
-__device__ inline void wait_vm() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
 
 __device__ inline int swz(int row) { return (row >> 1) & 7; }
 

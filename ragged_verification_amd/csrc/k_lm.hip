@@ -9,14 +9,20 @@
 //
 // Design (gfx950):
 //  * k_lm_gemm: z = X W^T with bf16 32x32x16 MFMAs (fp32 accumulation), a
-//    128x128 output tile per workgroup (four waves of 64x64), K-loop of 64
-//    staged through double-buffered LDS with register prefetch.  Workgroups
-//    whose rows lie past the packed total exit at once, so the work follows
-//    the real row count M, not the tier.  The epilogue never materialises the
-//    logits unless asked: per 64-column slab it reduces each row to (max,
-//    lowest argmax, sum of exp(z - max)) with cross-lane shuffles and writes
-//    16 bytes.  Column tiles of one vocabulary block sit on one XCD so the
-//    weight tile is fetched from HBM once per XCD-resident row tile group.
+//    128-row x 512-column output tile per workgroup; each of the four waves
+//    owns all 128 rows of a 128-column quarter (256 accumulator registers),
+//    so a weight fragment read from LDS feeds four MFMAs and a hidden-state
+//    fragment four.  Both operands arrive by direct global->LDS DMA into a
+//    three-stage ring of 32-wide K steps; the DMA of step k+2 is spread over
+//    the MFMAs of step k.  LDS rows are 64 bytes whose 16-byte chunks are
+//    XOR-swizzled by (row >> 2) & 3, so sixteen consecutive rows read at one
+//    k offset hit distinct banks.  Workgroups whose rows lie past the packed
+//    total exit at once, so the work follows the real row count M, not the
+//    tier.  The epilogue never materialises the logits unless asked: per
+//    64-column slab it reduces each row to (max, lowest argmax, sum of
+//    exp(z - max)) with cross-lane shuffles and writes 16 bytes.  The row
+//    tiles of one vocabulary tile sit on one XCD, so the weight tile is
+//    fetched from HBM once per XCD.
 //  * k_lm_f32: the same partials from fp32 inputs (plain dot products).
 //  * k_accept: one workgroup per request merges the slab partials of its
 //    rows, runs the greedy or rejection scan, and for rejection draws the
@@ -30,10 +36,18 @@
 namespace rv {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kSlab = 64;                 // columns per partial
+constexpr int kBM = 128, kBN = 512, kBK = 32;   // workgroup tile and K step
+constexpr int kSlab = 64;                        // columns per partial
 constexpr int kGemmThreads = 256;
-constexpr int kAStride = kBK + 8;         // bf16 per LDS row (16-byte pad)
+constexpr int kGRow = kBK * 2;                   // bytes per LDS row (4 chunks of 16)
+constexpr int kGStages = 3;
+constexpr int kGBOff = kBM * kGRow;              // B rows follow the A rows in a stage
+constexpr int kGStage = (kBM + kBN) * kGRow;     // 40 KB
+constexpr int kGLds = kGStages * kGStage;        // 120 KB
+constexpr int kGDmaA = kBM * 4 / 64;             // 1 KB DMA instructions per stage: A
+constexpr int kGDma = (kBM + kBN) * 4 / 64;      // ... in all (A then B)
+constexpr int kGDmaPerWave = kGDma / 4;
+static_assert(kGDma % 4 == 0 && kGDmaPerWave % 2 == 0, "DMA split over waves and K halves");
 
 struct GemmParams {
   const bf16_t* x;     // [rows][H]
@@ -49,9 +63,10 @@ __device__ inline void merge_best(float& v, int& idx, float ov, int oidx) {
   if (ov > v || (ov == v && oidx < idx)) { v = ov; idx = oidx; }
 }
 
+__device__ inline int gswz(int row) { return (row >> 2) & 3; }
+
 __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
-  __shared__ __align__(16) bf16_t As[2][kBM * kAStride];
-  __shared__ __align__(16) bf16_t Bs[2][kBN * kAStride];
+  extern __shared__ __align__(16) unsigned char smem[];
 
   // XCD-aware tile order: consecutive logical tiles stay on one XCD, and the
   // row tiles of a vocabulary tile are consecutive.
@@ -69,107 +84,149 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, lh = lane >> 5;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
 
-  // global -> register prefetch: 1024 chunks of 16 B per operand tile
-  u32x4_t ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // DMA: instruction q (0 .. kGDma-1) of a stage moves chunks 64q .. 64q+63
+  // (A rows first, then B rows); wave w issues q = w*kGDmaPerWave + e.  Chunk
+  // c sits at row c/4, physical position c%4 and holds logical chunk
+  // (c%4) ^ gswz(row).  Rows past the real ones read the last real row.
+  const unsigned char* baseA = reinterpret_cast<const unsigned char*>(p.x + (size_t)m0 * p.H);
+  const unsigned char* baseB = reinterpret_cast<const unsigned char*>(p.w + (size_t)v0 * p.H);
+  uint32_t doff[kGDmaPerWave];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = tid + e * kGemmThreads;
-      const int r = ch >> 3, c = (ch & 7) * 8;
-      const int gr = m0 + r;
-      ra[e] = (gr < M) ? *reinterpret_cast<const u32x4_t*>(p.x + (size_t)gr * p.H + k0 + c)
-                       : u32x4_t{0u, 0u, 0u, 0u};
-      const int gv = v0 + r;
-      rb[e] = (gv < p.V) ? *reinterpret_cast<const u32x4_t*>(p.w + (size_t)gv * p.H + k0 + c)
-                         : u32x4_t{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int ch = tid + e * kGemmThreads;
-      const int r = ch >> 3, c = (ch & 7) * 8;
-      *reinterpret_cast<u32x4_t*>(&As[buf][r * kAStride + c]) = ra[e];
-      *reinterpret_cast<u32x4_t*>(&Bs[buf][r * kAStride + c]) = rb[e];
-    }
+  for (int e = 0; e < kGDmaPerWave; ++e) {
+    const int q = wid * kGDmaPerWave + e;
+    const bool is_a = q < kGDmaA;
+    const int c = (is_a ? q : q - kGDmaA) * 64 + lane;
+    const int row = c >> 2;
+    const int lc = (c & 3) ^ gswz(row);
+    const int r = is_a ? min(row, M - 1 - m0) : min(row, p.V - 1 - v0);
+    doff[e] = (uint32_t)r * (uint32_t)(p.H * 2) + (uint32_t)lc * 16u;
+  }
+  auto dma = [&](int kt, int st, int e) {
+    const int q = wid * kGDmaPerWave + e;
+    const bool is_a = q < kGDmaA;   // uniform
+    const void* base = uniform_ptr((is_a ? baseA : baseB) + (size_t)kt * kGRow);
+    dma16_s(doff[e], base, __builtin_amdgcn_readfirstlane(lds + st * kGStage + q * 1024));
   };
 
-  f32x16_t acc[2][2];
+  // fragment reads: row 32*b + l32 of A (rows) or of this wave's B quarter,
+  // logical chunk 2*ks + lh
+  uint32_t foff[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int ks = 0; ks < 2; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
+  const uint32_t bq = (uint32_t)(kGBOff + wid * 128 * kGRow);
+
+  f32x16_t acc[4][4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
   const int nk = p.H / kBK;
-  gload(0);
-  sstore(0);
+  // prologue: steps 0 and 1 in flight
+#pragma unroll
+  for (int e = 0; e < kGDmaPerWave; ++e) dma(0, 0, e);
+#pragma unroll
+  for (int e = 0; e < kGDmaPerWave; ++e) dma(min(1, nk - 1), 1, e);
+  wait_vm<kGDmaPerWave>();
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      u32x4_t af[2], bfr[2];
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-        af[bm] = *reinterpret_cast<const u32x4_t*>(
-            &As[cur][(wm * 64 + bm * 32 + l32) * kAStride + ks * 16 + lh * 8]);
-#pragma unroll
-      for (int bn = 0; bn < 2; ++bn)
-        bfr[bn] = *reinterpret_cast<const u32x4_t*>(
-            &Bs[cur][(wn * 64 + bn * 32 + l32) * kAStride + ks * 16 + lh * 8]);
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int bn = 0; bn < 2; ++bn) acc[bm][bn] = mfma32(af[bm], bfr[bn], acc[bm][bn]);
-    }
-    if (kt + 1 < nk) {
-      sstore(cur ^ 1);
-      __syncthreads();
-    }
-  }
 
-  // ---- epilogue: lane holds column (l32) of rows 8*(j/4) + 4*lh + j%4 ------
-  const int slab = (v0 + wn * 64) / kSlab;
+  int st = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint32_t stg = lds + st * kGStage;
+    const int st2 = (st == 0) ? 2 : st - 1;   // stage of step kt+2 (= that of kt-1)
+    // past the end the DMA refetches the last step into that dead stage,
+    // which keeps this loop free of branches
+    const int kn = min(kt + 2, nk - 1);
+    u32x4_t fa[2][4], fb[2][4];
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int rl = wm * 64 + bm * 32 + (j / 4) * 8 + lh * 4 + (j % 4);
-      const int row = m0 + rl;
-      const int c0 = v0 + wn * 64 + l32;
-      const int c1 = c0 + 32;
-      float z0 = acc[bm][0][j], z1 = acc[bm][1][j];
-      if (p.logits && row < M) {
-        if (c0 < p.V) p.logits[(size_t)row * p.V + c0] = z0;
-        if (c1 < p.V) p.logits[(size_t)row * p.V + c1] = z1;
-      }
-      if (c0 >= p.V) z0 = -INFINITY;
-      if (c1 >= p.V) z1 = -INFINITY;
-      float best = z0;
-      int bi = c0;
-      merge_best(best, bi, z1, c1);
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float ov = __shfl_xor(best, off);
-        const int oi = __shfl_xor(bi, off);
-        merge_best(best, bi, ov, oi);
-      }
-      float se = 0.f;
-      if (p.with_sum) {
-        se = (z0 == -INFINITY ? 0.f : __expf(z0 - best)) + (z1 == -INFINITY ? 0.f : __expf(z1 - best));
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) se += __shfl_xor(se, off);
-      }
-      if (l32 == 0 && row < M && v0 + wn * 64 < p.V)
-        p.part[(size_t)row * p.n_slabs + slab] = make_float4(best, __int_as_float(bi), se, 0.f);
+    for (int b = 0; b < 4; ++b) {
+      fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
+      fb[0][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[0]);
     }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          fa[1][b] = lds_b128(stg + b * 32 * kGRow + foff[1]);
+          fb[1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[1]);
+        }
+      }
+#pragma unroll
+      for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn) {
+          acc[bm][bn] = mfma32(fa[ks][bm], fb[ks][bn], acc[bm][bn]);
+          // spread this wave's DMAs of step kt+2 over the MFMAs
+          const int slot = bm * 4 + bn;
+          if (slot % 3 == 1 && slot / 3 < kGDmaPerWave / 2) dma(kn, st2, ks * (kGDmaPerWave / 2) + slot / 3);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // step kt+1 must have landed (kt+2 may still be in flight); every wave
+    // is done with stage kt before it is refilled
+    wait_vm<kGDmaPerWave>();
+    __syncthreads();
+    st = (st == kGStages - 1) ? 0 : st + 1;
+  }
+  wait_vm<0>();
+  __syncthreads();   // every wave's last DMA has landed: the ring is free
+
+  // ---- epilogue through LDS: for each 32-row block the wave writes its
+  // 32 x 128 fp32 tile (rows padded to kERow floats), then lane t reduces
+  // row t % 32 over its 64-column slab t / 32 to (max, lowest argmax, sum of
+  // exp(z - max)).  Accumulator lane l holds column l % 32 of rows
+  // 8*(j/4) + 4*(l/32) + j%4.
+  constexpr int kERow = 132;                      // floats per padded LDS row
+  float* et = reinterpret_cast<float*>(smem) + wid * 32 * kERow;
+  const int er = lane & 31, es = lane >> 5;       // reduced row and slab
+  const int cslab = v0 + wid * 128 + es * kSlab;  // first column of the slab
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        et[((j / 4) * 8 + lh * 4 + (j % 4)) * kERow + bn * 32 + l32] = acc[bm][bn][j];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int row = m0 + bm * 32 + er;
+    const float* src = et + er * kERow + es * kSlab;
+    float z[kSlab];
+#pragma unroll
+    for (int i = 0; i < kSlab; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + i);
+      z[i] = v.x; z[i + 1] = v.y; z[i + 2] = v.z; z[i + 3] = v.w;
+    }
+    float best = -INFINITY;
+    int bi = cslab;
+#pragma unroll
+    for (int i = 0; i < kSlab; ++i) {
+      if (cslab + i >= p.V) z[i] = -INFINITY;
+      if (z[i] > best) { best = z[i]; bi = cslab + i; }   // strict: lowest index wins ties
+    }
+    float se = 0.f;
+    if (p.with_sum && best != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kSlab; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
+    }
+    if (row < M && cslab < p.V) {
+      p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
+      if (p.logits) {
+#pragma unroll
+        for (int i = 0; i < kSlab; ++i)
+          if (cslab + i < p.V) p.logits[(size_t)row * p.V + cslab + i] = z[i];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next block overwrites
   }
 }
 
@@ -437,7 +494,10 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     g.with_sum = rej ? 1 : 0;
     const int n_tiles = g.n_mt * g.n_vt;
     const int grid = ((n_tiles + 7) / 8) * 8;
-    hipLaunchKernelGGL(k_lm_gemm, dim3(grid), dim3(kGemmThreads), 0, s, g);
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, kGLds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_lm_gemm, dim3(grid), dim3(kGemmThreads), kGLds, s, g);
   } else {
     F32LmParams f;
     f.x = static_cast<const float*>(a.hidden);

@@ -57,6 +57,38 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// 16-byte LDS read at a raw 32-bit LDS byte address (constant parts fold
+// into the instruction's offset field)
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+__device__ inline u32x4_t lds_b128(uint32_t addr) { return *(const lds_u32x4_t*)(size_t)addr; }
+
+// ---- direct global -> LDS loads ----------------------------------------------
+// Issued from inline assembly so that the compiler does not wait for every
+// outstanding load before each LDS read; callers track the vector-memory
+// counter themselves with wait_vm (loads complete in issue order).
+// DMA of 16 bytes per lane: global (64-bit address) -> LDS at m0 + 16*lane
+__device__ inline void dma16(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr) : "memory", "m0");
+}
+// same with a wave-uniform 64-bit base and a per-lane 32-bit byte offset
+__device__ inline void dma16_s(uint32_t off, const void* base, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ inline const void* uniform_ptr(const void* x) {
+  const uint64_t v = reinterpret_cast<uint64_t>(x);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// s_waitcnt with only the vector-memory count limited (gfx9 encoding)
+template <int N>
+__device__ inline void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 __host__ __device__ inline int32_t* status_ptr(void* ws) { return reinterpret_cast<int32_t*>(ws); }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
