@@ -17,9 +17,11 @@ the CPU oracle's rate on a bounded sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -146,7 +148,7 @@ def measure(step, steps, warmup):
                 committed=committed)
 
 
-def cpu_baseline(inp, step, n_req=24):
+def cpu_baseline(inp, step, n_req=100):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     schedule and pack for the whole batch, then attention, LM head, accept and
     scatter for the rows of ``n_req`` requests."""
@@ -202,6 +204,27 @@ def cpu_baseline(inp, step, n_req=24):
                       f"and scatter for the {len(rows)} packed rows of the first {n_req} requests "
                       f"(numpy fp64, {dt:.1f} s, host has {cores} cores available)",
             "seconds": dt}
+
+
+COUNTERS_MD = os.path.join(ROOT, "profiles", "verify_attn_latent_bf16_B256_counters.md")
+ATTN_SRC = os.path.join(ROOT, "ragged_verification_amd", "csrc", "k_attn.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the latent attention kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel
+    of known size), or None when that summary was taken on another version of
+    the kernel source (its recorded sha256 differs from the file's)."""
+    try:
+        text = open(COUNTERS_MD).read()
+        src = open(ATTN_SRC, "rb").read()
+    except OSError:
+        return None
+    m_bytes = re.search(r"traffic_bytes_per_launch \(k_attn_mla\): (\d+)", text)
+    m_hash = re.search(r"source_sha256 \(ragged_verification_amd/csrc/k_attn.hip\): ([0-9a-f]{64})", text)
+    if not m_bytes or not m_hash or m_hash.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(m_bytes.group(1))
 
 
 def copy_calibration(mib):
@@ -269,8 +292,10 @@ def main():
     if wl.latent:
         dom, achieved = "verify_attn (latent, bf16 MFMA)", c["attn_flops"] / (attn_ms / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                "algorithmic_per_launch": c["attn_flops"], "launch_ms": attn_ms}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_per_launch": c["attn_flops"], "algorithmic_bytes_per_launch": c["attn_bytes"],
+                "launch_ms": attn_ms}
     else:
         achieved = c["attn_bytes"] / (attn_ms / 1e3) / 1e9
         roof = {"kernel": "verify_attn (GQA, bf16)", "bound": "hbm", "achieved": achieved,
