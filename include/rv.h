@@ -211,9 +211,9 @@ rv_status rv_pack(const rv_pack_args* a, void* stream);
  * [M, M_pad) get o = 0, lse = -inf; rows >= M_pad are not written.
  *
  * Built shapes: dtype RV_BF16 with (Dqk,Dv) = (576,512) latent, Hq % 64 == 0,
- * max_pages <= 2047;
- * or (128,128) with Hq/Hkv in {1,2,4,8,16}; dtype RV_F32 with Dqk = Dv <= 128
- * (any group).  bf16 accumulates in fp32. */
+ * or (128,128) with Hq/Hkv in {1,2,4,8,16}, both with max_pages <= 2047 (the
+ * bf16 kernels hold a request's page-table entries in an LDS window); dtype
+ * RV_F32 with Dqk = Dv <= 128 (any group).  bf16 accumulates in fp32. */
 typedef struct {
   const void* q;             /* [rows_cap][Hq][Dqk] packed queries, dtype */
   const void* k_cache;       /* [num_pages][page_size][Hkv][Dqk], dtype */

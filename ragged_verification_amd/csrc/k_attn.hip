@@ -264,7 +264,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
   }
 }
 
-// ---- main bf16 MFMA kernel ---------------------------------------------------
+// ---- bf16 attention kernels: shared parameters ---------------------------------
 struct MainParams {
   const bf16_t* q;
   const bf16_t* k;
@@ -286,34 +286,15 @@ struct MainParams {
   float scale_log2;       // sm_scale * log2(e)
 };
 
-template <int DQK, int DV, int NW, bool LATENT>
-struct AttnCfg {
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kQT = 16 * NW;
-  static constexpr int kKStride = DQK + 8;      // bf16 per K row in LDS (16-byte pad)
-  static constexpr int kVStride = DV + 8;       // bf16 per V row (separate V only)
-  static constexpr int kKChunks = kNK * DQK / 8;   // 16-byte chunks per K tile
-  static constexpr int kVChunks = LATENT ? 0 : kNK * DV / 8;
-  static constexpr int kKPer = (kKChunks + kThreads - 1) / kThreads;
-  static constexpr int kVPer = (kVChunks + kThreads - 1) / kThreads;
-  static constexpr int kLdsBytes = (kNK * kKStride + (LATENT ? 0 : kNK * kVStride)) * 2;
-};
-
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-// gfx950 transposing LDS read: within each 16-lane group, lane 4s+e receives
-// element e of the 4-element blocks addressed by lanes s, 4+s, 8+s, 12+s.
-// With lane r of the group addressing row (key0 + r/4), columns c0 + 4*(r%4)
-// of a row-major tile, lane m receives column c0 + m of rows key0..key0+3:
-// the k-contiguous MFMA operand fragment of a [keys x dims] tile.
-__device__ inline uint2 lds_read_tr16(const bf16_t* p) {
-  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
-// reads at raw 32-bit LDS byte addresses (constant parts fold into the
-// instruction's offset field)
+// gfx950 transposing LDS read at a raw 32-bit LDS byte address: within each
+// 16-lane group, lane 4s+e receives element e of the 4-element blocks
+// addressed by lanes s, 4+s, 8+s, 12+s.  With lane r of the group addressing
+// row (key0 + r/4), columns c0 + 4*(r%4) of a row-major tile, lane m receives
+// column c0 + m of rows key0..key0+3: the k-contiguous MFMA operand fragment
+// of a [keys x dims] tile.
 __device__ inline uint2 lds_tr16(uint32_t addr) {
   s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(size_t)addr);
   return __builtin_bit_cast(uint2, v);
@@ -339,253 +320,6 @@ __device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done
   }
   __syncthreads();
   return *s_item;
-}
-
-template <int DQK, int DV, int NW, bool LATENT>
-__device__ __forceinline__ void attn_mfma_item(const MainParams& p, int item, unsigned char* smem);
-
-template <int DQK, int DV, int NW, bool LATENT>
-__global__ __launch_bounds__(64 * NW) void k_attn_mfma(MainParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  __shared__ int s_item;
-  unsigned done = 0;
-  for (;;) {
-    const int item = next_item(p, &s_item, done);
-    if (item < 0) break;
-    attn_mfma_item<DQK, DV, NW, LATENT>(p, item, smem);
-  }
-}
-
-template <int DQK, int DV, int NW, bool LATENT>
-__device__ __forceinline__ void attn_mfma_item(const MainParams& p, int item, unsigned char* smem) {
-  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
-  bf16_t* Ks = reinterpret_cast<bf16_t*>(smem);
-  // the value rows: the latent layout reuses the key rows' first DV entries
-  bf16_t* Vs = LATENT ? Ks : Ks + kNK * Cfg::kKStride;
-  constexpr int kVs = LATENT ? Cfg::kKStride : Cfg::kVStride;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int n16 = lane & 15;
-  const int grp = lane >> 4;
-
-  const int4 rec = p.items[item];
-  const int i = rec.x, tile = rec.y, sp = rec.z;
-  const int4 info = p.req_info[i];
-  const int ns = info.x;
-  const int row_start = p.cu[i];
-  const int w = p.cu[i + 1] - row_start;
-  const int c = p.ctx[i];
-  const int rb = tile / (p.Hkv * p.n_hb);
-  const int rem = tile % (p.Hkv * p.n_hb);
-  const int g = rem / p.n_hb;
-  const int hb = rem % p.n_hb;
-  const int row0 = rb * p.RT;
-  const int rows_here = min(p.RT, w - row0);
-  const int L_tile = c + row0 + rows_here;
-  // chunk bounds: uniform split of the request's key range
-  const int chunk = p.hdr[1];
-  const int kv_begin = sp * chunk;
-  const int kv_end = min(kv_begin + chunk, L_tile);
-
-  // this lane's query vector
-  const int qv = wid * 16 + n16;
-  const int q_row_local = qv / p.NH;
-  const int head = g * p.G + hb * p.NH + (qv % p.NH);
-  const bool q_valid = q_row_local < rows_here;
-  const int q_row = row_start + row0 + q_row_local;
-  const int limit = c + row0 + q_row_local;   // last visible key position
-
-  // Q fragments (B operand of S^T = K Q^T)
-  u32x4_t qf[DQK / 32];
-#pragma unroll
-  for (int ks = 0; ks < DQK / 32; ++ks) {
-    if (q_valid) {
-      const bf16_t* src = p.q + ((size_t)q_row * p.Hq + head) * DQK + ks * 32 + grp * 8;
-      qf[ks] = *reinterpret_cast<const u32x4_t*>(src);
-    } else {
-      qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
-    }
-  }
-
-  f32x4_t oacc[DV / 16];
-#pragma unroll
-  for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_part = 0.f;
-
-  const int P = p.page_size;
-  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
-
-  // register prefetch buffers for one KV tile
-  u32x4_t kbuf[Cfg::kKPer];
-  u32x4_t vbuf[Cfg::kVPer > 0 ? Cfg::kVPer : 1];
-
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int e = 0; e < Cfg::kKPer; ++e) {
-      const int ch = tid + e * Cfg::kThreads;
-      u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-      if (ch < Cfg::kKChunks) {
-        const int kk = ch / (DQK / 8);
-        const int part = ch % (DQK / 8);
-        const int j = t0 + kk;
-        if (j < kv_end) {
-          int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
-          if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
-          const size_t tok = (size_t)pg * P + (j % P);
-          val = *reinterpret_cast<const u32x4_t*>(p.k + (tok * p.Hkv + g) * DQK + part * 8);
-        }
-      }
-      kbuf[e] = val;
-    }
-    if constexpr (!LATENT) {
-#pragma unroll
-      for (int e = 0; e < Cfg::kVPer; ++e) {
-        const int ch = tid + e * Cfg::kThreads;
-        u32x4_t val = u32x4_t{0u, 0u, 0u, 0u};
-        if (ch < Cfg::kVChunks) {
-          const int kk = ch / (DV / 8);
-          const int part = ch % (DV / 8);
-          const int j = t0 + kk;
-          if (j < kv_end) {
-            int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
-            if (pg < 0 || pg >= p.num_pages) pg = 0;
-            const size_t tok = (size_t)pg * P + (j % P);
-            val = *reinterpret_cast<const u32x4_t*>(p.v + (tok * p.Hkv + g) * DV + part * 8);
-          }
-        }
-        vbuf[e] = val;
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int e = 0; e < Cfg::kKPer; ++e) {
-      const int ch = tid + e * Cfg::kThreads;
-      if (ch < Cfg::kKChunks) {
-        const int kk = ch / (DQK / 8);
-        const int part = ch % (DQK / 8);
-        *reinterpret_cast<u32x4_t*>(Ks + kk * Cfg::kKStride + part * 8) = kbuf[e];
-      }
-    }
-    if constexpr (!LATENT) {
-#pragma unroll
-      for (int e = 0; e < Cfg::kVPer; ++e) {
-        const int ch = tid + e * Cfg::kThreads;
-        if (ch < Cfg::kVChunks) {
-          const int kk = ch / (DV / 8);
-          const int part = ch % (DV / 8);
-          *reinterpret_cast<u32x4_t*>(Vs + kk * Cfg::kVStride + part * 8) = vbuf[e];
-        }
-      }
-    }
-  };
-
-  if (kv_begin < kv_end) load_tile(kv_begin);
-  for (int t0 = kv_begin; t0 < kv_end; t0 += kNK) {
-    store_tile();
-    __syncthreads();
-    if (t0 + kNK < kv_end) load_tile(t0 + kNK);
-
-    // S^T (keys x query vectors): lane holds keys 16*mb + 4*grp + j of query n16
-    f32x4_t sacc[kNK / 16];
-#pragma unroll
-    for (int mb = 0; mb < kNK / 16; ++mb) {
-      sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < DQK / 32; ++ks) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-            Ks + (mb * 16 + n16) * Cfg::kKStride + ks * 32 + grp * 8);
-        sacc[mb] = mfma16(a, qf[ks], sacc[mb]);
-      }
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < kNK / 16; ++mb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kpos = t0 + mb * 16 + grp * 4 + j;
-        float s = sacc[mb][j] * p.scale_log2;
-        if (!q_valid || kpos >= kv_end || kpos > limit) s = -INFINITY;
-        sacc[mb][j] = s;
-        tmax = fmaxf(tmax, s);
-      }
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // no branch around the MFMAs: a fully masked query gets alpha = p = 0
-    const float m_new = fmaxf(m_run, tmax);
-    {
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < kNK / 16; ++mb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = sacc[mb][j];
-          const float pr = (s == -INFINITY) ? 0.f : exp2f(s - m_new);
-          sacc[mb][j] = pr;
-          psum += pr;
-        }
-      }
-      l_part = l_part * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int mb = 0; mb < DV / 16; ++mb) oacc[mb] *= alpha;
-      // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
-      u32x4_t pb;
-      pb[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
-      pb[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
-      pb[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
-      pb[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
-      // V^T fragments straight from the row-major value tile: k-slots
-      // 8*grp..+3 <- keys 4*grp..+3, k-slots 8*grp+4..+7 <- keys 16+4*grp..+3
-      const bf16_t* v_lo = Vs + (grp * 4 + (n16 >> 2)) * kVs + 4 * (n16 & 3);
-      const bf16_t* v_hi = v_lo + 16 * kVs;
-#pragma unroll
-      for (int mb = 0; mb < DV / 16; ++mb) {
-        const uint2 lo = lds_read_tr16(v_lo + mb * 16);
-        const uint2 hi = lds_read_tr16(v_hi + mb * 16);
-        const u32x4_t a = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        oacc[mb] = mfma16(a, pb, oacc[mb]);
-      }
-    }
-    __syncthreads();
-  }
-
-  // normaliser over the four lane groups that share a query vector
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!q_valid) return;
-
-  if (ns == 1) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    bf16_t* dst = p.o + ((size_t)q_row * p.Hq + head) * DV;
-#pragma unroll
-    for (int mb = 0; mb < DV / 16; ++mb) {
-      uint2 pk;
-      pk.x = pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv);
-      pk.y = pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv);
-      *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
-    }
-    if (p.lse && grp == 0)
-      p.lse[(size_t)q_row * p.Hq + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int slot = info.z + sp * info.w + tile;
-    if (slot < 0 || slot >= p.part_cap) return;   // the plan keeps slots below the cap
-    float* po = p.part_o + ((size_t)slot * Cfg::kQT + qv) * DV;
-#pragma unroll
-    for (int mb = 0; mb < DV / 16; ++mb)
-      *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[mb];
-    if (grp == 0) {
-      float* pml = p.part_ml + ((size_t)slot * Cfg::kQT + qv) * 2;
-      pml[0] = m_run;
-      pml[1] = l_tot;
-    }
-  }
 }
 
 // ---- latent (MLA-style) bf16 kernel: LDS DMA ring ---------------------------------
@@ -1083,6 +817,257 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   }
 }
 
+// ---- GQA bf16 kernel (head dim 128): LDS DMA ring -------------------------------
+//
+// One workgroup = NW waves = 16*NW query vectors (rows x query heads) of one
+// KV head against one key chunk, as in the latent kernel: K and V tiles of
+// 32 keys arrive by direct global->LDS DMA into a ring of stages issued one
+// stage short of the ring ahead (the kernel is bound by HBM, so what matters
+// is the bytes in flight), rows of 256 bytes whose 16-byte chunks are XOR-swizzled by
+// (row >> 1) & 7, the request's page-table entries for the chunk in an LDS
+// window.  Per tile the scores S^T = K Q^T and O^T += V^T P^T run on bf16
+// 16x16x32 MFMAs (V^T fragments through transposing LDS reads) with an online
+// softmax: a running max per query vector, the accumulators rescaled when it
+// grows.  Ring depth (measured): two-wave workgroups run one per CU
+// with six stages; four-wave workgroups run two per CU with four stages, so
+// one workgroup's softmax overlaps the other's loads.
+constexpr int kGqaD = 128;
+constexpr int kGqaRow = kGqaD * 2;                         // bytes per K or V row
+constexpr int kGqaStage = 2 * kNK * kGqaRow;               // K rows then V rows: 16 KB
+template <int NW>
+struct GqaCfg {
+  static constexpr int kStages = NW == 2 ? 6 : 4;
+  static constexpr int kLds = kStages * kGqaStage + kPageWin * 4;
+};
+
+template <int NW, bool FAST>
+__device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, unsigned char* smem) {
+  constexpr int NST = GqaCfg<NW>::kStages;
+  constexpr int kDmaPer = kGqaStage / 1024 / NW;   // 1 KB DMA instructions per wave and tile
+  constexpr int kChunksRow = kGqaRow / 16;         // 16
+  int* pwin = reinterpret_cast<int*>(smem + NST * kGqaStage);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int4 rec = p.items[item];
+  const int i = rec.x, tile = rec.y, sp = rec.z;
+  const int4 info = p.req_info[i];
+  const int ns = info.x;
+  const int row_start = p.cu[i];
+  const int w = p.cu[i + 1] - row_start;
+  const int c = p.ctx[i];
+  const int rb = tile / (p.Hkv * p.n_hb);
+  const int rem = tile % (p.Hkv * p.n_hb);
+  const int g = rem / p.n_hb;
+  const int hb = rem % p.n_hb;
+  const int row0 = rb * p.RT;
+  const int rows_here = min(p.RT, w - row0);
+  const int L_tile = c + row0 + rows_here;
+  const int chunk = p.hdr[1];
+  const int kv_begin = sp * chunk;
+  const int kv_end = min(kv_begin + chunk, L_tile);
+  const int P = p.page_size;
+
+  // page-table window for keys [kv_begin, kv_end)
+  const int pg0 = kv_begin / P;
+  int npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
+  if (npg > kPageWin) {                 // context longer than the page table allows
+    if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
+    npg = kPageWin;
+  }
+  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
+  for (int x = tid; x < npg; x += 64 * NW) {
+    int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
+    if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+    pwin[x] = pg;
+  }
+
+  // this lane's query vector
+  const int qv = wid * 16 + n16;
+  const int q_row_local = qv / p.NH;
+  const int head = g * p.G + hb * p.NH + (qv % p.NH);
+  const bool q_valid = q_row_local < rows_here;
+  const int q_row = row_start + row0 + q_row_local;
+  const int limit = c + row0 + q_row_local;   // last visible key position
+  u32x4_t qf[kGqaD / 32];
+#pragma unroll
+  for (int ks = 0; ks < kGqaD / 32; ++ks) {
+    if (q_valid) {
+      const bf16_t* src = p.q + ((size_t)q_row * p.Hq + head) * kGqaD + ks * 32 + grp * 8;
+      qf[ks] = *reinterpret_cast<const u32x4_t*>(src);
+    } else {
+      qf[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();   // page window visible
+
+  const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
+  const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
+  const size_t kv_head = (size_t)p.Hkv * kGqaD;   // elements between consecutive key rows
+
+  // DMA of tile t into stage st: this wave's instruction e moves chunks
+  // (wid*kDmaPer + e)*64 + lane of the stage (K rows 0..31, then V rows);
+  // chunk cc of a row sits at physical position cc and holds logical chunk
+  // cc ^ swz(row)
+  auto issue = [&](int t, int st) {
+    const int t0 = kv_begin + t * kNK;
+#pragma unroll
+    for (int e = 0; e < kDmaPer; ++e) {
+      const int q = wid * kDmaPer + e;
+      const int c_ = q * 64 + lane;
+      const int kv = c_ / (kNK * kChunksRow);        // 0: K, 1: V (uniform per instruction)
+      const int row = (c_ / kChunksRow) % kNK;
+      const int lc = (c_ % kChunksRow) ^ swz(row);
+      const int j = min(t0 + row, last);
+      int pg;
+      if constexpr (FAST) pg = __builtin_amdgcn_readfirstlane(pwin[(t0 >> p.log2P) - pg0]);
+      else pg = pwin[min(j / P - pg0, npg - 1)];
+      const size_t tok = (size_t)pg * P + (FAST ? (j & (P - 1)) : (j % P));
+      const bf16_t* src = (kv ? p.v : p.k) + (tok * p.Hkv + g) * kGqaD + lc * 8;
+      dma16(src, __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+    }
+    (void)kv_head;
+  };
+
+  // fragment offsets: QK A rows 16*mb + n16, logical chunk 4*ks + grp;
+  // V^T transposing reads rows kb + n16/4 (kb = 4*grp or 16 + 4*grp),
+  // elements 16*mb + 4*(n16 & 3): logical chunk 2*mb + ((n16 & 3) >> 1)
+  auto k_addr = [&](uint32_t stg, int mb, int ks) {
+    const int r = mb * 16 + n16;
+    return stg + (uint32_t)(r * kGqaRow + ((4 * ks + grp) ^ swz(r)) * 16);
+  };
+  auto v_addr = [&](uint32_t stg, int hh, int mb) {
+    const int r = hh * 16 + grp * 4 + (n16 >> 2);
+    const int lc = 2 * mb + ((n16 & 3) >> 1);
+    return stg + (uint32_t)(kNK * kGqaRow + r * kGqaRow + (lc ^ swz(r)) * 16 + (n16 & 1) * 8);
+  };
+
+  f32x4_t oacc[kGqaD / 16];
+#pragma unroll
+  for (int mb = 0; mb < kGqaD / 16; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_part = 0.f;
+
+  // prologue: tiles 0 .. NST-2 in flight
+#pragma unroll
+  for (int u = 0; u < NST - 1; ++u)
+    if (u < n_tiles) issue(u, u);
+  int st = 0;
+  for (int t = 0; t < n_tiles; ++t) {
+    // tile t has landed once at most the NST-2 younger tiles remain
+    if (t + NST - 2 < n_tiles) wait_vm<(NST - 2) * kDmaPer>();
+    else wait_vm<0>();
+    __syncthreads();   // tile t visible; every wave is done with tile t-1
+    if (t + NST - 1 < n_tiles) issue(t + NST - 1, (t + NST - 1) % NST);
+    const uint32_t stg = lds + st * kGqaStage;
+    st = (st == NST - 1) ? 0 : st + 1;
+    const int t0 = kv_begin + t * kNK;
+
+    // S^T (keys x query vectors): lane holds keys 16*mb + 4*grp + j of query n16
+    f32x4_t sacc[kNK / 16];
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb) {
+      sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kGqaD / 32; ++ks) sacc[mb] = mfma16(lds_b128(k_addr(stg, mb, ks)), qf[ks], sacc[mb]);
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kpos = t0 + mb * 16 + grp * 4 + j;
+        float s = sacc[mb][j] * p.scale_log2;
+        if (!q_valid || kpos >= kv_end || kpos > limit) s = -INFINITY;
+        sacc[mb][j] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    // no branch around the MFMAs: a fully masked query gets alpha = p = 0
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float s = sacc[mb][j];
+        const float pr = (s == -INFINITY) ? 0.f : exp2f(s - m_new);
+        sacc[mb][j] = pr;
+        psum += pr;
+      }
+    }
+    l_part = l_part * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb) oacc[mb] *= alpha;
+    // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
+    u32x4_t pb;
+    pb[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
+    pb[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
+    pb[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
+    pb[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb) {
+      const uint2 lo = lds_tr16(v_addr(stg, 0, mb));
+      const uint2 hi = lds_tr16(v_addr(stg, 1, mb));
+      oacc[mb] = mfma16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, oacc[mb]);
+    }
+  }
+  wait_vm<0>();   // no DMA in flight past the item
+
+  // normaliser over the four lane groups that share a query vector
+  float l_tot = l_part + __shfl_xor(l_part, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!q_valid) return;
+
+  if (ns == 1) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16_t* dst = p.o + ((size_t)q_row * p.Hq + head) * kGqaD;
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb) {
+      uint2 pk;
+      pk.x = pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv);
+      pk.y = pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv);
+      *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
+    }
+    if (p.lse && grp == 0)
+      p.lse[(size_t)q_row * p.Hq + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const int slot = info.z + sp * info.w + tile;
+    if (slot < 0 || slot >= p.part_cap) return;   // the plan keeps slots below the cap
+    float* po = p.part_o + ((size_t)slot * (16 * NW) + qv) * kGqaD;
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb)
+      *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[mb];
+    if (grp == 0) {
+      float* pml = p.part_ml + ((size_t)slot * (16 * NW) + qv) * 2;
+      pml[0] = m_run;
+      pml[1] = l_tot;
+    }
+  }
+}
+
+template <int NW, bool FAST>
+__global__ __launch_bounds__(64 * NW) void k_attn_gqa(MainParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_item;
+  unsigned done = 0;
+  for (;;) {
+    const int item = next_item(p, &s_item, done);
+    if (item < 0) break;
+    attn_gqa_item<NW, FAST>(p, item, smem);
+  }
+}
+
 // ---- combine split partials ----------------------------------------------------
 struct CombineParams {
   const int32_t* cu;
@@ -1353,24 +1338,28 @@ hipError_t persistent_grid(const void* kern, int threads, int lds, int* grid) {
   return hipSuccess;
 }
 
-template <int DQK, int DV, int NW, bool LATENT>
-hipError_t launch_main(const MainParams& mp, hipStream_t s) {
-  using Cfg = AttnCfg<DQK, DV, NW, LATENT>;
-  auto kern = k_attn_mfma<DQK, DV, NW, LATENT>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLdsBytes);
+template <int NW, bool FAST>
+hipError_t launch_gqa_t(const MainParams& mp, hipStream_t s) {
+  const void* kern = reinterpret_cast<const void*>(k_attn_gqa<NW, FAST>);
+  constexpr int lds = GqaCfg<NW>::kLds;
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(reinterpret_cast<const void*>(kern), Cfg::kThreads, Cfg::kLdsBytes, &grid)) != hipSuccess)
-    return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(Cfg::kThreads), Cfg::kLdsBytes, s, mp);
+  if ((e = persistent_grid(kern, 64 * NW, lds, &grid)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_attn_gqa<NW, FAST>), dim3(grid), dim3(64 * NW), lds, s, mp);
   return hipGetLastError();
+}
+
+// GQA bf16 (head dim 128): NW = 2 or 4 waves; FAST: power-of-two pages of at least 32 keys
+hipError_t launch_gqa(const MainParams& mp, int nw, bool fast, hipStream_t s) {
+  if (nw == 2) return fast ? launch_gqa_t<2, true>(mp, s) : launch_gqa_t<2, false>(mp, s);
+  return fast ? launch_gqa_t<4, true>(mp, s) : launch_gqa_t<4, false>(mp, s);
 }
 
 }  // namespace
 
 int attn_max_pages_limit(int dtype, bool latent) {
-  return (dtype == RV_BF16 && latent) ? kPageWin - 1 : (1 << 30);
+  return (dtype == RV_BF16) ? kPageWin - 1 : (1 << 30);   // bf16 kernels hold a page window
 }
 
 bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent) {
@@ -1494,7 +1483,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
-    e = (nw == 2) ? launch_main<128, 128, 2, false>(mp, s) : launch_main<128, 128, 4, false>(mp, s);
+    e = launch_gqa(mp, nw, mp.log2P >= 5, s);
   }
   if (e != hipSuccess) return e;
 
