@@ -39,6 +39,10 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
 
+def _json_default(o):
+    return o.item() if hasattr(o, "item") else str(o)
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -148,7 +152,46 @@ def measure(step, steps, warmup):
                 committed=committed)
 
 
-def cpu_baseline(inp, step, n_req=100):
+def sweep(steps, warmup):
+    """The mixed-confidence sweep: GQA shapes at each batch size of the sweep
+    list; request i has confidence class i mod 3.  Static, compact and
+    cap-accept run on identical inputs.  One JSON line per batch size: per mode
+    the five-stage time, packed rows and committed tokens per step, and (for
+    compact and cap-accept) the mean window and committed tokens per class;
+    cap-accept also reports its ceiling utilisation (tokens committed over the
+    tokens the verified full blocks would allow).  Also the verify-attention
+    call's HBM fraction in compact mode."""
+    for B in synth.SWEEP_BATCHES:
+        wl = synth.workload("sweep_gqa", B=B)
+        inp = synth.make_inputs(wl, device="cuda", B=B)
+        cls = np.arange(B) % 3
+        out = {"workload": "sweep_gqa", "B": B}
+        for mode in ("static", "compact", "cap_accept"):
+            step = VerifyStep(inp, mode=mode)
+            r = measure(step, steps, warmup)
+            rec = {"ms_per_step": r["five_stage_ms"], "packed_rows": r["M"], "tier_rows": r["M_pad"],
+                   "committed_per_step": r["committed"], "stages_ms": {k: round(v, 4) for k, v in r["per_stage_ms"].items()}}
+            wc = step.w_commit.cpu().numpy()
+            acc = step.accept.cpu().numpy().astype(np.int64)
+            if mode != "static":
+                rec["mean_window_by_class"] = [float(wc[cls == k].mean()) if (cls == k).any() else None for k in range(3)]
+                rec["committed_by_class"] = [int((acc[cls == k] + 1).sum()) for k in range(3)]
+            if mode == "cap_accept":
+                ceil = step.ceiling.cpu().numpy().astype(np.int64)
+                rec["ceiling_utilisation"] = float((acc + 1).sum() / (ceil + 1).sum())
+            if mode == "compact":
+                w = step.w_verify.cpu().numpy().astype(np.int64)
+                ctx = inp["ctx"].cpu().numpy().astype(np.int64)
+                gbs = attn_bytes(ctx, w, wl) / (r["per_stage_ms"]["attn"] / 1e3) / 1e9
+                rec["attn_hbm"] = {"achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+            out[mode] = rec
+            del step
+        print(json.dumps(out, default=_json_default), flush=True)
+        del inp
+        torch.cuda.empty_cache()
+
+
+def cpu_baseline(inp, step, n_req=130):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     schedule and pack for the whole batch, then attention, LM head, accept and
     scatter for the rows of ``n_req`` requests."""
@@ -249,6 +292,8 @@ def main():
     ap.add_argument("--workload", default="mla_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the mixed-confidence batch sweep (one JSON line per batch size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain elementwise copy of MIB MiB five times (HBM counter calibration)")
     args = ap.parse_args()
@@ -263,6 +308,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     rv.load()
+    if args.sweep:
+        sweep(args.steps, args.warmup)
+        return
     wl = synth.workload(args.workload)
     t0 = time.time()
     inp = synth.make_inputs(wl, device="cuda")
@@ -338,7 +386,7 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         line["cpu_baseline"] = cpu_baseline(inp, None)
-    print(json.dumps(line, default=lambda o: o.item() if hasattr(o, "item") else str(o)), flush=True)
+    print(json.dumps(line, default=_json_default), flush=True)
 
 
 if __name__ == "__main__":

@@ -825,7 +825,9 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 // stage short of the ring ahead (the kernel is bound by HBM, so what matters
 // is the bytes in flight), rows of 256 bytes whose 16-byte chunks are XOR-swizzled by
 // (row >> 1) & 7, the request's page-table entries for the chunk in an LDS
-// window.  Per tile the scores S^T = K Q^T and O^T += V^T P^T run on bf16
+// window (with power-of-two pages of at least 4 keys each DMA instruction's
+// four rows share a page, so the DMA is a uniform page base plus lane
+// offsets).  Per tile the scores S^T = K Q^T and O^T += V^T P^T run on bf16
 // 16x16x32 MFMAs (V^T fragments through transposing LDS reads) with an online
 // softmax: a running max per query vector, the accumulators rescaled when it
 // grows.  Ring depth (measured): two-wave workgroups run one per CU
@@ -893,6 +895,8 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const bool q_valid = q_row_local < rows_here;
   const int q_row = row_start + row0 + q_row_local;
   const int limit = c + row0 + q_row_local;   // last visible key position
+  // tiles ending at or before this key need no mask for any real row
+  const int full_lim = min(c + row0, kv_end - 1);
   u32x4_t qf[kGqaD / 32];
 #pragma unroll
   for (int ks = 0; ks < kGqaD / 32; ++ks) {
@@ -915,24 +919,53 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   // (wid*kDmaPer + e)*64 + lane of the stage (K rows 0..31, then V rows);
   // chunk cc of a row sits at physical position cc and holds logical chunk
   // cc ^ swz(row)
+  // this lane's row and logical chunk (bytes) in each of its DMA instructions
+  int drow[kDmaPer], dlc[kDmaPer];
+#pragma unroll
+  for (int e = 0; e < kDmaPer; ++e) {
+    const int c_ = (wid * kDmaPer + e) * 64 + lane;
+    drow[e] = (c_ / kChunksRow) % kNK;
+    dlc[e] = ((c_ % kChunksRow) ^ swz(drow[e])) * 16;
+  }
+  const unsigned char* gk = reinterpret_cast<const unsigned char*>(p.k + (size_t)g * kGqaD);
+  const unsigned char* gv = reinterpret_cast<const unsigned char*>(p.v + (size_t)g * kGqaD);
+  const size_t page_bytes = (size_t)P * kv_head * 2;
+  const uint32_t row_bytes = (uint32_t)(kv_head * 2);
+
   auto issue = [&](int t, int st) {
     const int t0 = kv_begin + t * kNK;
+    if constexpr (FAST) {
+      // instruction q's four rows (4*(q%8) ..) lie in one page, clamped rows
+      // included: a uniform page base plus a 32-bit lane offset; the page
+      // reads are issued together
+      int pgv[kDmaPer];
 #pragma unroll
-    for (int e = 0; e < kDmaPer; ++e) {
-      const int q = wid * kDmaPer + e;
-      const int c_ = q * 64 + lane;
-      const int kv = c_ / (kNK * kChunksRow);        // 0: K, 1: V (uniform per instruction)
-      const int row = (c_ / kChunksRow) % kNK;
-      const int lc = (c_ % kChunksRow) ^ swz(row);
-      const int j = min(t0 + row, last);
-      int pg;
-      if constexpr (FAST) pg = __builtin_amdgcn_readfirstlane(pwin[(t0 >> p.log2P) - pg0]);
-      else pg = pwin[min(j / P - pg0, npg - 1)];
-      const size_t tok = (size_t)pg * P + (FAST ? (j & (P - 1)) : (j % P));
-      const bf16_t* src = (kv ? p.v : p.k) + (tok * p.Hkv + g) * kGqaD + lc * 8;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+      for (int e = 0; e < kDmaPer; ++e) {
+        const int q = wid * kDmaPer + e;
+        const int jb = min(t0 + 4 * (q % (kNK / 4)), last);
+        pgv[e] = pwin[min((jb >> p.log2P) - pg0, npg - 1)];
+      }
+#pragma unroll
+      for (int e = 0; e < kDmaPer; ++e) {
+        const int q = wid * kDmaPer + e;
+        const bool is_v = q >= kNK * kChunksRow / 64;   // uniform: the V rows follow the K rows
+        const int pg = __builtin_amdgcn_readfirstlane(pgv[e]);
+        const void* base = uniform_ptr((is_v ? gv : gk) + (size_t)pg * page_bytes);
+        const int j = min(t0 + drow[e], last);
+        dma16_s((uint32_t)(j & (P - 1)) * row_bytes + (uint32_t)dlc[e], base,
+                __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kDmaPer; ++e) {
+        const int q = wid * kDmaPer + e;
+        const bool is_v = q >= kNK * kChunksRow / 64;
+        const int j = min(t0 + drow[e], last);
+        const int pg = pwin[min(j / P - pg0, npg - 1)];
+        const size_t tok = (size_t)pg * P + (j % P);
+        dma16((is_v ? gv : gk) + tok * row_bytes + dlc[e], __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+      }
     }
-    (void)kv_head;
   };
 
   // fragment offsets: QK A rows 16*mb + n16, logical chunk 4*ks + grp;
@@ -978,37 +1011,44 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
       for (int ks = 0; ks < kGqaD / 32; ++ks) sacc[mb] = mfma16(lds_b128(k_addr(stg, mb, ks)), qf[ks], sacc[mb]);
     }
     float tmax = -INFINITY;
+    const bool full = (t0 + kNK - 1 <= full_lim);   // uniform: no key past any real row's limit
 #pragma unroll
     for (int mb = 0; mb < kNK / 16; ++mb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int kpos = t0 + mb * 16 + grp * 4 + j;
         float s = sacc[mb][j] * p.scale_log2;
-        if (!q_valid || kpos >= kv_end || kpos > limit) s = -INFINITY;
+        if (!full) {
+          const int kpos = t0 + mb * 16 + grp * 4 + j;
+          if (kpos >= kv_end || kpos > limit) s = -INFINITY;
+        }
         sacc[mb][j] = s;
         tmax = fmaxf(tmax, s);
       }
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // no branch around the MFMAs: a fully masked query gets alpha = p = 0
+    // no branch around the MFMAs: a fully masked query gets p = 0
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < kNK / 16; ++mb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float s = sacc[mb][j];
-        const float pr = (s == -INFINITY) ? 0.f : exp2f(s - m_new);
+        const float pr = __builtin_amdgcn_exp2f(sacc[mb][j] - m_use);   // exp2(-inf) = 0
         sacc[mb][j] = pr;
         psum += pr;
       }
     }
-    l_part = l_part * alpha + psum;
-    m_run = m_new;
+    // rescale only when some vector's running max grew
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
 #pragma unroll
-    for (int mb = 0; mb < kGqaD / 16; ++mb) oacc[mb] *= alpha;
+      for (int mb = 0; mb < kGqaD / 16; ++mb) oacc[mb] *= alpha;
+    }
+    l_part += psum;
+    m_run = m_new;
     // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
     u32x4_t pb;
     pb[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
@@ -1350,7 +1390,7 @@ hipError_t launch_gqa_t(const MainParams& mp, hipStream_t s) {
   return hipGetLastError();
 }
 
-// GQA bf16 (head dim 128): NW = 2 or 4 waves; FAST: power-of-two pages of at least 32 keys
+// GQA bf16 (head dim 128): NW = 2 or 4 waves; FAST: power-of-two pages of at least 4 keys
 hipError_t launch_gqa(const MainParams& mp, int nw, bool fast, hipStream_t s) {
   if (nw == 2) return fast ? launch_gqa_t<2, true>(mp, s) : launch_gqa_t<2, false>(mp, s);
   return fast ? launch_gqa_t<4, true>(mp, s) : launch_gqa_t<4, false>(mp, s);
@@ -1483,7 +1523,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
-    e = launch_gqa(mp, nw, mp.log2P >= 5, s);
+    e = launch_gqa(mp, nw, mp.log2P >= 2, s);
   }
   if (e != hipSuccess) return e;
 
