@@ -48,6 +48,7 @@ struct AttnShape {
   int RT;                // rows per tile
   int n_hb;              // head blocks per KV head = G / NH
   int tpr_max;           // tiles per request at most
+  int target;            // work items the plan aims for
 };
 
 // Work header written by the plan: [0] items, [1] chunk, [2] partial slots
@@ -70,63 +71,112 @@ struct PlanParams {
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ---- plan: device-side varlen metadata -------------------------------------
-__global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
-  __shared__ long long red[1024];
-  __shared__ int scan_a[1024], scan_b[1024];
-  __shared__ int s_chunk;
+//
+// One workgroup of 1024 threads; thread t owns requests [t*seg, t*seg+seg)
+// (seg = ceil(B/1024)), whose (window, keys) pairs it caches in LDS.  Every
+// block-wide reduction and scan is a wave-level shuffle scan plus one pass
+// over the 16 wave totals, so each costs two barriers.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlanMaxB = RV_MAX_ROWS / 2;   // gamma >= 2
+
+template <int N>
+__device__ inline void wave_incl_scan(int (&v)[N]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int u = __shfl_up(v[k], off);
+      if (lane >= off) v[k] += u;
+    }
+  }
+}
+
+// Block-wide exclusive scan of N ints per thread (thread order); tot gets
+// the block totals.  buf holds kPlanWaves * N ints.
+template <int N>
+__device__ inline void block_excl_scan(const int (&v)[N], int (&ex)[N], int (&tot)[N], int* buf) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) inc[k] = v[k];
+  wave_incl_scan<N>(inc);
+  __syncthreads();   // buf is free
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) buf[wv * N + k] = inc[k];
+  }
+  __syncthreads();
+  int before[N], all[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) before[k] = all[k] = 0;
+#pragma unroll 1
+  for (int u = 0; u < kPlanWaves; ++u) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int x = buf[u * N + k];
+      before[k] += u < wv ? x : 0;
+      all[k] += x;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    ex[k] = before[k] + inc[k] - v[k];
+    tot[k] = all[k];
+  }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
+  __shared__ int2 s_wl[kPlanMaxB];            // per request: window, keys (ctx + window)
+  __shared__ int s_buf[kPlanWaves * 8];
+  __shared__ long long s_red[kPlanWaves];
+  __shared__ int hist[64];
   const int t = threadIdx.x;
+  const int lane = t & 63;
   const int B = p.B;
   const AttnShape& sh = p.sh;
+  const int seg = ceil_div(B, kPlanThreads);
+  const int i0 = t * seg;
+  const int i1 = min(i0 + seg, B);
+  auto tiles_of_w = [&](int w) { return ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb; };
 
   // total work: sum over tiles of keys visible to the tile's last row
   long long work = 0;
-  for (int i = t; i < B; i += 1024) {
+  for (int i = i0; i < i1; ++i) {
     const int w = p.cu[i + 1] - p.cu[i];
     const int L = p.ctx[i] + w;
-    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
-    work += (long long)tiles * L;
+    s_wl[i] = make_int2(w, L);
+    work += (long long)tiles_of_w(w) * L;
   }
-  red[t] = work;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) work += __shfl_xor(work, off);
+  if (lane == 0) s_red[t >> 6] = work;
+  if (t < 64) hist[t] = 0;
   __syncthreads();
-  for (int off = 512; off > 0; off >>= 1) {
-    if (t < off) red[t] += red[t + off];
-    __syncthreads();
-  }
-  if (t == 0) {
-    long long c = (red[0] + p.target - 1) / p.target;
-    c = (c + kNK - 1) / kNK * kNK;
-    if (c < kMinChunk) c = kMinChunk;
-    if (c > (1 << 30)) c = 1 << 30;
-    s_chunk = (int)c;
-  }
-  __syncthreads();
+  long long all_work = 0;
+  for (int u = 0; u < kPlanWaves; ++u) all_work += s_red[u];
+  long long c0 = (all_work + p.target - 1) / p.target;
+  c0 = (c0 + kNK - 1) / kNK * kNK;
+  if (c0 < kMinChunk) c0 = kMinChunk;
+  if (c0 > (1 << 30)) c0 = 1 << 30;
+  int C = (int)c0;
 
-  // grow the chunk until items and partial slots fit their buffers
+  // grow the chunk until items and partial slots fit their buffers (both
+  // counts fall as the chunk grows)
   for (int iter = 0; iter < 32; ++iter) {
-    const int C = s_chunk;
-    int n_items = 0, n_parts = 0;
-    for (int i = t; i < B; i += 1024) {
-      const int w = p.cu[i + 1] - p.cu[i];
-      const int L = p.ctx[i] + w;
-      const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
-      const int ns = L > 0 ? ceil_div(L, C) : 1;
-      n_items += ns * tiles;
-      n_parts += ns > 1 ? ns * tiles : 0;
+    int cnt[2] = {0, 0}, ex[2], tot[2];
+    for (int i = i0; i < i1; ++i) {
+      const int2 wl = s_wl[i];
+      const int tiles = tiles_of_w(wl.x);
+      const int ns = wl.y > 0 ? ceil_div(wl.y, C) : 1;
+      cnt[0] += ns * tiles;
+      cnt[1] += ns > 1 ? ns * tiles : 0;
     }
-    scan_a[t] = n_items;
-    scan_b[t] = n_parts;
-    __syncthreads();
-    for (int off = 512; off > 0; off >>= 1) {
-      if (t < off) { scan_a[t] += scan_a[t + off]; scan_b[t] += scan_b[t + off]; }
-      __syncthreads();
-    }
-    const bool fits = scan_a[0] <= p.item_cap && scan_b[0] <= p.part_cap;
-    __syncthreads();
-    if (fits || s_chunk >= (1 << 29)) break;
-    if (t == 0) s_chunk = s_chunk * 2;
-    __syncthreads();
+    block_excl_scan<2>(cnt, ex, tot, s_buf);
+    if ((tot[0] <= p.item_cap && tot[1] <= p.part_cap) || C >= (1 << 29)) break;
+    C *= 2;
   }
-  const int C = s_chunk;
 
   // A group is the set of tiles of one request that read one key chunk; its
   // tiles run on one XCD, one after another in that XCD's list, so the chunk
@@ -134,61 +184,36 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
   // first (counting sort over 64 length buckets) and dealt to the 8 lists in
   // snake order (ranks 8c..8c+7 go to XCDs 0..7 for even c, 7..0 for odd c),
   // which balances the lists and starts the longest items first.
-  __shared__ int hist[64];
-  if (t < 64) hist[t] = 0;
-  const int seg = ceil_div(B, 1024);
-  const int i0 = t * seg;
-  int my_groups = 0, my_parts = 0;
-  for (int s = 0; s < seg; ++s) {
-    const int i = i0 + s;
-    if (i >= B) break;
-    const int w = p.cu[i + 1] - p.cu[i];
-    const int L = p.ctx[i] + w;
-    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
-    const int ns = L > 0 ? ceil_div(L, C) : 1;
-    my_groups += ns;
-    my_parts += ns > 1 ? ns * tiles : 0;
+  int mine[2] = {0, 0}, off2[2], tot2[2];
+  for (int i = i0; i < i1; ++i) {
+    const int2 wl = s_wl[i];
+    const int ns = wl.y > 0 ? ceil_div(wl.y, C) : 1;
+    mine[0] += ns;
+    mine[1] += ns > 1 ? ns * tiles_of_w(wl.x) : 0;
   }
-  scan_a[t] = my_groups;
-  scan_b[t] = my_parts;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int a = t >= off ? scan_a[t - off] : 0;
-    const int b = t >= off ? scan_b[t - off] : 0;
-    __syncthreads();
-    scan_a[t] += a;
-    scan_b[t] += b;
-    __syncthreads();
-  }
-  const int n_groups = scan_a[1023];
-  const int n_parts = scan_b[1023];
-  int grp_off = scan_a[t] - my_groups;
-  int part_off = scan_b[t] - my_parts;
+  block_excl_scan<2>(mine, off2, tot2, s_buf);
+  const int n_groups = tot2[0];
+  const int n_parts = tot2[1];
+  int grp_off = off2[0], part_off = off2[1];
   // bucket of a chunk of `len` keys: 0 for a full chunk, up to 63 for the shortest
   auto bucket = [&](int len) { return (int)(((long long)(C - len) * 64) / C); };
-  for (int s = 0; s < seg; ++s) {
-    const int i = i0 + s;
-    if (i >= B) break;
-    const int L = p.ctx[i] + p.cu[i + 1] - p.cu[i];
+  for (int i = i0; i < i1; ++i) {
+    const int L = s_wl[i].y;
     const int ns = L > 0 ? ceil_div(L, C) : 1;
     for (int sp = 0; sp < ns; ++sp) atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
   }
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int b = 0; b < 64; ++b) {
-      const int n = hist[b];
-      hist[b] = run;
-      run += n;
-    }
+  if (t < 64) {   // exclusive scan of the 64 bucket counts by wave 0
+    int h[1] = {hist[t]};
+    const int own = h[0];
+    wave_incl_scan<1>(h);
+    hist[t] = h[0] - own;
   }
   __syncthreads();
-  for (int s = 0; s < seg; ++s) {
-    const int i = i0 + s;
-    if (i >= B) break;
-    const int w = p.cu[i + 1] - p.cu[i];
-    const int L = p.ctx[i] + w;
-    const int tiles = ceil_div(w, sh.RT) * sh.Hkv * sh.n_hb;
+  for (int i = i0; i < i1; ++i) {
+    const int2 wl = s_wl[i];
+    const int tiles = tiles_of_w(wl.x);
+    const int L = wl.y;
     const int ns = L > 0 ? ceil_div(L, C) : 1;
     p.req_info[i] = make_int4(ns, grp_off, ns > 1 ? part_off : -1, tiles);
     for (int sp = 0; sp < ns; ++sp) {
@@ -201,12 +226,10 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
   __syncthreads();   // the ranked groups are visible to the whole workgroup
 
   // items per (cycle, XCD) slot, scanned along the cycles of each XCD
-  __shared__ int xs[1024][8];
   const int nc = ceil_div(n_groups, 8);
-  const int segc = ceil_div(nc, 1024);
+  const int segc = ceil_div(nc, kPlanThreads);
   auto rank_of = [](int c, int x) { return 8 * c + ((c & 1) ? 7 - x : x); };
-  auto tiles_of = [&](int i) { return ceil_div(p.cu[i + 1] - p.cu[i], sh.RT) * sh.Hkv * sh.n_hb; };
-  int cnt[8];
+  int cnt[8], pos[8], xlen[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) cnt[x] = 0;
   for (int cc = 0; cc < segc; ++cc) {
@@ -215,28 +238,17 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int r = rank_of(c, x);
-      if (r < n_groups) cnt[x] += tiles_of(p.grp[r].x);
+      if (r < n_groups) cnt[x] += tiles_of_w(s_wl[p.grp[r].x].x);
     }
   }
-#pragma unroll
-  for (int x = 0; x < 8; ++x) xs[t][x] = cnt[x];
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int a[8];
-#pragma unroll
-    for (int x = 0; x < 8; ++x) a[x] = t >= off ? xs[t - off][x] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 8; ++x) xs[t][x] += a[x];
-    __syncthreads();
-  }
-  int xoff[8], pos[8];
+  block_excl_scan<8>(cnt, pos, xlen, s_buf);
+  int xoff[8];
   int total = 0;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
     xoff[x] = total;
-    total += xs[1023][x];
-    pos[x] = xoff[x] + xs[t][x] - cnt[x];
+    total += xlen[x];
+    pos[x] += xoff[x];
   }
   for (int cc = 0; cc < segc; ++cc) {
     const int c = t * segc + cc;
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
       const int r = rank_of(c, x);
       if (r >= n_groups) continue;
       const int2 g = p.grp[r];
-      const int tiles = tiles_of(g.x);
+      const int tiles = tiles_of_w(s_wl[g.x].x);
       for (int tl = 0; tl < tiles; ++tl) p.items[pos[x] + tl] = make_int4(g.x, tl, g.y, 0);
       pos[x] += tiles;
     }
@@ -258,7 +270,7 @@ __global__ __launch_bounds__(1024) void k_attn_plan(PlanParams p) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       p.hdr[kHdrXOff + x] = xoff[x];
-      p.hdr[kHdrXLen + x] = xs[1023][x];
+      p.hdr[kHdrXLen + x] = xlen[x];
       p.hdr[kHdrCtr + x] = 0;
     }
   }
@@ -303,18 +315,45 @@ __device__ inline uint2 lds_tr16(uint32_t addr) {
 // Persistent workers: the hardware places workgroup b on XCD b % 8.  A
 // workgroup takes the next item of its XCD's list (longest first) and, once
 // that list is empty, of the other lists; it returns -1 when all are empty,
-// so every workgroup ends after at most one failed take per list.
-__device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done) {
+// so every workgroup ends after at most one failed take per list.  Each
+// successful take also issues the take of the following item, so that
+// atomic's round trip overlaps the current item instead of stalling the
+// workgroup between items (a taken item is always run: the pending take is
+// resolved first on the next call).
+struct Taker {
+  unsigned done = 0;   // lists found empty
+  int pend_y = -1;     // list of the take issued ahead, or -1
+  int pend_k = 0;      // position it returned
+};
+
+__device__ inline int take_at(const MainParams& p, int y, int k, unsigned& done) {
+  if (k < p.hdr[kHdrXLen + y]) return p.hdr[kHdrXOff + y] + k;
+  done |= 1u << y;
+  return -1;
+}
+
+__device__ inline int next_item(const MainParams& p, int* s_item, Taker& tk) {
   __syncthreads();   // every thread has read the previous item
   if (threadIdx.x == 0) {
     const int x = blockIdx.x & 7;
     int it = -1;
+    if (tk.pend_y >= 0) {
+      it = take_at(p, tk.pend_y, tk.pend_k, tk.done);
+      tk.pend_y = -1;
+    }
     for (int probe = 0; probe < 8 && it < 0; ++probe) {
       const int y = (x + probe) & 7;
-      if (done & (1u << y)) continue;
-      const int k = atomicAdd(p.ctr + y, 1);
-      if (k < p.hdr[kHdrXLen + y]) it = p.hdr[kHdrXOff + y] + k;
-      else done |= 1u << y;
+      if (tk.done & (1u << y)) continue;
+      it = take_at(p, y, atomicAdd(p.ctr + y, 1), tk.done);
+    }
+    if (it >= 0) {
+      for (int probe = 0; probe < 8; ++probe) {
+        const int y = (x + probe) & 7;
+        if (tk.done & (1u << y)) continue;
+        tk.pend_y = y;
+        tk.pend_k = atomicAdd(p.ctr + y, 1);
+        break;
+      }
     }
     *s_item = it;
   }
@@ -397,9 +436,9 @@ template <bool FAST>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
-  unsigned done = 0;
+  Taker tk;
   for (;;) {
-    const int item = next_item(p, &s_item, done);
+    const int item = next_item(p, &s_item, tk);
     if (item < 0) break;
     attn_mla_item<FAST>(p, item, smem);
   }
@@ -817,41 +856,68 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   }
 }
 
+// Max over lanes l, l^16, l^32, l^48 through gfx950's lane-swap moves (VALU,
+// no LDS round trip): permlane32_swap exchanges the two 32-lane halves and
+// permlane16_swap the odd and even 16-lane rows; each returns both swapped
+// registers, so the max of the pair is the max over the partner lanes.
+__device__ inline float max_lanes_xor16_32(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // ---- GQA bf16 kernel (head dim 128): LDS DMA ring -------------------------------
 //
-// One workgroup = NW waves = 16*NW query vectors (rows x query heads) of one
-// KV head against one key chunk, as in the latent kernel: K and V tiles of
-// 32 keys arrive by direct global->LDS DMA into a ring of stages issued one
-// stage short of the ring ahead (the kernel is bound by HBM, so what matters
-// is the bytes in flight), rows of 256 bytes whose 16-byte chunks are XOR-swizzled by
-// (row >> 1) & 7, the request's page-table entries for the chunk in an LDS
-// window (with power-of-two pages of at least 4 keys each DMA instruction's
-// four rows share a page, so the DMA is a uniform page base plus lane
-// offsets).  Per tile the scores S^T = K Q^T and O^T += V^T P^T run on bf16
-// 16x16x32 MFMAs (V^T fragments through transposing LDS reads) with an online
-// softmax: a running max per query vector, the accumulators rescaled when it
-// grows.  Ring depth (measured): two-wave workgroups run one per CU
-// with six stages; four-wave workgroups run two per CU with four stages, so
-// one workgroup's softmax overlaps the other's loads.
+// One workgroup = NV*KS waves against 16*NV query vectors (rows x query
+// heads) of one KV head and one key chunk.  Wave w serves vector group
+// w % NV and key group w / NV: the keys advance in super-tiles of KS*32 keys
+// and key group k takes the k-th 32-key sub-tile of each, with an online
+// softmax of its own; the KS states of a vector are merged through LDS at
+// the end of the item.  Splitting the keys between waves puts a wave on
+// every SIMD of the CU while one workgroup per CU keeps the bytes in flight
+// (and so the memory latency) moderate.
+//
+// K and V sub-tiles arrive by direct global->LDS DMA into a ring of kStages
+// super-tiles issued one stage short of the ring ahead; rows of 256 bytes
+// whose 16-byte chunks are XOR-swizzled by (row >> 1) & 7; the request's
+// page-table entries for the chunk sit in an LDS window (with power-of-two
+// pages of at least 4 keys each DMA instruction's four rows share a page, so
+// the DMA is a uniform page base plus lane offsets).  Per sub-tile the
+// scores S^T = K Q^T and O^T += V^T P^T run on bf16 16x16x32 MFMAs (V^T
+// fragments through transposing LDS reads); the accumulators are rescaled
+// only when some vector's running max grows.
 constexpr int kGqaD = 128;
 constexpr int kGqaRow = kGqaD * 2;                         // bytes per K or V row
-constexpr int kGqaStage = 2 * kNK * kGqaRow;               // K rows then V rows: 16 KB
-template <int NW>
+constexpr int kGqaSub = 2 * kNK * kGqaRow;                 // one sub-tile: K rows then V rows, 16 KB
+constexpr int kGqaKS = 2;                                  // key groups per workgroup
+template <int NV>
 struct GqaCfg {
-  static constexpr int kStages = NW == 2 ? 6 : 4;
-  static constexpr int kLds = kStages * kGqaStage + kPageWin * 4;
+  static constexpr int kWaves = NV * kGqaKS;
+  static constexpr int kStages = 4;
+  static constexpr int kStage = kGqaKS * kGqaSub;
+  static constexpr int kLds = kStages * kStage + kPageWin * 4;
+  // the merge buffer (kGqaKS - 1 partner states of NV waves: 64 lanes x
+  // (32 accumulators + max + sum) floats) reuses the ring after the loop
+  static_assert((kGqaKS - 1) * NV * 64 * 34 * 4 <= kStages * kStage, "merge buffer");
 };
 
-template <int NW, bool FAST>
+template <int NV, bool FAST>
 __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, unsigned char* smem) {
-  constexpr int NST = GqaCfg<NW>::kStages;
-  constexpr int kDmaPer = kGqaStage / 1024 / NW;   // 1 KB DMA instructions per wave and tile
-  constexpr int kChunksRow = kGqaRow / 16;         // 16
-  int* pwin = reinterpret_cast<int*>(smem + NST * kGqaStage);
+  using Cfg = GqaCfg<NV>;
+  constexpr int NST = Cfg::kStages;
+  constexpr int NWV = Cfg::kWaves;
+  constexpr int kDmaPer = Cfg::kStage / 1024 / NWV;   // 1 KB DMA instructions per wave and super-tile
+  constexpr int kChunksRow = kGqaRow / 16;            // 16
+  constexpr int kInstSub = kGqaSub / 1024;            // 16 instructions per sub-tile
+  constexpr int kSuper = kGqaKS * kNK;                // keys per super-tile
+  int* pwin = reinterpret_cast<int*>(smem + NST * Cfg::kStage);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int vg = wid % NV;   // vector group
+  const int kg = wid / NV;   // key group
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
@@ -882,20 +948,20 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
     npg = kPageWin;
   }
   const int* pt_row = p.page_table + (size_t)i * p.max_pages;
-  for (int x = tid; x < npg; x += 64 * NW) {
+  for (int x = tid; x < npg; x += 64 * NWV) {
     int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
     if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
     pwin[x] = pg;
   }
 
   // this lane's query vector
-  const int qv = wid * 16 + n16;
+  const int qv = vg * 16 + n16;
   const int q_row_local = qv / p.NH;
   const int head = g * p.G + hb * p.NH + (qv % p.NH);
   const bool q_valid = q_row_local < rows_here;
   const int q_row = row_start + row0 + q_row_local;
   const int limit = c + row0 + q_row_local;   // last visible key position
-  // tiles ending at or before this key need no mask for any real row
+  // sub-tiles ending at or before this key need no mask for any real row
   const int full_lim = min(c + row0, kv_end - 1);
   u32x4_t qf[kGqaD / 32];
 #pragma unroll
@@ -910,75 +976,83 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   wait_vm<0>();
   __syncthreads();   // page window visible
 
-  const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
+  const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kSuper - 1) / kSuper : 0;
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
   const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
   const size_t kv_head = (size_t)p.Hkv * kGqaD;   // elements between consecutive key rows
 
-  // DMA of tile t into stage st: this wave's instruction e moves chunks
-  // (wid*kDmaPer + e)*64 + lane of the stage (K rows 0..31, then V rows);
-  // chunk cc of a row sits at physical position cc and holds logical chunk
-  // cc ^ swz(row)
-  // this lane's row and logical chunk (bytes) in each of its DMA instructions
-  int drow[kDmaPer], dlc[kDmaPer];
+  // DMA of super-tile t into stage st: this wave's instruction e is
+  // instruction q = wid*kDmaPer + e of the stage, i.e. instruction q % 16 of
+  // sub-tile q / 16, moving chunks (q % 16)*64 + lane of that sub-tile (K
+  // rows 0..31, then V rows); chunk cc of a row sits at physical position cc
+  // and holds logical chunk cc ^ swz(row).  Per lane: the key offset within
+  // the super-tile and the logical chunk (bytes) of each instruction.
+  int dkey[kDmaPer], dlc[kDmaPer];
 #pragma unroll
   for (int e = 0; e < kDmaPer; ++e) {
-    const int c_ = (wid * kDmaPer + e) * 64 + lane;
-    drow[e] = (c_ / kChunksRow) % kNK;
-    dlc[e] = ((c_ % kChunksRow) ^ swz(drow[e])) * 16;
+    const int q = wid * kDmaPer + e;
+    const int c_ = (q % kInstSub) * 64 + lane;
+    const int row = (c_ / kChunksRow) % kNK;
+    dkey[e] = (q / kInstSub) * kNK + row;
+    dlc[e] = ((c_ % kChunksRow) ^ swz(row)) * 16;
   }
   const unsigned char* gk = reinterpret_cast<const unsigned char*>(p.k + (size_t)g * kGqaD);
   const unsigned char* gv = reinterpret_cast<const unsigned char*>(p.v + (size_t)g * kGqaD);
-  const size_t page_bytes = (size_t)P * kv_head * 2;
+  const uint64_t page_bytes = (uint64_t)P * kv_head * 2;
   const uint32_t row_bytes = (uint32_t)(kv_head * 2);
 
-  auto issue = [&](int t, int st) {
-    const int t0 = kv_begin + t * kNK;
+  // FAST: instruction q's four rows lie in one page, clamped rows included,
+  // so its DMA is a uniform page base plus a 32-bit lane offset; the page
+  // reads of a super-tile are issued together ahead of the fragment reads
+  auto pages = [&](int t, int (&pgv)[kDmaPer]) {
+    const int t0 = kv_begin + t * kSuper;
+#pragma unroll
+    for (int e = 0; e < kDmaPer; ++e) {
+      const int q = wid * kDmaPer + e;
+      const int jb = min(t0 + (q / kInstSub) * kNK + 4 * (q % (kNK / 4)), last);
+      pgv[e] = pwin[min((jb >> p.log2P) - pg0, npg - 1)];
+    }
+  };
+  auto issue = [&](int t, int st, const int (&pgv)[kDmaPer]) {
+    const int t0 = kv_begin + t * kSuper;
     if constexpr (FAST) {
-      // instruction q's four rows (4*(q%8) ..) lie in one page, clamped rows
-      // included: a uniform page base plus a 32-bit lane offset; the page
-      // reads are issued together
-      int pgv[kDmaPer];
 #pragma unroll
       for (int e = 0; e < kDmaPer; ++e) {
         const int q = wid * kDmaPer + e;
-        const int jb = min(t0 + 4 * (q % (kNK / 4)), last);
-        pgv[e] = pwin[min((jb >> p.log2P) - pg0, npg - 1)];
-      }
-#pragma unroll
-      for (int e = 0; e < kDmaPer; ++e) {
-        const int q = wid * kDmaPer + e;
-        const bool is_v = q >= kNK * kChunksRow / 64;   // uniform: the V rows follow the K rows
-        const int pg = __builtin_amdgcn_readfirstlane(pgv[e]);
-        const void* base = uniform_ptr((is_v ? gv : gk) + (size_t)pg * page_bytes);
-        const int j = min(t0 + drow[e], last);
-        dma16_s((uint32_t)(j & (P - 1)) * row_bytes + (uint32_t)dlc[e], base,
-                __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+        const bool is_v = (q % kInstSub) >= kInstSub / 2;   // uniform: the V rows follow the K rows
+        const uint32_t pg = (uint32_t)__builtin_amdgcn_readfirstlane(pgv[e]);   // validated: >= 0
+        const void* base = uniform_ptr((is_v ? gv : gk) + (uint64_t)pg * page_bytes);
+        const int j = min(t0 + dkey[e], last);
+        // in-page row times row bytes: both below 2^24 (checked on the host)
+        dma16_s(__umul24((uint32_t)(j & (P - 1)), row_bytes) + (uint32_t)dlc[e], base,
+                __builtin_amdgcn_readfirstlane(lds + st * Cfg::kStage + q * 1024));
       }
     } else {
+      (void)pgv;
 #pragma unroll
       for (int e = 0; e < kDmaPer; ++e) {
         const int q = wid * kDmaPer + e;
-        const bool is_v = q >= kNK * kChunksRow / 64;
-        const int j = min(t0 + drow[e], last);
+        const bool is_v = (q % kInstSub) >= kInstSub / 2;
+        const int j = min(t0 + dkey[e], last);
         const int pg = pwin[min(j / P - pg0, npg - 1)];
         const size_t tok = (size_t)pg * P + (j % P);
-        dma16((is_v ? gv : gk) + tok * row_bytes + dlc[e], __builtin_amdgcn_readfirstlane(lds + st * kGqaStage + q * 1024));
+        dma16((is_v ? gv : gk) + tok * row_bytes + dlc[e],
+              __builtin_amdgcn_readfirstlane(lds + st * Cfg::kStage + q * 1024));
       }
     }
   };
 
-  // fragment offsets: QK A rows 16*mb + n16, logical chunk 4*ks + grp;
-  // V^T transposing reads rows kb + n16/4 (kb = 4*grp or 16 + 4*grp),
-  // elements 16*mb + 4*(n16 & 3): logical chunk 2*mb + ((n16 & 3) >> 1)
-  auto k_addr = [&](uint32_t stg, int mb, int ks) {
+  // fragment offsets within a sub-tile: QK A rows 16*mb + n16, logical
+  // chunk 4*ks + grp; V^T transposing reads rows kb + n16/4 (kb = 4*grp or
+  // 16 + 4*grp), elements 16*mb + 4*(n16 & 3): logical chunk 2*mb + ((n16 & 3) >> 1)
+  auto k_addr = [&](uint32_t sub, int mb, int ks) {
     const int r = mb * 16 + n16;
-    return stg + (uint32_t)(r * kGqaRow + ((4 * ks + grp) ^ swz(r)) * 16);
+    return sub + (uint32_t)(r * kGqaRow + ((4 * ks + grp) ^ swz(r)) * 16);
   };
-  auto v_addr = [&](uint32_t stg, int hh, int mb) {
+  auto v_addr = [&](uint32_t sub, int hh, int mb) {
     const int r = hh * 16 + grp * 4 + (n16 >> 2);
     const int lc = 2 * mb + ((n16 & 3) >> 1);
-    return stg + (uint32_t)(kNK * kGqaRow + r * kGqaRow + (lc ^ swz(r)) * 16 + (n16 & 1) * 8);
+    return sub + (uint32_t)(kNK * kGqaRow + r * kGqaRow + (lc ^ swz(r)) * 16 + (n16 & 1) * 8);
   };
 
   f32x4_t oacc[kGqaD / 16];
@@ -987,29 +1061,46 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   float m_run = -INFINITY;
   float l_part = 0.f;
 
-  // prologue: tiles 0 .. NST-2 in flight
+  // prologue: super-tiles 0 .. NST-2 in flight
 #pragma unroll
-  for (int u = 0; u < NST - 1; ++u)
-    if (u < n_tiles) issue(u, u);
+  for (int u = 0; u < NST - 1; ++u) {
+    if (u < n_tiles) {
+      int pgv[kDmaPer];
+      if constexpr (FAST) pages(u, pgv);
+      issue(u, u, pgv);
+    }
+  }
   int st = 0;
   for (int t = 0; t < n_tiles; ++t) {
-    // tile t has landed once at most the NST-2 younger tiles remain
+    // super-tile t has landed once at most the NST-2 younger ones remain
     if (t + NST - 2 < n_tiles) wait_vm<(NST - 2) * kDmaPer>();
     else wait_vm<0>();
-    __syncthreads();   // tile t visible; every wave is done with tile t-1
-    if (t + NST - 1 < n_tiles) issue(t + NST - 1, (t + NST - 1) % NST);
-    const uint32_t stg = lds + st * kGqaStage;
+    __syncthreads();   // super-tile t visible; every wave is done with t-1
+    const bool more = t + NST - 1 < n_tiles;
+    int pgv[kDmaPer];
+    if constexpr (FAST) {
+      if (more) pages(t + NST - 1, pgv);
+    }
+    const uint32_t sub = lds + st * Cfg::kStage + kg * kGqaSub;
+    // all K fragments of the sub-tile in flight before the DMA issue and the MFMAs
+    u32x4_t kf[kNK / 16][kGqaD / 32];
+#pragma unroll
+    for (int mb = 0; mb < kNK / 16; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < kGqaD / 32; ++ks) kf[mb][ks] = lds_b128(k_addr(sub, mb, ks));
+    if (more) issue(t + NST - 1, (t + NST - 1) % NST, pgv);
+    __builtin_amdgcn_sched_barrier(0);
     st = (st == NST - 1) ? 0 : st + 1;
-    const int t0 = kv_begin + t * kNK;
+    const int t0 = kv_begin + t * kSuper + kg * kNK;   // this wave's first key
 
     // S^T (keys x query vectors): lane holds keys 16*mb + 4*grp + j of query n16
     f32x4_t sacc[kNK / 16];
 #pragma unroll
-    for (int mb = 0; mb < kNK / 16; ++mb) {
-      sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < kNK / 16; ++mb) sacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kGqaD / 32; ++ks) sacc[mb] = mfma16(lds_b128(k_addr(stg, mb, ks)), qf[ks], sacc[mb]);
-    }
+    for (int ks = 0; ks < kGqaD / 32; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < kNK / 16; ++mb) sacc[mb] = mfma16(kf[mb][ks], qf[ks], sacc[mb]);
     float tmax = -INFINITY;
     const bool full = (t0 + kNK - 1 <= full_lim);   // uniform: no key past any real row's limit
 #pragma unroll
@@ -1025,8 +1116,7 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
         tmax = fmaxf(tmax, s);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = max_lanes_xor16_32(tmax);
     // no branch around the MFMAs: a fully masked query gets p = 0
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -1051,14 +1141,14 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
     m_run = m_new;
     // P^T as the B operand: k-slots 8*grp+x <-> keys 4*grp+x (x<4), 16+4*grp+x-4
     u32x4_t pb;
-    pb[0] = pack_bf16x2(sacc[0][0], sacc[0][1]);
-    pb[1] = pack_bf16x2(sacc[0][2], sacc[0][3]);
-    pb[2] = pack_bf16x2(sacc[1][0], sacc[1][1]);
-    pb[3] = pack_bf16x2(sacc[1][2], sacc[1][3]);
+    pb[0] = cvt_bf16x2(sacc[0][0], sacc[0][1]);
+    pb[1] = cvt_bf16x2(sacc[0][2], sacc[0][3]);
+    pb[2] = cvt_bf16x2(sacc[1][0], sacc[1][1]);
+    pb[3] = cvt_bf16x2(sacc[1][2], sacc[1][3]);
 #pragma unroll
     for (int mb = 0; mb < kGqaD / 16; ++mb) {
-      const uint2 lo = lds_tr16(v_addr(stg, 0, mb));
-      const uint2 hi = lds_tr16(v_addr(stg, 1, mb));
+      const uint2 lo = lds_tr16(v_addr(sub, 0, mb));
+      const uint2 hi = lds_tr16(v_addr(sub, 1, mb));
       oacc[mb] = mfma16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, oacc[mb]);
     }
   }
@@ -1067,6 +1157,35 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   // normaliser over the four lane groups that share a query vector
   float l_tot = l_part + __shfl_xor(l_part, 16);
   l_tot += __shfl_xor(l_tot, 32);
+
+  // merge the key groups: groups 1.. publish (accumulators, max, sum) per
+  // lane, group 0 rescales all of them to the common max and adds
+  __syncthreads();   // every wave is done reading the ring
+  float* xch = reinterpret_cast<float*>(smem);
+  if (kg > 0) {
+    float* dst = xch + ((size_t)((kg - 1) * NV + vg) * 64) * 34;
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb)
+      *reinterpret_cast<f32x4_t*>(dst + (mb * 64 + lane) * 4) = oacc[mb];
+    dst[32 * 64 + lane] = m_run;
+    dst[33 * 64 + lane] = l_tot;
+  }
+  __syncthreads();
+  if (kg > 0) return;
+#pragma unroll
+  for (int k = 1; k < kGqaKS; ++k) {
+    const float* src = xch + ((size_t)((k - 1) * NV + vg) * 64) * 34;
+    const float m_o = src[32 * 64 + lane];
+    const float l_o = src[33 * 64 + lane];
+    const float m_c = fmaxf(m_run, m_o);
+    const float a_s = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_c);
+    const float a_o = (m_o == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_o - m_c);
+#pragma unroll
+    for (int mb = 0; mb < kGqaD / 16; ++mb)
+      oacc[mb] = oacc[mb] * a_s + *reinterpret_cast<const f32x4_t*>(src + (mb * 64 + lane) * 4) * a_o;
+    l_tot = l_tot * a_s + l_o * a_o;
+    m_run = m_c;
+  }
   if (!q_valid) return;
 
   if (ns == 1) {
@@ -1075,8 +1194,8 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
 #pragma unroll
     for (int mb = 0; mb < kGqaD / 16; ++mb) {
       uint2 pk;
-      pk.x = pack_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv);
-      pk.y = pack_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv);
+      pk.x = cvt_bf16x2(oacc[mb][0] * inv, oacc[mb][1] * inv);
+      pk.y = cvt_bf16x2(oacc[mb][2] * inv, oacc[mb][3] * inv);
       *reinterpret_cast<uint2*>(dst + mb * 16 + grp * 4) = pk;
     }
     if (p.lse && grp == 0)
@@ -1084,27 +1203,27 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   } else {
     const int slot = info.z + sp * info.w + tile;
     if (slot < 0 || slot >= p.part_cap) return;   // the plan keeps slots below the cap
-    float* po = p.part_o + ((size_t)slot * (16 * NW) + qv) * kGqaD;
+    float* po = p.part_o + ((size_t)slot * (16 * NV) + qv) * kGqaD;
 #pragma unroll
     for (int mb = 0; mb < kGqaD / 16; ++mb)
       *reinterpret_cast<f32x4_t*>(po + mb * 16 + grp * 4) = oacc[mb];
     if (grp == 0) {
-      float* pml = p.part_ml + ((size_t)slot * (16 * NW) + qv) * 2;
+      float* pml = p.part_ml + ((size_t)slot * (16 * NV) + qv) * 2;
       pml[0] = m_run;
       pml[1] = l_tot;
     }
   }
 }
 
-template <int NW, bool FAST>
-__global__ __launch_bounds__(64 * NW) void k_attn_gqa(MainParams p) {
+template <int NV, bool FAST>
+__global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
-  unsigned done = 0;
+  Taker tk;
   for (;;) {
-    const int item = next_item(p, &s_item, done);
+    const int item = next_item(p, &s_item, tk);
     if (item < 0) break;
-    attn_gqa_item<NW, FAST>(p, item, smem);
+    attn_gqa_item<NV, FAST>(p, item, smem);
   }
 }
 
@@ -1331,24 +1450,26 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
   sh->RT = QT / sh->NH;
   sh->n_hb = G / sh->NH;
   sh->tpr_max = ((gamma + sh->RT - 1) / sh->RT) * Hkv * sh->n_hb;
+  sh->target = latent ? kTargetItemsLatent : kTargetItemsGqa;
   return true;
 }
 
 struct AttnScratch {
   size_t hdr, req_info, items, grp, part_ml, part_o, total;
-  int item_cap;
+  int item_cap, part_slots;
 };
 
 AttnScratch attn_layout(int B, const AttnShape& sh, int Dv) {
   AttnScratch L;
-  L.item_cap = kTargetItems + B * sh.tpr_max;
+  L.item_cap = sh.target + B * sh.tpr_max;
+  L.part_slots = (int)std::min<size_t>(kPartSlotsMax, kPartBytes / ((size_t)sh.QT * Dv * sizeof(float)));
   size_t off = 0;
   L.hdr = off; off = align_up(off + 256, 256);
   L.req_info = off; off = align_up(off + sizeof(int4) * (size_t)B, 256);
   L.items = off; off = align_up(off + sizeof(int4) * (size_t)L.item_cap, 256);
   L.grp = off; off = align_up(off + sizeof(int2) * (size_t)L.item_cap, 256);
-  L.part_ml = off; off = align_up(off + sizeof(float) * 2 * (size_t)kPartSlots * sh.QT, 256);
-  L.part_o = off; off = align_up(off + sizeof(float) * (size_t)kPartSlots * sh.QT * Dv, 256);
+  L.part_ml = off; off = align_up(off + sizeof(float) * 2 * (size_t)L.part_slots * sh.QT, 256);
+  L.part_o = off; off = align_up(off + sizeof(float) * (size_t)L.part_slots * sh.QT * Dv, 256);
   L.total = off;
   return L;
 }
@@ -1378,21 +1499,23 @@ hipError_t persistent_grid(const void* kern, int threads, int lds, int* grid) {
   return hipSuccess;
 }
 
-template <int NW, bool FAST>
+template <int NV, bool FAST>
 hipError_t launch_gqa_t(const MainParams& mp, hipStream_t s) {
-  const void* kern = reinterpret_cast<const void*>(k_attn_gqa<NW, FAST>);
-  constexpr int lds = GqaCfg<NW>::kLds;
+  const void* kern = reinterpret_cast<const void*>(k_attn_gqa<NV, FAST>);
+  constexpr int lds = GqaCfg<NV>::kLds;
+  constexpr int threads = 64 * GqaCfg<NV>::kWaves;
   hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
   int grid = 0;
-  if ((e = persistent_grid(kern, 64 * NW, lds, &grid)) != hipSuccess) return e;
-  hipLaunchKernelGGL((k_attn_gqa<NW, FAST>), dim3(grid), dim3(64 * NW), lds, s, mp);
+  if ((e = persistent_grid(kern, threads, lds, &grid)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_attn_gqa<NV, FAST>), dim3(grid), dim3(threads), lds, s, mp);
   return hipGetLastError();
 }
 
-// GQA bf16 (head dim 128): NW = 2 or 4 waves; FAST: power-of-two pages of at least 4 keys
-hipError_t launch_gqa(const MainParams& mp, int nw, bool fast, hipStream_t s) {
-  if (nw == 2) return fast ? launch_gqa_t<2, true>(mp, s) : launch_gqa_t<2, false>(mp, s);
+// GQA bf16 (head dim 128): 16*nv query vectors per tile (nv = 2 or 4); FAST:
+// power-of-two pages of at least 4 keys
+hipError_t launch_gqa(const MainParams& mp, int nv, bool fast, hipStream_t s) {
+  if (nv == 2) return fast ? launch_gqa_t<2, true>(mp, s) : launch_gqa_t<2, false>(mp, s);
   return fast ? launch_gqa_t<4, true>(mp, s) : launch_gqa_t<4, false>(mp, s);
 }
 
@@ -1457,6 +1580,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   AttnShape sh;
   int nw = 0;
   if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw)) return hipErrorInvalidValue;
+  if (a.B > kPlanMaxB) return hipErrorInvalidValue;   // the plan caches one pair per request in LDS
   const AttnScratch L = attn_layout(a.B, sh, a.Dv);
   char* base = ws + kStatusBytes;
 
@@ -1471,8 +1595,8 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.B = a.B;
   pp.gamma = a.gamma;
   pp.item_cap = L.item_cap;
-  pp.part_cap = kPartSlots;
-  pp.target = kTargetItems;
+  pp.part_cap = L.part_slots;
+  pp.target = sh.target;
   pp.sh = sh;
   hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(1024), 0, s, pp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1501,7 +1625,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   mp.NH = sh.NH;
   mp.RT = sh.RT;
   mp.n_hb = sh.n_hb;
-  mp.part_cap = kPartSlots;
+  mp.part_cap = L.part_slots;
   mp.log2P = -1;
   if ((a.page_size & (a.page_size - 1)) == 0) {
     int l2 = 0;
@@ -1523,7 +1647,10 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
-    e = launch_gqa(mp, nw, mp.log2P >= 2, s);
+    // FAST: power-of-two pages of 4 .. 2^16 keys, rows under 2^24 bytes (24-bit
+    // in-page offsets)
+    const bool fast = mp.log2P >= 2 && mp.log2P <= 16 && (long long)a.Hkv * kGqaD * 2 < (1 << 24);
+    e = launch_gqa(mp, nw, fast, s);
   }
   if (e != hipSuccess) return e;
 
@@ -1543,7 +1670,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   cp.QT = sh.QT;
   cp.DV = a.Dv;
   cp.tpr_max = sh.tpr_max;
-  cp.part_cap = kPartSlots;
+  cp.part_cap = L.part_slots;
   const dim3 cgrid(a.B * sh.tpr_max * (sh.QT / kCombVec));
   if (a.Dv == 512) hipLaunchKernelGGL(k_attn_combine<512>, cgrid, dim3(256), 0, s, cp);
   else hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, cp);

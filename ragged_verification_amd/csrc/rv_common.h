@@ -9,8 +9,10 @@
 namespace rv {
 
 constexpr int kStatusBytes = 256;        // status word + padding at workspace start
-constexpr int kTargetItems = 1024;       // attention work items aimed for per launch
-constexpr int kPartSlots = 1024;         // split-KV partial tiles held in workspace
+constexpr int kTargetItemsLatent = 1024; // latent attention: work items aimed for per launch
+constexpr int kTargetItemsGqa = 512;     // GQA attention: about two items per persistent workgroup
+constexpr size_t kPartBytes = 128u << 20; // split-KV partial outputs held in workspace
+constexpr int kPartSlotsMax = 8192;      // split-KV partial tiles at most
 constexpr int kMinChunk = 256;           // smallest split-KV chunk (keys)
 
 // ---- sticky device status: first error wins --------------------------------
