@@ -273,7 +273,8 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
 } rv_lm_args;
-/* Device errors: BAD_TOKEN for a draft outside [0,V) (it never matches;
+/* Host errors: UNSUPPORTED for the rejection rule with V above 2^22.
+ * Device errors: BAD_TOKEN for a draft outside [0,V) (it never matches;
  * under rejection it is rejected), BAD_WINDOW. */
 rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
 

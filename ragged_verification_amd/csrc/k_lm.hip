@@ -289,6 +289,8 @@ struct AcceptParams {
 };
 
 constexpr int kAccThreads = 256;
+constexpr int kAccSeg = 4096;      // tokens per vocabulary segment of the bonus draw
+constexpr int kAccMaxSeg = kMaxVocabRejection / kAccSeg;
 
 __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
   __shared__ float s_val[kAccThreads];
@@ -296,7 +298,9 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
   __shared__ double s_sum[kAccThreads];
   __shared__ int s_pred[RV_MAX_GAMMA];
   __shared__ float s_lse[RV_MAX_GAMMA];
-  __shared__ int s_row, s_qrow, s_c, s_a;
+  __shared__ int s_row, s_qrow, s_c, s_a, s_bonus;
+  __shared__ double s_seg[kAccMaxSeg], s_total;
+  __shared__ int s_seg_last[kAccMaxSeg];
   const int tid = threadIdx.x;
 
   if (blockIdx.x == p.B) {  // padding rows [M, M_pad)
@@ -418,45 +422,129 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
     const float pv = expf(z[v] - lse);
     return qd ? fmaxf(0.f, pv - qd[v]) : pv;
   };
-  const int per = (p.V + kAccThreads - 1) / kAccThreads;
-  const int v_lo = tid * per;
-  const int v_hi = min(v_lo + per, p.V);
-  double csum = 0.0;
-  int last_pos = -1;
-  for (int v = v_lo; v < v_hi; ++v) {
-    const float r = weight(v);
-    csum += (double)r;
-    if (r > 0.f) last_pos = v;
-  }
-  // inclusive scan of chunk sums
-  s_sum[tid] = csum;
-  s_idx[tid] = last_pos;
-  __syncthreads();
-  for (int off = 1; off < kAccThreads; off <<= 1) {
-    const double add = tid >= off ? s_sum[tid - off] : 0.0;
-    const int li = tid >= off ? s_idx[tid - off] : -1;
-    __syncthreads();
-    s_sum[tid] += add;
-    s_idx[tid] = max(s_idx[tid], li);
-    __syncthreads();
-  }
-  const double total = s_sum[kAccThreads - 1];
-  const int last_any = s_idx[kAccThreads - 1];
-  const double target = (double)p.u_bonus[i] * total;
-  // exclusive prefix taken from the neighbour's inclusive value, so the
-  // per-thread intervals [excl, incl) tile the line without gaps or overlap
-  const double excl = tid > 0 ? s_sum[tid - 1] : 0.0;
-  __shared__ int s_bonus;
-  if (tid == 0) s_bonus = last_any;   // target at or past the end: last positive
-  __syncthreads();
-  if (excl <= target && target < s_sum[tid] && csum > 0.0) {
-    double run = excl;
-    int pick = last_pos;               // rounding left the walk short: chunk's last
-    for (int v = v_lo; v < v_hi; ++v) {
-      run += (double)weight(v);
-      if (run > target) { pick = v; break; }
+  // The vocabulary in segments of kAccSeg consecutive tokens; wave w sums
+  // segments w, w+4, ... with lane l reading the float4 runs l, l+64, ...
+  // of the segment (coalesced 1 KB loads, all in flight together).
+  const int lane = tid & 63, wv_id = tid >> 6;
+  const int n_seg = (p.V + kAccSeg - 1) / kAccSeg;
+  // float4 runs when every row starts 16-byte aligned
+  const bool vec4 = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0 && ((uintptr_t)p.q_rows % 16) == 0;
+  for (int sg = wv_id; sg < n_seg; sg += kAccThreads / 64) {
+    double acc = 0.0;
+    int lastp = -1;
+    const int s0 = sg * kAccSeg;
+    if (vec4 && s0 + kAccSeg <= p.V) {
+      float4 zv[kAccSeg / 256], qv[kAccSeg / 256];
+#pragma unroll
+      for (int u = 0; u < kAccSeg / 256; ++u) {
+        zv[u] = *reinterpret_cast<const float4*>(z + s0 + 4 * (lane + 64 * u));
+        if (qd) qv[u] = *reinterpret_cast<const float4*>(qd + s0 + 4 * (lane + 64 * u));
+      }
+#pragma unroll
+      for (int u = 0; u < kAccSeg / 256; ++u) {
+        const float zz[4] = {zv[u].x, zv[u].y, zv[u].z, zv[u].w};
+        const float qq[4] = {qd ? qv[u].x : 0.f, qd ? qv[u].y : 0.f, qd ? qv[u].z : 0.f, qd ? qv[u].w : 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float pv = expf(zz[c] - lse);
+          const float r = qd ? fmaxf(0.f, pv - qq[c]) : pv;
+          acc += (double)r;
+          if (r > 0.f) lastp = s0 + 4 * (lane + 64 * u) + c;
+        }
+      }
+    } else {
+      for (int v = s0 + lane; v < min(s0 + kAccSeg, p.V); v += 64) {
+        const float r = weight(v);
+        acc += (double)r;
+        if (r > 0.f) lastp = v;
+      }
     }
-    s_bonus = pick;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      acc += __shfl_xor(acc, off);
+      lastp = max(lastp, __shfl_xor(lastp, off));
+    }
+    if (lane == 0) {
+      s_seg[sg] = acc;
+      s_seg_last[sg] = lastp;
+    }
+  }
+  __syncthreads();
+  // inclusive scan of the segment sums by wave 0 (each lane a run of
+  // consecutive segments), and the last token of positive weight
+  if (wv_id == 0) {
+    const int per = (n_seg + 63) / 64;
+    const int k0 = lane * per, k1 = min(k0 + per, n_seg);
+    double run = 0.0;
+    int lastp = -1;
+    for (int k = k0; k < k1; ++k) {
+      run += s_seg[k];
+      lastp = max(lastp, s_seg_last[k]);
+    }
+    double incl = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(incl, off);
+      if (lane >= off) incl += o;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) lastp = max(lastp, __shfl_xor(lastp, off));
+    const double up = __shfl_up(incl, 1);
+    double pre = lane > 0 ? up : 0.0;   // exclusive prefix: the previous lane's inclusive
+    for (int k = k0; k < k1; ++k) {
+      pre += s_seg[k];
+      s_seg[k] = pre;   // inclusive prefix through segment k
+    }
+    if (lane == 63) s_total = incl;
+    if (lane == 0) s_bonus = lastp;   // target at or past the end: last positive token
+  }
+  __syncthreads();
+  const double total = s_total;
+  const double target = (double)p.u_bonus[i] * total;
+  // the segment whose interval [excl, incl) holds the target: lane l of
+  // wave 0 sums its 64-token block of it, a wave scan finds the block that
+  // crosses the target, and that block's lane walks it token by token
+  if (wv_id == 0) {
+    int sel = -1;
+    for (int k = lane; k < n_seg; k += 64) {
+      const double excl = k > 0 ? s_seg[k - 1] : 0.0;
+      if (excl <= target && target < s_seg[k] && s_seg[k] > excl) sel = k;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sel = max(sel, __shfl_xor(sel, off));
+    if (sel >= 0) {
+      const double excl = sel > 0 ? s_seg[sel - 1] : 0.0;
+      const int b0 = sel * kAccSeg + 64 * lane;
+      const int b1 = min(b0 + 64, p.V);
+      double bs = 0.0;
+      for (int v = b0; v < b1; ++v) bs += (double)weight(v);
+      double incl = bs;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const unsigned long long hit = __ballot(excl + incl > target && bs > 0.0);
+      int pick = s_seg_last[sel];      // rounding left the walk short: the segment's last
+      if (hit) {
+        const int L = __ffsll((long long)hit) - 1;
+        if (lane == L) {
+          double run = excl + incl - bs;
+          int pk = -1;
+          for (int v = b0; v < b1; ++v) {
+            run += (double)weight(v);
+            if (run > target) { pk = v; break; }
+          }
+          if (pk < 0) {                // rounding: this block's last positive token
+            for (int v = b1 - 1; v >= b0; --v)
+              if (weight(v) > 0.f) { pk = v; break; }
+          }
+          s_bonus = pk;
+        }
+      } else if (lane == 0) {
+        s_bonus = pick;
+      }
+    }
   }
   __syncthreads();
   if (tid == 0) {

@@ -128,6 +128,7 @@ rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream) {
   if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
   if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
   if (a->H < 1 || a->V < 1) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_REJECTION && a->V > kMaxVocabRejection) return RV_ERR_UNSUPPORTED;
   if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
   if (a->dtype == RV_BF16 && a->H % 64 != 0) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + lm_scratch_bytes(a->B, a->gamma, a->V);

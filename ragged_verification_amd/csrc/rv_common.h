@@ -13,6 +13,7 @@ constexpr int kTargetItemsLatent = 1024; // latent attention: work items aimed f
 constexpr int kTargetItemsGqa = 512;     // GQA attention: about two items per persistent workgroup
 constexpr size_t kPartBytes = 128u << 20; // split-KV partial outputs held in workspace
 constexpr int kPartSlotsMax = 8192;      // split-KV partial tiles at most
+constexpr int kMaxVocabRejection = 1 << 22;  // vocabulary limit of the rejection rule
 constexpr int kMinChunk = 256;           // smallest split-KV chunk (keys)
 
 // ---- sticky device status: first error wins --------------------------------
