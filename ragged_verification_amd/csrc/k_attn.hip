@@ -315,45 +315,20 @@ __device__ inline uint2 lds_tr16(uint32_t addr) {
 // Persistent workers: the hardware places workgroup b on XCD b % 8.  A
 // workgroup takes the next item of its XCD's list (longest first) and, once
 // that list is empty, of the other lists; it returns -1 when all are empty,
-// so every workgroup ends after at most one failed take per list.  Each
-// successful take also issues the take of the following item, so that
-// atomic's round trip overlaps the current item instead of stalling the
-// workgroup between items (a taken item is always run: the pending take is
-// resolved first on the next call).
-struct Taker {
-  unsigned done = 0;   // lists found empty
-  int pend_y = -1;     // list of the take issued ahead, or -1
-  int pend_k = 0;      // position it returned
-};
-
-__device__ inline int take_at(const MainParams& p, int y, int k, unsigned& done) {
-  if (k < p.hdr[kHdrXLen + y]) return p.hdr[kHdrXOff + y] + k;
-  done |= 1u << y;
-  return -1;
-}
-
-__device__ inline int next_item(const MainParams& p, int* s_item, Taker& tk) {
+// so every workgroup ends after at most one failed take per list.  (Taking
+// the following item one item ahead, to hide the atomic's round trip, was
+// measured slower: it commits items early and unbalances the tail.)
+__device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done) {
   __syncthreads();   // every thread has read the previous item
   if (threadIdx.x == 0) {
     const int x = blockIdx.x & 7;
     int it = -1;
-    if (tk.pend_y >= 0) {
-      it = take_at(p, tk.pend_y, tk.pend_k, tk.done);
-      tk.pend_y = -1;
-    }
     for (int probe = 0; probe < 8 && it < 0; ++probe) {
       const int y = (x + probe) & 7;
-      if (tk.done & (1u << y)) continue;
-      it = take_at(p, y, atomicAdd(p.ctr + y, 1), tk.done);
-    }
-    if (it >= 0) {
-      for (int probe = 0; probe < 8; ++probe) {
-        const int y = (x + probe) & 7;
-        if (tk.done & (1u << y)) continue;
-        tk.pend_y = y;
-        tk.pend_k = atomicAdd(p.ctr + y, 1);
-        break;
-      }
+      if (done & (1u << y)) continue;
+      const int k = atomicAdd(p.ctr + y, 1);
+      if (k < p.hdr[kHdrXLen + y]) it = p.hdr[kHdrXOff + y] + k;
+      else done |= 1u << y;
     }
     *s_item = it;
   }
@@ -436,9 +411,9 @@ template <bool FAST>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
-  Taker tk;
+  unsigned done = 0;
   for (;;) {
-    const int item = next_item(p, &s_item, tk);
+    const int item = next_item(p, &s_item, done);
     if (item < 0) break;
     attn_mla_item<FAST>(p, item, smem);
   }
@@ -1219,9 +1194,9 @@ template <int NV, bool FAST>
 __global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
-  Taker tk;
+  unsigned done = 0;
   for (;;) {
-    const int item = next_item(p, &s_item, tk);
+    const int item = next_item(p, &s_item, done);
     if (item < 0) break;
     attn_gqa_item<NV, FAST>(p, item, smem);
   }

@@ -36,18 +36,22 @@
 namespace rv {
 namespace {
 
-constexpr int kBM = 128, kBN = 512, kBK = 32;   // workgroup tile and K step
+constexpr int kBM = 128, kBN = 512, kBK = 64;   // workgroup tile and K step
 constexpr int kSlab = 64;                        // columns per partial
 constexpr int kGemmThreads = 256;
-constexpr int kGRow = kBK * 2;                   // bytes per LDS row (4 chunks of 16)
-constexpr int kGStages = 3;
+constexpr int kGRow = kBK * 2;                   // bytes per LDS row: 8 chunks of 16, one 128-byte line
+constexpr int kGChunks = kGRow / 16;
+constexpr int kGStages = 2;
 constexpr int kGBOff = kBM * kGRow;              // B rows follow the A rows in a stage
-constexpr int kGStage = (kBM + kBN) * kGRow;     // 40 KB
-constexpr int kGLds = kGStages * kGStage;        // 120 KB
-constexpr int kGDmaA = kBM * 4 / 64;             // 1 KB DMA instructions per stage: A
-constexpr int kGDma = (kBM + kBN) * 4 / 64;      // ... in all (A then B)
+constexpr int kGStage = (kBM + kBN) * kGRow;     // 80 KB
+constexpr int kGLds = kGStages * kGStage;        // 160 KB
+constexpr int kGDmaA = kBM * kGChunks / 64;      // 1 KB DMA instructions per stage: A
+constexpr int kGDma = (kBM + kBN) * kGChunks / 64;   // ... in all (A then B)
 constexpr int kGDmaPerWave = kGDma / 4;
-static_assert(kGDma % 4 == 0 && kGDmaPerWave % 2 == 0, "DMA split over waves and K halves");
+constexpr int kGKs = kBK / 16;                   // 32x32x16 MFMA steps per K step
+constexpr int kGDmaGap = 2;                      // MFMAs between a wave's DMA instructions
+static_assert(kGDmaPerWave * kGDmaGap <= kGKs * 16, "DMA spread fits the step");
+static_assert(kGDma % 4 == 0, "DMA split over waves");
 
 struct GemmParams {
   const bf16_t* x;     // [rows][H]
@@ -63,7 +67,10 @@ __device__ inline void merge_best(float& v, int& idx, float ov, int oidx) {
   if (ov > v || (ov == v && oidx < idx)) { v = ov; idx = oidx; }
 }
 
-__device__ inline int gswz(int row) { return (row >> 2) & 3; }
+// 128-byte LDS rows: chunk c of row r sits at c ^ gswz(r), so the 16 rows
+// that one quarter-wave reads at one logical chunk (two rows per 256-byte
+// bank line) fall on 16 distinct bank groups
+__device__ inline int gswz(int row) { return (row >> 1) & 7; }
 
 __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -89,9 +96,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   const uint32_t lds = (uint32_t)(uintptr_t)smem;
 
   // DMA: instruction q (0 .. kGDma-1) of a stage moves chunks 64q .. 64q+63
-  // (A rows first, then B rows); wave w issues q = w*kGDmaPerWave + e.  Chunk
-  // c sits at row c/4, physical position c%4 and holds logical chunk
-  // (c%4) ^ gswz(row).  Rows past the real ones read the last real row.
+  // (A rows first, then B rows), eight whole 128-byte rows per instruction
+  // (a full cache line per row: half-line rows halve the DMA rate); wave w
+  // issues q = w*kGDmaPerWave + e.  Chunk c sits at row c/8, physical
+  // position c%8 and holds logical chunk (c%8) ^ gswz(row).  Rows past the
+  // real ones read the last real row.
   const unsigned char* baseA = reinterpret_cast<const unsigned char*>(p.x + (size_t)m0 * p.H);
   const unsigned char* baseB = reinterpret_cast<const unsigned char*>(p.w + (size_t)v0 * p.H);
   uint32_t doff[kGDmaPerWave];
@@ -100,8 +109,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
     const int q = wid * kGDmaPerWave + e;
     const bool is_a = q < kGDmaA;
     const int c = (is_a ? q : q - kGDmaA) * 64 + lane;
-    const int row = c >> 2;
-    const int lc = (c & 3) ^ gswz(row);
+    const int row = c / kGChunks;
+    const int lc = (c % kGChunks) ^ gswz(row);
     const int r = is_a ? min(row, M - 1 - m0) : min(row, p.V - 1 - v0);
     doff[e] = (uint32_t)r * (uint32_t)(p.H * 2) + (uint32_t)lc * 16u;
   }
@@ -114,9 +123,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
 
   // fragment reads: row 32*b + l32 of A (rows) or of this wave's B quarter,
   // logical chunk 2*ks + lh
-  uint32_t foff[2];
+  uint32_t foff[kGKs];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
+  for (int ks = 0; ks < kGKs; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
   const uint32_t bq = (uint32_t)(kGBOff + wid * 128 * kGRow);
 
   f32x16_t acc[4][4];
@@ -128,56 +137,55 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
   const int nk = p.H / kBK;
-  // prologue: steps 0 and 1 in flight
+  // double buffer: step kt+1 is fetched into the other stage while step kt
+  // is multiplied; its DMA goes out first thing in the step
 #pragma unroll
   for (int e = 0; e < kGDmaPerWave; ++e) dma(0, 0, e);
-#pragma unroll
-  for (int e = 0; e < kGDmaPerWave; ++e) dma(min(1, nk - 1), 1, e);
-  wait_vm<kGDmaPerWave>();
+  wait_vm<0>();
   __syncthreads();
 
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint32_t stg = lds + st * kGStage;
-    const int st2 = (st == 0) ? 2 : st - 1;   // stage of step kt+2 (= that of kt-1)
-    // past the end the DMA refetches the last step into that dead stage,
-    // which keeps this loop free of branches
-    const int kn = min(kt + 2, nk - 1);
     u32x4_t fa[2][4], fb[2][4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
       fb[0][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[0]);
     }
+    // past the end the DMA refetches the last step into the dead stage,
+    // which keeps the loop free of branches
+    const int kn = min(kt + 1, nk - 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      if (ks == 0) {
+    for (int ks = 0; ks < kGKs; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < kGKs) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          fa[1][b] = lds_b128(stg + b * 32 * kGRow + foff[1]);
-          fb[1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[1]);
+          fa[cur ^ 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
+          fb[cur ^ 1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[ks + 1]);
         }
       }
 #pragma unroll
-      for (int bm = 0; bm < 4; ++bm) {
+      for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
         for (int bn = 0; bn < 4; ++bn) {
-          acc[bm][bn] = mfma32(fa[ks][bm], fb[ks][bn], acc[bm][bn]);
-          // spread this wave's DMAs of step kt+2 over the MFMAs
-          const int slot = bm * 4 + bn;
-          if (slot % 3 == 1 && slot / 3 < kGDmaPerWave / 2) dma(kn, st2, ks * (kGDmaPerWave / 2) + slot / 3);
+          acc[bm][bn] = mfma32(fa[cur][bm], fb[cur][bn], acc[bm][bn]);
+          // the next step's DMA, one instruction every kGDmaGap MFMAs: the
+          // address unit takes about one 1 KB instruction per 16 clocks
+          // per CU, so a burst would hold the MFMAs back
+          const int slot = ks * 16 + bm * 4 + bn;
+          if (slot % kGDmaGap == 0 && slot / kGDmaGap < kGDmaPerWave) dma(kn, st ^ 1, slot / kGDmaGap);
         }
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // step kt+1 must have landed (kt+2 may still be in flight); every wave
-    // is done with stage kt before it is refilled
-    wait_vm<kGDmaPerWave>();
+    // step kt+1 has landed; every wave is done with stage kt before it is refilled
+    wait_vm<0>();
     __syncthreads();
-    st = (st == kGStages - 1) ? 0 : st + 1;
+    st ^= 1;
   }
-  wait_vm<0>();
-  __syncthreads();   // every wave's last DMA has landed: the ring is free
+  __syncthreads();   // the ring is free
 
   // ---- epilogue through LDS: for each 32-row block the wave writes its
   // 32 x 128 fp32 tile (rows padded to kERow floats), then lane t reduces
