@@ -250,20 +250,22 @@ def cpu_baseline(inp, step, n_req=130):
 
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "verify_attn_latent_bf16_B256_counters.md")
+COUNTERS_GQA_MD = os.path.join(ROOT, "profiles", "verify_attn_gqa_bf16_counters.md")
 ATTN_SRC = os.path.join(ROOT, "ragged_verification_amd", "csrc", "k_attn.hip")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the latent attention kernel from the committed
-    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel
-    of known size), or None when that summary was taken on another version of
-    the kernel source (its recorded sha256 differs from the file's)."""
+def measured_traffic(path=None, key="k_attn_mla"):
+    """HBM bytes per launch of an attention kernel (``key``: the kernel, and
+    for GQA the workload) from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known size), or None
+    when that summary was taken on another version of the kernel source (its
+    recorded sha256 differs from the file's)."""
     try:
-        text = open(COUNTERS_MD).read()
+        text = open(path or COUNTERS_MD).read()
         src = open(ATTN_SRC, "rb").read()
     except OSError:
         return None
-    m_bytes = re.search(r"traffic_bytes_per_launch \(k_attn_mla\): (\d+)", text)
+    m_bytes = re.search(r"traffic_bytes_per_launch \(" + re.escape(key) + r"\): (\d+)", text)
     m_hash = re.search(r"source_sha256 \(ragged_verification_amd/csrc/k_attn.hip\): ([0-9a-f]{64})", text)
     if not m_bytes or not m_hash or m_hash.group(1) != hashlib.sha256(src).hexdigest():
         return None
@@ -347,7 +349,9 @@ def main():
     else:
         achieved = c["attn_bytes"] / (attn_ms / 1e3) / 1e9
         roof = {"kernel": "verify_attn (GQA, bf16)", "bound": "hbm", "achieved": achieved,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "traffic": measured_traffic(COUNTERS_GQA_MD, f"k_attn_gqa, {wl.name}"),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_per_launch": c["attn_bytes"], "launch_ms": attn_ms}
     lm_tflops = c["lm_flops"] / (lm_ms / 1e3) / 1e12
     line = {

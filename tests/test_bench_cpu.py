@@ -33,6 +33,19 @@ def test_traffic_follows_source_hash(tmp_path):
     assert b.measured_traffic() is None
 
 
+def test_gqa_traffic_is_keyed_by_workload(tmp_path):
+    b = _bench()
+    md = tmp_path / "gqa.md"
+    import hashlib
+    h = hashlib.sha256(open(b.ATTN_SRC, "rb").read()).hexdigest()
+    md.write_text("- traffic_bytes_per_launch (k_attn_gqa, gqa_bf16): 111\n"
+                  "- traffic_bytes_per_launch (k_attn_gqa, rejection_bf16): 222\n"
+                  f"- source_sha256 (ragged_verification_amd/csrc/k_attn.hip): {h}\n")
+    assert b.measured_traffic(str(md), "k_attn_gqa, gqa_bf16") == 111
+    assert b.measured_traffic(str(md), "k_attn_gqa, rejection_bf16") == 222
+    assert b.measured_traffic(str(md), "k_attn_gqa, sweep_gqa") is None
+
+
 def test_gpus_other_than_one_exit():
     import subprocess
     import sys
