@@ -195,6 +195,8 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   constexpr int kERow = 132;                      // floats per padded LDS row
   float* et = reinterpret_cast<float*>(smem) + wid * 32 * kERow;
   const int er = lane & 31, es = lane >> 5;       // reduced row and slab
+  // float4 logits stores when every row starts 16-byte aligned
+  const bool vec_logits = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0;
   const int cslab = v0 + wid * 128 + es * kSlab;  // first column of the slab
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm) {
@@ -225,12 +227,28 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < kSlab; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
     }
-    if (row < M && cslab < p.V) {
+    if (row < M && cslab < p.V)
       p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
-      if (p.logits) {
+    if (p.logits) {
+      // row-contiguous stores of the wave's 32 x 128 block: lanes 0-31 write
+      // one row's 128 columns as float4 runs, lanes 32-63 the next row
+      const int c4 = (lane & 31) * 4;
+      const int gcol = v0 + wid * 128 + c4;
+#pragma unroll 4
+      for (int rr = 0; rr < 16; ++rr) {
+        const int rl = 2 * rr + lh;
+        const int grow = m0 + bm * 32 + rl;
+        if (grow >= M) continue;
+        const float4 v = *reinterpret_cast<const float4*>(et + rl * kERow + c4);
+        float* dst = p.logits + (size_t)grow * p.V + gcol;
+        if (vec_logits && gcol + 3 < p.V) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          const float e4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < kSlab; ++i)
-          if (cslab + i < p.V) p.logits[(size_t)row * p.V + cslab + i] = z[i];
+          for (int c = 0; c < 4; ++c)
+            if (gcol + c < p.V) dst[c] = e4[c];
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();

@@ -133,6 +133,14 @@ def test_rejection_reduced(mode):
     _full_parity(inp, mode, "bf16")
 
 
+def test_rejection_odd_vocab():
+    """A vocabulary that is neither a multiple of 4 nor of 64: the logits
+    rows are not 16-byte aligned (scalar stores in the GEMM epilogue, scalar
+    loads in the bonus draw) and the last slab and segment are partial."""
+    inp = pu.make_inputs("rejection_bf16", B=5, V=4229, H=128, ctx=("lognormal", 150, 1.0, 500))
+    _full_parity(inp, "compact", "bf16")
+
+
 def test_gqa_group8_and_split_kv():
     """Eight query heads per KV head (64 query vectors per tile) and one long
     request so the key range is split and merged."""
