@@ -55,6 +55,10 @@ struct AttnShape {
 // used, [8 + x] / [16 + x] start and length of XCD x's item list, [24 + x]
 // that list's take counter (zeroed by the plan, advanced by the workers).
 constexpr int kHdrXOff = 8, kHdrXLen = 16, kHdrCtr = 24;
+// Header of the balanced GQA plan: total super-tiles, super-tiles per
+// virtual worker, virtual workers, tiles, partial slots used.
+constexpr int kBalS = 0, kBalQ = 1, kBalVw = 2, kBalTiles = 3, kBalParts = 4;
+constexpr int kBalSuper = 64;   // keys per super-tile of the GQA kernel (two 32-key sub-tiles)
 
 struct PlanParams {
   const int32_t* cu;
@@ -65,6 +69,7 @@ struct PlanParams {
   int2* grp;             // scratch: {request, split} of each group by rank
   int32_t* hdr;
   int B, gamma, item_cap, part_cap, target;
+  int n_workers;         // balanced plan: persistent workgroups of the main kernel
   AttnShape sh;
 };
 
@@ -273,6 +278,91 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
       p.hdr[kHdrXLen + x] = xlen[x];
       p.hdr[kHdrCtr + x] = 0;
     }
+  }
+}
+
+// ---- balanced plan (GQA) ----------------------------------------------------
+//
+// The tiles of all requests, request-major, each cut into 64-key super-tiles,
+// form one sequence of S super-tiles; virtual worker v takes [v*q, v*q+q)
+// with q = ceil(S / workers), so the workers' loads differ by at most one
+// super-tile.  Outputs: req_info[i] = {tiles, first tile, 0, 0}; per tile
+// T (in items[]) {first super-tile, super-tiles, first partial slot or -1,
+// request}; after the n_tiles entries of items[], the first tile of each
+// virtual worker.  A tile whose super-tiles fall to k > 1 workers owns k
+// consecutive partial slots, one per worker in order.
+__global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
+  __shared__ int2 s_wc[kPlanMaxB];            // per request: window, context
+  __shared__ int s_buf[kPlanWaves * 8];
+  const int t = threadIdx.x;
+  const int B = p.B;
+  const AttnShape& sh = p.sh;
+  const int seg = ceil_div(B, kPlanThreads);
+  const int i0 = t * seg;
+  const int i1 = min(i0 + seg, B);
+  const int per_rb = sh.Hkv * sh.n_hb;   // tiles per row block
+  // super-tiles of one tile of row block rb
+  auto nst = [&](int w, int c, int rb) {
+    const int L_tile = c + min((rb + 1) * sh.RT, w);
+    return ceil_div(L_tile, kBalSuper);
+  };
+
+  int cnt[2] = {0, 0}, off[2], tot[2];   // tiles, super-tiles
+  for (int i = i0; i < i1; ++i) {
+    const int w = p.cu[i + 1] - p.cu[i];
+    const int c = p.ctx[i];
+    s_wc[i] = make_int2(w, c);
+    const int n_rb = ceil_div(w, sh.RT);
+    cnt[0] += n_rb * per_rb;
+    for (int rb = 0; rb < n_rb; ++rb) cnt[1] += per_rb * nst(w, c, rb);
+  }
+  block_excl_scan<2>(cnt, off, tot, s_buf);
+  const int n_tiles = tot[0], S = tot[1];
+  const int q = max(1, ceil_div(S, max(p.n_workers, 1)));
+  const int n_vw = ceil_div(S, q);
+
+  // partial slots: a tile split over k > 1 workers takes k
+  int parts[1] = {0}, poff[1], ptot[1];
+  {
+    int st = off[1];
+    for (int i = i0; i < i1; ++i) {
+      const int2 wc = s_wc[i];
+      const int n_rb = ceil_div(wc.x, sh.RT);
+      for (int rb = 0; rb < n_rb; ++rb) {
+        const int n = nst(wc.x, wc.y, rb);
+        for (int k = 0; k < per_rb; ++k, st += n) {
+          const int kseg = (st + n - 1) / q - st / q + 1;
+          parts[0] += kseg > 1 ? kseg : 0;
+        }
+      }
+    }
+  }
+  block_excl_scan<1>(parts, poff, ptot, s_buf);
+
+  int* vw_first = reinterpret_cast<int*>(p.items + n_tiles);
+  int T = off[0], st = off[1], slot = poff[0];
+  for (int i = i0; i < i1; ++i) {
+    const int2 wc = s_wc[i];
+    const int n_rb = ceil_div(wc.x, sh.RT);
+    p.req_info[i] = make_int4(n_rb * per_rb, T, 0, 0);
+    for (int rb = 0; rb < n_rb; ++rb) {
+      const int n = nst(wc.x, wc.y, rb);
+      for (int k = 0; k < per_rb; ++k, ++T, st += n) {
+        const int v_first = st / q, v_last = (st + n - 1) / q;
+        const int kseg = v_last - v_first + 1;
+        p.items[T] = make_int4(st, n, kseg > 1 ? slot : -1, i);
+        slot += kseg > 1 ? kseg : 0;
+        // workers whose range starts inside this tile
+        for (int v = ceil_div(st, q); v <= v_last; ++v) vw_first[v] = T;
+      }
+    }
+  }
+  if (t == 0) {
+    p.hdr[kBalS] = S;
+    p.hdr[kBalQ] = q;
+    p.hdr[kBalVw] = n_vw;
+    p.hdr[kBalTiles] = n_tiles;
+    p.hdr[kBalParts] = ptot[0];
   }
 }
 
@@ -877,8 +967,12 @@ struct GqaCfg {
   static_assert((kGqaKS - 1) * NV * 64 * 34 * 4 <= kStages * kStage, "merge buffer");
 };
 
+// Keys [kv_lo, min(kv_hi, the tile's key count)) of tile `tile` of request
+// i.  slot < 0: the range is the tile's whole key range and the normalised
+// output is written; otherwise fp32 partials go to partial slot `slot`.
 template <int NV, bool FAST>
-__device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, unsigned char* smem) {
+__device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int tile, int kv_lo, int kv_hi,
+                                               int slot, unsigned char* smem) {
   using Cfg = GqaCfg<NV>;
   constexpr int NST = Cfg::kStages;
   constexpr int NWV = Cfg::kWaves;
@@ -896,10 +990,6 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int4 rec = p.items[item];
-  const int i = rec.x, tile = rec.y, sp = rec.z;
-  const int4 info = p.req_info[i];
-  const int ns = info.x;
   const int row_start = p.cu[i];
   const int w = p.cu[i + 1] - row_start;
   const int c = p.ctx[i];
@@ -910,9 +1000,8 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const int row0 = rb * p.RT;
   const int rows_here = min(p.RT, w - row0);
   const int L_tile = c + row0 + rows_here;
-  const int chunk = p.hdr[1];
-  const int kv_begin = sp * chunk;
-  const int kv_end = min(kv_begin + chunk, L_tile);
+  const int kv_begin = kv_lo;
+  const int kv_end = min(kv_hi, L_tile);
   const int P = p.page_size;
 
   // page-table window for keys [kv_begin, kv_end)
@@ -1163,7 +1252,7 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   }
   if (!q_valid) return;
 
-  if (ns == 1) {
+  if (slot < 0) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16_t* dst = p.o + ((size_t)q_row * p.Hq + head) * kGqaD;
 #pragma unroll
@@ -1176,8 +1265,7 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
     if (p.lse && grp == 0)
       p.lse[(size_t)q_row * p.Hq + head] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    const int slot = info.z + sp * info.w + tile;
-    if (slot < 0 || slot >= p.part_cap) return;   // the plan keeps slots below the cap
+    if (slot >= p.part_cap) return;   // the plans keep slots below the cap
     float* po = p.part_o + ((size_t)slot * (16 * NV) + qv) * kGqaD;
 #pragma unroll
     for (int mb = 0; mb < kGqaD / 16; ++mb)
@@ -1186,6 +1274,48 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
       float* pml = p.part_ml + ((size_t)slot * (16 * NV) + qv) * 2;
       pml[0] = m_run;
       pml[1] = l_tot;
+    }
+  }
+}
+
+template <int NV, bool FAST>
+__device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, unsigned char* smem) {
+  const int4 rec = p.items[item];
+  const int i = rec.x, tile = rec.y, sp = rec.z;
+  const int4 info = p.req_info[i];
+  const int chunk = p.hdr[1];
+  const int kv_lo = sp * chunk;
+  const int kv_hi = (int)min((long long)kv_lo + chunk, (long long)INT32_MAX);
+  const int slot = info.x == 1 ? -1 : (info.z < 0 ? INT32_MAX : info.z + sp * info.w + tile);
+  attn_gqa_range<NV, FAST>(p, i, tile, kv_lo, kv_hi, slot, smem);
+}
+
+// Balanced schedule: virtual worker v takes super-tiles [v*q, v*q+q) of the
+// request-major sequence of every tile's 64-key super-tiles (the plan's
+// k_attn_plan_bal), one contiguous range per worker, so every workgroup
+// streams the same number of keys.  A range may start and end inside a
+// tile; a tile covered by several ranges writes one partial per range.
+template <int NV, bool FAST>
+__global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa_bal(MainParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kSuper = kGqaKS * kNK;
+  static_assert(kSuper == kBalSuper, "the plan's super-tile is the kernel's");
+  const int S = p.hdr[kBalS], q = p.hdr[kBalQ], n_vw = p.hdr[kBalVw], n_tiles = p.hdr[kBalTiles];
+  const int4* tinfo = p.items;                                          // per tile
+  const int* vw_first = reinterpret_cast<const int*>(p.items + n_tiles);
+  for (int vw = blockIdx.x; vw < n_vw; vw += gridDim.x) {
+    const int a = vw * q;
+    const int b = min(a + q, S);
+    for (int T = vw_first[vw]; T < n_tiles; ++T) {
+      const int4 ti = tinfo[T];   // {first super-tile, super-tiles, first slot or -1, request}
+      if (ti.x >= b) break;
+      const int s0 = max(a, ti.x) - ti.x, s1 = min(b, ti.x + ti.y) - ti.x;
+      if (s1 <= s0) continue;
+      const int i = ti.w;
+      const int tile = T - p.req_info[i].y;
+      const int slot = ti.z < 0 ? -1 : ti.z + (vw - ti.x / q);
+      __syncthreads();   // the previous range's merge and stores are done with the LDS
+      attn_gqa_range<NV, FAST>(p, i, tile, s0 * kSuper, s1 * kSuper, slot, smem);
     }
   }
 }
@@ -1206,6 +1336,9 @@ __global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa(MainParams
 struct CombineParams {
   const int32_t* cu;
   const int4* req_info;
+  const int4* tinfo;      // balanced plan: per tile {first super-tile, super-tiles, first slot or -1, request}
+  const int32_t* hdr;
+  int bal;                // 1: slots from the balanced plan, 0: from the chunked plan
   const float* part_o;
   const float* part_ml;
   bf16_t* o;
@@ -1231,9 +1364,23 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
   const int tile = (blockIdx.x / groups) % p.tpr_max;
   const int v0 = (blockIdx.x % groups) * kCombVec;
   const int4 info = p.req_info[i];
-  const int ns = info.x;
-  if (ns <= 1 || tile >= info.w) return;
-  if (info.z < 0 || info.z + (ns - 1) * info.w + tile >= p.part_cap) return;
+  // partials of this tile: ns slots at slot0 + s * sstride
+  int ns, slot0, sstride;
+  if (p.bal) {
+    if (tile >= info.x) return;
+    const int4 ti = p.tinfo[info.y + tile];
+    if (ti.z < 0) return;   // one worker covered the tile: written directly
+    const int q = p.hdr[kBalQ];
+    ns = (ti.x + ti.y - 1) / q - ti.x / q + 1;
+    slot0 = ti.z;
+    sstride = 1;
+  } else {
+    ns = info.x;
+    if (ns <= 1 || tile >= info.w || info.z < 0) return;
+    slot0 = info.z + tile;
+    sstride = info.w;
+  }
+  if (slot0 + (ns - 1) * sstride >= p.part_cap) return;
   const int row_start = p.cu[i];
   const int w = p.cu[i + 1] - row_start;
   const int rb = tile / (p.Hkv * p.n_hb);
@@ -1246,7 +1393,7 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
   const int vl = t % kCombVec, ss = t / kCombVec;   // 32 split lanes per vector
   constexpr int kLanes = 256 / kCombVec;
   const int qv = v0 + vl;
-  auto slot = [&](int s_) { return (size_t)(info.z + s_ * info.w + tile); };
+  auto slot = [&](int s_) { return (size_t)(slot0 + s_ * sstride); };
   auto ml = [&](int s_) { return p.part_ml + (slot(s_) * p.QT + qv) * 2; };
 
   // combined max and sum (empty partials carry max -inf and sum 0)
@@ -1487,6 +1634,37 @@ hipError_t launch_gqa_t(const MainParams& mp, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int NV, bool FAST>
+const void* gqa_bal_kernel() { return reinterpret_cast<const void*>(k_attn_gqa_bal<NV, FAST>); }
+
+const void* gqa_bal_kernel(int nv, bool fast) {
+  if (nv == 2) return fast ? gqa_bal_kernel<2, true>() : gqa_bal_kernel<2, false>();
+  return fast ? gqa_bal_kernel<4, true>() : gqa_bal_kernel<4, false>();
+}
+
+// Persistent grid of the balanced GQA kernel (its LDS attribute set first).
+hipError_t gqa_bal_grid(int nv, bool fast, int* grid) {
+  const void* kern = gqa_bal_kernel(nv, fast);
+  const int lds = nv == 2 ? GqaCfg<2>::kLds : GqaCfg<4>::kLds;
+  const int threads = 64 * (nv == 2 ? GqaCfg<2>::kWaves : GqaCfg<4>::kWaves);
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  return persistent_grid(kern, threads, lds, grid);
+}
+
+template <int NV, bool FAST>
+hipError_t launch_gqa_bal_t(const MainParams& mp, int grid, hipStream_t s) {
+  constexpr int lds = GqaCfg<NV>::kLds;
+  constexpr int threads = 64 * GqaCfg<NV>::kWaves;
+  hipLaunchKernelGGL((k_attn_gqa_bal<NV, FAST>), dim3(grid), dim3(threads), lds, s, mp);
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_bal(const MainParams& mp, int nv, bool fast, int grid, hipStream_t s) {
+  if (nv == 2) return fast ? launch_gqa_bal_t<2, true>(mp, grid, s) : launch_gqa_bal_t<2, false>(mp, grid, s);
+  return fast ? launch_gqa_bal_t<4, true>(mp, grid, s) : launch_gqa_bal_t<4, false>(mp, grid, s);
+}
+
 // GQA bf16 (head dim 128): 16*nv query vectors per tile (nv = 2 or 4); FAST:
 // power-of-two pages of at least 4 keys
 hipError_t launch_gqa(const MainParams& mp, int nv, bool fast, hipStream_t s) {
@@ -1559,6 +1737,21 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   const AttnScratch L = attn_layout(a.B, sh, a.Dv);
   char* base = ws + kStatusBytes;
 
+  // GQA: FAST DMA needs power-of-two pages of 4 .. 2^16 keys and rows under
+  // 2^24 bytes (24-bit in-page offsets).  The balanced schedule applies when
+  // its partial slots (at most workers + tiles) and worker list fit.
+  const int log2P = ((a.page_size & (a.page_size - 1)) == 0) ? __builtin_ctz((unsigned)a.page_size) : -1;
+  const bool fast_gqa = !latent && log2P >= 2 && log2P <= 16 && (long long)a.Hkv * kGqaD * 2 < (1 << 24);
+  int bal_grid = 0;
+  bool bal = false;
+  if (!latent) {
+    if ((e = gqa_bal_grid(nw, fast_gqa, &bal_grid)) != hipSuccess) return e;
+    const long long tiles_max = (long long)a.B * sh.tpr_max;
+    const long long st_max = ((long long)a.max_pages * a.page_size + kBalSuper - 1) / kBalSuper;
+    bal = bal_grid <= 4 * (L.item_cap - tiles_max) && bal_grid + tiles_max <= L.part_slots &&
+          tiles_max * st_max < INT32_MAX;
+  }
+
   PlanParams pp;
   pp.cu = a.cu;
   pp.ctx = a.ctx;
@@ -1572,8 +1765,10 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.item_cap = L.item_cap;
   pp.part_cap = L.part_slots;
   pp.target = sh.target;
+  pp.n_workers = bal_grid;
   pp.sh = sh;
-  hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(1024), 0, s, pp);
+  if (bal) hipLaunchKernelGGL(k_attn_plan_bal, dim3(1), dim3(kPlanThreads), 0, s, pp);
+  else hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, pp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   MainParams mp;
@@ -1622,16 +1817,16 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
-    // FAST: power-of-two pages of 4 .. 2^16 keys, rows under 2^24 bytes (24-bit
-    // in-page offsets)
-    const bool fast = mp.log2P >= 2 && mp.log2P <= 16 && (long long)a.Hkv * kGqaD * 2 < (1 << 24);
-    e = launch_gqa(mp, nw, fast, s);
+    e = bal ? launch_gqa_bal(mp, nw, fast_gqa, bal_grid, s) : launch_gqa(mp, nw, fast_gqa, s);
   }
   if (e != hipSuccess) return e;
 
   CombineParams cp;
   cp.cu = a.cu;
   cp.req_info = pp.req_info;
+  cp.tinfo = pp.items;
+  cp.hdr = pp.hdr;
+  cp.bal = bal ? 1 : 0;
   cp.part_o = mp.part_o;
   cp.part_ml = mp.part_ml;
   cp.o = mp.o;

@@ -141,6 +141,15 @@ def test_rejection_odd_vocab():
     _full_parity(inp, "compact", "bf16")
 
 
+def test_gqa_many_tiles_chunked_plan():
+    """One query head per KV head and 64 KV heads: 64 tiles per request, so
+    130 requests need more partial slots than the balanced GQA schedule may
+    claim (workers + tiles > 8192) and the chunked item plan runs instead."""
+    inp = pu.make_inputs("gqa_bf16", B=130, Hq=64, Hkv=64, V=200, H=64, tiers=(1024,),
+                         ctx=("uniform", 0, 60))
+    _full_parity(inp, "compact", "bf16")
+
+
 def test_gqa_group8_and_split_kv():
     """Eight query heads per KV head (64 query vectors per tile) and one long
     request so the key range is split and merged."""
