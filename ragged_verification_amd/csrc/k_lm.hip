@@ -31,27 +31,41 @@
 
 #include <float.h>
 
+#include <algorithm>
+
 #include "rv_common.h"
 
 namespace rv {
 namespace {
 
-constexpr int kBM = 128, kBN = 512, kBK = 64;   // workgroup tile and K step
+constexpr int kBM = 128, kBK = 64;             // workgroup rows and K step
 constexpr int kSlab = 64;                        // columns per partial
 constexpr int kGemmThreads = 256;
 constexpr int kGRow = kBK * 2;                   // bytes per LDS row: 8 chunks of 16, one 128-byte line
 constexpr int kGChunks = kGRow / 16;
 constexpr int kGStages = 2;
 constexpr int kGBOff = kBM * kGRow;              // B rows follow the A rows in a stage
-constexpr int kGStage = (kBM + kBN) * kGRow;     // 80 KB
-constexpr int kGLds = kGStages * kGStage;        // 160 KB
 constexpr int kGDmaA = kBM * kGChunks / 64;      // 1 KB DMA instructions per stage: A
-constexpr int kGDma = (kBM + kBN) * kGChunks / 64;   // ... in all (A then B)
-constexpr int kGDmaPerWave = kGDma / 4;
 constexpr int kGKs = kBK / 16;                   // 32x32x16 MFMA steps per K step
 constexpr int kGDmaGap = 2;                      // MFMAs between a wave's DMA instructions
-static_assert(kGDmaPerWave * kGDmaGap <= kGKs * 16, "DMA spread fits the step");
-static_assert(kGDma % 4 == 0, "DMA split over waves");
+
+// Workgroup tile 128 rows x BN vocabulary columns: 512 (each wave 128 x 128,
+// 256 accumulators) for large launches, 256 (each wave 128 x 64) when the
+// 512-wide grid would leave CUs idle.
+template <int BN>
+struct GemmCfg {
+  static constexpr int kWN = BN / 4;                          // columns per wave
+  static constexpr int kNB = kWN / 32;                        // 32-column blocks per wave
+  static constexpr int kStage = (kBM + BN) * kGRow;           // 80 KB / 48 KB
+  static constexpr int kLds = kGStages * kStage;              // 160 KB / 96 KB
+  static constexpr int kDma = (kBM + BN) * kGChunks / 64;     // 1 KB DMA instructions per stage
+  static constexpr int kDmaPerWave = kDma / 4;
+  static constexpr int kERow = kWN + 4;                       // floats per padded epilogue row
+  static constexpr int kSlabs = kWN / kSlab;                  // partial slabs per wave
+  static_assert(kDma % 4 == 0, "DMA split over waves");
+  static_assert(kDmaPerWave * kGDmaGap <= kGKs * 4 * kNB, "DMA spread fits the step");
+  static_assert(kGemmThreads / 64 * 32 * kERow * 4 <= kLds, "epilogue fits the ring");
+};
 
 struct GemmParams {
   const bf16_t* x;     // [rows][H]
@@ -72,8 +86,14 @@ __device__ inline void merge_best(float& v, int& idx, float ov, int oidx) {
 // bank line) fall on 16 distinct bank groups
 __device__ inline int gswz(int row) { return (row >> 1) & 7; }
 
+template <int BN>
 __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
+  using Cfg = GemmCfg<BN>;
+  constexpr int kGStage = Cfg::kStage;
+  constexpr int kGDmaPerWave = Cfg::kDmaPerWave;
+  constexpr int kNB = Cfg::kNB;
+  constexpr int kWN = Cfg::kWN;
 
   // XCD-aware tile order: consecutive logical tiles stay on one XCD, and the
   // row tiles of a vocabulary tile are consecutive.
@@ -87,7 +107,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   const int M = p.mm[0];
   const int m0 = mt * kBM;
   if (m0 >= M) return;
-  const int v0 = vt * kBN;
+  const int v0 = vt * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -121,18 +141,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
     dma16_s(doff[e], base, __builtin_amdgcn_readfirstlane(lds + st * kGStage + q * 1024));
   };
 
-  // fragment reads: row 32*b + l32 of A (rows) or of this wave's B quarter,
+  // fragment reads: row 32*b + l32 of A (rows) or of this wave's B columns,
   // logical chunk 2*ks + lh
   uint32_t foff[kGKs];
 #pragma unroll
   for (int ks = 0; ks < kGKs; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
-  const uint32_t bq = (uint32_t)(kGBOff + wid * 128 * kGRow);
+  const uint32_t bq = (uint32_t)(kGBOff + wid * kWN * kGRow);
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][kNB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
@@ -147,12 +167,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   int st = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const uint32_t stg = lds + st * kGStage;
-    u32x4_t fa[2][4], fb[2][4];
+    u32x4_t fa[2][4], fb[2][kNB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
-      fb[0][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[0]);
-    }
+    for (int b = 0; b < 4; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
+#pragma unroll
+    for (int b = 0; b < kNB; ++b) fb[0][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[0]);
     // past the end the DMA refetches the last step into the dead stage,
     // which keeps the loop free of branches
     const int kn = min(kt + 1, nk - 1);
@@ -162,20 +181,19 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
       const int cur = ks & 1;
       if (ks + 1 < kGKs) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          fa[cur ^ 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
-          fb[cur ^ 1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[ks + 1]);
-        }
+        for (int b = 0; b < 4; ++b) fa[cur ^ 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) fb[cur ^ 1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[ks + 1]);
       }
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn) {
+        for (int bn = 0; bn < kNB; ++bn) {
           acc[bm][bn] = mfma32(fa[cur][bm], fb[cur][bn], acc[bm][bn]);
           // the next step's DMA, one instruction every kGDmaGap MFMAs: the
           // address unit takes about one 1 KB instruction per 16 clocks
           // per CU, so a burst would hold the MFMAs back
-          const int slot = ks * 16 + bm * 4 + bn;
+          const int slot = (ks * 4 + bm) * kNB + bn;
           if (slot % kGDmaGap == 0 && slot / kGDmaGap < kGDmaPerWave) dma(kn, st ^ 1, slot / kGDmaGap);
         }
       __builtin_amdgcn_sched_barrier(0);
@@ -192,23 +210,24 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   // row t % 32 over its 64-column slab t / 32 to (max, lowest argmax, sum of
   // exp(z - max)).  Accumulator lane l holds column l % 32 of rows
   // 8*(j/4) + 4*(l/32) + j%4.
-  constexpr int kERow = 132;                      // floats per padded LDS row
+  constexpr int kERow = Cfg::kERow;               // floats per padded LDS row
   float* et = reinterpret_cast<float*>(smem) + wid * 32 * kERow;
   const int er = lane & 31, es = lane >> 5;       // reduced row and slab
   // float4 logits stores when every row starts 16-byte aligned
   const bool vec_logits = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0;
-  const int cslab = v0 + wid * 128 + es * kSlab;  // first column of the slab
+  const int cslab = v0 + wid * kWN + es * kSlab;  // first column of the slab
+  const bool reducer = es < Cfg::kSlabs;          // lanes with a slab to reduce
 #pragma unroll
   for (int bm = 0; bm < 4; ++bm) {
 #pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
+    for (int bn = 0; bn < kNB; ++bn)
 #pragma unroll
       for (int j = 0; j < 16; ++j)
         et[((j / 4) * 8 + lh * 4 + (j % 4)) * kERow + bn * 32 + l32] = acc[bm][bn][j];
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
     __builtin_amdgcn_wave_barrier();
     const int row = m0 + bm * 32 + er;
-    const float* src = et + er * kERow + es * kSlab;
+    const float* src = et + er * kERow + (reducer ? es : 0) * kSlab;
     float z[kSlab];
 #pragma unroll
     for (int i = 0; i < kSlab; i += 4) {
@@ -227,16 +246,18 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < kSlab; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
     }
-    if (row < M && cslab < p.V)
+    if (reducer && row < M && cslab < p.V)
       p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
     if (p.logits) {
-      // row-contiguous stores of the wave's 32 x 128 block: lanes 0-31 write
-      // one row's 128 columns as float4 runs, lanes 32-63 the next row
-      const int c4 = (lane & 31) * 4;
-      const int gcol = v0 + wid * 128 + c4;
+      // row-contiguous stores of the wave's 32 x kWN block: kWN/4 lanes
+      // write one row's columns as float4 runs, the other lanes the next rows
+      constexpr int kLanesRow = kWN / 4;
+      constexpr int kRowsPer = 64 / kLanesRow;
+      const int c4 = (lane % kLanesRow) * 4;
+      const int gcol = v0 + wid * kWN + c4;
 #pragma unroll 4
-      for (int rr = 0; rr < 16; ++rr) {
-        const int rl = 2 * rr + lh;
+      for (int rr = 0; rr < 32 / kRowsPer; ++rr) {
+        const int rl = kRowsPer * rr + lane / kLanesRow;
         const int grow = m0 + bm * 32 + rl;
         if (grow >= M) continue;
         const float4 v = *reinterpret_cast<const float4*>(et + rl * kERow + c4);
@@ -604,14 +625,34 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     g.n_slabs = n_slabs;
     const int rows = a.B * a.gamma;   // real rows never exceed one full block each
     g.n_mt = (rows + kBM - 1) / kBM;
-    g.n_vt = (a.V + kBN - 1) / kBN;
     g.with_sum = rej ? 1 : 0;
-    const int n_tiles = g.n_mt * g.n_vt;
-    const int grid = ((n_tiles + 7) / 8) * 8;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, kGLds)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(k_lm_gemm, dim3(grid), dim3(kGemmThreads), kGLds, s, g);
+    int cus = 0, dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    // Tile width by rounds of one tile per CU (row tiles counted at the
+    // B*gamma bound: the packed count is only known on the device).  A
+    // 256-wide tile takes about 0.65 of a 512-wide one's time (measured), so
+    // the narrow tiles go to launches where they add no round: small batches
+    // whose 512-wide grid leaves CUs idle.
+    const long long c = std::max(cus, 1);
+    const long long r512 = ((long long)g.n_mt * ((a.V + 511) / 512) + c - 1) / c;
+    const long long r256 = ((long long)g.n_mt * ((a.V + 255) / 256) + c - 1) / c;
+    const bool wide = r256 > r512;
+    if (wide) {
+      g.n_vt = (a.V + 511) / 512;
+      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm<512>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<512>::kLds)) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL(k_lm_gemm<512>, dim3(grid), dim3(kGemmThreads), GemmCfg<512>::kLds, s, g);
+    } else {
+      g.n_vt = (a.V + 255) / 256;
+      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm<256>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<256>::kLds)) != hipSuccess)
+        return e;
+      hipLaunchKernelGGL(k_lm_gemm<256>, dim3(grid), dim3(kGemmThreads), GemmCfg<256>::kLds, s, g);
+    }
   } else {
     F32LmParams f;
     f.x = static_cast<const float*>(a.hidden);
