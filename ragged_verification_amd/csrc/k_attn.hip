@@ -58,6 +58,8 @@ constexpr int kHdrXOff = 8, kHdrXLen = 16, kHdrCtr = 24;
 // Header of the balanced GQA plan: total super-tiles, super-tiles per
 // virtual worker, virtual workers, tiles, partial slots used.
 constexpr int kBalS = 0, kBalQ = 1, kBalVw = 2, kBalTiles = 3, kBalParts = 4;
+// Both plans: the number of tiles with split partials (listed in split[]).
+constexpr int kHdrSplit = 6;
 constexpr int kBalSuper = 64;   // keys per super-tile of the GQA kernel (two 32-key sub-tiles)
 
 struct PlanParams {
@@ -67,6 +69,7 @@ struct PlanParams {
   int4* req_info;        // per request: {n_splits, first group, part_off, tiles}
   int4* items;           // {request, tile, split, 0}, grouped by XCD list
   int2* grp;             // scratch: {request, split} of each group by rank
+  int2* split;           // {request, tile} of every tile with split partials
   int32_t* hdr;
   int B, gamma, item_cap, part_cap, target;
   int n_workers;         // balanced plan: persistent workgroups of the main kernel
@@ -189,17 +192,18 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   // first (counting sort over 64 length buckets) and dealt to the 8 lists in
   // snake order (ranks 8c..8c+7 go to XCDs 0..7 for even c, 7..0 for odd c),
   // which balances the lists and starts the longest items first.
-  int mine[2] = {0, 0}, off2[2], tot2[2];
+  int mine[3] = {0, 0, 0}, off2[3], tot2[3];
   for (int i = i0; i < i1; ++i) {
     const int2 wl = s_wl[i];
     const int ns = wl.y > 0 ? ceil_div(wl.y, C) : 1;
     mine[0] += ns;
     mine[1] += ns > 1 ? ns * tiles_of_w(wl.x) : 0;
+    mine[2] += ns > 1 ? tiles_of_w(wl.x) : 0;
   }
-  block_excl_scan<2>(mine, off2, tot2, s_buf);
+  block_excl_scan<3>(mine, off2, tot2, s_buf);
   const int n_groups = tot2[0];
   const int n_parts = tot2[1];
-  int grp_off = off2[0], part_off = off2[1];
+  int grp_off = off2[0], part_off = off2[1], split_off = off2[2];
   // bucket of a chunk of `len` keys: 0 for a full chunk, up to 63 for the shortest
   auto bucket = [&](int len) { return (int)(((long long)(C - len) * 64) / C); };
   for (int i = i0; i < i1; ++i) {
@@ -221,6 +225,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
     const int L = wl.y;
     const int ns = L > 0 ? ceil_div(L, C) : 1;
     p.req_info[i] = make_int4(ns, grp_off, ns > 1 ? part_off : -1, tiles);
+    if (ns > 1)
+      for (int tl = 0; tl < tiles; ++tl) p.split[split_off++] = make_int2(i, tl);
     for (int sp = 0; sp < ns; ++sp) {
       const int rank = atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
       p.grp[rank] = make_int2(i, sp);
@@ -272,6 +278,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
     p.hdr[0] = total;
     p.hdr[1] = C;
     p.hdr[2] = n_parts;
+    p.hdr[kHdrSplit] = tot2[2];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       p.hdr[kHdrXOff + x] = xoff[x];
@@ -321,8 +328,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
   const int q = max(1, ceil_div(S, max(p.n_workers, 1)));
   const int n_vw = ceil_div(S, q);
 
-  // partial slots: a tile split over k > 1 workers takes k
-  int parts[1] = {0}, poff[1], ptot[1];
+  // partial slots: a tile split over k > 1 workers takes k; and the split tiles
+  int parts[2] = {0, 0}, poff[2], ptot[2];
   {
     int st = off[1];
     for (int i = i0; i < i1; ++i) {
@@ -333,18 +340,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
         for (int k = 0; k < per_rb; ++k, st += n) {
           const int kseg = (st + n - 1) / q - st / q + 1;
           parts[0] += kseg > 1 ? kseg : 0;
+          parts[1] += kseg > 1 ? 1 : 0;
         }
       }
     }
   }
-  block_excl_scan<1>(parts, poff, ptot, s_buf);
+  block_excl_scan<2>(parts, poff, ptot, s_buf);
 
   int* vw_first = reinterpret_cast<int*>(p.items + n_tiles);
-  int T = off[0], st = off[1], slot = poff[0];
+  int T = off[0], st = off[1], slot = poff[0], split_at = poff[1];
   for (int i = i0; i < i1; ++i) {
     const int2 wc = s_wc[i];
     const int n_rb = ceil_div(wc.x, sh.RT);
     p.req_info[i] = make_int4(n_rb * per_rb, T, 0, 0);
+    const int T0 = T;
     for (int rb = 0; rb < n_rb; ++rb) {
       const int n = nst(wc.x, wc.y, rb);
       for (int k = 0; k < per_rb; ++k, ++T, st += n) {
@@ -352,6 +361,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
         const int kseg = v_last - v_first + 1;
         p.items[T] = make_int4(st, n, kseg > 1 ? slot : -1, i);
         slot += kseg > 1 ? kseg : 0;
+        if (kseg > 1) p.split[split_at++] = make_int2(i, T - T0);
         // workers whose range starts inside this tile
         for (int v = ceil_div(st, q); v <= v_last; ++v) vw_first[v] = T;
       }
@@ -363,6 +373,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
     p.hdr[kBalVw] = n_vw;
     p.hdr[kBalTiles] = n_tiles;
     p.hdr[kBalParts] = ptot[0];
+    p.hdr[kHdrSplit] = ptot[1];
   }
 }
 
@@ -1337,6 +1348,7 @@ struct CombineParams {
   const int32_t* cu;
   const int4* req_info;
   const int4* tinfo;      // balanced plan: per tile {first super-tile, super-tiles, first slot or -1, request}
+  const int2* split;      // {request, tile} of the tiles with split partials
   const int32_t* hdr;
   int bal;                // 1: slots from the balanced plan, 0: from the chunked plan
   const float* part_o;
@@ -1355,14 +1367,9 @@ constexpr int kCombVec = 8;       // query vectors per workgroup
 constexpr int kCombRound = 512;   // split weights held in LDS at once
 
 template <int DV>
-__global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
-  __shared__ float s_red[256];
-  __shared__ float s_w[kCombRound][kCombVec];
+__device__ __forceinline__ void combine_unit(const CombineParams& p, int i, int tile, int v0,
+                                             float* s_red, float (*s_w)[kCombVec]) {
   constexpr int kPer = kCombVec * DV / 4 / 256;   // float4 runs per thread
-  const int groups = p.QT / kCombVec;
-  const int i = blockIdx.x / (p.tpr_max * groups);
-  const int tile = (blockIdx.x / groups) % p.tpr_max;
-  const int v0 = (blockIdx.x % groups) * kCombVec;
   const int4 info = p.req_info[i];
   // partials of this tile: ns slots at slot0 + s * sstride
   int ns, slot0, sstride;
@@ -1458,6 +1465,22 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
     pk.x = pack_bf16x2(acc[k].x, acc[k].y);
     pk.y = pack_bf16x2(acc[k].z, acc[k].w);
     *reinterpret_cast<uint2*>(dst) = pk;
+  }
+}
+
+// Grid-stride over (tile with split partials, group of 8 query vectors); the
+// plan lists those tiles, so the grid is a fixed few workgroups per CU
+// instead of one per possible tile.
+template <int DV>
+__global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
+  __shared__ float s_red[256];
+  __shared__ float s_w[kCombRound][kCombVec];
+  const int groups = p.QT / kCombVec;
+  const int n_units = p.hdr[kHdrSplit] * groups;
+  for (int u = blockIdx.x; u < n_units; u += gridDim.x) {
+    const int2 it = p.split[u / groups];
+    __syncthreads();   // the previous unit is done with the LDS
+    combine_unit<DV>(p, it.x, it.y, (u % groups) * kCombVec, s_red, s_w);
   }
 }
 
@@ -1577,7 +1600,7 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
 }
 
 struct AttnScratch {
-  size_t hdr, req_info, items, grp, part_ml, part_o, total;
+  size_t hdr, req_info, items, grp, split, part_ml, part_o, total;
   int item_cap, part_slots;
 };
 
@@ -1590,6 +1613,7 @@ AttnScratch attn_layout(int B, const AttnShape& sh, int Dv) {
   L.req_info = off; off = align_up(off + sizeof(int4) * (size_t)B, 256);
   L.items = off; off = align_up(off + sizeof(int4) * (size_t)L.item_cap, 256);
   L.grp = off; off = align_up(off + sizeof(int2) * (size_t)L.item_cap, 256);
+  L.split = off; off = align_up(off + sizeof(int2) * (size_t)B * sh.tpr_max, 256);
   L.part_ml = off; off = align_up(off + sizeof(float) * 2 * (size_t)L.part_slots * sh.QT, 256);
   L.part_o = off; off = align_up(off + sizeof(float) * (size_t)L.part_slots * sh.QT * Dv, 256);
   L.total = off;
@@ -1760,6 +1784,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.items = reinterpret_cast<int4*>(base + L.items);
   pp.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
   pp.grp = reinterpret_cast<int2*>(base + L.grp);
+  pp.split = reinterpret_cast<int2*>(base + L.split);
   pp.B = a.B;
   pp.gamma = a.gamma;
   pp.item_cap = L.item_cap;
@@ -1825,6 +1850,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   cp.cu = a.cu;
   cp.req_info = pp.req_info;
   cp.tinfo = pp.items;
+  cp.split = pp.split;
   cp.hdr = pp.hdr;
   cp.bal = bal ? 1 : 0;
   cp.part_o = mp.part_o;
@@ -1841,7 +1867,11 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   cp.DV = a.Dv;
   cp.tpr_max = sh.tpr_max;
   cp.part_cap = L.part_slots;
-  const dim3 cgrid(a.B * sh.tpr_max * (sh.QT / kCombVec));
+  int cus = 0, dev = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  const dim3 cgrid((unsigned)std::max(1LL, std::min((long long)a.B * sh.tpr_max * (sh.QT / kCombVec),
+                                                     4LL * std::max(cus, 1))));
   if (a.Dv == 512) hipLaunchKernelGGL(k_attn_combine<512>, cgrid, dim3(256), 0, s, cp);
   else hipLaunchKernelGGL(k_attn_combine<128>, cgrid, dim3(256), 0, s, cp);
   return hipGetLastError();
