@@ -185,6 +185,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
 #pragma unroll
         for (int b = 0; b < kNB; ++b) fb[cur ^ 1][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[ks + 1]);
       }
+      // the next sub-step's fragment reads go out before this sub-step's
+      // MFMAs (left to itself the scheduler sinks them behind most of them)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
