@@ -83,57 +83,10 @@ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // One workgroup of 1024 threads; thread t owns requests [t*seg, t*seg+seg)
 // (seg = ceil(B/1024)), whose (window, keys) pairs it caches in LDS.  Every
 // block-wide reduction and scan is a wave-level shuffle scan plus one pass
-// over the 16 wave totals, so each costs two barriers.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
+// over the 16 wave totals (block_excl_scan), so each costs two barriers.
+constexpr int kPlanThreads = kScanThreads;
+constexpr int kPlanWaves = kScanWaves;
 constexpr int kPlanMaxB = RV_MAX_ROWS / 2;   // gamma >= 2
-
-template <int N>
-__device__ inline void wave_incl_scan(int (&v)[N]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      const int u = __shfl_up(v[k], off);
-      if (lane >= off) v[k] += u;
-    }
-  }
-}
-
-// Block-wide exclusive scan of N ints per thread (thread order); tot gets
-// the block totals.  buf holds kPlanWaves * N ints.
-template <int N>
-__device__ inline void block_excl_scan(const int (&v)[N], int (&ex)[N], int (&tot)[N], int* buf) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int inc[N];
-#pragma unroll
-  for (int k = 0; k < N; ++k) inc[k] = v[k];
-  wave_incl_scan<N>(inc);
-  __syncthreads();   // buf is free
-  if (lane == 63) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) buf[wv * N + k] = inc[k];
-  }
-  __syncthreads();
-  int before[N], all[N];
-#pragma unroll
-  for (int k = 0; k < N; ++k) before[k] = all[k] = 0;
-#pragma unroll 1
-  for (int u = 0; u < kPlanWaves; ++u) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) {
-      const int x = buf[u * N + k];
-      before[k] += u < wv ? x : 0;
-      all[k] += x;
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < N; ++k) {
-    ex[k] = before[k] + inc[k] - v[k];
-    tot[k] = all[k];
-  }
-}
 
 __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   __shared__ int2 s_wl[kPlanMaxB];            // per request: window, keys (ctx + window)

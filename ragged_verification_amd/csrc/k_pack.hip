@@ -34,7 +34,8 @@ struct PackParams {
 };
 
 __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
-  __shared__ int scan[kThreads];
+  static_assert(kThreads == kScanThreads, "block_excl_scan's workgroup");
+  __shared__ int s_buf[kScanWaves];
   __shared__ int s_M, s_Mpad;
   const int t = threadIdx.x;
   const int B = p.B;
@@ -56,17 +57,11 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
     local[s] = w;
     run += w;
   }
-  scan[t] = run;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = (t >= off) ? scan[t - off] : 0;
-    __syncthreads();
-    scan[t] += add;
-    __syncthreads();
-  }
-  int pre = scan[t] - run;
+  int v1[1] = {run}, ex1[1], tot1[1];
+  block_excl_scan<1>(v1, ex1, tot1, s_buf);
+  int pre = ex1[0];
   if (t == kThreads - 1) {
-    const int M = scan[t];
+    const int M = tot1[0];
     int Mpad = M;
     if (p.n_tiers > 0) {
       int found = -1;
@@ -89,21 +84,36 @@ __global__ __launch_bounds__(kThreads) void k_pack(PackParams p) {
     if (i >= B) break;
     p.cu[i] = pre;
     const int c = p.ctx[i];
-    for (int k = 0; k < local[s]; ++k) {
+    const int w = local[s];
+    // all loads of the request first (the stores could alias them, which
+    // would otherwise serialise one round trip per row)
+    int pgv[RV_MAX_GAMMA], tokv[RV_MAX_GAMMA];
+#pragma unroll
+    for (int k = 0; k < RV_MAX_GAMMA; ++k) {
+      pgv[k] = -1;
+      tokv[k] = -1;
+      if (k < w) {
+        const int pos = c + k;
+        const int pg_idx = pos / P;
+        if (pos >= 0 && pg_idx < p.max_pages) pgv[k] = p.page_table[(size_t)i * p.max_pages + pg_idx];
+        tokv[k] = (k == 0) ? p.anchor[i] : p.drafts[(size_t)i * g1 + (k - 1)];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < RV_MAX_GAMMA; ++k) {
+      if (k >= w) break;
       const int r = pre + k;
       const int pos = c + k;
-      const int pg_idx = pos / P;
-      int pg = -1;
-      if (pos >= 0 && pg_idx < p.max_pages) pg = p.page_table[(size_t)i * p.max_pages + pg_idx];
+      const int pg = pgv[k];
       int sl = -1;
       if (pg >= 0 && pg < p.num_pages) sl = pg * P + pos % P;
       else set_status(p.status, RV_DEV_BAD_PAGE);
       p.row_req[r] = i;
       p.row_pos[r] = pos;
-      p.tok[r] = (k == 0) ? p.anchor[i] : p.drafts[(size_t)i * g1 + (k - 1)];
+      p.tok[r] = tokv[k];
       p.slot[r] = sl;
     }
-    pre += local[s];
+    pre += w;
   }
   __syncthreads();
   for (int r = s_M + t; r < s_Mpad; r += kThreads) {

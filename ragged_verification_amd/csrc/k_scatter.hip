@@ -33,7 +33,8 @@ __device__ inline int rows_of(const rv_scatter_args& p, int i, int32_t* status) 
 
 __global__ __launch_bounds__(kThreads) void k_scatter(ScatterParams sp) {
   const rv_scatter_args& p = sp.a;
-  __shared__ int sc_c[kThreads], sc_f[kThreads];
+  static_assert(kThreads == kScanThreads, "block_excl_scan's workgroup");
+  __shared__ int s_buf[kScanWaves * 2];
   const int t = threadIdx.x;
   const int B = p.B;
   const int seg = (B + kThreads - 1) / kThreads;
@@ -57,22 +58,13 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ScatterParams sp) {
     }
     acc[s] = a;
   }
-  sc_c[t] = nc;
-  sc_f[t] = nf;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int x = t >= off ? sc_c[t - off] : 0;
-    const int y = t >= off ? sc_f[t - off] : 0;
-    __syncthreads();
-    sc_c[t] += x;
-    sc_f[t] += y;
-    __syncthreads();
-  }
-  int co = sc_c[t] - nc;
-  int fo = sc_f[t] - nf;
+  int v2[2] = {nc, nf}, ex2[2], tot2[2];
+  block_excl_scan<2>(v2, ex2, tot2, s_buf);
+  int co = ex2[0];
+  int fo = ex2[1];
   if (t == kThreads - 1) {
-    p.commit_cu[B] = sc_c[t];
-    p.free_count[0] = sc_f[t];
+    p.commit_cu[B] = tot2[0];
+    p.free_count[0] = tot2[1];
   }
   const int g1 = p.gamma - 1;
   for (int s = 0; s < seg; ++s) {
@@ -92,15 +84,29 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ScatterParams sp) {
       hist_ok = hl >= 0 && hl + a < p.hist_stride;
     }
     if (!r2t_ok || (p.hist && !hist_ok)) set_status(sp.status, RV_DEV_HIST_OVERFLOW);
-    for (int j = 0; j <= a; ++j) {
-      const int tok = (j < a) ? p.drafts[(size_t)i * g1 + j] : b;
-      const int sl = p.slot[base + j];
-      p.commit_tok[co + j] = tok;
-      p.commit_slot[co + j] = sl;
-      if (r2t_ok) p.req_to_token[(size_t)i * p.r2t_stride + c + j] = sl;
-      if (hist_ok) p.hist[(size_t)i * p.hist_stride + hl + j] = tok;
+    // all loads of the request first (the stores could alias them, which
+    // would otherwise serialise one round trip per row)
+    int tokv[RV_MAX_GAMMA], slv[RV_MAX_GAMMA];
+#pragma unroll
+    for (int j = 0; j < RV_MAX_GAMMA; ++j) {
+      tokv[j] = b;
+      slv[j] = -1;
+      if (j < wv) {
+        slv[j] = p.slot[base + j];
+        if (j < a) tokv[j] = p.drafts[(size_t)i * g1 + j];
+      }
     }
-    for (int j = a + 1; j < wv; ++j) p.free_slots[fo + (j - a - 1)] = p.slot[base + j];
+#pragma unroll
+    for (int j = 0; j < RV_MAX_GAMMA; ++j) {
+      if (j > a) break;
+      p.commit_tok[co + j] = tokv[j];
+      p.commit_slot[co + j] = slv[j];
+      if (r2t_ok) p.req_to_token[(size_t)i * p.r2t_stride + c + j] = slv[j];
+      if (hist_ok) p.hist[(size_t)i * p.hist_stride + hl + j] = tokv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < RV_MAX_GAMMA; ++j)
+      if (j > a && j < wv) p.free_slots[fo + (j - a - 1)] = slv[j];
     if (a < 0) continue;   // corrupt packing: state left unchanged
     if (p.hist) p.hist_len[i] = hl + a + 1;
     p.ctx[i] = c + a + 1;

@@ -111,4 +111,58 @@ size_t lm_scratch_bytes(int B, int gamma, int V);
 bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent);
 int attn_max_pages_limit(int dtype, bool latent);
 
+// ---- workgroup scans (one-workgroup metadata kernels) --------------------------
+constexpr int kScanThreads = 1024;
+constexpr int kScanWaves = kScanThreads / 64;
+
+// Inclusive scan of N ints per lane within a wave.
+template <int N>
+__device__ inline void wave_incl_scan(int (&v)[N]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int u = __shfl_up(v[k], off);
+      if (lane >= off) v[k] += u;
+    }
+  }
+}
+
+// Exclusive scan of N ints per thread (thread order) over a workgroup of
+// kScanThreads threads: wave shuffles, then one pass over the wave totals
+// (two barriers); tot gets the workgroup totals.  buf: kScanWaves * N ints
+// of LDS.
+template <int N>
+__device__ inline void block_excl_scan(const int (&v)[N], int (&ex)[N], int (&tot)[N], int* buf) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) inc[k] = v[k];
+  wave_incl_scan<N>(inc);
+  __syncthreads();   // buf is free
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) buf[wv * N + k] = inc[k];
+  }
+  __syncthreads();
+  int before[N], all[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) before[k] = all[k] = 0;
+#pragma unroll 1
+  for (int u = 0; u < kScanWaves; ++u) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int x = buf[u * N + k];
+      before[k] += u < wv ? x : 0;
+      all[k] += x;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    ex[k] = before[k] + inc[k] - v[k];
+    tot[k] = all[k];
+  }
+}
+
 }  // namespace rv
