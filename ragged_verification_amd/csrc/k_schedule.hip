@@ -45,29 +45,36 @@ __device__ inline long long fixed_of(double s) {
   return static_cast<long long>(floor(s * 1099511627776.0));
 }
 
-// Inclusive scan of one int64 per thread (Hillis-Steele in LDS).
-__device__ long long block_scan_incl(long long v, long long* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    long long add = (t >= off) ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// Inclusive scan of one int64 per thread: wave shuffles, then one pass over
+// the 16 wave totals (integer adds, so the order does not matter).  *total
+// gets the workgroup total.  buf holds kThreads / 64 values.
+__device__ long long block_scan_incl(long long v, long long* buf, long long* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-  long long r = buf[t];
+  __syncthreads();   // buf is free
+  if (lane == 63) buf[wv] = v;
   __syncthreads();
-  return r;
+  long long before = 0, all = 0;
+  for (int u = 0; u < kThreads / 64; ++u) {
+    const long long x = buf[u];
+    before += u < wv ? x : 0;
+    all += x;
+  }
+  *total = all;
+  return before + v;
 }
 
 __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   __shared__ uint64_t key[kMaxCand];      // ~bits(S): ascending = S descending
   __shared__ uint16_t cid[kMaxCand];      // candidate id = i*(gamma-1) + (k-1)
   __shared__ uint16_t rank_of[kMaxCand];  // sorted position of each candidate
-  __shared__ long long scan_buf[kThreads];
-  __shared__ double red_r[kThreads];
-  __shared__ int red_k[kThreads];
+  __shared__ long long scan_buf[kThreads / 64];
+  __shared__ double red_r[kThreads / 64];
+  __shared__ int red_k[kThreads / 64];
   __shared__ int bad_cost;
 
   const int t = threadIdx.x;
@@ -98,8 +105,8 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   const long long base = static_cast<long long>(B) << kShift;
 
   if (p.mode == RV_STATIC || p.mode == RV_NO_TRIM) {
-    block_scan_incl(local_sum, scan_buf);
-    const long long all = scan_buf[kThreads - 1];  // total; buf is stable now
+    long long all = 0;
+    block_scan_incl(local_sum, scan_buf, &all);
     for (int i = t; i < B; i += kThreads) {
       p.w_commit[i] = p.gamma;
       p.w_verify[i] = p.gamma;
@@ -119,6 +126,11 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
     cid[j] = 0xffff;
   }
   __syncthreads();
+  // Thread t compares pairs q = t, t+1024, ...; with stride <= 64 both
+  // elements of every pair lie in the 128-element block 2q/128, which only
+  // the wave of t touches, so such a stage needs only the wave's own LDS
+  // operations to be done before the next; a workgroup barrier follows any
+  // stage that crosses waves and any stage before one that does.
   for (int size = 2; size <= N; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int q = t; q < N / 2; q += kThreads) {
@@ -133,9 +145,16 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
           cid[lo] = ib; cid[hi] = ia;
         }
       }
-      __syncthreads();
+      const int next_stride = stride > 1 ? stride >> 1 : size;   // first stride of the next size
+      if (stride >= 128 || (next_stride >= 128 && size < N)) {
+        __syncthreads();
+      } else {
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+      }
     }
   }
+  __syncthreads();
 
   // ---- fixed-point prefix sums in ranked order ------------------------------
   const int seg = (n + kThreads - 1) / kThreads;  // <= 4
@@ -146,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
     run += fixed_of(S);
     rank_of[cid[j]] = static_cast<uint16_t>(j);
   }
-  const long long incl = block_scan_incl(run, scan_buf);
+  long long run_total = 0;
+  const long long incl = block_scan_incl(run, scan_buf, &run_total);
   long long pre = incl - run;  // exclusive prefix before j0
 
   // ---- ratio for every K, first arg-max -------------------------------------
@@ -167,18 +187,26 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
     eval(j + 1, base + pre);  // K = j+1 takes the first j+1 ranked candidates
   }
   if (bad) atomicOr(&bad_cost, 1);
-  red_r[t] = best_r;
-  red_k[t] = best_k;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (t < off) {
-      const double ra = red_r[t], rb = red_r[t + off];
-      const int ka = red_k[t], kb = red_k[t + off];
-      if (rb > ra || (rb == ra && kb < ka)) { red_r[t] = rb; red_k[t] = kb; }
-    }
-    __syncthreads();
+  // first arg-max: the larger ratio, the smaller K on ties (an exact order,
+  // so the shuffle tree gives the sequential answer)
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double rb = __shfl_xor(best_r, off);
+    const int kb = __shfl_xor(best_k, off);
+    if (rb > best_r || (rb == best_r && kb < best_k)) { best_r = rb; best_k = kb; }
   }
+  if ((t & 63) == 0) {
+    red_r[t >> 6] = best_r;
+    red_k[t >> 6] = best_k;
+  }
+  __syncthreads();
+  double rbest = red_r[0];
   int kst = red_k[0];
+  for (int u = 1; u < kThreads / 64; ++u) {
+    const double rb = red_r[u];
+    const int kb = red_k[u];
+    if (rb > rbest || (rb == rbest && kb < kst)) { rbest = rb; kst = kb; }
+  }
   if (bad_cost) {
     kst = 0;
     if (t == 0) set_status(p.status, RV_DEV_BAD_COST);
