@@ -43,7 +43,6 @@ constexpr int kSlab = 64;                        // columns per partial
 constexpr int kGemmThreads = 256;
 constexpr int kGRow = kBK * 2;                   // bytes per LDS row: 8 chunks of 16, one 128-byte line
 constexpr int kGChunks = kGRow / 16;
-constexpr int kGStages = 2;
 constexpr int kGBOff = kBM * kGRow;              // B rows follow the A rows in a stage
 constexpr int kGDmaA = kBM * kGChunks / 64;      // 1 KB DMA instructions per stage: A
 constexpr int kGKs = kBK / 16;                   // 32x32x16 MFMA steps per K step
@@ -57,7 +56,10 @@ struct GemmCfg {
   static constexpr int kWN = BN / 4;                          // columns per wave
   static constexpr int kNB = kWN / 32;                        // 32-column blocks per wave
   static constexpr int kStage = (kBM + BN) * kGRow;           // 80 KB / 48 KB
-  static constexpr int kLds = kGStages * kStage;              // 160 KB / 96 KB
+  // ring stages: two 80 KB (the whole LDS) or three 48 KB, so the narrow
+  // tiles keep two steps in flight (they stream weights with few MFMAs)
+  static constexpr int kStages = BN == 512 ? 2 : 3;
+  static constexpr int kLds = kStages * kStage;               // 160 KB / 144 KB
   static constexpr int kDma = (kBM + BN) * kGChunks / 64;     // 1 KB DMA instructions per stage
   static constexpr int kDmaPerWave = kDma / 4;
   static constexpr int kERow = kWN + 4;                       // floats per padded epilogue row
@@ -94,6 +96,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   constexpr int kGDmaPerWave = Cfg::kDmaPerWave;
   constexpr int kNB = Cfg::kNB;
   constexpr int kWN = Cfg::kWN;
+  constexpr int kGStages = Cfg::kStages;
 
   // XCD-aware tile order: consecutive logical tiles stay on one XCD, and the
   // row tiles of a vocabulary tile are consecutive.
@@ -157,11 +160,14 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
   const int nk = p.H / kBK;
-  // double buffer: step kt+1 is fetched into the other stage while step kt
-  // is multiplied; its DMA goes out first thing in the step
+  // ring: steps kt+1 .. kt+kGStages-1 are in flight while step kt is
+  // multiplied; the DMA of step kt+kGStages-1 is spread over its MFMAs
+  // (past the end: the last step again, into a dead stage)
 #pragma unroll
-  for (int e = 0; e < kGDmaPerWave; ++e) dma(0, 0, e);
-  wait_vm<0>();
+  for (int u = 0; u < kGStages - 1; ++u)
+#pragma unroll
+    for (int e = 0; e < kGDmaPerWave; ++e) dma(min(u, nk - 1), u, e);
+  wait_vm<(kGStages - 2) * kGDmaPerWave>();
   __syncthreads();
 
   int st = 0;
@@ -172,9 +178,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
     for (int b = 0; b < 4; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
 #pragma unroll
     for (int b = 0; b < kNB; ++b) fb[0][b] = lds_b128(stg + bq + b * 32 * kGRow + foff[0]);
-    // past the end the DMA refetches the last step into the dead stage,
-    // which keeps the loop free of branches
-    const int kn = min(kt + 1, nk - 1);
+    // the stage of step kt+kGStages-1 is the one step kt-1 used
+    const int kn = min(kt + kGStages - 1, nk - 1);
+    const int st_dma = (st == 0) ? kGStages - 1 : st - 1;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kGKs; ++ks) {
@@ -197,15 +203,17 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
           // address unit takes about one 1 KB instruction per 16 clocks
           // per CU, so a burst would hold the MFMAs back
           const int slot = (ks * 4 + bm) * kNB + bn;
-          if (slot % kGDmaGap == 0 && slot / kGDmaGap < kGDmaPerWave) dma(kn, st ^ 1, slot / kGDmaGap);
+          if (slot % kGDmaGap == 0 && slot / kGDmaGap < kGDmaPerWave) dma(kn, st_dma, slot / kGDmaGap);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // step kt+1 has landed; every wave is done with stage kt before it is refilled
-    wait_vm<0>();
+    // step kt+1 has landed (later steps may still be in flight); every wave
+    // is done with stage kt before it is refilled
+    wait_vm<(kGStages - 2) * kGDmaPerWave>();
     __syncthreads();
-    st ^= 1;
+    st = (st == kGStages - 1) ? 0 : st + 1;
   }
+  wait_vm<0>();
   __syncthreads();   // the ring is free
 
   // ---- epilogue through LDS: for each 32-row block the wave writes its
