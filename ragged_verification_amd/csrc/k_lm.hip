@@ -9,29 +9,27 @@
 //
 // Design (gfx950):
 //  * k_lm_gemm: z = X W^T with bf16 32x32x16 MFMAs (fp32 accumulation), a
-//    128-row x 512-column output tile per workgroup; each of the four waves
-//    owns all 128 rows of a 128-column quarter (256 accumulator registers),
-//    so a weight fragment read from LDS feeds four MFMAs and a hidden-state
-//    fragment four.  Both operands arrive by direct global->LDS DMA into a
-//    three-stage ring of 32-wide K steps; the DMA of step k+2 is spread over
-//    the MFMAs of step k.  LDS rows are 64 bytes whose 16-byte chunks are
-//    XOR-swizzled by (row >> 2) & 3, so sixteen consecutive rows read at one
-//    k offset hit distinct banks.  Workgroups whose rows lie past the packed
-//    total exit at once, so the work follows the real row count M, not the
-//    tier.  The epilogue never materialises the logits unless asked: per
-//    64-column slab it reduces each row to (max, lowest argmax, sum of
-//    exp(z - max)) with cross-lane shuffles and writes 16 bytes.  The row
-//    tiles of one vocabulary tile sit on one XCD, so the weight tile is
-//    fetched from HBM once per XCD.
+//    128-row x 256-column output tile per workgroup; each of the four waves
+//    owns all 128 rows of a 64-column quarter, so a weight fragment read from
+//    LDS feeds four MFMAs and a hidden-state fragment two.  Both operands
+//    arrive by direct global->LDS DMA into a three-stage ring of 64-wide K
+//    steps whose LDS rows are whole 128-byte lines (chunks XOR-swizzled by
+//    (row >> 1) & 7); the DMA of step k+2 is spread one instruction per two
+//    MFMAs over step k.  Workgroups whose rows lie past the packed total exit
+//    at once, so the work follows the real row count M, not the tier.  The
+//    epilogue goes through an LDS transpose: per 64-column slab each row is
+//    reduced to (max, lowest argmax, sum of exp(z - max)) in 16 bytes, and
+//    the logits are written (row-contiguous float4 runs) only when asked.
+//    The row tiles of one vocabulary tile sit on one XCD, so the weight tile
+//    is fetched from HBM once per XCD.
 //  * k_lm_f32: the same partials from fp32 inputs (plain dot products).
 //  * k_accept: one workgroup per request merges the slab partials of its
 //    rows, runs the greedy or rejection scan, and for rejection draws the
-//    bonus token by an inverse CDF over the vocabulary (fp64 chunk sums, one
-//    block scan, one sequential walk inside the chunk that holds the target).
+//    bonus token by an inverse CDF over the vocabulary (fp64 sums of
+//    4096-token segments, a scan of them, then a walk inside the segment
+//    that holds the target).
 
 #include <float.h>
-
-#include <algorithm>
 
 #include "rv_common.h"
 
@@ -48,9 +46,11 @@ constexpr int kGDmaA = kBM * kGChunks / 64;      // 1 KB DMA instructions per st
 constexpr int kGKs = kBK / 16;                   // 32x32x16 MFMA steps per K step
 constexpr int kGDmaGap = 2;                      // MFMAs between a wave's DMA instructions
 
-// Workgroup tile 128 rows x BN vocabulary columns: 512 (each wave 128 x 128,
-// 256 accumulators) for large launches, 256 (each wave 128 x 64) when the
-// 512-wide grid would leave CUs idle.
+// Workgroup tile 128 rows x BN vocabulary columns (each wave 128 x BN/4).
+// The launch uses BN = 256 (three 48 KB stages); BN = 512 (each wave
+// 128 x 128 in 256 accumulators, two 80 KB stages) compiles as well.
+constexpr int kGemmBN = 256;   // the launched tile width
+
 template <int BN>
 struct GemmCfg {
   static constexpr int kWN = BN / 4;                          // columns per wave
@@ -637,33 +637,15 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     const int rows = a.B * a.gamma;   // real rows never exceed one full block each
     g.n_mt = (rows + kBM - 1) / kBM;
     g.with_sum = rej ? 1 : 0;
-    int cus = 0, dev = 0;
-    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-    // Tile width by rounds of one tile per CU (row tiles counted at the
-    // B*gamma bound: the packed count is only known on the device).  A
-    // 256-wide tile takes about 0.65 of a 512-wide one's time (measured), so
-    // the narrow tiles go to launches where they add no round: small batches
-    // whose 512-wide grid leaves CUs idle.
-    const long long c = std::max(cus, 1);
-    const long long r512 = ((long long)g.n_mt * ((a.V + 511) / 512) + c - 1) / c;
-    const long long r256 = ((long long)g.n_mt * ((a.V + 255) / 256) + c - 1) / c;
-    const bool wide = r256 > r512;
-    if (wide) {
-      g.n_vt = (a.V + 511) / 512;
-      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm<512>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<512>::kLds)) != hipSuccess)
-        return e;
-      hipLaunchKernelGGL(k_lm_gemm<512>, dim3(grid), dim3(kGemmThreads), GemmCfg<512>::kLds, s, g);
-    } else {
-      g.n_vt = (a.V + 255) / 256;
-      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
-      if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm<256>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<256>::kLds)) != hipSuccess)
-        return e;
-      hipLaunchKernelGGL(k_lm_gemm<256>, dim3(grid), dim3(kGemmThreads), GemmCfg<256>::kLds, s, g);
-    }
+    // 128 x 256 tiles with three 48 KB stages: measured at or below the
+    // 128 x 512 double-buffered tiles on every workload but one (config 3,
+    // +2%): latent batch 1.75 against 1.81 ms, config 2 95 against 154 us
+    g.n_vt = (a.V + kGemmBN - 1) / kGemmBN;
+    const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm<kGemmBN>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, GemmCfg<kGemmBN>::kLds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_lm_gemm<kGemmBN>, dim3(grid), dim3(kGemmThreads), GemmCfg<kGemmBN>::kLds, s, g);
   } else {
     F32LmParams f;
     f.x = static_cast<const float*>(a.hidden);
