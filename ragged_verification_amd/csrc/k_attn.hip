@@ -1443,9 +1443,17 @@ __global__ __launch_bounds__(256) void k_attn_pad(const int32_t* mm, void* o, fl
   const int M = mm[0], Mpad = mm[1];
   const int row = M + blockIdx.x;
   if (row < 0 || row >= Mpad || row >= rows_cap) return;
-  const size_t n = (size_t)Hq * Dv * elem_bytes / 4;   // whole 32-bit words
-  uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<char*>(o) + (size_t)row * Hq * Dv * elem_bytes);
-  for (size_t k = threadIdx.x; k < n; k += blockDim.x) dst[k] = 0u;
+  const size_t row_bytes = (size_t)Hq * Dv * elem_bytes;   // a whole number of 32-bit words
+  char* base = static_cast<char*>(o) + (size_t)row * row_bytes;
+  size_t done = 0;
+  if (((uintptr_t)base % 16) == 0) {   // 16-byte stores over the aligned body
+    uint4* d16 = reinterpret_cast<uint4*>(base);
+    const size_t n16 = row_bytes / 16;
+    for (size_t k = threadIdx.x; k < n16; k += blockDim.x) d16[k] = make_uint4(0u, 0u, 0u, 0u);
+    done = n16 * 16;
+  }
+  uint32_t* d4 = reinterpret_cast<uint32_t*>(base + done);
+  for (size_t k = threadIdx.x; k < (row_bytes - done) / 4; k += blockDim.x) d4[k] = 0u;
   if (lse)
     for (int h = threadIdx.x; h < Hq; h += blockDim.x) lse[(size_t)row * Hq + h] = -INFINITY;
 }
