@@ -88,6 +88,10 @@ typedef int32_t rv_status;
 #define RV_F32 0
 #define RV_BF16 1
 
+/* LM-head weight layout (rv_lm_args.w_layout) */
+#define RV_W_ROWS 0    /* W is [V][H], row-major */
+#define RV_W_TILED 1   /* W is the tiled copy written by rv_lm_tile_weight (bf16) */
+
 /* Limits of this build. */
 #define RV_MAX_GAMMA 16
 #define RV_MAX_TIERS 16
@@ -253,7 +257,8 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream);
  *  mass exceeds u_bonus * total). */
 typedef struct {
   const void* hidden;        /* [rows_cap][H] packed final hidden states, dtype */
-  const void* W;             /* [V][H] LM-head weight, dtype */
+  const void* W;             /* [V][H] LM-head weight, dtype; or its tiled
+                                copy (w_layout = RV_W_TILED) */
   const int32_t* mm;         /* [2] {M, M_pad} */
   const int32_t* cu;         /* [B+1] */
   const int32_t* w_commit;   /* [B] */
@@ -263,7 +268,7 @@ typedef struct {
   const float* u;            /* [B][gamma-1] uniforms (rejection) */
   const float* u_bonus;      /* [B] uniforms (rejection) */
   int32_t B, gamma, rows_cap, H, V, dtype, rule;
-  int32_t _pad0;
+  int32_t w_layout;          /* RV_W_ROWS, or RV_W_TILED (bf16, H % 128 == 0) */
   int32_t* pred;             /* out [rows_cap] */
   int32_t* accept;           /* out [B] accepted drafts */
   int32_t* bonus;            /* out [B] bonus token */
@@ -277,6 +282,23 @@ typedef struct {
  * Device errors: BAD_TOKEN for a draft outside [0,V) (it never matches;
  * under rejection it is rejected), BAD_WINDOW. */
 rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
+
+/* The LM-head weight in MFMA fragment order, made once when the weight is
+ * loaded (as a serving system lays out its weights for its kernels), so that
+ * rv_lm_head_accept with w_layout = RV_W_TILED loads each wave's weight
+ * operand straight into registers with whole-line reads.  Layout: blocks of
+ * 32 vocabulary rows (V rounded up to a multiple of 32; the padding rows are
+ * zero), each a run of H/16 fragments of 1 KB; lane l (0..63) of fragment f
+ * of block cb holds the 8 bf16 W[32*cb + l%32][16*f + 8*(l/32) .. +7] at byte
+ * offset ((cb*(H/16) + f)*64 + l)*16.
+ *
+ * rv_lm_tiled_weight_bytes: host only, the size of that copy.
+ * rv_lm_tile_weight: W [V][H] bf16 (device, caller-owned) -> W_tiled
+ * (device, caller-owned, rv_lm_tiled_weight_bytes bytes, 16-byte aligned);
+ * enqueued on stream.  Host errors: NULL pointer, V < 1, H < 128 or H not a
+ * multiple of 128 (INVALID_ARG); dtype other than bf16 (UNSUPPORTED). */
+rv_status rv_lm_tiled_weight_bytes(int32_t V, int32_t H, int32_t dtype, size_t* bytes);
+rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, int32_t dtype, void* stream);
 
 /* ---- stage 5: compact scatter ------------------------------------------- */
 /* DSpark-in-SGLang page, section A2 "performance and zero-overhead

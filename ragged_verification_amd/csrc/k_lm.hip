@@ -77,6 +77,8 @@ struct GemmParams {
   float* logits;       // optional [rows][V]
   int H, V, n_slabs, n_mt, n_vt;
   int with_sum;
+  int ncb;             // 32-column blocks of the tiled weight
+  size_t w_bytes;      // bytes of the tiled weight
 };
 
 __device__ inline void merge_best(float& v, int& idx, float ov, int oidx) {
@@ -87,6 +89,83 @@ __device__ inline void merge_best(float& v, int& idx, float ov, int oidx) {
 // that one quarter-wave reads at one logical chunk (two rows per 256-byte
 // bank line) fall on 16 distinct bank groups
 __device__ inline int gswz(int row) { return (row >> 1) & 7; }
+
+// Epilogue of both GEMM kernels, through LDS (the operand ring is free): for
+// each 32-row block the wave writes its 32 x WN fp32 tile (rows padded to
+// WN + 4 floats), then lane t reduces row t % 32 over its 64-column slab
+// t / 32 to (max, lowest argmax, sum of exp(z - max)).  Accumulator lane l
+// holds column l % 32 of rows 8*(j/4) + 4*(l/32) + j%4.
+template <int WN>
+__device__ __forceinline__ void lm_epilogue(f32x16_t (&acc)[4][WN / 32], unsigned char* smem,
+                                            const GemmParams& p, int wid, int lane, int m0, int v0, int M) {
+  constexpr int kNB = WN / 32;
+  const int l32 = lane & 31, lh = lane >> 5;
+  constexpr int kERow = WN + 4;               // floats per padded LDS row
+  float* et = reinterpret_cast<float*>(smem) + wid * 32 * kERow;
+  const int er = lane & 31, es = lane >> 5;       // reduced row and slab
+  // float4 logits stores when every row starts 16-byte aligned
+  const bool vec_logits = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0;
+  const int cslab = v0 + wid * WN + es * kSlab;  // first column of the slab
+  const bool reducer = es < WN / kSlab;          // lanes with a slab to reduce
+#pragma unroll
+  for (int bm = 0; bm < 4; ++bm) {
+#pragma unroll
+    for (int bn = 0; bn < kNB; ++bn)
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        et[((j / 4) * 8 + lh * 4 + (j % 4)) * kERow + bn * 32 + l32] = acc[bm][bn][j];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    const int row = m0 + bm * 32 + er;
+    const float* src = et + er * kERow + (reducer ? es : 0) * kSlab;
+    float z[kSlab];
+#pragma unroll
+    for (int i = 0; i < kSlab; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + i);
+      z[i] = v.x; z[i + 1] = v.y; z[i + 2] = v.z; z[i + 3] = v.w;
+    }
+    float best = -INFINITY;
+    int bi = cslab;
+#pragma unroll
+    for (int i = 0; i < kSlab; ++i) {
+      if (cslab + i >= p.V) z[i] = -INFINITY;
+      if (z[i] > best) { best = z[i]; bi = cslab + i; }   // strict: lowest index wins ties
+    }
+    float se = 0.f;
+    if (p.with_sum && best != -INFINITY) {
+#pragma unroll
+      for (int i = 0; i < kSlab; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
+    }
+    if (reducer && row < M && cslab < p.V)
+      p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
+    if (p.logits) {
+      // row-contiguous stores of the wave's 32 x WN block: WN/4 lanes
+      // write one row's columns as float4 runs, the other lanes the next rows
+      constexpr int kLanesRow = WN / 4;
+      constexpr int kRowsPer = 64 / kLanesRow;
+      const int c4 = (lane % kLanesRow) * 4;
+      const int gcol = v0 + wid * WN + c4;
+#pragma unroll 4
+      for (int rr = 0; rr < 32 / kRowsPer; ++rr) {
+        const int rl = kRowsPer * rr + lane / kLanesRow;
+        const int grow = m0 + bm * 32 + rl;
+        if (grow >= M) continue;
+        const float4 v = *reinterpret_cast<const float4*>(et + rl * kERow + c4);
+        float* dst = p.logits + (size_t)grow * p.V + gcol;
+        if (vec_logits && gcol + 3 < p.V) {
+          *reinterpret_cast<float4*>(dst) = v;
+        } else {
+          const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (gcol + c < p.V) dst[c] = e4[c];
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next block overwrites
+  }
+}
 
 template <int BN>
 __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
@@ -216,76 +295,188 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm(GemmParams p) {
   wait_vm<0>();
   __syncthreads();   // the ring is free
 
-  // ---- epilogue through LDS: for each 32-row block the wave writes its
-  // 32 x 128 fp32 tile (rows padded to kERow floats), then lane t reduces
-  // row t % 32 over its 64-column slab t / 32 to (max, lowest argmax, sum of
-  // exp(z - max)).  Accumulator lane l holds column l % 32 of rows
-  // 8*(j/4) + 4*(l/32) + j%4.
-  constexpr int kERow = Cfg::kERow;               // floats per padded LDS row
-  float* et = reinterpret_cast<float*>(smem) + wid * 32 * kERow;
-  const int er = lane & 31, es = lane >> 5;       // reduced row and slab
-  // float4 logits stores when every row starts 16-byte aligned
-  const bool vec_logits = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0;
-  const int cslab = v0 + wid * kWN + es * kSlab;  // first column of the slab
-  const bool reducer = es < Cfg::kSlabs;          // lanes with a slab to reduce
+  lm_epilogue<kWN>(acc, smem, p, wid, lane, m0, v0, M);
+}
+
+// ---- LM head over the tiled weight ----------------------------------------------
+// The tiled weight (rv_lm_tile_weight) stores W in MFMA fragment order:
+// 32-column blocks, each a run of H/16 fragments of 1 KB, where lane l of
+// fragment f of block cb holds W[32*cb + l%32][16*f + 8*(l/32) .. +7] (rows
+// past V are zero).  One wave's B operand for one 32x32x16 MFMA is then a
+// single fully coalesced 1 KB load straight into registers.  No other wave
+// reads those weights, so they skip LDS altogether: LDS carries only the
+// hidden rows, which all four waves share (16 KB of DMA-free staging and
+// 64 KB of fragment reads per 64-wide K step, against 2x64 KB more for
+// weights staged through LDS).
+constexpr int kBufFlags = 0x00020000;   // buffer resource word 3 (gfx9 family: 32-bit data format)
+constexpr int kTRing = 8;             // weight sub-steps (16-wide K) held in registers
+constexpr int kTDist = kTRing - 1;    // sub-steps between a weight load and its MFMAs
+
+template <int WN>
+struct TiledCfg {
+  static constexpr int kNB = WN / 32;                 // 32-column blocks per wave
+  static constexpr int kBN = 4 * WN;                  // workgroup columns
+  static constexpr int kStage = kBM * kGRow;          // 16 KB of hidden rows per K step
+  static constexpr int kEpi = 4 * 32 * (WN + 4) * 4;  // epilogue transpose area
+  static constexpr int kLds = 2 * kStage > kEpi ? 2 * kStage : kEpi;
+};
+
+__device__ inline void lds_w128(uint32_t addr, const u32x4_t& v) { *(lds_u32x4_t*)(size_t)addr = v; }
+
+template <int WN>
+__global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  using Cfg = TiledCfg<WN>;
+  constexpr int kNB = Cfg::kNB;
+  constexpr int BN = Cfg::kBN;
+
+  // XCD-aware tile order as in k_lm_gemm: the row tiles of one vocabulary
+  // tile run on one XCD at about the same time, so its weights come from HBM
+  // once and from that XCD's L2 for the other row tiles
+  const int n_tiles = p.n_mt * p.n_vt;
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int kloc = blockIdx.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + kloc;
+  if (kloc >= per_xcd || logical >= n_tiles) return;
+  const int vt = logical / p.n_mt;
+  const int mt = logical % p.n_mt;
+  const int M = p.mm[0];
+  const int m0 = mt * kBM;
+  if (m0 >= M) return;
+  const int v0 = vt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
+  const int nk = p.H / kBK;      // even (H % 128 == 0)
+  const int nsub = p.H / 16;     // fragments per column block
+
+  // hidden rows: wave w stages rows 32w .. 32w+31 of every K step, four
+  // 16-byte chunks per lane, eight lanes per 128-byte row (whole lines);
+  // rows past the packed total read the last real row.  Buffer loads: the
+  // tile's rows as one resource, the K step as the scalar offset.
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(p.x) + (size_t)m0 * p.H, 0, kBM * p.H * 2, kBufFlags);
+  uint32_t aoff[4], adst[4];
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
-#pragma unroll
-    for (int bn = 0; bn < kNB; ++bn)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        et[((j / 4) * 8 + lh * 4 + (j % 4)) * kERow + bn * 32 + l32] = acc[bm][bn][j];
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's LDS writes are done
-    __builtin_amdgcn_wave_barrier();
-    const int row = m0 + bm * 32 + er;
-    const float* src = et + er * kERow + (reducer ? es : 0) * kSlab;
-    float z[kSlab];
-#pragma unroll
-    for (int i = 0; i < kSlab; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(src + i);
-      z[i] = v.x; z[i + 1] = v.y; z[i + 2] = v.z; z[i + 3] = v.w;
-    }
-    float best = -INFINITY;
-    int bi = cslab;
-#pragma unroll
-    for (int i = 0; i < kSlab; ++i) {
-      if (cslab + i >= p.V) z[i] = -INFINITY;
-      if (z[i] > best) { best = z[i]; bi = cslab + i; }   // strict: lowest index wins ties
-    }
-    float se = 0.f;
-    if (p.with_sum && best != -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < kSlab; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
-    }
-    if (reducer && row < M && cslab < p.V)
-      p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
-    if (p.logits) {
-      // row-contiguous stores of the wave's 32 x kWN block: kWN/4 lanes
-      // write one row's columns as float4 runs, the other lanes the next rows
-      constexpr int kLanesRow = kWN / 4;
-      constexpr int kRowsPer = 64 / kLanesRow;
-      const int c4 = (lane % kLanesRow) * 4;
-      const int gcol = v0 + wid * kWN + c4;
-#pragma unroll 4
-      for (int rr = 0; rr < 32 / kRowsPer; ++rr) {
-        const int rl = kRowsPer * rr + lane / kLanesRow;
-        const int grow = m0 + bm * 32 + rl;
-        if (grow >= M) continue;
-        const float4 v = *reinterpret_cast<const float4*>(et + rl * kERow + c4);
-        float* dst = p.logits + (size_t)grow * p.V + gcol;
-        if (vec_logits && gcol + 3 < p.V) {
-          *reinterpret_cast<float4*>(dst) = v;
-        } else {
-          const float e4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (gcol + c < p.V) dst[c] = e4[c];
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the next block overwrites
+  for (int e = 0; e < 4; ++e) {
+    const int rl = 32 * wid + 8 * e + (lane >> 3);
+    const int c = lane & 7;
+    aoff[e] = (uint32_t)(min(rl, M - 1 - m0) * p.H * 2 + c * 16);
+    adst[e] = (uint32_t)(rl * kGRow + ((c ^ gswz(rl)) * 16));
   }
+  auto load_a = [&](u32x4_t (&ar)[4], int kt) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ar[e] = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff[e], kt * kGRow, 0);
+  };
+
+  // weights: this wave's kNB column blocks as one buffer resource ending at
+  // the tiled weight's end, so blocks past it read as zeros (their columns
+  // are masked in the epilogue); the sub-step is the scalar offset
+  const size_t wbase = (size_t)((v0 + wid * WN) / 32) * nsub * 1024;
+  const size_t wspan = (size_t)kNB * nsub * 1024;
+  const size_t wleft = p.w_bytes > wbase ? p.w_bytes - wbase : 0;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<unsigned char*>(const_cast<bf16_t*>(p.w)) + (wleft ? wbase : 0), 0,
+      (int)(wleft < wspan ? wleft : wspan), kBufFlags);
+  uint32_t woff[kNB];
+#pragma unroll
+  for (int bn = 0; bn < kNB; ++bn) woff[bn] = (uint32_t)(bn * nsub * 1024 + lane * 16);
+  auto load_w = [&](u32x4_t (&dst)[kNB], int sub) {
+#pragma unroll
+    for (int bn = 0; bn < kNB; ++bn) dst[bn] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff[bn], sub * 1024, 0);
+  };
+
+  // fragment reads of the hidden rows: row 32*b + l32, logical chunk 2*ks + lh
+  uint32_t foff[kGKs];
+#pragma unroll
+  for (int ks = 0; ks < kGKs; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
+
+  f32x16_t acc[4][kNB];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < kNB; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
+
+  // register ring of weight fragments: sub-step s sits in slot s % kTRing
+  // and is loaded kTDist sub-steps before its MFMAs (past the end: the last
+  // sub-step again).  The prologue issues its loads in the order the loop
+  // does (weights of sub-steps 0..6 with the hidden rows of steps 0 and 1
+  // where steps -2 and -1 would have put them), so that the compiler's
+  // load counting sees the same queue on entry as around the loop.
+  u32x4_t br[kTRing][kNB];
+  u32x4_t ar[4], ar0[4];
+  load_w(br[0], 0);
+  load_a(ar0, 0);
+  load_w(br[1], min(1, nsub - 1));
+  load_w(br[2], min(2, nsub - 1));
+  load_w(br[3], min(3, nsub - 1));
+  load_w(br[4], min(4, nsub - 1));
+  load_a(ar, min(1, nk - 1));
+  load_w(br[5], min(5, nsub - 1));
+  load_w(br[6], min(6, nsub - 1));
+  // hidden rows of step 0 into stage 0; step 1 stays in registers
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lds_w128(lds + adst[e], ar0[e]);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; kt += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k = kt + u;
+      const uint32_t stg = lds + u * Cfg::kStage;   // step k sits in stage k & 1 == u
+      u32x4_t fa[2][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
+#pragma unroll
+      for (int ks = 0; ks < kGKs; ++ks) {
+        const int j = 4 * u + ks;                      // ring slot of this sub-step
+        const int jn = (j + kTDist) % kTRing;          // slot of the sub-step kTDist ahead
+        load_w(br[jn], min(4 * k + ks + kTDist, nsub - 1));
+        if (ks == 1) {
+          // step k+1's hidden rows into the other stage (read by every wave
+          // during step k-1, before the last barrier), then load step k+2
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lds_w128(lds + (u ^ 1) * Cfg::kStage + adst[e], ar[e]);
+          load_a(ar, min(k + 2, nk - 1));
+        }
+        if (ks + 1 < kGKs) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) fa[(ks + 1) & 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+          for (int bn = 0; bn < kNB; ++bn) acc[bm][bn] = mfma32(fa[ks & 1][bm], br[j][bn], acc[bm][bn]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // step k+1 is in LDS; every wave is done with stage u
+      __syncthreads();
+    }
+  }
+
+  lm_epilogue<WN>(acc, smem, p, wid, lane, m0, v0, M);
+}
+
+// W [V][H] -> tiled copy: one thread per (fragment, lane), 16 bytes each
+__global__ __launch_bounds__(256) void k_lm_tile_weight(const bf16_t* __restrict__ w, u32x4_t* __restrict__ out,
+                                                        int V, int H, long long n_chunks) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_chunks) return;
+  const int lane = (int)(i & 63);
+  const long long frag = i >> 6;
+  const int nsub = H / 16;
+  const int cb = (int)(frag / nsub);
+  const int f = (int)(frag % nsub);
+  const int row = cb * 32 + (lane & 31);
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (row < V) v = *reinterpret_cast<const u32x4_t*>(w + (size_t)row * H + f * 16 + 8 * (lane >> 5));
+  out[i] = v;
 }
 
 // ---- fp32 path ------------------------------------------------------------------
@@ -614,6 +805,16 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
 
 }  // namespace
 
+size_t lm_tiled_weight_bytes(int V, int H) { return (size_t)((V + 31) / 32) * 32 * (size_t)H * 2; }
+
+hipError_t launch_lm_tile_weight(const void* W, void* W_tiled, int V, int H, hipStream_t s) {
+  const long long n_chunks = (long long)((V + 31) / 32) * (H / 16) * 64;
+  const long long grid = (n_chunks + 255) / 256;
+  hipLaunchKernelGGL(k_lm_tile_weight, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const bf16_t*>(W),
+                     static_cast<u32x4_t*>(W_tiled), V, H, n_chunks);
+  return hipGetLastError();
+}
+
 size_t lm_scratch_bytes(int B, int gamma, int V) {
   const size_t n_slabs = (size_t)(V + kSlab - 1) / kSlab;
   return align_up(sizeof(float4) * (size_t)B * gamma * n_slabs, 256);
@@ -624,7 +825,29 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
   float4* part = reinterpret_cast<float4*>(static_cast<char*>(a.workspace) + kStatusBytes);
   const bool rej = (a.rule == RV_REJECTION);
   hipError_t e;
-  if (a.dtype == RV_BF16) {
+  if (a.dtype == RV_BF16 && a.w_layout == RV_W_TILED) {
+    GemmParams g;
+    g.x = static_cast<const bf16_t*>(a.hidden);
+    g.w = static_cast<const bf16_t*>(a.W);
+    g.mm = a.mm;
+    g.part = part;
+    g.logits = a.logits;
+    g.H = a.H;
+    g.V = a.V;
+    g.n_slabs = n_slabs;
+    g.n_mt = (a.B * a.gamma + kBM - 1) / kBM;
+    g.with_sum = rej ? 1 : 0;
+    g.ncb = (a.V + 31) / 32;
+    g.w_bytes = lm_tiled_weight_bytes(a.V, a.H);
+    constexpr int kWN = 128;   // 128 x 512 workgroup tiles
+    using Cfg = TiledCfg<kWN>;
+    g.n_vt = (a.V + Cfg::kBN - 1) / Cfg::kBN;
+    const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm_tiled<kWN>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds)) != hipSuccess)
+      return e;
+    hipLaunchKernelGGL(k_lm_gemm_tiled<kWN>, dim3(grid), dim3(kGemmThreads), Cfg::kLds, s, g);
+  } else if (a.dtype == RV_BF16) {
     GemmParams g;
     g.x = static_cast<const bf16_t*>(a.hidden);
     g.w = static_cast<const bf16_t*>(a.W);

@@ -131,9 +131,26 @@ rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream) {
   if (a->rule == RV_REJECTION && a->V > kMaxVocabRejection) return RV_ERR_UNSUPPORTED;
   if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
   if (a->dtype == RV_BF16 && a->H % 64 != 0) return RV_ERR_UNSUPPORTED;
+  if (a->w_layout != RV_W_ROWS && a->w_layout != RV_W_TILED) return RV_ERR_INVALID_ARG;
+  if (a->w_layout == RV_W_TILED && (a->dtype != RV_BF16 || a->H % 128 != 0)) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + lm_scratch_bytes(a->B, a->gamma, a->V);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
   return hip_status(launch_lm(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_lm_tiled_weight_bytes(int32_t V, int32_t H, int32_t dtype, size_t* bytes) {
+  if (!bytes || V < 1 || H < 128 || H % 128 != 0) return RV_ERR_INVALID_ARG;
+  if (dtype != RV_BF16) return RV_ERR_UNSUPPORTED;
+  *bytes = lm_tiled_weight_bytes(V, H);
+  return RV_OK;
+}
+
+rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, int32_t dtype, void* stream) {
+  if (!W || !W_tiled || V < 1 || H < 128 || H % 128 != 0) return RV_ERR_INVALID_ARG;
+  if (dtype != RV_BF16) return RV_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(W) % 16 != 0 || reinterpret_cast<uintptr_t>(W_tiled) % 16 != 0)
+    return RV_ERR_INVALID_ARG;
+  return hip_status(launch_lm_tile_weight(W, W_tiled, V, H, static_cast<hipStream_t>(stream)));
 }
 
 rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream) {
@@ -193,7 +210,7 @@ int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap) {
       int64_t t[] = {sizeof(S), RV_OFF(S, hidden), RV_OFF(S, W), RV_OFF(S, mm), RV_OFF(S, cu),
                      RV_OFF(S, w_commit), RV_OFF(S, w_verify), RV_OFF(S, drafts), RV_OFF(S, q_rows),
                      RV_OFF(S, u), RV_OFF(S, u_bonus), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, rows_cap),
-                     RV_OFF(S, H), RV_OFF(S, V), RV_OFF(S, dtype), RV_OFF(S, rule), RV_OFF(S, _pad0),
+                     RV_OFF(S, H), RV_OFF(S, V), RV_OFF(S, dtype), RV_OFF(S, rule), RV_OFF(S, w_layout),
                      RV_OFF(S, pred), RV_OFF(S, accept), RV_OFF(S, bonus), RV_OFF(S, ceiling),
                      RV_OFF(S, logits), RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
       n = sizeof(t) / sizeof(t[0]);

@@ -108,6 +108,8 @@ hipError_t launch_clear_status(void* ws, hipStream_t s);
 // host-side sizing helpers shared by the API layer and the launchers
 size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, int dtype);
 size_t lm_scratch_bytes(int B, int gamma, int V);
+size_t lm_tiled_weight_bytes(int V, int H);
+hipError_t launch_lm_tile_weight(const void* W, void* W_tiled, int V, int H, hipStream_t s);
 bool attn_shape_supported(int Hq, int Hkv, int Dqk, int Dv, int dtype, bool latent);
 int attn_max_pages_limit(int dtype, bool latent);
 

@@ -20,7 +20,7 @@ from . import rv
 
 class VerifyStep:
     def __init__(self, inp, mode="compact", with_logits=False, rows_cap=None, r2t_extra=64,
-                 hist_cap=64, stream=None):
+                 hist_cap=64, stream=None, w_layout="tiled"):
         wl = inp["workload"]
         self.inp, self.wl = inp, wl
         self.mode = mode
@@ -85,6 +85,14 @@ class VerifyStep:
         self.q_flat = inp["q_block"].reshape(B * gamma, wl.Hq, wl.Dqk)
         self.h_flat = inp["hidden_block"].reshape(B * gamma, wl.H)
         self.stream = stream
+        # LM-head weight in MFMA fragment order, made once per weight (a
+        # serving system does this when it loads the model); bf16 with
+        # H % 128 == 0 only, otherwise the row-major weight is read
+        self.W_tiled = None
+        if w_layout == "tiled" and self.dtype == torch.bfloat16 and wl.H % 128 == 0:
+            if inp.get("W_tiled") is None:
+                inp["W_tiled"] = rv.rv_lm_tile_weight(inp["W"], stream=stream)
+            self.W_tiled = inp["W_tiled"]
 
     # ---- stages ------------------------------------------------------------------
     def schedule(self):
@@ -119,7 +127,7 @@ class VerifyStep:
         rv.rv_lm_head_accept(self.hidden, i["W"], self.mm, self.cu, self.w_commit, self.w_verify, i["drafts"],
                              self.rule, self.pred, self.accept, self.bonus, self.ceiling, self.workspace,
                              logits=self.logits, q_rows=i.get("q_rows"), u=i.get("u"), u_bonus=i.get("u_bonus"),
-                             stream=self.stream)
+                             stream=self.stream, W_tiled=self.W_tiled)
 
     def scatter(self):
         i = self.inp

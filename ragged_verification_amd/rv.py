@@ -25,6 +25,7 @@ RV_STATIC, RV_COMPACT, RV_CAP_ACCEPT, RV_NO_TRIM = 0, 1, 2, 3
 MODES = {"static": RV_STATIC, "compact": RV_COMPACT, "cap_accept": RV_CAP_ACCEPT, "no_trim": RV_NO_TRIM}
 RV_GREEDY, RV_REJECTION = 0, 1
 RV_F32, RV_BF16 = 0, 1
+RV_W_ROWS, RV_W_TILED = 0, 1
 RV_MAX_GAMMA, RV_MAX_TIERS, RV_MAX_ROWS = 16, 16, 8192
 
 _vp, _i32, _f32, _f64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
@@ -62,7 +63,7 @@ class LmArgs(ctypes.Structure):
     _fields_ = [("hidden", _vp), ("W", _vp), ("mm", _vp), ("cu", _vp), ("w_commit", _vp),
                 ("w_verify", _vp), ("drafts", _vp), ("q_rows", _vp), ("u", _vp), ("u_bonus", _vp),
                 ("B", _i32), ("gamma", _i32), ("rows_cap", _i32), ("H", _i32), ("V", _i32),
-                ("dtype", _i32), ("rule", _i32), ("_pad0", _i32), ("pred", _vp), ("accept", _vp),
+                ("dtype", _i32), ("rule", _i32), ("w_layout", _i32), ("pred", _vp), ("accept", _vp),
                 ("bonus", _vp), ("ceiling", _vp), ("logits", _vp), ("workspace", _vp),
                 ("workspace_bytes", _sz)]
 
@@ -78,7 +79,8 @@ class ScatterArgs(ctypes.Structure):
 
 STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims]
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
-           "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout"]
+           "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
+           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight"]
 
 _LIB = None
 
@@ -110,6 +112,10 @@ def load(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = _i32
         fn.argtypes = [ctypes.POINTER(st), _vp]
+    lib.rv_lm_tiled_weight_bytes.restype = _i32
+    lib.rv_lm_tiled_weight_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
+    lib.rv_lm_tile_weight.restype = _i32
+    lib.rv_lm_tile_weight.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp]
     lib.rv_abi_layout.restype = _i32
     lib.rv_abi_layout.argtypes = [_i32, ctypes.POINTER(ctypes.c_int64), _i32]
     for which, st in enumerate(STRUCTS):
@@ -234,17 +240,41 @@ def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, c
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
 
 
+def rv_lm_tiled_weight_bytes(V, H, dtype=RV_BF16):
+    n = _sz(0)
+    _check("rv_lm_tiled_weight_bytes", load().rv_lm_tiled_weight_bytes(V, H, dtype, ctypes.byref(n)))
+    return n.value
+
+
+def rv_lm_tile_weight(W, W_tiled=None, stream=None):
+    """Write the tiled copy of W [V][H] (bf16) made for w_layout=RV_W_TILED;
+    allocates it with torch when W_tiled is None.  Returns W_tiled."""
+    V, H = W.shape
+    n = rv_lm_tiled_weight_bytes(V, H, _dtype_code(W))
+    if W_tiled is None:
+        W_tiled = torch.empty(n, dtype=torch.uint8, device=W.device)
+    if W_tiled.numel() * W_tiled.element_size() < n:
+        raise ValueError(f"W_tiled holds {W_tiled.numel() * W_tiled.element_size()} bytes, needs {n}")
+    _check("rv_lm_tile_weight", load().rv_lm_tile_weight(_ptr(W, W.dtype, "W"), _ptr(W_tiled, name="W_tiled"),
+                                                         V, H, _dtype_code(W), _stream(stream)))
+    return W_tiled
+
+
 def rv_lm_head_accept(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
-                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None):
+                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None, W_tiled=None):
+    """W [V][H] gives the vocabulary size; with W_tiled (rv_lm_tile_weight of
+    W) the kernel reads the tiled copy instead."""
     rows_cap, H = hidden.shape
     V = W.shape[0]
     B, g1 = drafts.shape
-    a = LmArgs(hidden=_ptr(hidden, hidden.dtype, "hidden"), W=_ptr(W, hidden.dtype, "W"),
+    Wp = _ptr(W, hidden.dtype, "W") if W_tiled is None else _ptr(W_tiled, name="W_tiled")
+    a = LmArgs(hidden=_ptr(hidden, hidden.dtype, "hidden"), W=Wp,
                mm=_ptr(mm, torch.int32, "mm"), cu=_ptr(cu, torch.int32, "cu"),
                w_commit=_ptr(w_commit, torch.int32, "w_commit"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
                drafts=_ptr(drafts, torch.int32, "drafts"), q_rows=_ptr(q_rows, torch.float32, "q_rows"),
                u=_ptr(u, torch.float32, "u"), u_bonus=_ptr(u_bonus, torch.float32, "u_bonus"),
                B=B, gamma=g1 + 1, rows_cap=rows_cap, H=H, V=V, dtype=_dtype_code(hidden), rule=rule,
+               w_layout=RV_W_ROWS if W_tiled is None else RV_W_TILED,
                pred=_ptr(pred, torch.int32, "pred"), accept=_ptr(accept, torch.int32, "accept"),
                bonus=_ptr(bonus, torch.int32, "bonus"), ceiling=_ptr(ceiling, torch.int32, "ceiling"),
                logits=_ptr(logits, torch.float32, "logits"),

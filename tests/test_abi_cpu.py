@@ -116,6 +116,21 @@ def test_attn_validation(lib):
     assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
 
 
+def test_tiled_weight_size_and_validation(lib):
+    n = ctypes.c_size_t(0)
+    # V rounded up to 32 rows, 2 bytes per element
+    assert lib.rv_lm_tiled_weight_bytes(1000, 256, rv.RV_BF16, ctypes.byref(n)) == rv.RV_OK
+    assert n.value == 1024 * 256 * 2
+    assert lib.rv_lm_tiled_weight_bytes(129280, 7168, rv.RV_BF16, ctypes.byref(n)) == rv.RV_OK
+    assert n.value == 129280 * 7168 * 2
+    assert lib.rv_lm_tiled_weight_bytes(1000, 192, rv.RV_BF16, ctypes.byref(n)) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_lm_tiled_weight_bytes(1000, 256, rv.RV_F32, ctypes.byref(n)) == rv.RV_ERR_UNSUPPORTED
+    assert lib.rv_lm_tiled_weight_bytes(0, 256, rv.RV_BF16, ctypes.byref(n)) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_lm_tile_weight(None, _fake(), 1000, 256, rv.RV_BF16, None) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_lm_tile_weight(_fake(), _fake(), 1000, 64, rv.RV_BF16, None) == rv.RV_ERR_INVALID_ARG
+    assert lib.rv_lm_tile_weight(_fake(), _fake(), 1000, 256, rv.RV_F32, None) == rv.RV_ERR_UNSUPPORTED
+
+
 def test_lm_and_scatter_validation(lib):
     a = rv.LmArgs()
     for f in ("hidden", "W", "mm", "cu", "w_commit", "w_verify", "drafts", "pred", "accept", "bonus",
@@ -127,6 +142,12 @@ def test_lm_and_scatter_validation(lib):
     assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
     a.H, a.rule = 128, rv.RV_REJECTION   # rejection needs q_rows, u, u_bonus, logits
     assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.rule, a.w_layout = rv.RV_GREEDY, 7      # unknown weight layout
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.w_layout, a.H = rv.RV_W_TILED, 192      # tiled weight needs H % 128 == 0
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.H, a.dtype = 128, rv.RV_F32             # tiled weight is bf16 only
+    assert lib.rv_lm_head_accept(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
     s = rv.ScatterArgs()
     for f in ("cu", "w_verify", "accept", "bonus", "drafts", "slot", "ctx", "anchor", "req_to_token",
               "commit_cu", "commit_tok", "commit_slot", "free_slots", "free_count"):

@@ -74,10 +74,10 @@ def _check_scatter(step, sc, B):
     assert np.array_equal(pu.npi(step.hist_len), sc["hist_len"])
 
 
-def _full_parity(inp, mode, dtype):
-    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode}")
+def _full_parity(inp, mode, dtype, w_layout="tiled"):
+    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode} weight={w_layout}")
     ref = pu.oracle_schedule_pack(inp, mode)
-    step = pu.run_gpu(inp, mode, with_logits=True)
+    step = pu.run_gpu(inp, mode, with_logits=True, w_layout=w_layout)
     assert step.status() == 0
     pu.check_schedule_pack(step, ref)
     want = _oracle_full(inp, ref, mode)
@@ -139,6 +139,33 @@ def test_rejection_odd_vocab():
     loads in the bonus draw) and the last slab and segment are partial."""
     inp = pu.make_inputs("rejection_bf16", B=5, V=4229, H=128, ctx=("lognormal", 150, 1.0, 500))
     _full_parity(inp, "compact", "bf16")
+
+
+def test_lm_row_major_weight():
+    """The LM head reading W [V][H] row-major (w_layout RV_W_ROWS) instead of
+    its tiled copy; V = 4229 leaves a partial last slab."""
+    inp = pu.make_inputs("rejection_bf16", B=5, V=4229, H=256, ctx=("lognormal", 150, 1.0, 500))
+    _full_parity(inp, "compact", "bf16", w_layout="rows")
+    inp = pu.make_inputs("mla_bf16", B=3, V=1000, H=512, ctx=("uniform", 60, 700))
+    _full_parity(inp, "static", "bf16", w_layout="rows")
+
+
+def test_tiled_weight_layout():
+    """rv_lm_tile_weight against the layout written out with torch view
+    operations: lane l of fragment f of block cb holds
+    W[32*cb + l%32][16*f + 8*(l//32) .. +7]; rows past V are zero."""
+    from ragged_verification_amd import rv
+    g = torch.Generator().manual_seed(7)
+    for V, H in ((1000, 256), (4229, 128), (64, 384)):
+        W = torch.randn(V, H, generator=g).to(torch.bfloat16)
+        t = rv.rv_lm_tile_weight(W.cuda())
+        torch.cuda.synchronize()
+        Vp = (V + 31) // 32 * 32
+        Wp = torch.zeros(Vp, H, dtype=torch.bfloat16)
+        Wp[:V] = W
+        want = Wp.view(Vp // 32, 32, H // 16, 2, 8).permute(0, 2, 3, 1, 4).contiguous()
+        got = t.cpu().view(torch.bfloat16).view(Vp // 32, H // 16, 2, 32, 8)
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), (V, H)
 
 
 def test_gqa_many_tiles_chunked_plan():
