@@ -318,7 +318,7 @@ struct TiledCfg {
   static constexpr int kBN = 4 * WN;                  // workgroup columns
   static constexpr int kStage = kBM * kGRow;          // 16 KB of hidden rows per K step
   static constexpr int kEpi = 4 * 32 * (WN + 4) * 4;  // epilogue transpose area
-  static constexpr int kLds = 2 * kStage > kEpi ? 2 * kStage : kEpi;
+  static constexpr int kLds = 4 * kStage > kEpi ? 4 * kStage : kEpi;   // four-stage ring
 };
 
 __device__ inline void lds_w128(uint32_t addr, const u32x4_t& v) { *(lds_u32x4_t*)(size_t)addr = v; }
@@ -404,31 +404,51 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
 
   // register ring of weight fragments: sub-step s sits in slot s % kTRing
   // and is loaded kTDist sub-steps before its MFMAs (past the end: the last
-  // sub-step again).  The prologue issues its loads in the order the loop
-  // does (weights of sub-steps 0..6 with the hidden rows of steps 0 and 1
-  // where steps -2 and -1 would have put them), so that the compiler's
-  // load counting sees the same queue on entry as around the loop.
+  // sub-step again).  Hidden rows: a four-stage LDS ring, step k in stage
+  // k % 4, written during step k-2 from registers ar[k % 2] that were loaded
+  // during step k-4; so one barrier per two steps suffices (it separates the
+  // reads of stage k % 4 during steps k and k+1 from its refill during step
+  // k+2, and that refill from its reads), and waiting for hidden rows never
+  // waits for weights loaded less than seven sub-steps ahead.  The prologue
+  // issues its loads in the order the loop does (scheduling barriers keep
+  // it), so that the compiler's load counting sees the same queue on entry as
+  // around the loop.
   u32x4_t br[kTRing][kNB];
-  u32x4_t ar[4], ar0[4];
-  load_w(br[0], 0);
+  u32x4_t ar[2][4], ar0[4], ar1[4];
   load_a(ar0, 0);
-  load_w(br[1], min(1, nsub - 1));
-  load_w(br[2], min(2, nsub - 1));
-  load_w(br[3], min(3, nsub - 1));
-  load_w(br[4], min(4, nsub - 1));
-  load_a(ar, min(1, nk - 1));
-  load_w(br[5], min(5, nsub - 1));
-  load_w(br[6], min(6, nsub - 1));
-  // hidden rows of step 0 into stage 0; step 1 stays in registers
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(ar1, min(1, nk - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(br[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(ar[0], min(2, nk - 1));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) lds_w128(lds + adst[e], ar0[e]);
+  for (int j = 1; j < 5; ++j) {
+    load_w(br[j], min(j, nsub - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_a(ar[1], min(3, nk - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(br[5], min(5, nsub - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(br[6], min(6, nsub - 1));
+  __builtin_amdgcn_sched_barrier(0);
+  // hidden rows of steps 0 and 1 into stages 0 and 1
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lds_w128(lds + adst[e], ar0[e]);
+    lds_w128(lds + Cfg::kStage + adst[e], ar1[e]);
+  }
   __syncthreads();
 
   for (int kt = 0; kt < nk; kt += 2) {
+    const uint32_t half = (uint32_t)(kt & 2) * Cfg::kStage;   // stages of steps kt, kt+1
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int k = kt + u;
-      const uint32_t stg = lds + u * Cfg::kStage;   // step k sits in stage k & 1 == u
+      const uint32_t stg = lds + half + u * Cfg::kStage;                   // stage k % 4
+      const uint32_t nxt = lds + (half ^ (2 * Cfg::kStage)) + u * Cfg::kStage;   // stage (k+2) % 4
       u32x4_t fa[2][4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
@@ -438,11 +458,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
         const int jn = (j + kTDist) % kTRing;          // slot of the sub-step kTDist ahead
         load_w(br[jn], min(4 * k + ks + kTDist, nsub - 1));
         if (ks == 1) {
-          // step k+1's hidden rows into the other stage (read by every wave
-          // during step k-1, before the last barrier), then load step k+2
+          // step k+2's hidden rows (ar[u]) into stage (k+2) % 4, then step
+          // k+4 into the same registers
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lds_w128(lds + (u ^ 1) * Cfg::kStage + adst[e], ar[e]);
-          load_a(ar, min(k + 2, nk - 1));
+          for (int e = 0; e < 4; ++e) lds_w128(nxt + adst[e], ar[u][e]);
+          load_a(ar[u], min(k + 4, nk - 1));
         }
         if (ks + 1 < kGKs) {
 #pragma unroll
@@ -455,9 +475,10 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
           for (int bn = 0; bn < kNB; ++bn) acc[bm][bn] = mfma32(fa[ks & 1][bm], br[j][bn], acc[bm][bn]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // step k+1 is in LDS; every wave is done with stage u
-      __syncthreads();
     }
+    // steps kt+2 and kt+3 are in LDS; every wave is done with the stages of
+    // steps kt and kt+1
+    __syncthreads();
   }
 
   lm_epilogue<WN>(acc, smem, p, wid, lane, m0, v0, M);
@@ -835,18 +856,31 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     g.H = a.H;
     g.V = a.V;
     g.n_slabs = n_slabs;
-    g.n_mt = (a.B * a.gamma + kBM - 1) / kBM;
+    g.n_mt = (a.B * a.gamma + kBM - 1) / kBM;   // real rows never exceed one full block each
     g.with_sum = rej ? 1 : 0;
     g.ncb = (a.V + 31) / 32;
     g.w_bytes = lm_tiled_weight_bytes(a.V, a.H);
-    constexpr int kWN = 128;   // 128 x 512 workgroup tiles
-    using Cfg = TiledCfg<kWN>;
-    g.n_vt = (a.V + Cfg::kBN - 1) / Cfg::kBN;
-    const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
-    if ((e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm_tiled<kWN>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds)) != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(k_lm_gemm_tiled<kWN>, dim3(grid), dim3(kGemmThreads), Cfg::kLds, s, g);
+    // 128 x 512 tiles; 128 x 256 tiles when they need no more rounds of one
+    // tile per CU (counted at the B*gamma row bound): small batches, whose
+    // 512-wide grid leaves CUs idle (the 156-row GQA batch: 118 -> 87 us;
+    // the latent batch's 815 rows: 1.73 ms with 256-wide tiles, 1.52 ms
+    // with 512-wide ones)
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int t512 = g.n_mt * ((a.V + 511) / 512), t256 = g.n_mt * ((a.V + 255) / 256);
+    const bool narrow = (t256 + cus - 1) / cus <= (t512 + cus - 1) / cus;
+    auto launch = [&](auto kern, int bn, int lds_bytes) -> hipError_t {
+      g.n_vt = (a.V + bn - 1) / bn;
+      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), lds_bytes, s, g);
+      return hipSuccess;
+    };
+    e = narrow ? launch(k_lm_gemm_tiled<64>, TiledCfg<64>::kBN, TiledCfg<64>::kLds)
+               : launch(k_lm_gemm_tiled<128>, TiledCfg<128>::kBN, TiledCfg<128>::kLds);
+    if (e != hipSuccess) return e;
   } else if (a.dtype == RV_BF16) {
     GemmParams g;
     g.x = static_cast<const bf16_t*>(a.hidden);
