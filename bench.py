@@ -152,6 +152,35 @@ def measure(step, steps, warmup):
                 committed=committed)
 
 
+def measure_graph(step, steps, warmup):
+    """The same step replayed from its HIP graphs (VerifyStep.capture): front
+    (schedule, pack) and back (attention, LM head + accept, scatter) timed
+    with HIP events around each replay; staging and state restore between
+    them are not counted, as in the eager timing."""
+    step.capture()
+    for _ in range(warmup):
+        step.restore()
+        step.replay()
+    torch.cuda.synchronize()
+    timer = StageTimer(["front", "staging", "back"])
+    for _ in range(steps):
+        step.restore()
+        timer.start("front")
+        step.g_front.replay()
+        timer.stop("front")
+        timer.start("staging")
+        step.stage_payload()
+        timer.stop("staging")
+        timer.start("back")
+        step.g_back.replay()
+        timer.stop("back")
+    timer.finish()
+    assert step.status() == 0, f"device status {rv.DEV_NAMES.get(step.status())}"
+    per = {k: v / steps for k, v in timer.acc.items()}
+    return {"ms_per_step": per["front"] + per["back"], "front_ms": per["front"], "back_ms": per["back"],
+            "staging_ms": per["staging"]}
+
+
 def sweep(steps, warmup):
     """The mixed-confidence sweep: GQA shapes at each batch size of the sweep
     list; request i has confidence class i mod 3.  Static, compact and
@@ -180,6 +209,9 @@ def sweep(steps, warmup):
                 ceil = step.ceiling.cpu().numpy().astype(np.int64)
                 rec["ceiling_utilisation"] = float((acc + 1).sum() / (ceil + 1).sum())
             if mode == "compact":
+                g = measure_graph(step, steps, warmup)
+                rec["graph"] = {"ms_per_step": g["ms_per_step"], "front_ms": round(g["front_ms"], 4),
+                                "back_ms": round(g["back_ms"], 4)}
                 w = step.w_verify.cpu().numpy().astype(np.int64)
                 ctx = inp["ctx"].cpu().numpy().astype(np.int64)
                 gbs = attn_bytes(ctx, w, wl) / (r["per_stage_ms"]["attn"] / 1e3) / 1e9
@@ -294,6 +326,8 @@ def main():
     ap.add_argument("--workload", default="mla_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time each mode replayed from HIP graphs (VerifyStep.capture)")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the mixed-confidence batch sweep (one JSON line per batch size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -329,6 +363,8 @@ def main():
         r["attn_flops"] = attn_flops(ctx, w, wl.Hq, wl.Dqk, wl.Dv)
         r["attn_bytes"] = attn_bytes(ctx, w, wl)
         r["lm_flops"] = lm_flops(r["M"], wl.H, wl.V)
+        if args.graph:
+            r["graph"] = measure_graph(step, args.steps, args.warmup)
         results[mode] = r
         log(f"{mode}: M={r['M']} M_pad={r['M_pad']} five-stage {r['five_stage_ms']:.3f} ms "
             f"stages {({k: round(v, 4) for k, v in r['per_stage_ms'].items()})}")
@@ -379,12 +415,19 @@ def main():
                     "frac": lm_tflops / PEAK_BF16_TFLOPS, "launch_ms": lm_ms},
         "roofline": roof,
     }
+    if "graph" in c:
+        g = c["graph"]
+        line["graph"] = {"ms_per_step": g["ms_per_step"], "packed_tok_s": c["M"] / (g["ms_per_step"] / 1e3),
+                         "accepted_tok_s": c["committed"] / (g["ms_per_step"] / 1e3),
+                         "front_ms": round(g["front_ms"], 4), "back_ms": round(g["back_ms"], 4)}
     if "static" in results:
         s = results["static"]
         line["static"] = {"packed_rows": s["M"], "ms_per_step": s["five_stage_ms"],
                           "packed_tok_s": s["M"] / (s["five_stage_ms"] / 1e3),
                           "accepted_tok_s": s["committed"] / (s["five_stage_ms"] / 1e3),
                           "stages_ms": {k: round(v, 4) for k, v in s["per_stage_ms"].items()}}
+        if "graph" in s:
+            line["static"]["graph_ms_per_step"] = s["graph"]["ms_per_step"]
         line["compact_vs_static"] = {"row_ratio": c["M"] / s["M"],
                                      "time_ratio": c["five_stage_ms"] / s["five_stage_ms"]}
     if not args.no_cpu_baseline:

@@ -152,5 +152,43 @@ class VerifyStep:
         self.lm()
         self.scatter()
 
+    # ---- HIP graphs ------------------------------------------------------------
+    def capture(self):
+        """Record the step into two HIP graphs on a side stream: ``front``
+        (schedule, pack) and ``back`` (verify attention, LM head + accept,
+        compact scatter); the staging gather stays outside them (harness
+        work).  One pair of graphs serves every capture tier: the kernels
+        read the packed counts (M, M_pad) on the device and size their grids
+        by host-known capacities, so nothing in a launch depends on the tier.
+        Replays see the device buffers as they are at replay time; the mutated
+        state (ctx, anchors, req_to_token, history) is restored outside."""
+        if self.stream is not None:
+            raise ValueError("capture records on torch's current stream; build the step without stream=")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):   # warm-up outside capture: sets kernel attributes once
+            self.restore()
+            self.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.restore()
+        torch.cuda.synchronize()
+        self.g_front = torch.cuda.CUDAGraph()
+        self.g_back = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_front, capture_error_mode="thread_local"):
+            self.schedule()
+            self.pack()
+        with torch.cuda.graph(self.g_back, capture_error_mode="thread_local"):
+            self.attn()
+            self.lm()
+            self.scatter()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        """One step from the captured graphs (capture() first)."""
+        self.g_front.replay()
+        self.stage_payload()
+        self.g_back.replay()
+
     def status(self):
         return rv.rv_device_status(self.workspace, self.stream)

@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import parity_util as pu
+from ragged_verification_amd.pipeline import VerifyStep
 
 pytestmark = pytest.mark.gpu
 
@@ -259,6 +260,41 @@ def test_deterministic_replay():
     a.run()
     torch.cuda.synchronize()
     assert torch.equal(a.o, o1) and torch.equal(a.logits, z1)
+
+
+def _outputs(step):
+    names = ("w_commit", "w_verify", "k_star", "e_star", "cu", "mm", "row_req", "row_pos", "tok", "slot", "o",
+             "lse", "pred", "accept", "bonus", "ceiling", "logits", "ctx", "anchor", "req_to_token", "hist",
+             "hist_len", "commit_cu", "commit_tok", "commit_slot", "free_slots", "free_count")
+    return {n: getattr(step, n).clone() for n in names}
+
+
+@pytest.mark.parametrize("wl,kw", [("mla_bf16", dict(B=3, V=1000, H=512, ctx=("uniform", 60, 700))),
+                                   ("rejection_bf16", dict(B=6, V=3000, H=256,
+                                                           ctx=("lognormal", 200, 1.0, 600)))])
+def test_graph_replay_equals_eager(wl, kw):
+    """The step captured in HIP graphs: every replay, with the program's own
+    eager work and synchronisations between replays, equals the eager step
+    bit for bit (every output buffer, including the mutated state)."""
+    inp = pu.make_inputs(wl, **kw)
+    ref = pu.run_gpu(inp, "compact", with_logits=True)
+    want = _outputs(ref)
+    step = VerifyStep(inp, mode="compact", with_logits=True)
+    step.capture()
+    for rep in range(3):
+        step.restore()
+        step.replay()
+        torch.cuda.synchronize()
+        got = _outputs(step)
+        for n, t in want.items():
+            assert torch.equal(got[n], t), (rep, n)
+        assert step.status() == 0
+        # eager work between replays: the reference step again, and torch ops
+        ref.restore()
+        ref.run()
+        torch.cuda.synchronize()
+        _ = (inp["q_block"].float() * 2).sum().item()
+        assert torch.equal(ref.o, want["o"])
 
 
 def test_mla_two_rows_per_tile_and_long_split():
