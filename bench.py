@@ -223,6 +223,59 @@ def sweep(steps, warmup):
         torch.cuda.empty_cache()
 
 
+def fit_cost(steps, warmup):
+    """Cost-table profiling on this GPU: the mixed-confidence workload at every
+    batch size of the sweep, static and compact (the sweep's cost table), gives
+    samples (bs, M, five-stage ms); rv_fit_cost_model fits
+    T = bias + a*bs + th*M; compact then runs again with the fitted tables.
+    One JSON line per batch size (measured against predicted time, and the
+    committed tokens per ms of static, compact with the sweep's table and
+    compact with the fitted table), then one line with the fit."""
+    samples, runs = [], {}
+    for B in synth.SWEEP_BATCHES:
+        wl = synth.workload("sweep_gqa", B=B)
+        inp = synth.make_inputs(wl, device="cuda", B=B)
+        for mode in ("static", "compact"):
+            step = VerifyStep(inp, mode=mode)
+            r = measure(step, steps, warmup)
+            samples.append((B, r["M"], r["five_stage_ms"]))
+            runs[(B, mode)] = r
+            del step
+        del inp
+        torch.cuda.empty_cache()
+    bs, Ms, ts = zip(*samples)
+    B_max = max(synth.SWEEP_BATCHES)
+    gamma = synth.workload("sweep_gqa").gamma
+    coef, alpha, theta = rv.rv_fit_cost_model(bs, Ms, ts, alpha_len=B_max + 1, theta_len=B_max * gamma + 1)
+    resid = [t - (coef[0] + coef[1] * b + coef[2] * m) for b, m, t in samples]
+    for B in synth.SWEEP_BATCHES:
+        wl = synth.workload("sweep_gqa", B=B)
+        inp = synth.make_inputs(wl, device="cuda", B=B)
+        inp["cost_bias"] = coef[0]
+        inp["cost_alpha"] = torch.tensor(alpha, dtype=torch.float64, device="cuda")
+        inp["cost_theta"] = torch.tensor(theta, dtype=torch.float64, device="cuda")
+        step = VerifyStep(inp, mode="compact")
+        r = measure(step, steps, warmup)
+        cls = np.arange(B) % 3
+        wc = step.w_commit.cpu().numpy()
+        pred = lambda m: coef[0] + coef[1] * B + coef[2] * m
+        out = {"workload": "sweep_gqa", "B": B, "fit": "cost_table"}
+        for mode in ("static", "compact"):
+            q = runs[(B, mode)]
+            out[mode] = {"ms_per_step": q["five_stage_ms"], "predicted_ms": pred(q["M"]), "packed_rows": q["M"],
+                         "committed_per_ms": q["committed"] / q["five_stage_ms"]}
+        out["compact_fitted"] = {"ms_per_step": r["five_stage_ms"], "predicted_ms": pred(r["M"]),
+                                 "packed_rows": r["M"], "committed_per_ms": r["committed"] / r["five_stage_ms"],
+                                 "mean_window_by_class": [float(wc[cls == k].mean()) if (cls == k).any() else None
+                                                          for k in range(3)]}
+        print(json.dumps(out, default=_json_default), flush=True)
+        del step, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"fit": {"bias_ms": coef[0], "alpha_ms_per_request": coef[1], "theta_ms_per_row": coef[2],
+                              "samples": len(samples), "rms_residual_ms": float(np.sqrt(np.mean(np.square(resid)))),
+                              "max_abs_residual_ms": float(np.max(np.abs(resid)))}}), flush=True)
+
+
 def cpu_baseline(inp, step, n_req=130):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     schedule and pack for the whole batch, then attention, LM head, accept and
@@ -328,6 +381,8 @@ def main():
     ap.add_argument("--no-static", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="also time each mode replayed from HIP graphs (VerifyStep.capture)")
+    ap.add_argument("--fit-cost", action="store_true",
+                    help="only run cost-table profiling: fit the step-time model on this GPU and rerun compact with it")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the mixed-confidence batch sweep (one JSON line per batch size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -346,6 +401,9 @@ def main():
     rv.load()
     if args.sweep:
         sweep(args.steps, args.warmup)
+        return
+    if args.fit_cost:
+        fit_cost(args.steps, args.warmup)
         return
     wl = synth.workload(args.workload)
     t0 = time.time()

@@ -300,6 +300,26 @@ rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
 rv_status rv_lm_tiled_weight_bytes(int32_t V, int32_t H, int32_t dtype, size_t* bytes);
 rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, int32_t dtype, void* stream);
 
+/* ---- cost-table profiling (outside the per-step path) -------------------- */
+/* DSpark-in-SGLang page, section A2 "cost-table profiling and modelling"
+ * (with the additive model of section 速读): the step time
+ * T(bs, K) = bias + alpha(bs) + theta(M), M = bs + K, is profiled and the
+ * scheduler reads the resulting table.  The pages give neither the form of
+ * alpha and theta nor the fitting method; here both are linear and fitted by
+ * ordinary least squares: t ~ bias + a*bs + th*M over n recorded samples,
+ * solved by modified Gram-Schmidt QR (with one reorthogonalisation) in fp64.
+ *
+ * Host only, pure; every pointer is host memory.  In: bs[n], M[n], t[n].
+ * Out: coef[3] = {bias, a, th}; when alpha (theta) is not NULL,
+ * alpha[b] = a*b for b < alpha_len (theta[m] = th*m for m < theta_len): the
+ * tables rv_schedule_args takes, with bias as cost_bias.
+ * Errors (nothing is written): NULL bs/M/t/coef, n < 3, a negative table
+ * length, a non-finite sample, or samples that do not determine the three
+ * coefficients (a column within 1e-12 of the span of the previous ones):
+ * INVALID_ARG. */
+rv_status rv_fit_cost_model(const double* bs, const double* M, const double* t, int32_t n, double* coef,
+                            double* alpha, int32_t alpha_len, double* theta, int32_t theta_len);
+
 /* ---- stage 5: compact scatter ------------------------------------------- */
 /* DSpark-in-SGLang page, section A2 "performance and zero-overhead
  * scheduling": a fused compact-scatter kernel writes the accepted results

@@ -24,6 +24,7 @@ Five stages, one module each:
 ``accept``             greedy / min(1,p/q) acceptance, cap-accept ceiling
 ``scatter``            compact scatter of committed tokens and KV slots
 ``dense``              fixed-shape padded verify (the static-graph baseline)
+``cost_fit``           least-squares fit of the step-time model's table
 =====================  ======================================================
 
 Every array argument is a numpy array; bf16 inputs arrive as their exact
@@ -39,6 +40,7 @@ from .accept import (GREEDY, REJECTION, accept_greedy, accept_rejection,
                      residual_sample)
 from .scatter import compact_scatter
 from .dense import dense_padded_verify
+from .cost_fit import fit_cost_model, cost_tables
 
 __all__ = [
     "STATIC", "COMPACT", "CAP_ACCEPT", "NO_TRIM", "FIXED_SHIFT",
@@ -46,4 +48,5 @@ __all__ = [
     "verify_attention", "attention_row", "lm_head_logits", "lm_head_pred",
     "GREEDY", "REJECTION", "accept_greedy", "accept_rejection",
     "residual_sample", "compact_scatter", "dense_padded_verify",
+    "fit_cost_model", "cost_tables",
 ]

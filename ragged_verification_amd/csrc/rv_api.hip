@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <vector>
+
 #include "rv_common.h"
 
 namespace rv {
@@ -151,6 +153,54 @@ rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, 
   if (reinterpret_cast<uintptr_t>(W) % 16 != 0 || reinterpret_cast<uintptr_t>(W_tiled) % 16 != 0)
     return RV_ERR_INVALID_ARG;
   return hip_status(launch_lm_tile_weight(W, W_tiled, V, H, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_fit_cost_model(const double* bs, const double* M, const double* t, int32_t n, double* coef,
+                            double* alpha, int32_t alpha_len, double* theta, int32_t theta_len) {
+  if (!bs || !M || !t || !coef || n < 3) return RV_ERR_INVALID_ARG;
+  if ((alpha && alpha_len < 0) || (theta && theta_len < 0)) return RV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (!isfinite(bs[i]) || !isfinite(M[i]) || !isfinite(t[i])) return RV_ERR_INVALID_ARG;
+  // columns of the design matrix: 1, bs, M; orthonormalised in place
+  std::vector<double> q[3];
+  for (int j = 0; j < 3; ++j) q[j].resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    q[0][i] = 1.0;
+    q[1][i] = bs[i];
+    q[2][i] = M[i];
+  }
+  auto dot = [n](const std::vector<double>& x, const std::vector<double>& y) {
+    double acc = 0.0;
+    for (int32_t i = 0; i < n; ++i) acc += x[i] * y[i];
+    return acc;
+  };
+  double R[3][3] = {{0.0}};
+  for (int j = 0; j < 3; ++j) {
+    const double norm0 = sqrt(dot(q[j], q[j]));
+    for (int pass = 0; pass < 2; ++pass)   // Gram-Schmidt twice keeps Q orthogonal
+      for (int k = 0; k < j; ++k) {
+        const double r = dot(q[k], q[j]);
+        R[k][j] += r;
+        for (int32_t i = 0; i < n; ++i) q[j][i] -= r * q[k][i];
+      }
+    R[j][j] = sqrt(dot(q[j], q[j]));
+    if (!(norm0 > 0.0) || !(R[j][j] > 1e-12 * norm0)) return RV_ERR_INVALID_ARG;
+    for (int32_t i = 0; i < n; ++i) q[j][i] /= R[j][j];
+  }
+  std::vector<double> tv(t, t + n);
+  double y[3], x[3];
+  for (int j = 0; j < 3; ++j) y[j] = dot(q[j], tv);
+  for (int j = 2; j >= 0; --j) {
+    double acc = y[j];
+    for (int k = j + 1; k < 3; ++k) acc -= R[j][k] * x[k];
+    x[j] = acc / R[j][j];
+  }
+  for (int j = 0; j < 3; ++j) coef[j] = x[j];
+  if (alpha)
+    for (int32_t b = 0; b < alpha_len; ++b) alpha[b] = x[1] * (double)b;
+  if (theta)
+    for (int32_t m = 0; m < theta_len; ++m) theta[m] = x[2] * (double)m;
+  return RV_OK;
 }
 
 rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream) {

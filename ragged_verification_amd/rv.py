@@ -80,7 +80,7 @@ class ScatterArgs(ctypes.Structure):
 STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims]
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
            "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
-           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight"]
+           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model"]
 
 _LIB = None
 
@@ -116,6 +116,9 @@ def load(path=LIB_PATH):
     lib.rv_lm_tiled_weight_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
     lib.rv_lm_tile_weight.restype = _i32
     lib.rv_lm_tile_weight.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp]
+    _pd = ctypes.POINTER(_f64)
+    lib.rv_fit_cost_model.restype = _i32
+    lib.rv_fit_cost_model.argtypes = [_pd, _pd, _pd, _i32, _pd, _pd, _i32, _pd, _i32]
     lib.rv_abi_layout.restype = _i32
     lib.rv_abi_layout.argtypes = [_i32, ctypes.POINTER(ctypes.c_int64), _i32]
     for which, st in enumerate(STRUCTS):
@@ -238,6 +241,21 @@ def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, c
                  sm_scale=float(sm_scale), o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
+
+
+def rv_fit_cost_model(bs, M, t, alpha_len=0, theta_len=0):
+    """Least-squares fit of the step-time model from host samples (sequences
+    of numbers).  Returns (coef [bias, a, th], alpha table, theta table) as
+    Python lists; the tables are empty when their length is 0."""
+    n = len(bs)
+    arr = lambda xs: (_f64 * max(len(xs), 1))(*[float(x) for x in xs])
+    coef = (_f64 * 3)()
+    al = (_f64 * max(alpha_len, 1))()
+    th = (_f64 * max(theta_len, 1))()
+    _check("rv_fit_cost_model", load().rv_fit_cost_model(arr(bs), arr(M), arr(t), n, coef,
+                                                         al if alpha_len else None, alpha_len,
+                                                         th if theta_len else None, theta_len))
+    return list(coef), list(al[:alpha_len]), list(th[:theta_len])
 
 
 def rv_lm_tiled_weight_bytes(V, H, dtype=RV_BF16):
