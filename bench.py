@@ -423,6 +423,11 @@ def main():
         r["lm_flops"] = lm_flops(r["M"], wl.H, wl.V)
         if args.graph:
             r["graph"] = measure_graph(step, args.steps, args.warmup)
+        if wl.rule == "greedy":   # observability, after the timed steps
+            cal = step.calibration(10)
+            r["calibration"] = {"ece_10_bins": float(cal["ece"].item()),
+                                "verified_drafts": int(cal["req_verified"].sum().item()),
+                                "matched_drafts": int(cal["req_matched"].sum().item())}
         results[mode] = r
         log(f"{mode}: M={r['M']} M_pad={r['M_pad']} five-stage {r['five_stage_ms']:.3f} ms "
             f"stages {({k: round(v, 4) for k, v in r['per_stage_ms'].items()})}")
@@ -473,6 +478,8 @@ def main():
                     "frac": lm_tflops / PEAK_BF16_TFLOPS, "launch_ms": lm_ms},
         "roofline": roof,
     }
+    if "calibration" in c:
+        line["calibration"] = {m: results[m]["calibration"] for m in results}
     if "graph" in c:
         g = c["graph"]
         line["graph"] = {"ms_per_step": g["ms_per_step"], "packed_tok_s": c["M"] / (g["ms_per_step"] / 1e3),

@@ -300,6 +300,44 @@ rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
 rv_status rv_lm_tiled_weight_bytes(int32_t V, int32_t H, int32_t dtype, size_t* bytes);
 rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, int32_t dtype, void* stream);
 
+/* ---- observability: confidence calibration ------------------------------- */
+/* DSpark-in-SGLang page, section A2 "observability and ceiling recovery":
+ * per-request confidence and calibration metrics (ECE) for post-hoc
+ * analysis.  Compact verifies only the scheduled window, so only drafts
+ * 1..w_verify-1 carry a verdict; cap-accept verifies the whole block.
+ *
+ * Per verified draft j of request i (1 <= j <= w_verify[i]-1): confidence
+ * c = conf[i][j-1], label = (drafts[i][j-1] == pred[cu[i]+j-1]) (the greedy
+ * per-token verdict), bin b = min(floor(c * n_bins), n_bins-1) with c*n_bins
+ * one fp64 product.  Outputs (device, caller-owned, written in full):
+ * bin_count[b], bin_match[b], bin_conf_fx[b] = sum of floor(c * 2^48) (int64
+ * fixed point, so sums are exact and order-free), ece[0] =
+ * (sum_b |bin_match[b]*2^48 - bin_conf_fx[b]|) / 2^48 / N (0 when N = 0),
+ * and, when not NULL, req_verified[i] (drafts verified) and req_matched[i]
+ * (verified drafts equal to the target's prediction).
+ * Host errors: NULL required pointer, bad B/gamma, n_bins outside
+ * [1, RV_MAX_CALIB_BINS], rows_cap < B*gamma, small workspace.  Device
+ * errors: BAD_WINDOW (a w_verify outside [1, gamma]: that request is
+ * skipped). */
+#define RV_MAX_CALIB_BINS 1024
+typedef struct {
+  const float* conf;         /* [B][gamma-1] */
+  const int32_t* drafts;     /* [B][gamma-1] */
+  const int32_t* pred;       /* [rows_cap] from rv_lm_head_accept */
+  const int32_t* cu;         /* [B+1] from rv_pack */
+  const int32_t* w_verify;   /* [B] */
+  int32_t B, gamma, rows_cap, n_bins;
+  int64_t* bin_count;        /* out [n_bins] */
+  int64_t* bin_match;        /* out [n_bins] */
+  int64_t* bin_conf_fx;      /* out [n_bins] */
+  double* ece;               /* out [1] */
+  int32_t* req_verified;     /* out [B] or NULL */
+  int32_t* req_matched;      /* out [B] or NULL */
+  void* workspace;           /* status word at its start */
+  size_t workspace_bytes;
+} rv_calib_args;
+rv_status rv_calibration(const rv_calib_args* a, void* stream);
+
 /* ---- cost-table profiling (outside the per-step path) -------------------- */
 /* DSpark-in-SGLang page, section A2 "cost-table profiling and modelling"
  * (with the additive model of section 速读): the step time
@@ -362,7 +400,7 @@ rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream);
 /* ---- ABI self-description ----------------------------------------------- */
 /* Fills out[0] = sizeof(struct), out[1..] = offsetof of each field in
  * declaration order, for struct `which` (0 schedule, 1 pack, 2 attn, 3 lm,
- * 4 scatter, 5 dims).  Returns the number of values written, or -1 if `cap`
+ * 4 scatter, 5 dims, 6 calibration).  Returns the number of values written, or -1 if `cap`
  * is too small or `which` unknown.  Host-only; lets a binding verify its
  * struct mirror. */
 int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap);

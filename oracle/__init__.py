@@ -25,6 +25,7 @@ Five stages, one module each:
 ``scatter``            compact scatter of committed tokens and KV slots
 ``dense``              fixed-shape padded verify (the static-graph baseline)
 ``cost_fit``           least-squares fit of the step-time model's table
+``calibration``        per-request confidence statistics and ECE
 =====================  ======================================================
 
 Every array argument is a numpy array; bf16 inputs arrive as their exact
@@ -41,6 +42,7 @@ from .accept import (GREEDY, REJECTION, accept_greedy, accept_rejection,
 from .scatter import compact_scatter
 from .dense import dense_padded_verify
 from .cost_fit import fit_cost_model, cost_tables
+from .calibration import calibration
 
 __all__ = [
     "STATIC", "COMPACT", "CAP_ACCEPT", "NO_TRIM", "FIXED_SHIFT",
@@ -48,5 +50,5 @@ __all__ = [
     "verify_attention", "attention_row", "lm_head_logits", "lm_head_pred",
     "GREEDY", "REJECTION", "accept_greedy", "accept_rejection",
     "residual_sample", "compact_scatter", "dense_padded_verify",
-    "fit_cost_model", "cost_tables",
+    "fit_cost_model", "cost_tables", "calibration",
 ]

@@ -155,6 +155,17 @@ rv_status rv_lm_tile_weight(const void* W, void* W_tiled, int32_t V, int32_t H, 
   return hip_status(launch_lm_tile_weight(W, W_tiled, V, H, static_cast<hipStream_t>(stream)));
 }
 
+rv_status rv_calibration(const rv_calib_args* a, void* stream) {
+  if (!a || !a->conf || !a->drafts || !a->pred || !a->cu || !a->w_verify || !a->bin_count || !a->bin_match ||
+      !a->bin_conf_fx || !a->ece)
+    return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if (a->n_bins < 1 || a->n_bins > RV_MAX_CALIB_BINS) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_calibration(*a, static_cast<hipStream_t>(stream)));
+}
+
 rv_status rv_fit_cost_model(const double* bs, const double* M, const double* t, int32_t n, double* coef,
                             double* alpha, int32_t alpha_len, double* theta, int32_t theta_len) {
   if (!bs || !M || !t || !coef || n < 3) return RV_ERR_INVALID_ARG;
@@ -275,6 +286,17 @@ int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap) {
                      RV_OFF(S, hist), RV_OFF(S, hist_len), RV_OFF(S, commit_cu), RV_OFF(S, commit_tok),
                      RV_OFF(S, commit_slot), RV_OFF(S, free_slots), RV_OFF(S, free_count),
                      RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 6: {
+      typedef rv_calib_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, conf), RV_OFF(S, drafts), RV_OFF(S, pred), RV_OFF(S, cu),
+                     RV_OFF(S, w_verify), RV_OFF(S, B), RV_OFF(S, gamma), RV_OFF(S, rows_cap), RV_OFF(S, n_bins),
+                     RV_OFF(S, bin_count), RV_OFF(S, bin_match), RV_OFF(S, bin_conf_fx), RV_OFF(S, ece),
+                     RV_OFF(S, req_verified), RV_OFF(S, req_matched), RV_OFF(S, workspace),
+                     RV_OFF(S, workspace_bytes)};
       n = sizeof(t) / sizeof(t[0]);
       for (int k = 0; k < n; ++k) v[k] = t[k];
       break;

@@ -103,6 +103,7 @@ hipError_t launch_pack(const rv_pack_args& a, hipStream_t s);
 hipError_t launch_attn(const rv_attn_args& a, hipStream_t s);
 hipError_t launch_lm(const rv_lm_args& a, hipStream_t s);
 hipError_t launch_scatter(const rv_scatter_args& a, hipStream_t s);
+hipError_t launch_calibration(const rv_calib_args& a, hipStream_t s);
 hipError_t launch_clear_status(void* ws, hipStream_t s);
 
 // host-side sizing helpers shared by the API layer and the launchers

@@ -152,6 +152,26 @@ class VerifyStep:
         self.lm()
         self.scatter()
 
+    # ---- observability -----------------------------------------------------------
+    def calibration(self, n_bins=10):
+        """Confidence calibration of this step's verified drafts (rv_calibration,
+        after lm()): returns the device tensors (bin_count, bin_match,
+        bin_conf_fx, ece, req_verified, req_matched)."""
+        dev = self.w_verify.device
+        if getattr(self, "_calib_bins", None) != n_bins:
+            i64 = dict(dtype=torch.int64, device=dev)
+            self.calib = dict(bin_count=torch.zeros(n_bins, **i64), bin_match=torch.zeros(n_bins, **i64),
+                              bin_conf_fx=torch.zeros(n_bins, **i64),
+                              ece=torch.zeros(1, dtype=torch.float64, device=dev),
+                              req_verified=torch.zeros(self.B, dtype=torch.int32, device=dev),
+                              req_matched=torch.zeros(self.B, dtype=torch.int32, device=dev))
+            self._calib_bins = n_bins
+        c = self.calib
+        rv.rv_calibration(self.inp["conf"], self.inp["drafts"], self.pred, self.cu, self.w_verify, n_bins,
+                          c["bin_count"], c["bin_match"], c["bin_conf_fx"], c["ece"], self.workspace,
+                          req_verified=c["req_verified"], req_matched=c["req_matched"], stream=self.stream)
+        return c
+
     # ---- HIP graphs ------------------------------------------------------------
     def capture(self):
         """Record the step into two HIP graphs on a side stream: ``front``

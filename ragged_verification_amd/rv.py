@@ -77,10 +77,17 @@ class ScatterArgs(ctypes.Structure):
                 ("workspace_bytes", _sz)]
 
 
-STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims]
+class CalibArgs(ctypes.Structure):
+    _fields_ = [("conf", _vp), ("drafts", _vp), ("pred", _vp), ("cu", _vp), ("w_verify", _vp), ("B", _i32),
+                ("gamma", _i32), ("rows_cap", _i32), ("n_bins", _i32), ("bin_count", _vp), ("bin_match", _vp),
+                ("bin_conf_fx", _vp), ("ece", _vp), ("req_verified", _vp), ("req_matched", _vp),
+                ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims, CalibArgs]
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
            "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
-           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model"]
+           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model", "rv_calibration"]
 
 _LIB = None
 
@@ -108,7 +115,8 @@ def load(path=LIB_PATH):
     lib.rv_clear_status.restype = _i32
     lib.rv_clear_status.argtypes = [_vp, _vp]
     for name, st in (("rv_schedule", ScheduleArgs), ("rv_pack", PackArgs), ("rv_verify_attn", AttnArgs),
-                     ("rv_lm_head_accept", LmArgs), ("rv_compact_scatter", ScatterArgs)):
+                     ("rv_lm_head_accept", LmArgs), ("rv_compact_scatter", ScatterArgs),
+                     ("rv_calibration", CalibArgs)):
         fn = getattr(lib, name)
         fn.restype = _i32
         fn.argtypes = [ctypes.POINTER(st), _vp]
@@ -241,6 +249,21 @@ def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, c
                  sm_scale=float(sm_scale), o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
+
+
+def rv_calibration(conf, drafts, pred, cu, w_verify, n_bins, bin_count, bin_match, bin_conf_fx, ece, workspace,
+                   req_verified=None, req_matched=None, stream=None):
+    B, g1 = drafts.shape
+    a = CalibArgs(conf=_ptr(conf, torch.float32, "conf"), drafts=_ptr(drafts, torch.int32, "drafts"),
+                  pred=_ptr(pred, torch.int32, "pred"), cu=_ptr(cu, torch.int32, "cu"),
+                  w_verify=_ptr(w_verify, torch.int32, "w_verify"), B=B, gamma=g1 + 1, rows_cap=pred.numel(),
+                  n_bins=n_bins, bin_count=_ptr(bin_count, torch.int64, "bin_count"),
+                  bin_match=_ptr(bin_match, torch.int64, "bin_match"),
+                  bin_conf_fx=_ptr(bin_conf_fx, torch.int64, "bin_conf_fx"), ece=_ptr(ece, torch.float64, "ece"),
+                  req_verified=_ptr(req_verified, torch.int32, "req_verified"),
+                  req_matched=_ptr(req_matched, torch.int32, "req_matched"),
+                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_calibration", load().rv_calibration(ctypes.byref(a), _stream(stream)))
 
 
 def rv_fit_cost_model(bs, M, t, alpha_len=0, theta_len=0):

@@ -56,6 +56,7 @@ class Workload:
     latent: bool = False     # MLA-style: value = first Dv entries of the key row
     contiguous: bool = False  # one page per request, identity page table
     plant_beta: float = 14.0
+    plant_power: float = 1.0  # a draft matches its target with probability conf ** plant_power
     seed: int = 1000
     modes: tuple = ("static", "compact")
 
@@ -238,7 +239,10 @@ def make_inputs(wl, device="cpu", B=None, seed=None):
         hidden = (x.reshape(B * gamma, H) + wl.plant_beta * unit).reshape(B, gamma, H).to(dt)
         gd = S.gen("drafts")
         coin = torch.rand((B, gamma - 1), generator=gd, device=dev, dtype=torch.float64)
-        correct = coin < conf.to(torch.float64)
+        match_p = conf.to(torch.float64)
+        if wl.plant_power != 1.0:   # miscalibrated confidences (observability tests)
+            match_p = match_p ** wl.plant_power
+        correct = coin < match_p
         other = torch.randint(0, V - 1, (B, gamma - 1), generator=gd, device=dev, dtype=torch.int64)
         t_prev = targets[:, :gamma - 1]
         other = other + (other >= t_prev).to(torch.int64)

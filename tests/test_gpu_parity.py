@@ -297,6 +297,47 @@ def test_graph_replay_equals_eager(wl, kw):
         assert torch.equal(ref.o, want["o"])
 
 
+def _check_calibration(step, inp, n_bins):
+    c = step.calibration(n_bins)
+    torch.cuda.synchronize()
+    assert step.status() == 0
+    want = oracle.calibration(inp["conf"].cpu().numpy(), pu.npi(inp["drafts"]), pu.npi(step.pred), pu.npi(step.cu), pu.npi(step.w_verify),
+                              n_bins)
+    cnt, match, cfx, ece, rver, rmat = want
+    assert c["bin_count"].cpu().tolist() == cnt
+    assert c["bin_match"].cpu().tolist() == match
+    assert c["bin_conf_fx"].cpu().tolist() == cfx
+    assert float(c["ece"].item()) == ece
+    assert c["req_verified"].cpu().tolist() == rver
+    assert c["req_matched"].cpu().tolist() == rmat
+    return ece
+
+
+@pytest.mark.parametrize("mode", ["compact", "cap_accept", "static"])
+def test_calibration_matches_oracle(mode):
+    """Bins, fixed-point confidence sums, ECE and per-request counts, bit for
+    bit; under compact only the scheduled window is counted."""
+    inp = pu.make_inputs("gqa_bf16", B=40, V=1000, H=256, ctx=("uniform", 40, 300), tiers=(512,))
+    step = pu.run_gpu(inp, mode)
+    for n_bins in (10, 1, 37):
+        _check_calibration(step, inp, n_bins)
+    if mode != "compact":
+        assert step.calib["req_verified"].sum().item() == 40 * (inp["gamma"] - 1)
+
+
+def test_calibration_separates_miscalibrated_drafts():
+    """Drafts planted with probability conf (calibrated) against conf^2
+    (overconfident), all positions verified (cap-accept): the GPU's ECE equals
+    the oracle's, and the overconfident batch's is the larger."""
+    eces = []
+    for power in (1.0, 2.0):
+        inp = pu.make_inputs("gqa_bf16", B=256, V=500, H=128, ctx=("uniform", 8, 40), plant_power=power,
+                             tiers=(2048,))
+        step = pu.run_gpu(inp, "cap_accept")
+        eces.append(_check_calibration(step, inp, 10))
+    assert eces[1] > eces[0] + 0.05, eces
+
+
 def test_mla_two_rows_per_tile_and_long_split():
     """64 latent heads (one head block per row) and one long request whose
     key range is split into chunks and merged."""
