@@ -95,8 +95,8 @@ __device__ inline int gswz(int row) { return (row >> 1) & 7; }
 // WN + 4 floats), then lane t reduces row t % 32 over its 64-column slab
 // t / 32 to (max, lowest argmax, sum of exp(z - max)).  Accumulator lane l
 // holds column l % 32 of rows 8*(j/4) + 4*(l/32) + j%4.
-template <int WN>
-__device__ __forceinline__ void lm_epilogue(f32x16_t (&acc)[4][WN / 32], unsigned char* smem,
+template <int WN, int BMB = 4>
+__device__ __forceinline__ void lm_epilogue(f32x16_t (&acc)[BMB][WN / 32], unsigned char* smem,
                                             const GemmParams& p, int wid, int lane, int m0, int v0, int M) {
   constexpr int kNB = WN / 32;
   const int l32 = lane & 31, lh = lane >> 5;
@@ -108,7 +108,7 @@ __device__ __forceinline__ void lm_epilogue(f32x16_t (&acc)[4][WN / 32], unsigne
   const int cslab = v0 + wid * WN + es * kSlab;  // first column of the slab
   const bool reducer = es < WN / kSlab;          // lanes with a slab to reduce
 #pragma unroll
-  for (int bm = 0; bm < 4; ++bm) {
+  for (int bm = 0; bm < BMB; ++bm) {
 #pragma unroll
     for (int bn = 0; bn < kNB; ++bn)
 #pragma unroll
@@ -482,6 +482,78 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
   }
 
   lm_epilogue<WN>(acc, smem, p, wid, lane, m0, v0, M);
+}
+
+// ---- LM head for at most 32 rows over the tiled weight ---------------------------
+// With so few rows the MFMAs are cheap and the stage streams the weight: its
+// speed is the weight bytes in flight.  One wave per workgroup owns a
+// 32-row x 64-column tile (the 128-row tiles would multiply mostly padding,
+// and four waves per workgroup would halve the workgroups); both operands
+// come straight from memory into a 16-deep register ring (hidden-row
+// fragments are 16 bytes per lane, L2-resident), so every wait is for loads
+// issued fifteen sub-steps earlier.  Two waves fit per SIMD.
+constexpr int kSmallRing = 16;
+
+__global__ __launch_bounds__(64) void k_lm_gemm_small(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int kNB = 2, kRows = 32, kCols = 64;
+  constexpr int kRing = kSmallRing, kDist = kSmallRing - 1;
+  const int n_tiles = p.n_mt * p.n_vt;
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int kloc = blockIdx.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + kloc;
+  if (kloc >= per_xcd || logical >= n_tiles) return;
+  const int vt = logical / p.n_mt;
+  const int mt = logical % p.n_mt;
+  const int M = p.mm[0];
+  const int m0 = mt * kRows;
+  if (m0 >= M) return;
+  const int v0 = vt * kCols;
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, lh = lane >> 5;
+  const int nsub = p.H / 16;   // a multiple of kRing (H % 256 == 0)
+
+  // hidden rows: lane l reads row m0 + l%32 (rows past M: the last real
+  // row), 8 bf16 at K = 16*s + 8*(l/32) for sub-step s
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(p.x) + (size_t)m0 * p.H, 0, kRows * p.H * 2, kBufFlags);
+  const uint32_t aoff = (uint32_t)(min(l32, M - 1 - m0) * p.H * 2 + lh * 16);
+  // weights: the tile's two column blocks, ending at the tiled weight's end
+  const size_t wbase = (size_t)(v0 / 32) * nsub * 1024;
+  const size_t wspan = (size_t)kNB * nsub * 1024;
+  const size_t wleft = p.w_bytes > wbase ? p.w_bytes - wbase : 0;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<unsigned char*>(const_cast<bf16_t*>(p.w)) + (wleft ? wbase : 0), 0,
+      (int)(wleft < wspan ? wleft : wspan), kBufFlags);
+  const uint32_t woff0 = (uint32_t)(lane * 16), woff1 = (uint32_t)(nsub * 1024 + lane * 16);
+
+  u32x4_t ra[kRing], rb[kRing][kNB];
+  auto load = [&](int slot, int sub) {
+    ra[slot] = __builtin_amdgcn_raw_buffer_load_b128(xr, aoff, sub * 32, 0);
+    rb[slot][0] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff0, sub * 1024, 0);
+    rb[slot][1] = __builtin_amdgcn_raw_buffer_load_b128(wr, woff1, sub * 1024, 0);
+  };
+  f32x16_t acc[1][kNB];
+#pragma unroll
+  for (int b = 0; b < kNB; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[0][b][j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kDist; ++j) {
+    load(j, j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int s0 = 0; s0 < nsub; s0 += kRing) {
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) {
+      load((j + kDist) % kRing, min(s0 + j + kDist, nsub - 1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int bn = 0; bn < kNB; ++bn) acc[0][bn] = mfma32(ra[j], rb[j][bn], acc[0][bn]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  lm_epilogue<kCols, 1>(acc, smem, p, 0, lane, m0, v0, M);
 }
 
 // W [V][H] -> tiled copy: one thread per (fragment, lane), 16 bytes each
@@ -878,8 +950,21 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
       hipLaunchKernelGGL(kern, dim3(grid), dim3(kGemmThreads), lds_bytes, s, g);
       return hipSuccess;
     };
-    e = narrow ? launch(k_lm_gemm_tiled<64>, TiledCfg<64>::kBN, TiledCfg<64>::kLds)
-               : launch(k_lm_gemm_tiled<128>, TiledCfg<128>::kBN, TiledCfg<128>::kLds);
+    if (a.B * a.gamma <= 32 && a.H % 256 == 0) {
+      // one row tile's worth of rows: one-wave 32 x 64 tiles streaming the
+      // weight (batch 1 of the GQA shapes, 8 rows x 4096 x 32000: 77 -> 60 us
+      // with accept; with two row tiles the weight is streamed twice and
+      // the 128 x 256 tiles win)
+      g.n_mt = 1;
+      g.n_vt = (a.V + 63) / 64;
+      const int grid = ((g.n_mt * g.n_vt + 7) / 8) * 8;
+      constexpr int kSmallLds = 32 * (64 + 4) * 4;   // the epilogue's transpose
+      hipLaunchKernelGGL(k_lm_gemm_small, dim3(grid), dim3(64), kSmallLds, s, g);
+      e = hipSuccess;
+    } else {
+      e = narrow ? launch(k_lm_gemm_tiled<64>, TiledCfg<64>::kBN, TiledCfg<64>::kLds)
+                 : launch(k_lm_gemm_tiled<128>, TiledCfg<128>::kBN, TiledCfg<128>::kLds);
+    }
     if (e != hipSuccess) return e;
   } else if (a.dtype == RV_BF16) {
     GemmParams g;

@@ -151,6 +151,15 @@ def test_lm_row_major_weight():
     _full_parity(inp, "static", "bf16", w_layout="rows")
 
 
+@pytest.mark.parametrize("B", [1, 4])
+def test_lm_few_rows_odd_vocab(B):
+    """At most 32 packed rows take the one-wave weight-streaming kernel; with
+    V = 4229 its last tile's second column block lies past the tiled
+    weight's end (read as zeros, masked)."""
+    inp = pu.make_inputs("mla_bf16", B=B, V=4229, H=256, ctx=("uniform", 60, 300))
+    _full_parity(inp, "static", "bf16")
+
+
 def test_tiled_weight_layout():
     """rv_lm_tile_weight against the layout written out with torch view
     operations: lane l of fragment f of block cb holds
