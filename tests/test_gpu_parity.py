@@ -235,6 +235,21 @@ def test_edge_cases():
     assert np.all(pu.npi(step.w_verify) == 1)
 
 
+def test_maximum_sizes():
+    """The scheduler's limit (4095 of at most 4096 candidates: 273 requests
+    of block width 16) in compact mode, the row limit (8192 rows: 512 x 16) in
+    static mode, and one candidate past the limit, which the host rejects."""
+    from ragged_verification_amd import rv
+    small = dict(Hq=8, Hkv=2, V=600, H=128, ctx=("uniform", 0, 40), tiers=(), gamma=16)
+    inp = pu.make_inputs("gqa_bf16", B=273, **small)
+    _full_parity(inp, "compact", "bf16")
+    inp = pu.make_inputs("gqa_bf16", B=512, **small)
+    _full_parity(inp, "static", "bf16")
+    inp = pu.make_inputs("gqa_bf16", B=274, **small)     # 274 * 15 = 4110 candidates
+    with pytest.raises(rv.RVError):
+        pu.run_gpu(inp, "compact")
+
+
 def test_device_status_errors():
     """Bad data found on the device raises the sticky status and keeps every
     access in bounds."""
