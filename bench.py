@@ -109,22 +109,24 @@ def run_steps(step, n, timer=None):
             timer.collect()
 
 
-def attn_flops(ctx, w, Hq, Dqk, Dv):
+def attn_flops(ctx, w, Hq, Dqk, Dv, window=0):
     """Algorithmic attention flops of one launch: every real row r of request
-    i at position ctx_i + k sees ctx_i + k + 1 keys, each costing a Dqk-wide
-    dot product and a Dv-wide accumulation per query head."""
+    i at position ctx_i + k sees ctx_i + k + 1 keys (at most `window` with a
+    sliding window), each costing a Dqk-wide dot product and a Dv-wide
+    accumulation per query head."""
     tot = 0
     for c, wi in zip(ctx, w):
-        keys = sum(c + k + 1 for k in range(wi))
+        keys = sum(min(c + k + 1, window) if window else c + k + 1 for k in range(wi))
         tot += 2 * Hq * (Dqk + Dv) * keys
     return tot
 
 
-def attn_bytes(ctx, w, wl, elem=2):
-    """Algorithmic attention bytes: each request's visible KV once plus the
-    packed queries and outputs."""
+def attn_bytes(ctx, w, wl, elem=2, window=0):
+    """Algorithmic attention bytes: each request's visible KV once (keys
+    max(0, ctx_i - window + 1) .. ctx_i + w_i - 1 with a sliding window) plus
+    the packed queries and outputs."""
     kv_row = wl.Hkv * (wl.Dqk + (0 if wl.latent else wl.Dv)) * elem
-    kv = sum((c + wi) * kv_row for c, wi in zip(ctx, w))
+    kv = sum((c + wi - (max(0, c - window + 1) if window else 0)) * kv_row for c, wi in zip(ctx, w))
     M = sum(w)
     return kv + M * wl.Hq * (wl.Dqk + wl.Dv) * elem
 
@@ -379,6 +381,8 @@ def main():
     ap.add_argument("--workload", default="mla_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding-window attention of this many keys (0: full causal)")
     ap.add_argument("--graph", action="store_true",
                     help="also time each mode replayed from HIP graphs (VerifyStep.capture)")
     ap.add_argument("--fit-cost", action="store_true",
@@ -414,12 +418,12 @@ def main():
 
     results = {}
     for mode in ["compact"] + ([] if args.no_static else ["static"]):
-        step = VerifyStep(inp, mode=mode)
+        step = VerifyStep(inp, mode=mode, window=args.window)
         r = measure(step, args.steps, args.warmup)
         w = step.w_verify.cpu().numpy().astype(np.int64)
         ctx = inp["ctx"].cpu().numpy().astype(np.int64)
-        r["attn_flops"] = attn_flops(ctx, w, wl.Hq, wl.Dqk, wl.Dv)
-        r["attn_bytes"] = attn_bytes(ctx, w, wl)
+        r["attn_flops"] = attn_flops(ctx, w, wl.Hq, wl.Dqk, wl.Dv, args.window)
+        r["attn_bytes"] = attn_bytes(ctx, w, wl, window=args.window)
         r["lm_flops"] = lm_flops(r["M"], wl.H, wl.V)
         if args.graph:
             r["graph"] = measure_graph(step, args.steps, args.warmup)
@@ -441,7 +445,7 @@ def main():
     if wl.latent:
         dom, achieved = "verify_attn (latent, bf16 MFMA)", c["attn_flops"] / (attn_ms / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None if args.window else measured_traffic(),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_per_launch": c["attn_flops"], "algorithmic_bytes_per_launch": c["attn_bytes"],
                 "launch_ms": attn_ms}
@@ -449,7 +453,7 @@ def main():
         achieved = c["attn_bytes"] / (attn_ms / 1e3) / 1e9
         roof = {"kernel": "verify_attn (GQA, bf16)", "bound": "hbm", "achieved": achieved,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "traffic": measured_traffic(COUNTERS_GQA_MD, f"k_attn_gqa, {wl.name}"),
+                "traffic": None if args.window else measured_traffic(COUNTERS_GQA_MD, f"k_attn_gqa, {wl.name}"),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_per_launch": c["attn_bytes"], "launch_ms": attn_ms}
     lm_tflops = c["lm_flops"] / (lm_ms / 1e3) / 1e12
@@ -469,7 +473,7 @@ def main():
         "config": {"workload": f"{wl.name}: B={wl.B}, gamma={wl.gamma}, Hq={wl.Hq}, Hkv={wl.Hkv}, "
                                f"Dqk={wl.Dqk}, Dv={wl.Dv}, page={wl.page_size}, ctx={wl.ctx}, H={wl.H}, "
                                f"V={wl.V}, {wl.rule}, tiers={wl.tiers}",
-                   "mode": "compact", "B": wl.B, "gamma": wl.gamma},
+                   "mode": "compact", "B": wl.B, "gamma": wl.gamma, "window": args.window},
         "accepted_tok_s": c["committed"] / t_s,
         "packed_rows": c["M"], "tier_rows": c["M_pad"], "committed_per_step": c["committed"],
         "stages_ms": {k: round(v, 4) for k, v in c["per_stage_ms"].items()},

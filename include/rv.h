@@ -209,7 +209,8 @@ rv_status rv_pack(const rv_pack_args* a, void* stream);
  *
  * For every real row r (request i, row k, position p = ctx[i]+k) and query
  * head h (KV head g = h / (Hq/Hkv)): o[r,h] = softmax_j(sm_scale * q[r,h] .
- * K[i,j,g]) V[i,j,g] over keys j = 0..p read through the page table;
+ * K[i,j,g]) V[i,j,g] over keys j = 0..p read through the page table (with
+ * window W > 0, the sliding-window layers' attention: keys j = max(0,p-W+1)..p);
  * lse[r,h] = natural log of the softmax normaliser.  Latent layout
  * (v_cache == NULL, Hkv == 1): V[i,j] = first Dv entries of K[i,j].  Rows
  * [M, M_pad) get o = 0, lse = -inf; rows >= M_pad are not written.
@@ -230,6 +231,8 @@ typedef struct {
   int32_t rows_cap, max_pages, page_size, num_pages;
   int32_t Hq, Hkv, Dqk, Dv, dtype;
   float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(Dqk)) */
+  int32_t window;            /* sliding window in keys; 0 = full causal */
+  int32_t _pad1;
   void* o;                   /* out [rows_cap][Hq][Dv], dtype */
   float* lse;                /* out [rows_cap][Hq] or NULL */
   void* workspace;

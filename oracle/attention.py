@@ -20,6 +20,10 @@ Readings taken where the pages are silent:
   the value is the first ``Dv`` entries of that same row (``v_cache is None``).
 * ``sm_scale`` multiplies the raw dot products (callers pass ``1/sqrt(Dqk)``).
 * Padding rows (``row_req < 0``) produce zeros; their ``lse`` is ``-inf``.
+* Sliding-window layers (the pages name SWA page indexing among the fused
+  kernels but do not define it): with a window of ``W`` keys the row at
+  position ``p`` attends to keys ``max(0, p-W+1)..p``; ``W = 0`` is full
+  causal attention.
 
 Arithmetic: fp64 throughout; ``lse`` is the natural log of the softmax
 normaliser of the scaled scores.
@@ -54,14 +58,14 @@ def attention_row(q_row, keys, values, sm_scale):
     return o, lse
 
 
-def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv):
-    """Keys/values of positions ``0..length-1`` read through the page table.
+def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv, start=0):
+    """Keys/values of positions ``start..length-1`` read through the page table.
 
     ``k_cache`` [num_pages, P, Hkv, Dqk]; ``v_cache`` same with ``Dv`` or None
     (latent layout: value = first ``Dv`` entries of the key row).
     """
     P = int(page_size)
-    pos = np.arange(length)
+    pos = np.arange(start, length)
     pages = np.asarray(page_table_row)[pos // P]
     if np.any(pages < 0) or np.any(pages >= k_cache.shape[0]):
         raise IndexError("page index out of range")
@@ -74,8 +78,9 @@ def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv):
 
 
 def verify_attention(q, k_cache, v_cache, page_table, page_size, row_req,
-                     row_pos, M_pad, sm_scale, Dv=None, rows=None):
-    """Attention for packed rows.
+                     row_pos, M_pad, sm_scale, Dv=None, rows=None, window=0):
+    """Attention for packed rows (``window`` > 0: sliding window of that many
+    keys).
 
     ``q`` [>=M_pad, Hq, Dqk] (packed order).  Returns ``(o, lse)`` shaped
     ``[M_pad, Hq, Dv]`` and ``[M_pad, Hq]``; if ``rows`` is given only those
@@ -93,7 +98,8 @@ def verify_attention(q, k_cache, v_cache, page_table, page_size, row_req,
         if i < 0:
             continue
         p = int(row_pos[r])
+        start = max(0, p - int(window) + 1) if window else 0
         keys, values = gather_kv(k_cache, v_cache, page_table[i], page_size,
-                                 p + 1, Dv)
+                                 p + 1, Dv, start=start)
         o[r], lse[r] = attention_row(q[r], keys, values, sm_scale)
     return o, lse

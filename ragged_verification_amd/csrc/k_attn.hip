@@ -73,10 +73,19 @@ struct PlanParams {
   int32_t* hdr;
   int B, gamma, item_cap, part_cap, target;
   int n_workers;         // balanced plan: persistent workgroups of the main kernel
+  int window;            // sliding window (keys), 0 = full causal
   AttnShape sh;
 };
 
 __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Sliding window of W keys (W > 0): the row at position p sees keys
+// [p - W + 1, p].  A request's key range then starts at its first row's
+// bound, aligned down to 64 keys so that tiles and super-tiles stay aligned
+// (page-uniform DMA); keys below a row's bound are masked.  W = 0: full causal.
+__device__ inline int win_origin(int ctx, int W) { return W > 0 ? (max(0, ctx - W + 1) & ~63) : 0; }
+// lowest visible key of the row at position pos (INT_MIN without a window)
+__device__ inline int win_low(int pos, int W) { return W > 0 ? pos - W + 1 : INT32_MIN; }
 
 // ---- plan: device-side varlen metadata -------------------------------------
 //
@@ -106,7 +115,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   long long work = 0;
   for (int i = i0; i < i1; ++i) {
     const int w = p.cu[i + 1] - p.cu[i];
-    const int L = p.ctx[i] + w;
+    const int L = p.ctx[i] + w - win_origin(p.ctx[i], p.window);   // keys from the origin
     s_wl[i] = make_int2(w, L);
     work += (long long)tiles_of_w(w) * L;
   }
@@ -264,7 +273,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
   // super-tiles of one tile of row block rb
   auto nst = [&](int w, int c, int rb) {
     const int L_tile = c + min((rb + 1) * sh.RT, w);
-    return ceil_div(L_tile, kBalSuper);
+    return ceil_div(L_tile - win_origin(c, p.window), kBalSuper);
   };
 
   int cnt[2] = {0, 0}, off[2], tot[2];   // tiles, super-tiles
@@ -349,6 +358,7 @@ struct MainParams {
   int32_t* status;
   int max_pages, page_size, num_pages, Hq, Hkv, G, NH, RT, n_hb, part_cap;
   int log2P;              // log2(page_size) when it is a power of two, else -1
+  int window;             // sliding window (keys), 0 = full causal
   float scale_log2;       // sm_scale * log2(e)
 };
 
@@ -501,7 +511,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   const int rows_here = min(p.RT, w - row0);
   const int L_tile = c + row0 + rows_here;
   const int chunk = p.hdr[1];
-  const int kv_begin = sp * chunk;
+  const int kv_begin = win_origin(c, p.window) + sp * chunk;
   const int kv_end = min(kv_begin + chunk, L_tile);
   const int P = p.page_size;
 
@@ -520,7 +530,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   }
 
   // query fragments: both 16-vector blocks of the pair, all 576 dims
-  int q_row[2], head[2], lim[2];
+  int q_row[2], head[2], lim[2], low[2];
   bool q_valid[2];
   u32x4_t qf[2][18];
 #pragma unroll
@@ -531,12 +541,16 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     q_valid[qb] = rl < rows_here;
     q_row[qb] = row_start + row0 + (q_valid[qb] ? rl : 0);
     lim[qb] = min(c + row0 + rl, kv_end - 1);   // last key this vector may see here
+    low[qb] = win_low(c + row0 + rl, p.window);  // first key it may see
     const bf16_t* qsrc = p.q + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
   }
-  // tiles ending at or before this key need no mask for any valid vector
+  // tiles ending at or before this key need no mask for any valid vector;
+  // with a window, neither do tiles starting at or after every row's bound
   const int full_lim = min(c + row0, kv_end - 1);
+  const int low_max = win_low(c + row0 + rows_here - 1, p.window);
+  auto is_full = [&](int t0) { return t0 + kNK - 1 <= full_lim && t0 >= low_max; };
   wait_vm<0>();
   __syncthreads();   // page window visible
 
@@ -681,10 +695,10 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] = sc[j] * p.scale_log2;
-      if (!full) {   // tail tile: keys past this vector's limit get probability 0
+      if (!full) {   // edge tile: keys outside this vector's [low, lim] get probability 0
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (t0 + key_lane + j > lim[qb]) v[j] = -INFINITY;
+          if (t0 + key_lane + j > lim[qb] || t0 + key_lane + j < low[qb]) v[j] = -INFINITY;
       }
       m_seen[qb] = fmaxf(m_seen[qb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
       float e[4];
@@ -716,7 +730,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) m_ref[qb] = fmaxf(mx[qb], red_m[((wid ^ 1) * 2 + qb) * 16 + n16]);
       }
-      const bool full0 = (kv_begin + kNK - 1 <= full_lim);
+      const bool full0 = is_full(kv_begin);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         uint32_t po[2];
@@ -755,7 +769,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       const uint32_t stg_next = smem_lds + st_cur * kMlaStageBytes;
       const bool more = t + 1 < n_tiles;   // uniform
       const int t0n = kv_begin + (t + 1) * kNK;
-      const bool full_n = (t0n + kNK - 1 <= full_lim);
+      const bool full_n = is_full(t0n);
 
       f32x4_t sc[2];
       auto spread_dma = [&](int ks) {
@@ -989,8 +1003,11 @@ __device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int t
   const bool q_valid = q_row_local < rows_here;
   const int q_row = row_start + row0 + q_row_local;
   const int limit = c + row0 + q_row_local;   // last visible key position
-  // sub-tiles ending at or before this key need no mask for any real row
+  const int low = win_low(limit, p.window);   // first visible key position
+  // sub-tiles ending at or before this key need no mask for any real row;
+  // with a window, neither do sub-tiles starting at or after every row's bound
   const int full_lim = min(c + row0, kv_end - 1);
+  const int low_max = win_low(c + row0 + rows_here - 1, p.window);
   u32x4_t qf[kGqaD / 32];
 #pragma unroll
   for (int ks = 0; ks < kGqaD / 32; ++ks) {
@@ -1130,7 +1147,7 @@ __device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int t
 #pragma unroll
       for (int mb = 0; mb < kNK / 16; ++mb) sacc[mb] = mfma16(kf[mb][ks], qf[ks], sacc[mb]);
     float tmax = -INFINITY;
-    const bool full = (t0 + kNK - 1 <= full_lim);   // uniform: no key past any real row's limit
+    const bool full = (t0 + kNK - 1 <= full_lim) && t0 >= low_max;   // uniform: no key outside any real row's range
 #pragma unroll
     for (int mb = 0; mb < kNK / 16; ++mb) {
 #pragma unroll
@@ -1138,7 +1155,7 @@ __device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int t
         float s = sacc[mb][j] * p.scale_log2;
         if (!full) {
           const int kpos = t0 + mb * 16 + grp * 4 + j;
-          if (kpos >= kv_end || kpos > limit) s = -INFINITY;
+          if (kpos >= kv_end || kpos > limit || kpos < low) s = -INFINITY;
         }
         sacc[mb][j] = s;
         tmax = fmaxf(tmax, s);
@@ -1248,7 +1265,7 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const int i = rec.x, tile = rec.y, sp = rec.z;
   const int4 info = p.req_info[i];
   const int chunk = p.hdr[1];
-  const int kv_lo = sp * chunk;
+  const int kv_lo = win_origin(p.ctx[i], p.window) + sp * chunk;
   const int kv_hi = (int)min((long long)kv_lo + chunk, (long long)INT32_MAX);
   const int slot = info.x == 1 ? -1 : (info.z < 0 ? INT32_MAX : info.z + sp * info.w + tile);
   attn_gqa_range<NV, FAST>(p, i, tile, kv_lo, kv_hi, slot, smem);
@@ -1279,7 +1296,8 @@ __global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa_bal(MainPa
       const int tile = T - p.req_info[i].y;
       const int slot = ti.z < 0 ? -1 : ti.z + (vw - ti.x / q);
       __syncthreads();   // the previous range's merge and stores are done with the LDS
-      attn_gqa_range<NV, FAST>(p, i, tile, s0 * kSuper, s1 * kSuper, slot, smem);
+      const int org = win_origin(p.ctx[i], p.window);
+      attn_gqa_range<NV, FAST>(p, i, tile, org + s0 * kSuper, org + s1 * kSuper, slot, smem);
     }
   }
 }
@@ -1471,6 +1489,7 @@ struct F32Params {
   float* lse;
   int32_t* status;
   int B, max_pages, page_size, num_pages, Hq, Hkv, D, Dv;
+  int window;             // sliding window (keys), 0 = full causal
   float sm_scale;
 };
 
@@ -1492,7 +1511,8 @@ __global__ __launch_bounds__(128) void k_attn_f32(F32Params p) {
   const float* qv = p.q + ((size_t)row * p.Hq + h) * p.D;
   const int P = p.page_size;
   float m = -INFINITY, l = 0.f, acc = 0.f;   // thread tid owns output dim tid
-  for (int j0 = 0; j0 <= pos; j0 += 128) {
+  const int j_lo = max(0, win_low(pos, p.window));
+  for (int j0 = j_lo; j0 <= pos; j0 += 128) {
     const int j = j0 + tid;
     float s = -INFINITY;
     if (j <= pos) {
@@ -1710,6 +1730,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     f.Hkv = a.Hkv;
     f.D = a.Dqk;
     f.Dv = a.Dv;
+    f.window = a.window;
     f.sm_scale = a.sm_scale;
     hipLaunchKernelGGL(k_attn_f32, dim3(a.rows_cap, a.Hq), dim3(128), 0, s, f);
     return hipGetLastError();
@@ -1752,6 +1773,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.part_cap = L.part_slots;
   pp.target = sh.target;
   pp.n_workers = bal_grid;
+  pp.window = a.window;
   pp.sh = sh;
   if (bal) hipLaunchKernelGGL(k_attn_plan_bal, dim3(1), dim3(kPlanThreads), 0, s, pp);
   else hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, pp);
@@ -1789,6 +1811,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     mp.log2P = l2;
   }
   mp.scale_log2 = a.sm_scale * kLog2e;
+  mp.window = a.window;
   mp.ctr = pp.hdr + kHdrCtr;
 
   if (latent) {

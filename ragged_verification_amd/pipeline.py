@@ -20,7 +20,7 @@ from . import rv
 
 class VerifyStep:
     def __init__(self, inp, mode="compact", with_logits=False, rows_cap=None, r2t_extra=64,
-                 hist_cap=64, stream=None, w_layout="tiled"):
+                 hist_cap=64, stream=None, w_layout="tiled", window=0):
         wl = inp["workload"]
         self.inp, self.wl = inp, wl
         self.mode = mode
@@ -85,6 +85,7 @@ class VerifyStep:
         self.q_flat = inp["q_block"].reshape(B * gamma, wl.Hq, wl.Dqk)
         self.h_flat = inp["hidden_block"].reshape(B * gamma, wl.H)
         self.stream = stream
+        self.window = window   # sliding-window attention (keys), 0 = full causal
         # LM-head weight in MFMA fragment order, made once per weight (a
         # serving system does this when it loads the model); bf16 with
         # H % 128 == 0 only, otherwise the row-major weight is read
@@ -120,7 +121,7 @@ class VerifyStep:
         i = self.inp
         rv.rv_verify_attn(self.q, i["k_cache"], i["v_cache"], i["page_table"], i["page_size"], i["num_pages"],
                           self.ctx, self.cu, self.mm, self.gamma, i["sm_scale"], self.o, self.lse,
-                          self.workspace, self.stream)
+                          self.workspace, self.stream, window=self.window)
 
     def lm(self):
         i = self.inp

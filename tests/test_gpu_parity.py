@@ -20,7 +20,7 @@ from ragged_verification_amd.pipeline import VerifyStep
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_full(inp, ref, mode):
+def _oracle_full(inp, ref, mode, window=0):
     """Oracle stages 3-5 on every real row (small cases only)."""
     wl = inp["workload"]
     gamma = inp["gamma"]
@@ -29,7 +29,7 @@ def _oracle_full(inp, ref, mode):
     q = pu.np64(inp["q_block"].reshape(-1, wl.Hq, wl.Dqk))[bidx]
     o, lse = oracle.verify_attention(q, pu.np64(inp["k_cache"]), pu.np64(inp["v_cache"]),
                                      pu.npi(inp["page_table"]), inp["page_size"], ref["row_req"],
-                                     ref["row_pos"], ref["M_pad"], inp["sm_scale"], Dv=wl.Dv)
+                                     ref["row_pos"], ref["M_pad"], inp["sm_scale"], Dv=wl.Dv, window=window)
     x = pu.np64(inp["hidden_block"].reshape(-1, wl.H))[bidx]
     z = oracle.lm_head_logits(x, pu.np64(inp["W"]))
     pred = oracle.lm_head_pred(z)
@@ -75,13 +75,13 @@ def _check_scatter(step, sc, B):
     assert np.array_equal(pu.npi(step.hist_len), sc["hist_len"])
 
 
-def _full_parity(inp, mode, dtype, w_layout="tiled"):
-    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode} weight={w_layout}")
+def _full_parity(inp, mode, dtype, w_layout="tiled", window=0):
+    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode} weight={w_layout} window={window}")
     ref = pu.oracle_schedule_pack(inp, mode)
-    step = pu.run_gpu(inp, mode, with_logits=True, w_layout=w_layout)
+    step = pu.run_gpu(inp, mode, with_logits=True, w_layout=w_layout, window=window)
     assert step.status() == 0
     pu.check_schedule_pack(step, ref)
-    want = _oracle_full(inp, ref, mode)
+    want = _oracle_full(inp, ref, mode, window=window)
     M, M_pad = ref["M"], ref["M_pad"]
     o = step.o.float().cpu().numpy()
     err = np.max(np.abs(o[:M] - want["o"][:M]))
@@ -149,6 +149,40 @@ def test_lm_row_major_weight():
     _full_parity(inp, "compact", "bf16", w_layout="rows")
     inp = pu.make_inputs("mla_bf16", B=3, V=1000, H=512, ctx=("uniform", 60, 700))
     _full_parity(inp, "static", "bf16", w_layout="rows")
+
+
+@pytest.mark.parametrize("window", [1, 37, 200])
+def test_sliding_window_latent(window):
+    """Sliding-window attention on the latent kernel: windows inside the
+    first tile of a chunk, across chunks, and one key (W = 1)."""
+    inp = pu.make_inputs("mla_bf16", B=3, V=1000, H=512, ctx=("uniform", 60, 700))
+    _full_parity(inp, "compact", "bf16", window=window)
+
+
+@pytest.mark.parametrize("window", [1, 64, 100])
+def test_sliding_window_gqa(window):
+    """GQA balanced schedule with a sliding window (64: super-tile aligned)."""
+    inp = pu.make_inputs("gqa_bf16", B=6, V=1000, H=256, ctx=("uniform", 40, 900))
+    _full_parity(inp, "static", "bf16", window=window)
+
+
+def test_sliding_window_split_and_chunked():
+    """A window on long split requests (partials of ranges that lie wholly
+    below some rows' windows merge as empty), on the chunked GQA plan, on
+    pages that are not a power of two (per-row DMA addressing) and on the
+    fp32 kernel."""
+    inp = pu.make_inputs("gqa_bf16", B=2, Hq=64, V=700, H=128, ctx=("uniform", 2500, 3000))
+    _full_parity(inp, "compact", "bf16", window=700)
+    inp = pu.make_inputs("gqa_bf16", B=130, Hq=64, Hkv=64, V=200, H=64, tiers=(1024,), ctx=("uniform", 0, 60))
+    _full_parity(inp, "compact", "bf16", window=17)
+    inp = pu.make_inputs("mla_bf16", B=2, Hq=64, V=500, H=256, ctx=("uniform", 3000, 5000))
+    _full_parity(inp, "compact", "bf16", window=1500)
+    inp = pu.make_inputs("mla_bf16", B=3, V=500, H=256, page_size=48, ctx=("uniform", 100, 600))
+    _full_parity(inp, "static", "bf16", window=130)
+    inp = pu.make_inputs("gqa_bf16", B=4, V=500, H=256, page_size=12, ctx=("uniform", 100, 600))
+    _full_parity(inp, "static", "bf16", window=77)
+    inp = pu.make_inputs("tiny_f32")
+    _full_parity(inp, "static", "f32", window=3)
 
 
 @pytest.mark.parametrize("B", [1, 4])

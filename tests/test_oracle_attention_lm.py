@@ -67,6 +67,47 @@ def test_attention_matches_torch_sdpa(latent):
         np.testing.assert_allclose(lse[r], torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12)
 
 
+@pytest.mark.parametrize("latent", [False, True])
+@pytest.mark.parametrize("window", [1, 2, 5])
+def test_sliding_window_matches_sdpa_with_band_mask(latent, window):
+    """Sliding window of W keys against torch's scaled_dot_product_attention
+    over every position 0..p of the request with an explicit boolean band
+    mask (keys p-W+1..p visible)."""
+    c = _paged_case(4, Hq=6, Hkv=1 if latent else 3, D=10, Dv=7 if latent else None, latent=latent)
+    scale = 0.41
+    o, lse = verify_attention(c["q"], c["k"], c["v"], c["pt"], c["P"], c["row_req"],
+                              c["row_pos"], c["M"], scale, Dv=c["Dv"], window=window)
+    group = c["Hq"] // c["Hkv"]
+    kflat = c["k"].reshape(-1, c["Hkv"], c["D"])
+    for r in range(c["M"]):
+        i, p = int(c["row_req"][r]), int(c["row_pos"][r])
+        slots = [int(c["pt"][i][pos // c["P"]]) * c["P"] + pos % c["P"] for pos in range(p + 1)]
+        K = torch.tensor(kflat[slots])
+        Vv = K[:, :, :c["Dv"]] if latent else torch.tensor(c["v"].reshape(-1, c["Hkv"], c["Dv"])[slots])
+        Kh = K.repeat_interleave(group, dim=1).permute(1, 0, 2)[None]
+        Vh = Vv.repeat_interleave(group, dim=1).permute(1, 0, 2)[None]
+        qh = torch.tensor(c["q"][r])[None, :, None, :]
+        band = torch.tensor([pos >= p - window + 1 for pos in range(p + 1)])[None, None, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(qh, Kh, Vh, attn_mask=band, scale=scale)
+        np.testing.assert_allclose(o[r], ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_sliding_window_special_cases():
+    """W = 1: the row's own value exactly; W past the row's position: the
+    full causal result."""
+    c = _paged_case(5, Hq=4, Hkv=2, D=8)
+    args = (c["q"], c["k"], c["v"], c["pt"], c["P"], c["row_req"], c["row_pos"], c["M"], 0.3)
+    o1, lse1 = verify_attention(*args, window=1)
+    vflat = c["v"].reshape(-1, c["Hkv"], c["Dv"])
+    for r in range(c["M"]):
+        i, p = int(c["row_req"][r]), int(c["row_pos"][r])
+        slot = int(c["pt"][i][p // c["P"]]) * c["P"] + p % c["P"]
+        assert np.array_equal(o1[r], np.repeat(vflat[slot], c["Hq"] // c["Hkv"], axis=0))
+    o_full, _ = verify_attention(*args)
+    o_big, _ = verify_attention(*args, window=10_000)
+    assert np.array_equal(o_full, o_big)
+
+
 def test_attention_special_cases():
     rng = np.random.default_rng(2)
     q = rng.standard_normal((4, 16))
