@@ -381,6 +381,8 @@ def main():
     ap.add_argument("--workload", default="mla_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="latent workloads: sparse attention over per-row key lists of this many entries")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding-window attention of this many keys (0: full causal)")
     ap.add_argument("--graph", action="store_true",
@@ -418,12 +420,18 @@ def main():
 
     results = {}
     for mode in ["compact"] + ([] if args.no_static else ["static"]):
-        step = VerifyStep(inp, mode=mode, window=args.window)
+        step = VerifyStep(inp, mode=mode, window=args.window, topk=args.topk)
         r = measure(step, args.steps, args.warmup)
         w = step.w_verify.cpu().numpy().astype(np.int64)
         ctx = inp["ctx"].cpu().numpy().astype(np.int64)
-        r["attn_flops"] = attn_flops(ctx, w, wl.Hq, wl.Dqk, wl.Dv, args.window)
-        r["attn_bytes"] = attn_bytes(ctx, w, wl, window=args.window)
+        if args.topk:
+            # each row reads its own listed keys: min(topk, p + 1) per row
+            keys = sum(min(args.topk, c + k + 1) for c, wi in zip(ctx, w) for k in range(wi))
+            r["attn_flops"] = 2 * wl.Hq * (wl.Dqk + wl.Dv) * keys
+            r["attn_bytes"] = keys * wl.Dqk * 2 + int(w.sum()) * wl.Hq * (wl.Dqk + wl.Dv) * 2
+        else:
+            r["attn_flops"] = attn_flops(ctx, w, wl.Hq, wl.Dqk, wl.Dv, args.window)
+            r["attn_bytes"] = attn_bytes(ctx, w, wl, window=args.window)
         r["lm_flops"] = lm_flops(r["M"], wl.H, wl.V)
         if args.graph:
             r["graph"] = measure_graph(step, args.steps, args.warmup)
@@ -445,7 +453,7 @@ def main():
     if wl.latent:
         dom, achieved = "verify_attn (latent, bf16 MFMA)", c["attn_flops"] / (attn_ms / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None if args.window else measured_traffic(),
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None if (args.window or args.topk) else measured_traffic(),
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_per_launch": c["attn_flops"], "algorithmic_bytes_per_launch": c["attn_bytes"],
                 "launch_ms": attn_ms}
@@ -473,7 +481,8 @@ def main():
         "config": {"workload": f"{wl.name}: B={wl.B}, gamma={wl.gamma}, Hq={wl.Hq}, Hkv={wl.Hkv}, "
                                f"Dqk={wl.Dqk}, Dv={wl.Dv}, page={wl.page_size}, ctx={wl.ctx}, H={wl.H}, "
                                f"V={wl.V}, {wl.rule}, tiers={wl.tiers}",
-                   "mode": "compact", "B": wl.B, "gamma": wl.gamma, "window": args.window},
+                   "mode": "compact", "B": wl.B, "gamma": wl.gamma, "window": args.window,
+                   "topk": args.topk},
         "accepted_tok_s": c["committed"] / t_s,
         "packed_rows": c["M"], "tier_rows": c["M_pad"], "committed_per_step": c["committed"],
         "stages_ms": {k: round(v, 4) for k, v in c["per_stage_ms"].items()},

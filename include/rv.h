@@ -97,6 +97,7 @@ typedef int32_t rv_status;
 #define RV_MAX_TIERS 16
 #define RV_MAX_SCHED_CANDIDATES 4096   /* B * (gamma - 1), compact/cap-accept */
 #define RV_MAX_ROWS 8192               /* B * gamma */
+#define RV_MAX_TOPK 2048               /* sparse latent attention: index entries per row */
 
 /* ---- sizing ------------------------------------------------------------- */
 /* Upper bounds of the problem a workspace must serve.  Any field may be 0 when
@@ -210,7 +211,12 @@ rv_status rv_pack(const rv_pack_args* a, void* stream);
  * For every real row r (request i, row k, position p = ctx[i]+k) and query
  * head h (KV head g = h / (Hq/Hkv)): o[r,h] = softmax_j(sm_scale * q[r,h] .
  * K[i,j,g]) V[i,j,g] over keys j = 0..p read through the page table (with
- * window W > 0, the sliding-window layers' attention: keys j = max(0,p-W+1)..p);
+ * window W > 0, the sliding-window layers' attention: keys j = max(0,p-W+1)..p;
+ * with topk_idx, sparse latent attention as on the DeepSeek-V4 path (the
+ * page names its sparse-MLA kernel): the keys are the positions
+ * topk_idx[r][0..topk-1] in list order, entries outside 0..p (e.g. -1 for
+ * unused slots) skipped; a repeated position counts once per entry; latent
+ * bf16 layout only, topk <= 2048, window 0);
  * lse[r,h] = natural log of the softmax normaliser.  Latent layout
  * (v_cache == NULL, Hkv == 1): V[i,j] = first Dv entries of K[i,j].  Rows
  * [M, M_pad) get o = 0, lse = -inf; rows >= M_pad are not written.
@@ -232,7 +238,8 @@ typedef struct {
   int32_t Hq, Hkv, Dqk, Dv, dtype;
   float sm_scale;            /* multiplies q.k (e.g. 1/sqrt(Dqk)) */
   int32_t window;            /* sliding window in keys; 0 = full causal */
-  int32_t _pad1;
+  int32_t topk;              /* entries per row of topk_idx */
+  const int32_t* topk_idx;   /* NULL, or [rows_cap][topk] sparse key positions */
   void* o;                   /* out [rows_cap][Hq][Dv], dtype */
   float* lse;                /* out [rows_cap][Hq] or NULL */
   void* workspace;

@@ -24,6 +24,11 @@ Readings taken where the pages are silent:
   kernels but do not define it): with a window of ``W`` keys the row at
   position ``p`` attends to keys ``max(0, p-W+1)..p``; ``W = 0`` is full
   causal attention.
+* Sparse latent attention (the pages name DeepSeek-V4's native sparse-MLA
+  path, not its selector): a row given a key list attends to the listed
+  positions in list order, entries outside ``0..p`` (``-1`` pads) skipped; a
+  repeated position counts once per entry; a row with no listed position
+  gets ``o = 0`` and ``lse = -inf``.
 
 Arithmetic: fp64 throughout; ``lse`` is the natural log of the softmax
 normaliser of the scaled scores.
@@ -58,14 +63,15 @@ def attention_row(q_row, keys, values, sm_scale):
     return o, lse
 
 
-def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv, start=0):
-    """Keys/values of positions ``start..length-1`` read through the page table.
+def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv, start=0, positions=None):
+    """Keys/values of positions ``start..length-1`` (or of the listed
+    ``positions``) read through the page table.
 
     ``k_cache`` [num_pages, P, Hkv, Dqk]; ``v_cache`` same with ``Dv`` or None
     (latent layout: value = first ``Dv`` entries of the key row).
     """
     P = int(page_size)
-    pos = np.arange(start, length)
+    pos = np.arange(start, length) if positions is None else np.asarray(positions, dtype=np.int64)
     pages = np.asarray(page_table_row)[pos // P]
     if np.any(pages < 0) or np.any(pages >= k_cache.shape[0]):
         raise IndexError("page index out of range")
@@ -78,9 +84,9 @@ def gather_kv(k_cache, v_cache, page_table_row, page_size, length, Dv, start=0):
 
 
 def verify_attention(q, k_cache, v_cache, page_table, page_size, row_req,
-                     row_pos, M_pad, sm_scale, Dv=None, rows=None, window=0):
+                     row_pos, M_pad, sm_scale, Dv=None, rows=None, window=0, topk_idx=None):
     """Attention for packed rows (``window`` > 0: sliding window of that many
-    keys).
+    keys; ``topk_idx`` [>=M_pad, K]: each row's sparse key list).
 
     ``q`` [>=M_pad, Hq, Dqk] (packed order).  Returns ``(o, lse)`` shaped
     ``[M_pad, Hq, Dv]`` and ``[M_pad, Hq]``; if ``rows`` is given only those
@@ -99,7 +105,12 @@ def verify_attention(q, k_cache, v_cache, page_table, page_size, row_req,
             continue
         p = int(row_pos[r])
         start = max(0, p - int(window) + 1) if window else 0
+        positions = None
+        if topk_idx is not None:
+            positions = [int(j) for j in topk_idx[r] if 0 <= int(j) <= p]
+            if not positions:   # nothing listed: o = 0, lse = -inf, as for padding
+                continue
         keys, values = gather_kv(k_cache, v_cache, page_table[i], page_size,
-                                 p + 1, Dv, start=start)
+                                 p + 1, Dv, start=start, positions=positions)
         o[r], lse[r] = attention_row(q[r], keys, values, sm_scale)
     return o, lse

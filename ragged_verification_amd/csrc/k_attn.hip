@@ -74,6 +74,7 @@ struct PlanParams {
   int B, gamma, item_cap, part_cap, target;
   int n_workers;         // balanced plan: persistent workgroups of the main kernel
   int window;            // sliding window (keys), 0 = full causal
+  int topk;              // sparse latent attention: index entries per row (0: dense)
   AttnShape sh;
 };
 
@@ -115,7 +116,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   long long work = 0;
   for (int i = i0; i < i1; ++i) {
     const int w = p.cu[i + 1] - p.cu[i];
-    const int L = p.ctx[i] + w - win_origin(p.ctx[i], p.window);   // keys from the origin
+    // keys from the origin; sparse: each row's tile walks its topk index slots
+    const int L = p.topk > 0 ? p.topk : p.ctx[i] + w - win_origin(p.ctx[i], p.window);
     s_wl[i] = make_int2(w, L);
     work += (long long)tiles_of_w(w) * L;
   }
@@ -359,6 +361,8 @@ struct MainParams {
   int max_pages, page_size, num_pages, Hq, Hkv, G, NH, RT, n_hb, part_cap;
   int log2P;              // log2(page_size) when it is a power of two, else -1
   int window;             // sliding window (keys), 0 = full causal
+  const int32_t* topk_idx;  // sparse latent attention: [rows][topk] key positions, or nullptr
+  int topk;
   float scale_log2;       // sm_scale * log2(e)
 };
 
@@ -457,7 +461,9 @@ __device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
 // barrier into the stage that tile t-1 used.
 constexpr int kMlaXBytes = 2 * 4 * 64 * 16;       // probabilities [buffer][block][lane], 16 B each
 constexpr int kMlaRedBytes = 2 * 4 * 2 * 16 * 4;   // column max and sum [wave][block][16]
-constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kMlaXBytes + kMlaRedBytes + kPageWin * 4;
+constexpr int kMaxTopk = RV_MAX_TOPK;   // sparse latent attention: index entries per row at most
+constexpr int kMlaLdsBytes = kMlaStages * kMlaStageBytes + kMlaXBytes + kMlaRedBytes + kPageWin * 4 + kMaxTopk * 4;
+static_assert(kMlaLdsBytes <= 160 * 1024, "latent kernel LDS");
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
@@ -468,10 +474,12 @@ __device__ inline void lds_st_b64(uint32_t addr, uint32_t lo, uint32_t hi) {
   *(lds_u32x2_t*)(size_t)addr = u32x2_t{lo, hi};
 }
 
-template <bool FAST>
+template <bool FAST, bool SPARSE>
 __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, unsigned char* smem);
 
-template <bool FAST>
+// SPARSE: each row attends to the key positions its index list names (the
+// rows of a latent tile are one row: 64 heads), walked in list order.
+template <bool FAST, bool SPARSE>
 __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
@@ -479,16 +487,18 @@ __global__ __launch_bounds__(256) void k_attn_mla(MainParams p) {
   for (;;) {
     const int item = next_item(p, &s_item, done);
     if (item < 0) break;
-    attn_mla_item<FAST>(p, item, smem);
+    attn_mla_item<FAST, SPARSE>(p, item, smem);
   }
 }
 
-template <bool FAST>
+template <bool FAST, bool SPARSE>
 __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, unsigned char* smem) {
+  static_assert(!(FAST && SPARSE), "sparse keys do not lie in one page per tile");
   constexpr int kRing = kMlaStages * kMlaStageBytes;
   float* red_m = reinterpret_cast<float*>(smem + kRing + kMlaXBytes);
   float* red_l = red_m + 4 * 2 * 16;
   int* pwin = reinterpret_cast<int*>(smem + kRing + kMlaXBytes + kMlaRedBytes);
+  int* sidx = pwin + kPageWin;   // SPARSE: the item's index slots, -1 where masked
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -509,15 +519,19 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   const int hb = tile % p.n_hb;
   const int row0 = rb * p.RT;
   const int rows_here = min(p.RT, w - row0);
-  const int L_tile = c + row0 + rows_here;
+  // SPARSE: keys [kv_begin, kv_end) are index slots of the tile's one row,
+  // whose positions lie in 0 .. c + row0
+  const int L_tile = SPARSE ? p.topk : c + row0 + rows_here;
   const int chunk = p.hdr[1];
-  const int kv_begin = win_origin(c, p.window) + sp * chunk;
+  const int kv_begin = (SPARSE ? 0 : win_origin(c, p.window)) + sp * chunk;
   const int kv_end = min(kv_begin + chunk, L_tile);
   const int P = p.page_size;
 
-  // page-table window for keys [kv_begin, kv_end)
-  const int pg0 = kv_begin / P;
-  int npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
+  // page-table window for keys [kv_begin, kv_end) (SPARSE: every page up to
+  // the row's position)
+  const int pg0 = SPARSE ? 0 : kv_begin / P;
+  int npg = SPARSE ? (kv_end > kv_begin ? (c + row0) / P + 1 : 0)
+                   : (kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0);
   if (npg > kPageWin) {                 // context longer than the page table allows
     if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
     npg = kPageWin;
@@ -527,6 +541,15 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
     if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
     pwin[x] = pg;
+  }
+  if constexpr (SPARSE) {
+    // the row's index slots of this item; positions outside 0 .. its own
+    // position (and -1 entries) are masked
+    const int32_t* src = p.topk_idx + (size_t)(row_start + row0) * p.topk;
+    for (int x = tid; x < kv_end - kv_begin; x += 256) {
+      const int j = src[kv_begin + x];
+      sidx[x] = (j >= 0 && j <= c + row0) ? j : -1;
+    }
   }
 
   // query fragments: both 16-vector blocks of the pair, all 576 dims
@@ -540,8 +563,8 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     head[qb] = hb * p.NH + (qv % p.NH);
     q_valid[qb] = rl < rows_here;
     q_row[qb] = row_start + row0 + (q_valid[qb] ? rl : 0);
-    lim[qb] = min(c + row0 + rl, kv_end - 1);   // last key this vector may see here
-    low[qb] = win_low(c + row0 + rl, p.window);  // first key it may see
+    lim[qb] = SPARSE ? kv_end - 1 : min(c + row0 + rl, kv_end - 1);   // last key (slot) it may see here
+    low[qb] = SPARSE ? INT32_MIN : win_low(c + row0 + rl, p.window);  // first key it may see
     const bf16_t* qsrc = p.q + ((size_t)q_row[qb] * p.Hq + head[qb]) * kMlaD + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qf[qb][ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 32);
@@ -550,7 +573,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   // with a window, neither do tiles starting at or after every row's bound
   const int full_lim = min(c + row0, kv_end - 1);
   const int low_max = win_low(c + row0 + rows_here - 1, p.window);
-  auto is_full = [&](int t0) { return t0 + kNK - 1 <= full_lim && t0 >= low_max; };
+  auto is_full = [&](int t0) { return !SPARSE && t0 + kNK - 1 <= full_lim && t0 >= low_max; };
   wait_vm<0>();
   __syncthreads();   // page window visible
 
@@ -607,7 +630,8 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
         const int cidx = cbase + e * 64;
         const int row = cidx / kMlaChunksPerRow;
         const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
-        const int j = min(t0 + row, last);
+        int j = min(t0 + row, last);
+        if constexpr (SPARSE) j = max(sidx[j - kv_begin], 0);   // masked slots read key 0
         const int pg = pwin[min(j / P - pg0, npg - 1)];
         const unsigned char* g = reinterpret_cast<const unsigned char*>(p.k) +
                                  ((size_t)pg * P + (j % P)) * kMlaRowBytes + lg;
@@ -697,8 +721,12 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       for (int j = 0; j < 4; ++j) v[j] = sc[j] * p.scale_log2;
       if (!full) {   // edge tile: keys outside this vector's [low, lim] get probability 0
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (t0 + key_lane + j > lim[qb] || t0 + key_lane + j < low[qb]) v[j] = -INFINITY;
+        for (int j = 0; j < 4; ++j) {
+          const int k = t0 + key_lane + j;
+          bool out = k > lim[qb] || k < low[qb];
+          if constexpr (SPARSE) out = out || sidx[min(k, kv_end - 1) - kv_begin] < 0;
+          if (out) v[j] = -INFINITY;
+        }
       }
       m_seen[qb] = fmaxf(m_seen[qb], fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
       float e[4];
@@ -1774,6 +1802,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.target = sh.target;
   pp.n_workers = bal_grid;
   pp.window = a.window;
+  pp.topk = a.topk_idx ? a.topk : 0;
   pp.sh = sh;
   if (bal) hipLaunchKernelGGL(k_attn_plan_bal, dim3(1), dim3(kPlanThreads), 0, s, pp);
   else hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, pp);
@@ -1812,18 +1841,23 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   }
   mp.scale_log2 = a.sm_scale * kLog2e;
   mp.window = a.window;
+  mp.topk_idx = a.topk_idx;
+  mp.topk = a.topk_idx ? a.topk : 0;
   mp.ctr = pp.hdr + kHdrCtr;
 
   if (latent) {
-    const bool fast = mp.log2P >= 5;   // power-of-two pages of at least 32 keys
-    const void* kern = fast ? reinterpret_cast<const void*>(k_attn_mla<true>)
-                            : reinterpret_cast<const void*>(k_attn_mla<false>);
+    const bool sparse = a.topk_idx != nullptr;
+    const bool fast = !sparse && mp.log2P >= 5;   // power-of-two pages of at least 32 keys
+    const void* kern = sparse ? reinterpret_cast<const void*>(k_attn_mla<false, true>)
+                       : fast ? reinterpret_cast<const void*>(k_attn_mla<true, false>)
+                              : reinterpret_cast<const void*>(k_attn_mla<false, false>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMlaLdsBytes);
     if (e != hipSuccess) return e;
     int grid = 0;
     if ((e = persistent_grid(kern, 256, kMlaLdsBytes, &grid)) != hipSuccess) return e;
-    if (fast) hipLaunchKernelGGL((k_attn_mla<true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
-    else hipLaunchKernelGGL((k_attn_mla<false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    if (sparse) hipLaunchKernelGGL((k_attn_mla<false, true>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    else if (fast) hipLaunchKernelGGL((k_attn_mla<true, false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
+    else hipLaunchKernelGGL((k_attn_mla<false, false>), dim3(grid), dim3(256), kMlaLdsBytes, s, mp);
     e = hipGetLastError();
   } else {
     e = bal ? launch_gqa_bal(mp, nw, fast_gqa, bal_grid, s) : launch_gqa(mp, nw, fast_gqa, s);

@@ -115,6 +115,8 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
   const bool latent = (a->v_cache == nullptr);
   if (latent && (a->Hkv != 1 || a->Dv > a->Dqk)) return RV_ERR_UNSUPPORTED;
   if (!attn_shape_supported(a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype, latent)) return RV_ERR_UNSUPPORTED;
+  if (a->topk_idx && (!latent || a->dtype != RV_BF16 || a->window != 0)) return RV_ERR_UNSUPPORTED;
+  if (a->topk_idx && (a->topk < 1 || a->topk > RV_MAX_TOPK)) return RV_ERR_INVALID_ARG;
   if (a->max_pages > attn_max_pages_limit(a->dtype, latent)) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + attn_scratch_bytes(a->B, a->gamma, a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
@@ -260,7 +262,7 @@ int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap) {
                      RV_OFF(S, ctx), RV_OFF(S, cu), RV_OFF(S, mm), RV_OFF(S, B), RV_OFF(S, gamma),
                      RV_OFF(S, rows_cap), RV_OFF(S, max_pages), RV_OFF(S, page_size), RV_OFF(S, num_pages),
                      RV_OFF(S, Hq), RV_OFF(S, Hkv), RV_OFF(S, Dqk), RV_OFF(S, Dv), RV_OFF(S, dtype),
-                     RV_OFF(S, sm_scale), RV_OFF(S, window), RV_OFF(S, _pad1), RV_OFF(S, o), RV_OFF(S, lse), RV_OFF(S, workspace),
+                     RV_OFF(S, sm_scale), RV_OFF(S, window), RV_OFF(S, topk), RV_OFF(S, topk_idx), RV_OFF(S, o), RV_OFF(S, lse), RV_OFF(S, workspace),
                      RV_OFF(S, workspace_bytes)};
       n = sizeof(t) / sizeof(t[0]);
       for (int k = 0; k < n; ++k) v[k] = t[k];

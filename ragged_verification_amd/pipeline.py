@@ -15,12 +15,12 @@ anchor, req_to_token, history) so repeated steps see identical inputs.
 
 import torch
 
-from . import rv
+from . import rv, synth
 
 
 class VerifyStep:
     def __init__(self, inp, mode="compact", with_logits=False, rows_cap=None, r2t_extra=64,
-                 hist_cap=64, stream=None, w_layout="tiled", window=0):
+                 hist_cap=64, stream=None, w_layout="tiled", window=0, topk=0):
         wl = inp["workload"]
         self.inp, self.wl = inp, wl
         self.mode = mode
@@ -86,6 +86,15 @@ class VerifyStep:
         self.h_flat = inp["hidden_block"].reshape(B * gamma, wl.H)
         self.stream = stream
         self.window = window   # sliding-window attention (keys), 0 = full causal
+        # sparse latent attention: block-major key lists (inp["topk_block"],
+        # [B, gamma, topk]) gathered into packed order with the payload
+        self.topk_idx = None
+        if topk:
+            if inp.get("topk_block") is None or inp["topk_block"].shape[2] != topk:
+                inp["topk_block"] = synth.topk_indices(inp["ctx"], gamma, topk, inp["workload"].seed + 77,
+                                                       device=dev)
+            self.topk_flat = inp["topk_block"].reshape(B * gamma, topk)
+            self.topk_idx = torch.full((R, topk), -1, **i32)
         # LM-head weight in MFMA fragment order, made once per weight (a
         # serving system does this when it loads the model); bf16 with
         # H % 128 == 0 only, otherwise the row-major weight is read
@@ -116,12 +125,14 @@ class VerifyStep:
                           torch.zeros_like(req))
         torch.index_select(self.q_flat, 0, src, out=self.q)
         torch.index_select(self.h_flat, 0, src, out=self.hidden)
+        if self.topk_idx is not None:
+            torch.index_select(self.topk_flat, 0, src, out=self.topk_idx)
 
     def attn(self):
         i = self.inp
         rv.rv_verify_attn(self.q, i["k_cache"], i["v_cache"], i["page_table"], i["page_size"], i["num_pages"],
                           self.ctx, self.cu, self.mm, self.gamma, i["sm_scale"], self.o, self.lse,
-                          self.workspace, self.stream, window=self.window)
+                          self.workspace, self.stream, window=self.window, topk_idx=self.topk_idx)
 
     def lm(self):
         i = self.inp

@@ -56,7 +56,7 @@ class AttnArgs(ctypes.Structure):
                 ("cu", _vp), ("mm", _vp), ("B", _i32), ("gamma", _i32), ("rows_cap", _i32),
                 ("max_pages", _i32), ("page_size", _i32), ("num_pages", _i32), ("Hq", _i32),
                 ("Hkv", _i32), ("Dqk", _i32), ("Dv", _i32), ("dtype", _i32), ("sm_scale", _f32),
-                ("window", _i32), ("_pad1", _i32), ("o", _vp), ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+                ("window", _i32), ("topk", _i32), ("topk_idx", _vp), ("o", _vp), ("lse", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
 
 
 class LmArgs(ctypes.Structure):
@@ -236,7 +236,7 @@ def rv_pack(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tie
 
 
 def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                   o, lse, workspace, stream=None, window=0):
+                   o, lse, workspace, stream=None, window=0, topk_idx=None):
     rows_cap, Hq, Dqk = q.shape
     Hkv = k_cache.shape[2]
     Dv = o.shape[2]
@@ -246,7 +246,9 @@ def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, c
                  ctx=_ptr(ctx, torch.int32, "ctx"), cu=_ptr(cu, torch.int32, "cu"), mm=_ptr(mm, torch.int32, "mm"),
                  B=ctx.numel(), gamma=gamma, rows_cap=rows_cap, max_pages=page_table.shape[1],
                  page_size=page_size, num_pages=num_pages, Hq=Hq, Hkv=Hkv, Dqk=Dqk, Dv=Dv, dtype=dt,
-                 sm_scale=float(sm_scale), window=int(window), o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
+                 sm_scale=float(sm_scale), window=int(window),
+                 topk=0 if topk_idx is None else topk_idx.shape[1], topk_idx=_ptr(topk_idx, torch.int32, "topk_idx"),
+                 o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
 

@@ -181,6 +181,26 @@ def _dtype(wl):
     return torch.float32 if wl.dtype == "f32" else torch.bfloat16
 
 
+def topk_indices(ctx, gamma, K, seed, device="cpu"):
+    """Synthetic sparse-attention key lists, block-major int32 [B, gamma, K]:
+    block position k of request i (sequence position p = ctx_i + k) lists
+    min(K, p + 1) distinct positions drawn uniformly from 0..p, ascending,
+    padded with -1.  (The pages name the sparse-MLA path of DeepSeek-V4 but
+    not how its selector picks keys; uniform draws stand in for it.)"""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    ctx = ctx.to("cpu").to(torch.int64)
+    B = ctx.numel()
+    out = torch.full((B, gamma, K), -1, dtype=torch.int32)
+    for i in range(B):
+        for k in range(gamma):
+            p = int(ctx[i]) + k
+            n = min(K, p + 1)
+            sel = torch.randperm(p + 1, generator=g)[:n].sort().values
+            out[i, k, :n] = sel.to(torch.int32)
+    return out.to(device)
+
+
 def make_inputs(wl, device="cpu", B=None, seed=None):
     """Draw every input of one verify step for workload ``wl``.
 

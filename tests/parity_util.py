@@ -49,8 +49,8 @@ def npi(t):
     return t.detach().cpu().numpy().astype(np.int64)
 
 
-def run_gpu(inp, mode, with_logits=False, w_layout="tiled", window=0):
-    step = VerifyStep(inp, mode=mode, with_logits=with_logits, w_layout=w_layout, window=window)
+def run_gpu(inp, mode, with_logits=False, w_layout="tiled", window=0, topk=0):
+    step = VerifyStep(inp, mode=mode, with_logits=with_logits, w_layout=w_layout, window=window, topk=topk)
     step.run()
     torch.cuda.synchronize()
     return step

@@ -114,6 +114,18 @@ def test_attn_validation(lib):
     assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
     a.sm_scale = float("nan")
     assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.sm_scale, a.window = 0.1, -1        # negative window
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.window, a.v_cache = 0, _fake()      # sparse key lists: latent layout only
+    a.topk, a.topk_idx = 64, _fake()
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.v_cache, a.Hkv, a.Hq, a.Dqk, a.Dv = None, 1, 128, 576, 512
+    a.topk = 4096                          # past RV_MAX_TOPK
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    a.topk, a.window = 64, 100             # no window with key lists
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_UNSUPPORTED
+    a.window = 0
+    assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
 
 
 def test_tiled_weight_size_and_validation(lib):

@@ -20,7 +20,7 @@ from ragged_verification_amd.pipeline import VerifyStep
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_full(inp, ref, mode, window=0):
+def _oracle_full(inp, ref, mode, window=0, topk=0):
     """Oracle stages 3-5 on every real row (small cases only)."""
     wl = inp["workload"]
     gamma = inp["gamma"]
@@ -29,7 +29,8 @@ def _oracle_full(inp, ref, mode, window=0):
     q = pu.np64(inp["q_block"].reshape(-1, wl.Hq, wl.Dqk))[bidx]
     o, lse = oracle.verify_attention(q, pu.np64(inp["k_cache"]), pu.np64(inp["v_cache"]),
                                      pu.npi(inp["page_table"]), inp["page_size"], ref["row_req"],
-                                     ref["row_pos"], ref["M_pad"], inp["sm_scale"], Dv=wl.Dv, window=window)
+                                     ref["row_pos"], ref["M_pad"], inp["sm_scale"], Dv=wl.Dv, window=window,
+                                     topk_idx=pu.npi(inp["topk_block"].reshape(-1, topk))[bidx] if topk else None)
     x = pu.np64(inp["hidden_block"].reshape(-1, wl.H))[bidx]
     z = oracle.lm_head_logits(x, pu.np64(inp["W"]))
     pred = oracle.lm_head_pred(z)
@@ -75,13 +76,13 @@ def _check_scatter(step, sc, B):
     assert np.array_equal(pu.npi(step.hist_len), sc["hist_len"])
 
 
-def _full_parity(inp, mode, dtype, w_layout="tiled", window=0):
-    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode} weight={w_layout} window={window}")
+def _full_parity(inp, mode, dtype, w_layout="tiled", window=0, topk=0):
+    pu.log(f"case {inp['workload'].name} B={inp['B']} mode={mode} weight={w_layout} window={window} topk={topk}")
     ref = pu.oracle_schedule_pack(inp, mode)
-    step = pu.run_gpu(inp, mode, with_logits=True, w_layout=w_layout, window=window)
+    step = pu.run_gpu(inp, mode, with_logits=True, w_layout=w_layout, window=window, topk=topk)
     assert step.status() == 0
     pu.check_schedule_pack(step, ref)
-    want = _oracle_full(inp, ref, mode, window=window)
+    want = _oracle_full(inp, ref, mode, window=window, topk=topk)
     M, M_pad = ref["M"], ref["M_pad"]
     o = step.o.float().cpu().numpy()
     err = np.max(np.abs(o[:M] - want["o"][:M]))
@@ -183,6 +184,30 @@ def test_sliding_window_split_and_chunked():
     _full_parity(inp, "static", "bf16", window=77)
     inp = pu.make_inputs("tiny_f32")
     _full_parity(inp, "static", "f32", window=3)
+
+
+@pytest.mark.parametrize("topk", [1, 64, 300])
+def test_sparse_latent(topk):
+    """Sparse latent attention over per-row key lists (ascending positions
+    drawn from 0..p, -1 padded where p + 1 < topk)."""
+    inp = pu.make_inputs("mla_bf16", B=3, V=1000, H=512, ctx=("uniform", 60, 700))
+    _full_parity(inp, "compact", "bf16", topk=topk)
+
+
+def test_sparse_latent_split_and_empty_rows():
+    """2048-entry lists over long contexts (chunks split and merged); then
+    lists whose entries all lie past their rows (nothing visible: o = 0 and
+    lse = -inf, also through the split merge)."""
+    inp = pu.make_inputs("mla_bf16", B=2, Hq=64, V=500, H=256, ctx=("uniform", 3000, 5000))
+    _full_parity(inp, "static", "bf16", topk=2048)
+    inp = pu.make_inputs("mla_bf16", B=2, Hq=64, V=500, H=256, ctx=("uniform", 100, 300))
+    blk = torch.full((2, inp["gamma"], 600), 10**6, dtype=torch.int32, device="cuda")
+    blk[0, 0, 5] = 3   # one visible key for one row
+    inp["topk_block"] = blk
+    step, ref, want = _full_parity(inp, "static", "bf16", topk=600)
+    M = ref["M"]
+    o = step.o.float().cpu().numpy()
+    assert np.all(o[1:M] == 0) and np.all(np.isneginf(step.lse.cpu().numpy()[1:M]))
 
 
 @pytest.mark.parametrize("B", [1, 4])

@@ -108,6 +108,50 @@ def test_sliding_window_special_cases():
     assert np.array_equal(o_full, o_big)
 
 
+def test_sparse_key_lists():
+    """A list naming every position 0..p (in any order, padded with -1)
+    equals full causal attention; a one-entry list gives that key's value
+    exactly; listing a position twice equals doubling its weight (checked
+    against torch SDPA with the key repeated)."""
+    c = _paged_case(6, Hq=4, Hkv=1, D=8, Dv=5, latent=True)
+    args = (c["q"], c["k"], None, c["pt"], c["P"], c["row_req"], c["row_pos"], c["M"], 0.3)
+    rng = np.random.default_rng(1)
+    K = 16
+    full_list = np.full((c["M"], K), -1)
+    one = np.full((c["M"], K), -1)
+    for r in range(c["M"]):
+        p = int(c["row_pos"][r])
+        full_list[r, :p + 1] = rng.permutation(p + 1)
+        one[r, 3] = rng.integers(0, p + 1)
+    o_full, lse_full = verify_attention(*args, Dv=5)
+    o_list, lse_list = verify_attention(*args, Dv=5, topk_idx=full_list)
+    np.testing.assert_allclose(o_list, o_full, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse_list, lse_full, rtol=1e-12)
+    o_one, _ = verify_attention(*args, Dv=5, topk_idx=one)
+    kflat = c["k"].reshape(-1, 1, c["D"])
+    for r in range(c["M"]):
+        i, j = int(c["row_req"][r]), int(one[r, 3])
+        slot = int(c["pt"][i][j // c["P"]]) * c["P"] + j % c["P"]
+        assert np.array_equal(o_one[r], np.repeat(kflat[slot, :, :5], c["Hq"], axis=0))
+    # a position beyond the row is skipped
+    bad = one.copy()
+    bad[:, 0] = 10_000
+    assert np.array_equal(verify_attention(*args, Dv=5, topk_idx=bad)[0], o_one)
+    # a repeated entry
+    r = c["M"] - 1
+    p = int(c["row_pos"][r])
+    lst = np.full((c["M"], K), -1)
+    lst[r, :3] = [0, p, p]
+    o_rep, _ = verify_attention(*args, Dv=5, topk_idx=lst)
+    i = int(c["row_req"][r])
+    slots = [int(c["pt"][i][j // c["P"]]) * c["P"] + j % c["P"] for j in (0, p, p)]
+    Kt = torch.tensor(kflat[slots])[:, 0, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(c["q"][r])[:, None, :], Kt[None].expand(c["Hq"], -1, -1),
+        Kt[None, :, :5].expand(c["Hq"], -1, -1), scale=0.3)
+    np.testing.assert_allclose(o_rep[r], ref[:, 0].numpy(), rtol=1e-12, atol=1e-12)
+
+
 def test_attention_special_cases():
     rng = np.random.default_rng(2)
     q = rng.standard_normal((4, 16))
