@@ -498,7 +498,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   float* red_m = reinterpret_cast<float*>(smem + kRing + kMlaXBytes);
   float* red_l = red_m + 4 * 2 * 16;
   int* pwin = reinterpret_cast<int*>(smem + kRing + kMlaXBytes + kMlaRedBytes);
-  int* sidx = pwin + kPageWin;   // SPARSE: the item's index slots, -1 where masked
+  int* sidx = pwin + kPageWin;   // SPARSE: the item's index slots as cache rows, -1 where masked
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -530,8 +530,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   // page-table window for keys [kv_begin, kv_end) (SPARSE: every page up to
   // the row's position)
   const int pg0 = SPARSE ? 0 : kv_begin / P;
-  int npg = SPARSE ? (kv_end > kv_begin ? (c + row0) / P + 1 : 0)
-                   : (kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0);
+  int npg = SPARSE ? 0 : (kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0);
   if (npg > kPageWin) {                 // context longer than the page table allows
     if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
     npg = kPageWin;
@@ -543,12 +542,19 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
     pwin[x] = pg;
   }
   if constexpr (SPARSE) {
-    // the row's index slots of this item; positions outside 0 .. its own
-    // position (and -1 entries) are masked
+    // the row's index slots of this item as cache rows (page table read
+    // directly); positions outside 0 .. its own position (and -1 entries)
+    // are -1, masked
     const int32_t* src = p.topk_idx + (size_t)(row_start + row0) * p.topk;
     for (int x = tid; x < kv_end - kv_begin; x += 256) {
       const int j = src[kv_begin + x];
-      sidx[x] = (j >= 0 && j <= c + row0) ? j : -1;
+      int r = -1;
+      if (j >= 0 && j <= c + row0) {
+        int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
+        if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+        r = pg * P + j % P;
+      }
+      sidx[x] = r;
     }
   }
 
@@ -625,17 +631,25 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 #pragma unroll
       for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(d, e);
     } else {
+      // every source row first (the LDS reads overlap), then the DMAs: the
+      // asm statements order memory, so reads between them would serialise
+      int krow[kMlaDmaPerWave];
+#pragma unroll
+      for (int e = 0; e < kMlaDmaPerWave; ++e) {
+        const int row = (cbase + e * 64) / kMlaChunksPerRow;
+        const int j = min(t0 + row, last);
+        if constexpr (SPARSE) {
+          krow[e] = max(sidx[j - kv_begin], 0);   // masked slots read cache row 0
+        } else {
+          krow[e] = pwin[min(j / P - pg0, npg - 1)] * P + (j % P);
+        }
+      }
 #pragma unroll
       for (int e = 0; e < kMlaDmaPerWave; ++e) {
         const int cidx = cbase + e * 64;
         const int row = cidx / kMlaChunksPerRow;
         const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
-        int j = min(t0 + row, last);
-        if constexpr (SPARSE) j = max(sidx[j - kv_begin], 0);   // masked slots read key 0
-        const int pg = pwin[min(j / P - pg0, npg - 1)];
-        const unsigned char* g = reinterpret_cast<const unsigned char*>(p.k) +
-                                 ((size_t)pg * P + (j % P)) * kMlaRowBytes + lg;
-        dma16(g, lds0 + e * 1024);
+        dma16(reinterpret_cast<const unsigned char*>(p.k) + (size_t)krow[e] * kMlaRowBytes + lg, lds0 + e * 1024);
       }
     }
   };

@@ -117,6 +117,7 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
   if (!attn_shape_supported(a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype, latent)) return RV_ERR_UNSUPPORTED;
   if (a->topk_idx && (!latent || a->dtype != RV_BF16 || a->window != 0)) return RV_ERR_UNSUPPORTED;
   if (a->topk_idx && (a->topk < 1 || a->topk > RV_MAX_TOPK)) return RV_ERR_INVALID_ARG;
+  if (a->topk_idx && (long long)a->num_pages * a->page_size >= (1ll << 31)) return RV_ERR_UNSUPPORTED;
   if (a->max_pages > attn_max_pages_limit(a->dtype, latent)) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + attn_scratch_bytes(a->B, a->gamma, a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
