@@ -679,23 +679,26 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
       const float4 q = pr[s];
       merge_best(best, bi, q.x, __float_as_int(q.y));
     }
-    s_val[tid] = best;
-    s_idx[tid] = bi;
-    __syncthreads();
-    for (int off = kAccThreads / 2; off > 0; off >>= 1) {
-      if (tid < off) {
-        float b = s_val[tid];
-        int bb = s_idx[tid];
-        merge_best(b, bb, s_val[tid + off], s_idx[tid + off]);
-        s_val[tid] = b;
-        s_idx[tid] = bb;
-      }
-      __syncthreads();
+    // wave shuffles, then the four wave results (an exact order: the
+    // lowest index wins ties, so the result does not depend on the tree)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      merge_best(best, bi, ob, oi);
     }
-    const float mx = s_val[0];
+    if ((tid & 63) == 0) {
+      s_val[tid >> 6] = best;
+      s_idx[tid >> 6] = bi;
+    }
+    __syncthreads();
+    float mx = s_val[0];
+    int mi = s_idx[0];
+#pragma unroll
+    for (int u = 1; u < kAccThreads / 64; ++u) merge_best(mx, mi, s_val[u], s_idx[u]);
     if (tid == 0) {
-      s_pred[k] = s_idx[0];
-      p.pred[base + k] = s_idx[0];
+      s_pred[k] = mi;
+      p.pred[base + k] = mi;
     }
     if (p.rule == RV_REJECTION) {
       double acc = 0.0;
@@ -703,13 +706,15 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
         const float4 q = pr[s];
         acc += (double)q.z * exp((double)q.x - (double)mx);
       }
-      s_sum[tid] = acc;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+      if ((tid & 63) == 0) s_sum[tid >> 6] = acc;
       __syncthreads();
-      for (int off = kAccThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) s_sum[tid] += s_sum[tid + off];
-        __syncthreads();
+      if (tid == 0) {
+        double t = 0.0;
+        for (int u = 0; u < kAccThreads / 64; ++u) t += s_sum[u];
+        s_lse[k] = mx + (float)log(t);
       }
-      if (tid == 0) s_lse[k] = mx + (float)log(s_sum[0]);
     }
     __syncthreads();
   }
