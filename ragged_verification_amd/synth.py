@@ -57,6 +57,7 @@ class Workload:
     contiguous: bool = False  # one page per request, identity page table
     plant_beta: float = 14.0
     plant_power: float = 1.0  # a draft matches its target with probability conf ** plant_power
+    spare_tokens: int = 0     # KV pages for this many positions past ctx + gamma (multi-step runs)
     seed: int = 1000
     modes: tuple = ("static", "compact")
 
@@ -223,7 +224,7 @@ def make_inputs(wl, device="cpu", B=None, seed=None):
             raise ValueError("contiguous layout needs ctx + gamma <= page_size")
         pages_per = torch.ones(B, dtype=torch.int64, device=dev)
     else:
-        pages_per = (ctx + gamma + P - 1) // P
+        pages_per = (ctx + gamma + wl.spare_tokens + P - 1) // P
     num_pages = int(pages_per.sum())
     max_pages = int(pages_per.max())
     if wl.contiguous:

@@ -309,6 +309,49 @@ def test_maximum_sizes():
         pu.run_gpu(inp, "compact")
 
 
+def test_multi_step_state():
+    """Three verify steps in a row with the state carried on the device (ctx,
+    anchors, req_to_token, history): each step's packing, argmax, accepts and
+    scatter equal the oracle run step by step on the oracle's own state."""
+    from ragged_verification_amd.pipeline import VerifyStep
+    inp = pu.make_inputs("mla_bf16", B=4, V=1000, H=512, ctx=("uniform", 60, 400), spare_tokens=3 * 8)
+    gamma, B = inp["gamma"], inp["B"]
+    step = VerifyStep(inp, mode="compact", with_logits=True)
+    conf = inp["conf"].cpu().numpy()
+    drafts = pu.npi(inp["drafts"])
+    pt = pu.npi(inp["page_table"])
+    ctx, anchor = pu.npi(inp["ctx"]), pu.npi(inp["anchor"])
+    r2t = np.full(tuple(step.req_to_token.shape), -1)
+    hist = np.full(tuple(step.hist.shape), -1)
+    hist_len = np.zeros(B, dtype=np.int64)
+    wl = inp["workload"]
+    for s_ in range(3):
+        step.run()
+        torch.cuda.synchronize()
+        assert step.status() == 0
+        wc, wv, k_star, e_star = oracle.schedule(conf, gamma, oracle.COMPACT, inp["cost_bias"],
+                                                 inp["cost_alpha"].cpu().numpy(), inp["cost_theta"].cpu().numpy())
+        cu, M, M_pad, row_req, row_pos, tok, slot = oracle.pack(wv, anchor, drafts, ctx, pt, inp["page_size"],
+                                                                inp["tiers"])
+        assert np.array_equal(pu.npi(step.cu), cu)
+        assert np.array_equal(pu.npi(step.tok)[:M_pad], tok) and np.array_equal(pu.npi(step.slot)[:M_pad], slot)
+        ref = dict(M=M, row_req=row_req, cu=cu)
+        bidx = pu.packed_block_index(ref, gamma)
+        q = pu.np64(inp["q_block"].reshape(-1, wl.Hq, wl.Dqk))[bidx]
+        o, _ = oracle.verify_attention(q, pu.np64(inp["k_cache"]), None, pt, inp["page_size"], row_req[:M],
+                                       row_pos[:M], M, inp["sm_scale"], Dv=wl.Dv)
+        assert np.max(np.abs(step.o[:M].float().cpu().numpy() - o)) <= pu.ATTN_TOL["bf16"]
+        z = oracle.lm_head_logits(pu.np64(inp["hidden_block"].reshape(-1, wl.H))[bidx], pu.np64(inp["W"]))
+        pred = oracle.lm_head_pred(z)
+        assert np.array_equal(pu.npi(step.pred)[:M], pred)
+        acc, bonus, ceil = oracle.accept_greedy(pred, cu, wc, wv, drafts)
+        assert np.array_equal(pu.npi(step.accept), acc) and np.array_equal(pu.npi(step.bonus), bonus)
+        sc = oracle.compact_scatter(cu, wv, acc, bonus, drafts, slot, ctx, anchor, r2t, hist, hist_len)
+        _check_scatter(step, sc, B)
+        ctx, anchor, r2t, hist, hist_len = sc["ctx"], sc["anchor"], sc["req_to_token"], sc["hist"], sc["hist_len"]
+    assert int(hist_len.min()) >= 3
+
+
 def test_device_status_errors():
     """Bad data found on the device raises the sticky status and keeps every
     access in bounds."""
