@@ -61,6 +61,10 @@ constexpr int kBalS = 0, kBalQ = 1, kBalVw = 2, kBalTiles = 3, kBalParts = 4;
 // Both plans: the number of tiles with split partials (listed in split[]).
 constexpr int kHdrSplit = 6;
 constexpr int kBalSuper = 64;   // keys per super-tile of the GQA kernel (two 32-key sub-tiles)
+// A range's prologue (page window, queries, first DMA) costs about two
+// super-tiles of streaming (3.3 us against 1.43 us per super-tile, measured),
+// so the balanced plan charges each tile that much on top of its super-tiles.
+constexpr int kBalPro = 2;
 
 struct PlanParams {
   const int32_t* cu;
@@ -254,11 +258,12 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
 
 // ---- balanced plan (GQA) ----------------------------------------------------
 //
-// The tiles of all requests, request-major, each cut into 64-key super-tiles,
-// form one sequence of S super-tiles; virtual worker v takes [v*q, v*q+q)
-// with q = ceil(S / workers), so the workers' loads differ by at most one
-// super-tile.  Outputs: req_info[i] = {tiles, first tile, 0, 0}; per tile
-// T (in items[]) {first super-tile, super-tiles, first partial slot or -1,
+// The tiles of all requests, request-major, each cut into 64-key super-tiles
+// and charged kBalPro units of prologue before them, form one cost sequence
+// of S units; virtual worker v takes [v*q, v*q+q) with q = ceil(S /
+// workers), so the workers' loads differ by about one unit.  Outputs:
+// req_info[i] = {tiles, first tile, 0, 0}; per tile T (in items[]) {cost
+// position of its first super-tile, super-tiles, first partial slot or -1,
 // request}; after the n_tiles entries of items[], the first tile of each
 // virtual worker.  A tile whose super-tiles fall to k > 1 workers owns k
 // consecutive partial slots, one per worker in order.
@@ -285,7 +290,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
     s_wc[i] = make_int2(w, c);
     const int n_rb = ceil_div(w, sh.RT);
     cnt[0] += n_rb * per_rb;
-    for (int rb = 0; rb < n_rb; ++rb) cnt[1] += per_rb * nst(w, c, rb);
+    for (int rb = 0; rb < n_rb; ++rb) cnt[1] += per_rb * (nst(w, c, rb) + kBalPro);
   }
   block_excl_scan<2>(cnt, off, tot, s_buf);
   const int n_tiles = tot[0], S = tot[1];
@@ -301,8 +306,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
       const int n_rb = ceil_div(wc.x, sh.RT);
       for (int rb = 0; rb < n_rb; ++rb) {
         const int n = nst(wc.x, wc.y, rb);
-        for (int k = 0; k < per_rb; ++k, st += n) {
-          const int kseg = (st + n - 1) / q - st / q + 1;
+        for (int k = 0; k < per_rb; ++k, st += n + kBalPro) {
+          const int s0 = st + kBalPro;   // cost position of the tile's first super-tile
+          const int kseg = (s0 + n - 1) / q - s0 / q + 1;
           parts[0] += kseg > 1 ? kseg : 0;
           parts[1] += kseg > 1 ? 1 : 0;
         }
@@ -320,10 +326,11 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
     const int T0 = T;
     for (int rb = 0; rb < n_rb; ++rb) {
       const int n = nst(wc.x, wc.y, rb);
-      for (int k = 0; k < per_rb; ++k, ++T, st += n) {
-        const int v_first = st / q, v_last = (st + n - 1) / q;
+      for (int k = 0; k < per_rb; ++k, ++T, st += n + kBalPro) {
+        const int s0 = st + kBalPro;   // cost position of the tile's first super-tile
+        const int v_first = s0 / q, v_last = (s0 + n - 1) / q;
         const int kseg = v_last - v_first + 1;
-        p.items[T] = make_int4(st, n, kseg > 1 ? slot : -1, i);
+        p.items[T] = make_int4(s0, n, kseg > 1 ? slot : -1, i);
         slot += kseg > 1 ? kseg : 0;
         if (kseg > 1) p.split[split_at++] = make_int2(i, T - T0);
         // workers whose range starts inside this tile
@@ -1795,7 +1802,7 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   if (!latent) {
     if ((e = gqa_bal_grid(nw, fast_gqa, &bal_grid)) != hipSuccess) return e;
     const long long tiles_max = (long long)a.B * sh.tpr_max;
-    const long long st_max = ((long long)a.max_pages * a.page_size + kBalSuper - 1) / kBalSuper;
+    const long long st_max = ((long long)a.max_pages * a.page_size + kBalSuper - 1) / kBalSuper + kBalPro;
     bal = bal_grid <= 4 * (L.item_cap - tiles_max) && bal_grid + tiles_max <= L.part_slots &&
           tiles_max * st_max < INT32_MAX;
   }
