@@ -1375,7 +1375,8 @@ struct CombineParams {
   const float* part_ml;
   bf16_t* o;
   float* lse;
-  int Hq, Hkv, G, NH, RT, n_hb, QT, DV, tpr_max, part_cap;
+  const int32_t* mm;      // {M, M_pad}: rows [M, M_pad) are padding
+  int Hq, Hkv, G, NH, RT, n_hb, QT, DV, tpr_max, part_cap, rows_cap;
 };
 
 // One workgroup per (request, tile with split keys, group of 8 query
@@ -1501,6 +1502,16 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombineParams p) {
     const int2 it = p.split[u / groups];
     __syncthreads();   // the previous unit is done with the LDS
     combine_unit<DV>(p, it.x, it.y, (u % groups) * kCombVec, s_red, s_w);
+  }
+  // padding rows [M, M_pad): o = 0 (16-byte stores; a row is Hq*DV bf16, a
+  // multiple of 16 bytes), lse = -inf
+  const int M = p.mm[0], Mpad = min(p.mm[1], p.rows_cap);
+  const size_t n16 = (size_t)p.Hq * DV * 2 / 16;
+  for (int r = max(M, 0) + blockIdx.x; r < Mpad; r += gridDim.x) {
+    uint4* d = reinterpret_cast<uint4*>(p.o + (size_t)r * p.Hq * DV);
+    for (size_t k = threadIdx.x; k < n16; k += 256) d[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (p.lse)
+      for (int h = threadIdx.x; h < p.Hq; h += 256) p.lse[(size_t)r * p.Hq + h] = -INFINITY;
   }
 }
 
@@ -1755,11 +1766,11 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   int32_t* status = status_ptr(a.workspace);
   hipError_t e;
 
-  hipLaunchKernelGGL(k_attn_pad, dim3(a.rows_cap), dim3(256), 0, s, a.mm, a.o, a.lse, a.Hq, a.Dv,
-                     a.dtype == RV_F32 ? 4 : 2, a.rows_cap);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-
   if (a.dtype == RV_F32) {
+    // padding rows here; the bf16 path's combine kernel writes them
+    hipLaunchKernelGGL(k_attn_pad, dim3(a.rows_cap), dim3(256), 0, s, a.mm, a.o, a.lse, a.Hq, a.Dv, 4,
+                       a.rows_cap);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     F32Params f;
     f.q = static_cast<const float*>(a.q);
     f.k = static_cast<const float*>(a.k_cache);
@@ -1906,6 +1917,8 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   cp.DV = a.Dv;
   cp.tpr_max = sh.tpr_max;
   cp.part_cap = L.part_slots;
+  cp.mm = a.mm;
+  cp.rows_cap = a.rows_cap;
   int cus = 0, dev = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
