@@ -1123,14 +1123,19 @@ __device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int t
       }
     } else {
       (void)pgv;
+      // every source row first (the LDS reads overlap), then the DMAs: the
+      // asm statements order memory, so reads between them would serialise
+      int tok[kDmaPer];
+#pragma unroll
+      for (int e = 0; e < kDmaPer; ++e) {
+        const int j = min(t0 + dkey[e], last);
+        tok[e] = pwin[min(j / P - pg0, npg - 1)] * P + (j % P);
+      }
 #pragma unroll
       for (int e = 0; e < kDmaPer; ++e) {
         const int q = wid * kDmaPer + e;
         const bool is_v = (q % kInstSub) >= kInstSub / 2;
-        const int j = min(t0 + dkey[e], last);
-        const int pg = pwin[min(j / P - pg0, npg - 1)];
-        const size_t tok = (size_t)pg * P + (j % P);
-        dma16((is_v ? gv : gk) + tok * row_bytes + dlc[e],
+        dma16((is_v ? gv : gk) + (size_t)tok[e] * row_bytes + dlc[e],
               __builtin_amdgcn_readfirstlane(lds + st * Cfg::kStage + q * 1024));
       }
     }
