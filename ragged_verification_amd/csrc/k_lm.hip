@@ -78,6 +78,7 @@ struct GemmParams {
   int H, V, n_slabs, n_mt, n_vt;
   int with_sum;
   int ncb;             // 32-column blocks of the tiled weight
+  int cus;             // compute units of the device
   size_t w_bytes;      // bytes of the tiled weight
 };
 
@@ -323,27 +324,12 @@ struct TiledCfg {
 
 __device__ inline void lds_w128(uint32_t addr, const u32x4_t& v) { *(lds_u32x4_t*)(size_t)addr = v; }
 
-template <int WN>
-__global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
-  extern __shared__ __align__(16) unsigned char smem[];
+// BMB: 32-row blocks of the tile that hold packed rows (1, 2 or 4); the
+// MFMAs, fragment reads and epilogue of the blocks past them are skipped
+template <int WN, int BMB>
+__device__ __forceinline__ void lm_tiled_body(const GemmParams& p, unsigned char* smem, int m0, int v0, int M) {
   using Cfg = TiledCfg<WN>;
   constexpr int kNB = Cfg::kNB;
-  constexpr int BN = Cfg::kBN;
-
-  // XCD-aware tile order as in k_lm_gemm: the row tiles of one vocabulary
-  // tile run on one XCD at about the same time, so its weights come from HBM
-  // once and from that XCD's L2 for the other row tiles
-  const int n_tiles = p.n_mt * p.n_vt;
-  const int per_xcd = (n_tiles + 7) / 8;
-  const int kloc = blockIdx.x / 8;
-  const int logical = (blockIdx.x % 8) * per_xcd + kloc;
-  if (kloc >= per_xcd || logical >= n_tiles) return;
-  const int vt = logical / p.n_mt;
-  const int mt = logical % p.n_mt;
-  const int M = p.mm[0];
-  const int m0 = mt * kBM;
-  if (m0 >= M) return;
-  const int v0 = vt * BN;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,9 +380,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
 #pragma unroll
   for (int ks = 0; ks < kGKs; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
 
-  f32x16_t acc[4][kNB];
+  f32x16_t acc[BMB][kNB];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < BMB; ++a)
 #pragma unroll
     for (int b = 0; b < kNB; ++b)
 #pragma unroll
@@ -449,9 +435,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
       const int k = kt + u;
       const uint32_t stg = lds + half + u * Cfg::kStage;                   // stage k % 4
       const uint32_t nxt = lds + (half ^ (2 * Cfg::kStage)) + u * Cfg::kStage;   // stage (k+2) % 4
-      u32x4_t fa[2][4];
+      u32x4_t fa[2][BMB];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
+      for (int b = 0; b < BMB; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
 #pragma unroll
       for (int ks = 0; ks < kGKs; ++ks) {
         const int j = 4 * u + ks;                      // ring slot of this sub-step
@@ -466,11 +452,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
         }
         if (ks + 1 < kGKs) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) fa[(ks + 1) & 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
+          for (int b = 0; b < BMB; ++b) fa[(ks + 1) & 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm)
+        for (int bm = 0; bm < BMB; ++bm)
 #pragma unroll
           for (int bn = 0; bn < kNB; ++bn) acc[bm][bn] = mfma32(fa[ks & 1][bm], br[j][bn], acc[bm][bn]);
         __builtin_amdgcn_sched_barrier(0);
@@ -481,7 +467,39 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
     __syncthreads();
   }
 
-  lm_epilogue<WN>(acc, smem, p, wid, lane, m0, v0, M);
+  lm_epilogue<WN, BMB>(acc, smem, p, wid, lane, m0, v0, M);
+}
+
+template <int WN>
+__global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  // XCD-aware tile order as in k_lm_gemm: the row tiles of one vocabulary
+  // tile run on one XCD at about the same time, so its weights come from HBM
+  // once and from that XCD's L2 for the other row tiles
+  const int n_tiles = p.n_mt * p.n_vt;
+  const int per_xcd = (n_tiles + 7) / 8;
+  const int kloc = blockIdx.x / 8;
+  const int logical = (blockIdx.x % 8) * per_xcd + kloc;
+  if (kloc >= per_xcd || logical >= n_tiles) return;
+  const int vt = logical / p.n_mt;
+  const int mt = logical % p.n_mt;
+  const int M = p.mm[0];
+  const int m0 = mt * kBM;
+  if (m0 >= M) return;
+  const int v0 = vt * TiledCfg<WN>::kBN;
+  // The last row tile of a ragged batch is mostly padding: MFMAs only for
+  // its 32-row blocks that hold packed rows.  Except when every live tile
+  // runs at once (one round on the CUs) and a vocabulary tile has several
+  // row tiles: then the short tile would run ahead of its partners, fetch the
+  // weights from HBM on its own, and gain nothing, as the full tiles set the
+  // time (GQA shapes, 148 rows x 32000: 86 -> 96 us with accept; 48 rows,
+  // one row tile: 74 -> 63 us; 278 rows, a round and a half: 122 -> 116 us).
+  const int live_mt = (M + kBM - 1) / kBM;
+  const bool lockstep = live_mt > 1 && live_mt * p.n_vt <= p.cus;
+  const int rows = lockstep ? kBM : M - m0;
+  if (rows > 64) lm_tiled_body<WN, 4>(p, smem, m0, v0, M);
+  else if (rows > 32) lm_tiled_body<WN, 2>(p, smem, m0, v0, M);
+  else lm_tiled_body<WN, 1>(p, smem, m0, v0, M);
 }
 
 // ---- LM head for at most 32 rows over the tiled weight ---------------------------
@@ -630,16 +648,15 @@ struct AcceptParams {
   int B, gamma, V, n_slabs, rule;
 };
 
-constexpr int kAccThreads = 256;
+constexpr int kAccThreads = 512;   // eight waves: one per row of a gamma-8 window
+constexpr int kAccDepth = 16;     // slab partials per lane in flight while merging
 constexpr int kAccSeg = 4096;      // tokens per vocabulary segment of the bonus draw
 constexpr int kAccMaxSeg = kMaxVocabRejection / kAccSeg;
 
 __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
-  __shared__ float s_val[kAccThreads];
-  __shared__ int s_idx[kAccThreads];
-  __shared__ double s_sum[kAccThreads];
   __shared__ int s_pred[RV_MAX_GAMMA];
   __shared__ float s_lse[RV_MAX_GAMMA];
+  __shared__ int s_flag[RV_MAX_GAMMA];
   __shared__ int s_row, s_qrow, s_c, s_a, s_bonus;
   __shared__ double s_seg[kAccMaxSeg], s_total;
   __shared__ int s_seg_last[kAccMaxSeg];
@@ -670,64 +687,88 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
   }
   const int g1 = p.gamma - 1;
 
-  // merge slab partials: argmax (lowest index on ties) and log-sum-exp
-  for (int k = 0; k < wv; ++k) {
+  // merge slab partials, one wave per row (rows in parallel, no workgroup
+  // barrier per row): argmax (lowest index on ties, an exact merge whose
+  // result does not depend on the order) and, for the rejection rule,
+  // log-sum-exp in fp64
+  const int lane = tid & 63, wv_id = tid >> 6;
+  for (int k = wv_id; k < wv; k += kAccThreads / 64) {
     const float4* pr = p.part + (size_t)(base + k) * p.n_slabs;
     float best = -INFINITY;
     int bi = 0x7fffffff;
-    for (int s = tid; s < p.n_slabs; s += kAccThreads) {
-      const float4 q = pr[s];
-      merge_best(best, bi, q.x, __float_as_int(q.y));
+    // kAccDepth loads per lane in flight, then their merges
+    for (int s0 = lane; s0 < p.n_slabs; s0 += 64 * kAccDepth) {
+      float4 q[kAccDepth];
+#pragma unroll
+      for (int u = 0; u < kAccDepth; ++u) {
+        const int s = s0 + 64 * u;
+        q[u] = s < p.n_slabs ? pr[s] : make_float4(-INFINITY, __int_as_float(0x7fffffff), 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kAccDepth; ++u) merge_best(best, bi, q[u].x, __float_as_int(q[u].y));
     }
-    // wave shuffles, then the four wave results (an exact order: the
-    // lowest index wins ties, so the result does not depend on the tree)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       const float ob = __shfl_xor(best, off);
       const int oi = __shfl_xor(bi, off);
       merge_best(best, bi, ob, oi);
     }
-    if ((tid & 63) == 0) {
-      s_val[tid >> 6] = best;
-      s_idx[tid >> 6] = bi;
-    }
-    __syncthreads();
-    float mx = s_val[0];
-    int mi = s_idx[0];
-#pragma unroll
-    for (int u = 1; u < kAccThreads / 64; ++u) merge_best(mx, mi, s_val[u], s_idx[u]);
-    if (tid == 0) {
-      s_pred[k] = mi;
-      p.pred[base + k] = mi;
+    if (lane == 0) {
+      s_pred[k] = bi;
+      p.pred[base + k] = bi;
     }
     if (p.rule == RV_REJECTION) {
       double acc = 0.0;
-      for (int s = tid; s < p.n_slabs; s += kAccThreads) {
-        const float4 q = pr[s];
-        acc += (double)q.z * exp((double)q.x - (double)mx);
+      for (int s0 = lane; s0 < p.n_slabs; s0 += 64 * kAccDepth) {
+        float4 q[kAccDepth];
+#pragma unroll
+        for (int u = 0; u < kAccDepth; ++u) {
+          const int s = s0 + 64 * u;
+          q[u] = s < p.n_slabs ? pr[s] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kAccDepth; ++u)
+          if (s0 + 64 * u < p.n_slabs) acc += (double)q[u].z * exp((double)q[u].x - (double)best);
       }
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-      if ((tid & 63) == 0) s_sum[tid >> 6] = acc;
-      __syncthreads();
-      if (tid == 0) {
-        double t = 0.0;
-        for (int u = 0; u < kAccThreads / 64; ++u) t += s_sum[u];
-        s_lse[k] = mx + (float)log(t);
+      if (lane == 0) s_lse[k] = best + (float)log(acc);
+    }
+  }
+  __syncthreads();
+
+  // Every draft's test at once (lane t: draft t against row t), then the scan
+  // for the first failure: 2 = invalid token, 1 = kept, 0 = stop.
+  if (tid < wv - 1) {
+    const int t = tid;
+    const int d = p.drafts[(size_t)i * g1 + t];
+    int f = 2;
+    if (d >= 0 && d < p.V) {
+      if (p.rule == RV_GREEDY) {
+        f = d == s_pred[t] ? 1 : 0;
+      } else {
+        const float zd = p.logits[(size_t)(base + t) * p.V + d];
+        const float pd = expf(zd - s_lse[t]);
+        const float qd = p.q_rows[((size_t)i * g1 + t) * p.V + d];
+        f = p.u[(size_t)i * g1 + t] * qd < pd ? 1 : 0;
       }
     }
-    __syncthreads();
+    s_flag[t] = f;
   }
+  __syncthreads();
+  auto scan = [&]() {
+    int c = 0;
+    while (c < wv - 1) {
+      if (s_flag[c] == 2) { set_status(p.status, RV_DEV_BAD_TOKEN); break; }
+      if (s_flag[c] == 0) break;
+      ++c;
+    }
+    return c;
+  };
 
   if (p.rule == RV_GREEDY) {
     if (tid == 0) {
-      int c = 0;
-      while (c < wv - 1) {
-        const int d = p.drafts[(size_t)i * g1 + c];
-        if (d < 0 || d >= p.V) { set_status(p.status, RV_DEV_BAD_TOKEN); break; }
-        if (d != s_pred[c]) break;
-        ++c;
-      }
+      const int c = scan();
       const int a = min(c, wc - 1);
       p.ceiling[i] = c;
       p.accept[i] = a;
@@ -738,17 +779,7 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
 
   // ---- rejection sampling -------------------------------------------------------
   if (tid == 0) {
-    int c = 0;
-    while (c < wv - 1) {
-      const int j = c + 1;
-      const int d = p.drafts[(size_t)i * g1 + (j - 1)];
-      if (d < 0 || d >= p.V) { set_status(p.status, RV_DEV_BAD_TOKEN); break; }
-      const float zd = p.logits[(size_t)(base + j - 1) * p.V + d];
-      const float pd = expf(zd - s_lse[j - 1]);
-      const float qd = p.q_rows[((size_t)i * g1 + (j - 1)) * p.V + d];
-      if (p.u[(size_t)i * g1 + (j - 1)] * qd < pd) ++c;
-      else break;
-    }
+    const int c = scan();
     const int a = min(c, wc - 1);
     s_c = c;
     s_a = a;
@@ -770,9 +801,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
     return qd ? fmaxf(0.f, pv - qd[v]) : pv;
   };
   // The vocabulary in segments of kAccSeg consecutive tokens; wave w sums
-  // segments w, w+4, ... with lane l reading the float4 runs l, l+64, ...
+  // segments w, w+8, ... with lane l reading the float4 runs l, l+64, ...
   // of the segment (coalesced 1 KB loads, all in flight together).
-  const int lane = tid & 63, wv_id = tid >> 6;
   const int n_seg = (p.V + kAccSeg - 1) / kAccSeg;
   // float4 runs when every row starts 16-byte aligned
   const bool vec4 = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0 && ((uintptr_t)p.q_rows % 16) == 0;
@@ -924,7 +954,7 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
   const bool rej = (a.rule == RV_REJECTION);
   hipError_t e;
   if (a.dtype == RV_BF16 && a.w_layout == RV_W_TILED) {
-    GemmParams g;
+    GemmParams g{};
     g.x = static_cast<const bf16_t*>(a.hidden);
     g.w = static_cast<const bf16_t*>(a.W);
     g.mm = a.mm;
@@ -944,6 +974,7 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     // with 512-wide ones)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    g.cus = cus;
     const int t512 = g.n_mt * ((a.V + 511) / 512), t256 = g.n_mt * ((a.V + 255) / 256);
     const bool narrow = (t256 + cus - 1) / cus <= (t512 + cus - 1) / cus;
     auto launch = [&](auto kern, int bn, int lds_bytes) -> hipError_t {
@@ -972,7 +1003,7 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     }
     if (e != hipSuccess) return e;
   } else if (a.dtype == RV_BF16) {
-    GemmParams g;
+    GemmParams g{};
     g.x = static_cast<const bf16_t*>(a.hidden);
     g.w = static_cast<const bf16_t*>(a.W);
     g.mm = a.mm;
