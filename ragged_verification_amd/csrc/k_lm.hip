@@ -657,6 +657,8 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
   __shared__ int s_pred[RV_MAX_GAMMA];
   __shared__ float s_lse[RV_MAX_GAMMA];
   __shared__ int s_flag[RV_MAX_GAMMA];
+  __shared__ int s_sel;
+  __shared__ float s_w[kAccSeg + kAccSeg / 64];   // the selected segment's token weights
   __shared__ int s_row, s_qrow, s_c, s_a, s_bonus;
   __shared__ double s_seg[kAccMaxSeg], s_total;
   __shared__ int s_seg_last[kAccMaxSeg];
@@ -878,9 +880,11 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
   __syncthreads();
   const double total = s_total;
   const double target = (double)p.u_bonus[i] * total;
-  // the segment whose interval [excl, incl) holds the target: lane l of
-  // wave 0 sums its 64-token block of it, a wave scan finds the block that
-  // crosses the target, and that block's lane walks it token by token
+  // the segment whose interval [excl, incl) holds the target; its token
+  // weights are staged in LDS by the whole workgroup (one coalesced pass),
+  // then lane l of wave 0 sums its 64-token block of them, a wave scan finds
+  // the block that crosses the target, and that block's lane walks it token
+  // by token
   if (wv_id == 0) {
     int sel = -1;
     for (int k = lane; k < n_seg; k += 64) {
@@ -889,12 +893,25 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) sel = max(sel, __shfl_xor(sel, off));
+    if (lane == 0) s_sel = sel;
+  }
+  __syncthreads();
+  const int sel = s_sel;
+  const int sbase = sel * kAccSeg;
+  // token t of the segment at t + t/64: the 64 lanes' blocks start in
+  // different banks
+  auto wslot = [](int t) { return t + (t >> 6); };
+  if (sel >= 0) {
+    for (int t = tid; t < kAccSeg; t += kAccThreads) s_w[wslot(t)] = sbase + t < p.V ? weight(sbase + t) : 0.f;
+  }
+  __syncthreads();
+  if (wv_id == 0) {
     if (sel >= 0) {
       const double excl = sel > 0 ? s_seg[sel - 1] : 0.0;
-      const int b0 = sel * kAccSeg + 64 * lane;
+      const int b0 = sbase + 64 * lane;
       const int b1 = min(b0 + 64, p.V);
       double bs = 0.0;
-      for (int v = b0; v < b1; ++v) bs += (double)weight(v);
+      for (int v = b0; v < b1; ++v) bs += (double)s_w[wslot(v - sbase)];
       double incl = bs;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -909,12 +926,12 @@ __global__ __launch_bounds__(kAccThreads) void k_accept(AcceptParams p) {
           double run = excl + incl - bs;
           int pk = -1;
           for (int v = b0; v < b1; ++v) {
-            run += (double)weight(v);
+            run += (double)s_w[wslot(v - sbase)];
             if (run > target) { pk = v; break; }
           }
           if (pk < 0) {                // rounding: this block's last positive token
             for (int v = b1 - 1; v >= b0; --v)
-              if (weight(v) > 0.f) { pk = v; break; }
+              if (s_w[wslot(v - sbase)] > 0.f) { pk = v; break; }
           }
           s_bonus = pk;
         }
