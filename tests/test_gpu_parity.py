@@ -219,6 +219,18 @@ def test_lm_few_rows_odd_vocab(B):
     _full_parity(inp, "static", "bf16")
 
 
+@pytest.mark.parametrize("B,V", [(3, 900), (6, 900), (11, 900), (17, 900), (50, 40000)])
+def test_lm_row_blocks_of_last_tile(B, V):
+    """Static windows of 8 give 8*B packed rows.  With H = 128 the tiled
+    kernel runs even for 24 rows: 24, 48 and 88 rows use one, two and four
+    32-row blocks of their single row tile; 136 rows over four vocabulary
+    tiles run in one round, so both row tiles compute all four blocks; 400
+    rows over 79 tiles of 512 columns take two rounds, so the last tile's
+    16 rows compute one block.  Every row's logits are compared."""
+    inp = pu.make_inputs("gqa_bf16", B=B, V=V, H=128, tiers=(), ctx=("uniform", 10, 60))
+    _full_parity(inp, "static", "bf16")
+
+
 def test_tiled_weight_layout():
     """rv_lm_tile_weight against the layout written out with torch view
     operations: lane l of fragment f of block cb holds
