@@ -85,9 +85,15 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   // ---- survival products, sequential per request ----------------------------
   long long local_sum = 0;
   for (int i = t; i < B; i += kThreads) {
+    // all of the request's confidences in flight at once, then the products
+    float cv[RV_MAX_GAMMA - 1];
+#pragma unroll
+    for (int k = 1; k < RV_MAX_GAMMA; ++k) cv[k - 1] = k <= g1 ? p.conf[i * g1 + (k - 1)] : 0.0f;
     double S = 1.0;
-    for (int k = 1; k <= g1; ++k) {
-      float c = p.conf[i * g1 + (k - 1)];
+#pragma unroll
+    for (int k = 1; k < RV_MAX_GAMMA; ++k) {
+      if (k > g1) break;
+      float c = cv[k - 1];
       if (!(c >= 0.0f && c <= 1.0f)) {
         set_status(p.status, RV_DEV_BAD_CONF);
         c = 0.0f;
@@ -171,20 +177,28 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
 
   // ---- ratio for every K, first arg-max -------------------------------------
   const double ba = p.bias + p.alpha[B];
+  // the theta entries this thread evaluates, loaded together
+  constexpr int kSegMax = kMaxCand / kThreads;
+  double th[kSegMax];
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u) th[u] = (u < seg && j0 + u < n) ? p.theta[B + j0 + u + 1] : 0.0;
   double best_r = -1.0;
   int best_k = 0x7fffffff;
   bool bad = false;
-  auto eval = [&](int K, long long nk) {
-    const double T = ba + p.theta[B + K];
+  auto eval = [&](int K, long long nk, double theta) {
+    const double T = ba + theta;
     if (!(T > 0.0) || !(T < 1e300)) { bad = true; return; }
     const double r = static_cast<double>(nk) / T;
     if (r > best_r) { best_r = r; best_k = K; }
   };
-  if (t == 0) eval(0, base);
-  for (int j = j0; j < j0 + seg && j < n; ++j) {
+  if (t == 0) eval(0, base, p.theta[B]);
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u) {
+    const int j = j0 + u;
+    if (u >= seg || j >= n) break;
     const double S = __longlong_as_double(static_cast<long long>(~key[j]));
     pre += fixed_of(S);
-    eval(j + 1, base + pre);  // K = j+1 takes the first j+1 ranked candidates
+    eval(j + 1, base + pre, th[u]);  // K = j+1 takes the first j+1 ranked candidates
   }
   if (bad) atomicOr(&bad_cost, 1);
   // first arg-max: the larger ratio, the smaller K on ties (an exact order,
