@@ -82,9 +82,24 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   const int n = B * g1;
   if (t == 0) bad_cost = 0;
 
+  // The cost-table entries this thread evaluates after the sort (K = j+1
+  // for its ranked slots j, and K = 0 on thread 0), loaded now so that their
+  // latency overlaps the survival products and the sort.
+  const int seg = (n + kThreads - 1) / kThreads;  // <= 4
+  const int j0 = t * seg;
+  constexpr int kSegMax = kMaxCand / kThreads;
+  double th[kSegMax];
+  double alpha_b = 0.0, theta0 = 0.0;
+  if (p.mode == RV_COMPACT || p.mode == RV_CAP_ACCEPT) {
+#pragma unroll
+    for (int u = 0; u < kSegMax; ++u) th[u] = (u < seg && j0 + u < n) ? p.theta[B + j0 + u + 1] : 0.0;
+    alpha_b = p.alpha[B];
+    if (t == 0) theta0 = p.theta[B];
+  }
+
   // ---- survival products, sequential per request ----------------------------
   long long local_sum = 0;
-  for (int i = t; i < B; i += kThreads) {
+  auto survive = [&](int i) {
     // all of the request's confidences in flight at once, then the products
     float cv[RV_MAX_GAMMA - 1];
 #pragma unroll
@@ -107,7 +122,12 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
         local_sum += fixed_of(S);
       }
     }
-  }
+  };
+  // the first request of each thread outside any loop, so that its loads
+  // share one round trip with the cost-table loads above (a loop head would
+  // wait for those first)
+  if (t < B) survive(t);
+  for (int i = t + kThreads; i < B; i += kThreads) survive(i);
   const long long base = static_cast<long long>(B) << kShift;
 
   if (p.mode == RV_STATIC || p.mode == RV_NO_TRIM) {
@@ -163,8 +183,6 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   __syncthreads();
 
   // ---- fixed-point prefix sums in ranked order ------------------------------
-  const int seg = (n + kThreads - 1) / kThreads;  // <= 4
-  const int j0 = t * seg;
   long long run = 0;
   for (int j = j0; j < j0 + seg && j < n; ++j) {
     const double S = __longlong_as_double(static_cast<long long>(~key[j]));
@@ -176,12 +194,7 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
   long long pre = incl - run;  // exclusive prefix before j0
 
   // ---- ratio for every K, first arg-max -------------------------------------
-  const double ba = p.bias + p.alpha[B];
-  // the theta entries this thread evaluates, loaded together
-  constexpr int kSegMax = kMaxCand / kThreads;
-  double th[kSegMax];
-#pragma unroll
-  for (int u = 0; u < kSegMax; ++u) th[u] = (u < seg && j0 + u < n) ? p.theta[B + j0 + u + 1] : 0.0;
+  const double ba = p.bias + alpha_b;
   double best_r = -1.0;
   int best_k = 0x7fffffff;
   bool bad = false;
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
     const double r = static_cast<double>(nk) / T;
     if (r > best_r) { best_r = r; best_k = K; }
   };
-  if (t == 0) eval(0, base, p.theta[B]);
+  if (t == 0) eval(0, base, theta0);
 #pragma unroll
   for (int u = 0; u < kSegMax; ++u) {
     const int j = j0 + u;
