@@ -502,6 +502,200 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
   else lm_tiled_body<WN, 1>(p, smem, m0, v0, M);
 }
 
+// ---- LM head with every packed row in one tile (at most 256 rows) -------------------
+// With 128-row tiles a batch of 129..256 rows has two row tiles per
+// vocabulary tile: both stream the same weights (shared through L2 only
+// while they keep pace) and the second is mostly padding.  Here one
+// workgroup takes all rows against 128 vocabulary columns: each wave owns
+// one 32-column block and all 32-row blocks that hold packed rows (BMB), so
+// every weight byte is loaded by one wave only, once, and a weight fragment
+// feeds BMB MFMAs.  The hidden rows reach LDS by DMA (no registers) three K
+// steps ahead into a four-stage ring; the weights come straight into a
+// 16-deep register ring, loaded fifteen sub-steps ahead (a wait for a
+// hidden-row DMA three steps old never waits for weights needed later than
+// the next step).  The epilogue writes the fp32 tile to LDS and reduces
+// each (row, 64-column slab) in column order, as the other kernels do.
+constexpr int kRRing = 16, kRDist = 15, kRAhead = 3;
+constexpr int kRMaxRows = 256;
+constexpr int kRBN = 128;                             // columns per workgroup
+constexpr int kRStage = kRMaxRows * kGRow;            // 32 KB of hidden rows per K step
+constexpr int kRERow = kRBN + 4;                      // floats per padded epilogue row
+constexpr int kREpi = kRMaxRows * kRERow * 4;         // the fp32 tile of all rows
+constexpr int kRLds = 4 * kRStage > kREpi ? 4 * kRStage : kREpi;
+
+template <int BMB>
+__device__ __forceinline__ void lm_rows_body(const GemmParams& p, unsigned char* smem, int v0, int M) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, lh = lane >> 5;
+  const uint32_t lds = (uint32_t)(uintptr_t)smem;
+  const int nk = p.H / kBK;      // a multiple of 4 (H % 256 == 0)
+  const int nsub = p.H / 16;
+
+  // hidden rows: DMA instruction e of wave w moves chunks (BMB*w + e)*64 +
+  // lane of the step (BMB*32 rows of eight 16-byte chunks); chunk c goes to
+  // row c/8 at physical position c%8 and holds logical chunk (c%8) ^
+  // gswz(row); rows past the packed total read the last real row
+  const unsigned char* xa = reinterpret_cast<const unsigned char*>(p.x);
+  uint32_t doff[BMB];
+#pragma unroll
+  for (int e = 0; e < BMB; ++e) {
+    const int c = (wid * BMB + e) * 64 + lane;
+    const int row = c / kGChunks;
+    const int lc = (c % kGChunks) ^ gswz(row);
+    doff[e] = (uint32_t)min(row, M - 1) * (uint32_t)(p.H * 2) + (uint32_t)lc * 16u;
+  }
+  auto dma_a = [&](int kt) {   // K step kt into stage kt % 4
+    const void* base = uniform_ptr(xa + (size_t)min(kt, nk - 1) * kGRow);
+    const uint32_t dst = lds + (uint32_t)((kt & 3) * kRStage);
+#pragma unroll
+    for (int e = 0; e < BMB; ++e)
+      dma16_s(doff[e], base, __builtin_amdgcn_readfirstlane(dst + (wid * BMB + e) * 1024));
+  };
+
+  // weights: this wave's column block as one buffer resource ending at the
+  // tiled weight's end (a block past it reads as zeros, masked below)
+  const size_t wbase = (size_t)((v0 + wid * 32) / 32) * nsub * 1024;
+  const size_t wspan = (size_t)nsub * 1024;
+  const size_t wleft = p.w_bytes > wbase ? p.w_bytes - wbase : 0;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<unsigned char*>(const_cast<bf16_t*>(p.w)) + (wleft ? wbase : 0), 0,
+      (int)(wleft < wspan ? wleft : wspan), kBufFlags);
+  const uint32_t woff = (uint32_t)(lane * 16);
+  auto load_w = [&](u32x4_t& dst, int sub) { dst = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, sub * 1024, 0); };
+
+  uint32_t foff[kGKs];
+#pragma unroll
+  for (int ks = 0; ks < kGKs; ++ks) foff[ks] = (uint32_t)(l32 * kGRow + (((2 * ks + lh) ^ gswz(l32)) * 16));
+
+  f32x16_t acc[BMB];
+#pragma unroll
+  for (int a = 0; a < BMB; ++a)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[a][j] = 0.f;
+
+  // prologue in the loop's order (the compiler's load counting then sees
+  // the same queue at the loop head as inside it)
+  u32x4_t br[kRRing];
+#pragma unroll
+  for (int k = 0; k < kRAhead; ++k) dma_a(k);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < kRDist; ++j) {
+    load_w(br[j], min(j, nsub - 1));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // step 0 landed: the DMAs of steps 1 and 2 and the fifteen weight loads
+  // may still be in flight
+  wait_vm<(kRAhead - 1) * BMB + kRDist>();
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; kt += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = kt + u;
+      const uint32_t stg = lds + (uint32_t)(u * kRStage);   // stage k % 4 (kt % 4 == 0)
+      // step k+3 into stage (k+3) % 4, last read during step k-1, before the
+      // last barrier (past the end: the last step again, never read)
+      dma_a(k + kRAhead);
+      u32x4_t fa[2][BMB];
+#pragma unroll
+      for (int b = 0; b < BMB; ++b) fa[0][b] = lds_b128(stg + b * 32 * kGRow + foff[0]);
+#pragma unroll
+      for (int ks = 0; ks < kGKs; ++ks) {
+        const int j = 4 * u + ks;   // ring slot of sub-step 4k + ks
+        load_w(br[(j + kRDist) % kRRing], min(4 * k + ks + kRDist, nsub - 1));
+        if (ks + 1 < kGKs) {
+#pragma unroll
+          for (int b = 0; b < BMB; ++b) fa[(ks + 1) & 1][b] = lds_b128(stg + b * 32 * kGRow + foff[ks + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int bm = 0; bm < BMB; ++bm) acc[bm] = mfma32(fa[ks & 1][bm], br[j], acc[bm]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // step k+1's DMA (issued at the start of step k-2) has landed: after
+      // it this wave issued four weight loads in each of steps k-2 .. k and
+      // the DMAs of steps k+2 and k+3
+      wait_vm<(kRAhead - 1) * BMB + kRAhead * kGKs>();
+      __syncthreads();
+    }
+  }
+  wait_vm<0>();
+  __syncthreads();   // the ring is free for the epilogue
+
+  // epilogue: the fp32 tile [rows][128] into LDS, then one thread per
+  // (row, 64-column slab): max, lowest argmax, sum of exp(z - max)
+  float* et = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int bm = 0; bm < BMB; ++bm)
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      et[(bm * 32 + (j / 4) * 8 + lh * 4 + (j % 4)) * kRERow + wid * 32 + l32] = acc[bm][j];
+  __syncthreads();
+  const int rows = min(M, BMB * 32);
+  for (int q = tid; q < rows * (kRBN / kSlab); q += kGemmThreads) {
+    const int row = q / (kRBN / kSlab), sl = q % (kRBN / kSlab);
+    const int cslab = v0 + sl * kSlab;
+    if (cslab >= p.V) continue;
+    const float* src = et + row * kRERow + sl * kSlab;
+    float best = -INFINITY;
+    int bi = cslab;
+    for (int i = 0; i < kSlab; ++i) {
+      const float z = cslab + i < p.V ? src[i] : -INFINITY;
+      if (z > best) { best = z; bi = cslab + i; }   // strict: lowest index wins ties
+    }
+    float se = 0.f;
+    if (p.with_sum && best != -INFINITY) {
+      for (int i = 0; i < kSlab; ++i) {
+        const float z = cslab + i < p.V ? src[i] : -INFINITY;
+        se += (z == -INFINITY) ? 0.f : __expf(z - best);
+      }
+    }
+    p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
+  }
+  if (p.logits) {
+    // row-contiguous float4 runs: 32 lanes per row, eight rows per pass
+    const bool vec_logits = (p.V % 4) == 0 && ((uintptr_t)p.logits % 16) == 0;
+    const int c4 = (tid & 31) * 4;
+    const int gcol = v0 + c4;
+    for (int r = tid >> 5; r < rows; r += kGemmThreads / 32) {
+      const float4 v = *reinterpret_cast<const float4*>(et + r * kRERow + c4);
+      float* dst = p.logits + (size_t)r * p.V + gcol;
+      if (vec_logits && gcol + 3 < p.V) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        const float e4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (gcol + c < p.V) dst[c] = e4[c];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_rows(GemmParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int vt = blockIdx.x;
+  if (vt >= p.n_vt) return;
+  // at most kRMaxRows rows (the launcher's B*gamma bound); the clamp only
+  // keeps a corrupt count inside the LDS tile
+  const int M = min(p.mm[0], kRMaxRows);
+  if (M <= 0) return;
+  const int v0 = vt * kRBN;
+  switch ((M + 31) / 32) {
+    case 1: lm_rows_body<1>(p, smem, v0, M); break;
+    case 2: lm_rows_body<2>(p, smem, v0, M); break;
+    case 3: lm_rows_body<3>(p, smem, v0, M); break;
+    case 4: lm_rows_body<4>(p, smem, v0, M); break;
+    case 5: lm_rows_body<5>(p, smem, v0, M); break;
+    case 6: lm_rows_body<6>(p, smem, v0, M); break;
+    case 7: lm_rows_body<7>(p, smem, v0, M); break;
+    default: lm_rows_body<8>(p, smem, v0, M); break;
+  }
+}
+
 // ---- LM head for at most 32 rows over the tiled weight ---------------------------
 // With so few rows the MFMAs are cheap and the stage streams the weight: its
 // speed is the weight bytes in flight.  One wave per workgroup owns a
@@ -1014,6 +1208,9 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
       constexpr int kSmallLds = 32 * (64 + 4) * 4;   // the epilogue's transpose
       hipLaunchKernelGGL(k_lm_gemm_small, dim3(grid), dim3(64), kSmallLds, s, g);
       e = hipSuccess;
+    } else if (a.B * a.gamma <= kRMaxRows && a.H % 256 == 0) {
+      g.n_mt = 1;
+      e = launch(k_lm_gemm_rows, kRBN, kRLds);
     } else {
       e = narrow ? launch(k_lm_gemm_tiled<64>, TiledCfg<64>::kBN, TiledCfg<64>::kLds)
                  : launch(k_lm_gemm_tiled<128>, TiledCfg<128>::kBN, TiledCfg<128>::kLds);
