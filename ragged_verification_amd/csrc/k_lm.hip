@@ -506,8 +506,9 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
 // With 128-row tiles a batch of 129..256 rows has two row tiles per
 // vocabulary tile: both stream the same weights (shared through L2 only
 // while they keep pace) and the second is mostly padding.  Here one
-// workgroup takes all rows against 128 vocabulary columns: each wave owns
-// one 32-column block and all 32-row blocks that hold packed rows (BMB), so
+// workgroup takes all rows (up to 224) against 128 vocabulary columns: each
+// wave owns one 32-column block and all 32-row blocks that hold packed rows
+// (BMB), so
 // every weight byte is loaded by one wave only, once, and a weight fragment
 // feeds BMB MFMAs.  The hidden rows reach LDS by DMA (no registers) three K
 // steps ahead into a four-stage ring; the weights come straight into a
@@ -675,14 +676,33 @@ __device__ __forceinline__ void lm_rows_body(const GemmParams& p, unsigned char*
   }
 }
 
+// Past seven 32-row blocks the fragment reads (every wave reads every
+// block) outweigh what the single tile saves: 256 rows took 96 us here
+// against 89 us for two 128-row tiles in lockstep (GQA shapes, with accept),
+// 148 rows 63 against 79 us.  So the packed count, known only on the device,
+// picks the layout: the grid covers both (2 * ceil(V/256) >= ceil(V/128)).
+constexpr int kRTiledAbove = 224;
+
 __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_rows(GemmParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int vt = blockIdx.x;
-  if (vt >= p.n_vt) return;
   // at most kRMaxRows rows (the launcher's B*gamma bound); the clamp only
   // keeps a corrupt count inside the LDS tile
   const int M = min(p.mm[0], kRMaxRows);
   if (M <= 0) return;
+  if (M > kRTiledAbove) {
+    // two 128-row tiles per 256 columns, XCD-aware as in k_lm_gemm_tiled;
+    // both hold more than 96 rows, so all four blocks of each are computed
+    const int n_vt = (p.V + TiledCfg<64>::kBN - 1) / TiledCfg<64>::kBN;
+    const int n_tiles = 2 * n_vt;
+    const int per_xcd = (n_tiles + 7) / 8;
+    const int kloc = blockIdx.x / 8;
+    const int logical = (blockIdx.x % 8) * per_xcd + kloc;
+    if (kloc >= per_xcd || logical >= n_tiles) return;
+    lm_tiled_body<64, 4>(p, smem, (logical % 2) * kBM, (logical / 2) * TiledCfg<64>::kBN, M);
+    return;
+  }
+  const int vt = blockIdx.x;
+  if (vt >= p.n_vt) return;
   const int v0 = vt * kRBN;
   switch ((M + 31) / 32) {
     case 1: lm_rows_body<1>(p, smem, v0, M); break;
@@ -691,8 +711,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_rows(GemmParams p) {
     case 4: lm_rows_body<4>(p, smem, v0, M); break;
     case 5: lm_rows_body<5>(p, smem, v0, M); break;
     case 6: lm_rows_body<6>(p, smem, v0, M); break;
-    case 7: lm_rows_body<7>(p, smem, v0, M); break;
-    default: lm_rows_body<8>(p, smem, v0, M); break;
+    default: lm_rows_body<7>(p, smem, v0, M); break;
   }
 }
 
@@ -1210,7 +1229,13 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
       e = hipSuccess;
     } else if (a.B * a.gamma <= kRMaxRows && a.H % 256 == 0) {
       g.n_mt = 1;
-      e = launch(k_lm_gemm_rows, kRBN, kRLds);
+      g.n_vt = (a.V + kRBN - 1) / kRBN;
+      const int n_t = 2 * ((a.V + TiledCfg<64>::kBN - 1) / TiledCfg<64>::kBN);
+      const int grid = ((g.n_vt > n_t ? g.n_vt : n_t) + 7) / 8 * 8;
+      constexpr int kLds = kRLds > TiledCfg<64>::kLds ? kRLds : TiledCfg<64>::kLds;
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_lm_gemm_rows),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+      if (e == hipSuccess) hipLaunchKernelGGL(k_lm_gemm_rows, dim3(grid), dim3(kGemmThreads), kLds, s, g);
     } else {
       e = narrow ? launch(k_lm_gemm_tiled<64>, TiledCfg<64>::kBN, TiledCfg<64>::kLds)
                  : launch(k_lm_gemm_tiled<128>, TiledCfg<128>::kBN, TiledCfg<128>::kLds);

@@ -220,17 +220,18 @@ def test_lm_few_rows_odd_vocab(B):
 
 
 @pytest.mark.parametrize("H", [128, 256])
-@pytest.mark.parametrize("B,V", [(3, 900), (6, 900), (11, 900), (17, 900), (50, 40000)])
+@pytest.mark.parametrize("B,V", [(3, 900), (6, 900), (11, 900), (17, 900), (32, 900), (50, 40000)])
 def test_lm_row_blocks_of_last_tile(B, V, H):
     """Static windows of 8 give 8*B packed rows.  With H = 128 the 128-row
     tiled kernel runs for every count: 24, 48 and 88 rows use one, two and
-    four 32-row blocks of their single row tile; 136 rows over four
+    four 32-row blocks of their single row tile; 136 and 256 rows over four
     vocabulary tiles run in one round, so both row tiles compute all four
     blocks; 400 rows over 79 tiles of 512 columns take two rounds, so the
     last tile's 16 rows compute one block.  With H = 256, 24 rows take the
-    one-wave kernel and 48, 88 and 136 rows the all-rows kernel (two, three
+    one-wave kernel, 48, 88 and 136 rows the all-rows kernel (two, three
     and five 32-row blocks; 900 columns end inside its last 128-column
-    tile).  Every row's logits are compared."""
+    tile), and 256 rows that kernel's two-tile branch.  Every row's logits
+    are compared."""
     inp = pu.make_inputs("gqa_bf16", B=B, V=V, H=H, tiers=(), ctx=("uniform", 10, 60))
     _full_parity(inp, "static", "bf16")
 
