@@ -508,14 +508,16 @@ __global__ __launch_bounds__(kGemmThreads) void k_lm_gemm_tiled(GemmParams p) {
 // while they keep pace) and the second is mostly padding.  Here one
 // workgroup takes all rows (up to 224) against 128 vocabulary columns: each
 // wave owns one 32-column block and all 32-row blocks that hold packed rows
-// (BMB), so
-// every weight byte is loaded by one wave only, once, and a weight fragment
-// feeds BMB MFMAs.  The hidden rows reach LDS by DMA (no registers) three K
-// steps ahead into a four-stage ring; the weights come straight into a
-// 16-deep register ring, loaded fifteen sub-steps ahead (a wait for a
-// hidden-row DMA three steps old never waits for weights needed later than
-// the next step).  The epilogue writes the fp32 tile to LDS and reduces
-// each (row, 64-column slab) in column order, as the other kernels do.
+// (BMB), so every weight byte is loaded by one wave only, once, and a
+// weight fragment feeds BMB MFMAs.  The hidden rows reach LDS by DMA (no
+// registers) three K steps ahead into a four-stage ring; the weights come
+// straight into a 16-deep register ring, loaded fifteen sub-steps ahead (a
+// wait for a hidden-row DMA three steps old never waits for weights needed
+// later than the next step; the compiler's own waits before the MFMAs count
+// only the weight loads, so they also wait for the DMAs issued since, which
+// shortens the weights' lead when BMB is large).  The epilogue writes the
+// fp32 tile to LDS and reduces each (row, 64-column slab) in column order,
+// as the other kernels do.
 constexpr int kRRing = 16, kRDist = 15, kRAhead = 3;
 constexpr int kRMaxRows = 256;
 constexpr int kRBN = 128;                             // columns per workgroup
