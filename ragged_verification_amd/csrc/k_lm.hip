@@ -1201,9 +1201,10 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
     g.w_bytes = lm_tiled_weight_bytes(a.V, a.H);
     // 128 x 512 tiles; 128 x 256 tiles when they need no more rounds of one
     // tile per CU (counted at the B*gamma row bound): small batches, whose
-    // 512-wide grid leaves CUs idle (the 156-row GQA batch: 118 -> 87 us;
-    // the latent batch's 815 rows: 1.73 ms with 256-wide tiles, 1.52 ms
-    // with 512-wide ones)
+    // 512-wide grid leaves CUs idle (the 156-row GQA batch: 118 -> 87 us,
+    // before the all-rows kernel took row bounds up to 256; the latent
+    // batch's 815 rows: 1.73 ms with 256-wide tiles, 1.52 ms with 512-wide
+    // ones)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     g.cus = cus;
