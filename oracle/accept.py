@@ -65,10 +65,13 @@ def softmax(z):
 def residual_sample(r, u):
     """Inverse CDF of the non-negative weights ``r`` in index order.
 
-    Returns ``(index, margin)``: the smallest ``v`` with
-    ``cumsum(r)[v] > u * sum(r)`` and the distance of ``u * sum(r)`` to the
-    nearest cumulative boundary relative to ``sum(r)`` (used by tests to tell a
-    well-posed draw from one decided by rounding).
+    Returns ``(index, margin, neighbour)``: the smallest ``v`` with
+    ``cumsum(r)[v] > u * sum(r)``; the distance of ``u * sum(r)`` to the
+    nearest cumulative boundary relative to ``sum(r)``; and the token on the
+    other side of that nearest boundary (the largest earlier ``v`` of non-zero
+    weight when the lower boundary is nearer, else the smallest later one; the
+    index itself when there is none).  Tests use the last two to tell a
+    well-posed draw from one that rounding may move to the neighbouring token.
     """
     r = np.asarray(r, dtype=np.float64)
     cdf = np.cumsum(r)
@@ -78,8 +81,16 @@ def residual_sample(r, u):
     if idx >= len(r):  # rounding pushed the target past the last step
         idx = int(np.nonzero(r > 0)[0][-1])
     lo = cdf[idx - 1] if idx > 0 else 0.0
-    margin = min(abs(target - lo), abs(cdf[idx] - target)) / total
-    return idx, margin
+    d_lo, d_hi = abs(target - lo), abs(cdf[idx] - target)
+    margin = min(d_lo, d_hi) / total
+    nz = np.nonzero(r > 0)[0]
+    if d_lo <= d_hi:
+        before = nz[nz < idx]
+        neighbour = int(before[-1]) if len(before) else idx
+    else:
+        after = nz[nz > idx]
+        neighbour = int(after[0]) if len(after) else idx
+    return idx, margin, neighbour
 
 
 def accept_rejection(z_rows, cu, w_commit, w_verify, drafts, q_rows, u,
@@ -90,7 +101,7 @@ def accept_rejection(z_rows, cu, w_commit, w_verify, drafts, q_rows, u,
     draft distributions; ``u`` [B, gamma-1]; ``u_bonus`` [B].  Returns
     ``(accept, bonus, ceiling)``.  If ``diag`` is a dict it receives, per
     request, the relative margins of every accept decision and of the bonus
-    draw.
+    draw, and the token across the bonus draw's nearest CDF step.
     """
     B = len(w_commit)
     accept = np.zeros(B, dtype=np.int64)
@@ -116,9 +127,10 @@ def accept_rejection(z_rows, cu, w_commit, w_verify, drafts, q_rows, u,
             r = np.maximum(0.0, p - np.asarray(q_rows[i][c], dtype=np.float64))
         else:
             r = softmax(z_rows[base + wc - 1])
-        b, margin = residual_sample(r, float(u_bonus[i]))
+        b, margin, neighbour = residual_sample(r, float(u_bonus[i]))
         ceiling[i], accept[i], bonus[i] = c, a, b
         if diag is not None:
             diag.setdefault("decision_margin", []).append(dec_margins)
             diag.setdefault("bonus_margin", []).append(margin)
+            diag.setdefault("bonus_neighbour", []).append(neighbour)
     return accept, bonus, ceiling

@@ -113,6 +113,9 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
         set_status(p.status, RV_DEV_BAD_CONF);
         c = 0.0f;
       }
+      // -0.0 is a valid zero; as +0.0 its survival key sorts with the other
+      // zeros (the sort compares bit patterns)
+      if (c == 0.0f) c = 0.0f;
       S = S * static_cast<double>(c);
       const int id = i * g1 + (k - 1);
       if (p.mode == RV_COMPACT || p.mode == RV_CAP_ACCEPT) {

@@ -156,3 +156,49 @@ def check_pred_gap(z, frac=1e-3):
     gap = part[:, -1] - part[:, -2]
     scale = np.max(np.abs(z), axis=1)
     assert np.all(gap >= frac * scale), "argmax decision too close to call: inputs violate the guard"
+
+
+def check_bonus(step_bonus, ref_bonus, diag, thresh=1e-6):
+    """Rejection bonus draws compare exactly unless the oracle's target lies
+    within ``thresh`` (relative) of a CDF step, where fp32 and fp64 may
+    legitimately pick the token on the other side of that step: then the GPU's
+    token must be one of the two tokens bracketing it.  Returns the requests
+    whose GPU bonus is that neighbour."""
+    moved = []
+    for i, (g, r) in enumerate(zip(step_bonus, ref_bonus)):
+        if diag and diag["bonus_margin"][i] < thresh:
+            nb = diag["bonus_neighbour"][i]
+            assert int(g) in (int(r), int(nb)), (i, g, r, nb)
+            if int(g) != int(r):
+                moved.append(i)
+        else:
+            assert int(g) == int(r), (i, g, r)
+    return moved
+
+
+def check_scatter(step, sc, B, moved=()):
+    """Scatter outputs against the oracle's, bit for bit.  For requests in
+    ``moved`` (a bonus draw that rounding legitimately moved to the
+    neighbouring token) the bonus-dependent entries (the last committed
+    token, the new anchor, the last history entry) must equal the GPU's own
+    bonus; every other entry is compared exactly."""
+    n = int(sc["commit_cu"][-1])
+    assert np.array_equal(npi(step.commit_cu), sc["commit_cu"])
+    want_tok = sc["commit_tok"].copy()
+    want_anchor = sc["anchor"].copy()
+    want_hist = sc["hist"].copy()
+    gb = npi(step.bonus)
+    for i in moved:
+        want_tok[int(sc["commit_cu"][i + 1]) - 1] = gb[i]
+        want_anchor[i] = gb[i]
+        want_hist[i, int(sc["hist_len"][i]) - 1] = gb[i]
+    assert np.array_equal(npi(step.commit_tok)[:n], want_tok)
+    assert np.array_equal(npi(step.commit_slot)[:n], sc["commit_slot"])
+    nf = int(step.free_count.item())
+    assert nf == len(sc["free_slots"])
+    assert np.array_equal(npi(step.free_slots)[:nf], sc["free_slots"])
+    assert np.array_equal(npi(step.ctx), sc["ctx"])
+    assert np.array_equal(npi(step.anchor), want_anchor)
+    assert np.array_equal(npi(step.req_to_token), sc["req_to_token"])
+    assert np.array_equal(npi(step.hist), want_hist)
+    assert np.array_equal(npi(step.hist_len), sc["hist_len"])

@@ -28,6 +28,17 @@ def _sample_rows(ref, ctx, k_random=4, seed=0):
     return sorted(rows)
 
 
+def _block_rows(M, seed=1, block=32):
+    """One random row in every 32-row block of the packed rows (so every row
+    block of every 128-row LM tile holds a compared row), the first row and
+    the last real row."""
+    rng = np.random.default_rng(seed)
+    rows = {0, M - 1}
+    for b0 in range(0, M, block):
+        rows.add(int(rng.integers(b0, min(b0 + block, M))))
+    return sorted(rows)
+
+
 def _planted_accept(inp, ref):
     """Greedy accept lengths known from the planting: leading drafts equal to
     the planted target, capped by the verify and commit windows."""
@@ -46,7 +57,7 @@ def _planted_accept(inp, ref):
     return acc, bonus, ceil
 
 
-def _greedy_full(name, mode, B=None, attn_rows=6, logit_rows=3):
+def _greedy_full(name, mode, B=None, attn_rows=6):
     inp = pu.make_inputs(name, B=B, gen_on_gpu=True)
     pu.log(f"full {name} B={inp['B']} mode={mode}")
     ref = pu.oracle_schedule_pack(inp, mode)
@@ -67,8 +78,8 @@ def _greedy_full(name, mode, B=None, attn_rows=6, logit_rows=3):
     pred = pu.npi(step.pred)
     assert np.array_equal(pred[:M], targets)
     assert np.all(pred[M:M_pad] == -1)
-    # sampled rows against the oracle's fp64 logits
-    lr = rows[:logit_rows]
+    # logits of a row in every 32-row block against the oracle's fp64 logits
+    lr = _block_rows(M)
     z = pu.oracle_logits_rows(inp, ref, lr)
     pu.check_pred_gap(z)
     assert np.array_equal(oracle.lm_head_pred(z), pred[lr])
@@ -118,7 +129,7 @@ def test_full_gqa_compact():
 
 @pytest.mark.parametrize("B", [1, 32, 256])
 def test_full_sweep_cap_accept(B):
-    _greedy_full("sweep_gqa", "cap_accept", B=B, attn_rows=3, logit_rows=2)
+    _greedy_full("sweep_gqa", "cap_accept", B=B, attn_rows=3)
 
 
 def test_full_rejection():
@@ -134,37 +145,51 @@ def test_full_rejection():
     rows = _sample_rows(ref, ctx, k_random=3)
     worst = pu.check_attention(step, inp, ref, rows, "bf16")
     pu.log(f"attention rows {rows} max err {worst:.3g}")
-    # acceptance for sampled requests: all their rows' logits from the oracle
-    reqs = [int(np.argmax(ctx)), 0, 7]
+    M = ref["M"]
     cu = ref["cu"]
+    # logits of a row in every 32-row block
+    lr = _block_rows(M)
+    z = pu.oracle_logits_rows(inp, ref, lr)
+    rel = np.max(np.abs(step.logits.cpu().numpy()[lr] - z), axis=1) / np.max(np.abs(z), axis=1)
+    assert np.all(rel <= pu.LOGIT_TOL["bf16"]), rel
+    # acceptance for 16 requests spread over the batch plus the longest
+    # context: all their rows' logits from the oracle
+    B = inp["B"]
+    reqs = sorted({int(x) for x in np.linspace(0, B - 1, 16).round()} | {int(np.argmax(ctx))})
     rows = [r for i in reqs for r in range(cu[i], cu[i + 1])]
     z = pu.oracle_logits_rows(inp, ref, rows)
     zg = step.logits.cpu().numpy()[rows]
     rel = np.max(np.abs(zg - z), axis=1) / np.max(np.abs(z), axis=1)
     assert np.all(rel <= pu.LOGIT_TOL["bf16"]), rel
-    zfull = np.zeros((ref["M"], z.shape[1]))
-    zfull[rows] = z
     diag = {}
     sub_cu = np.zeros(len(reqs) + 1, dtype=np.int64)
-    zs = []
     for j, i in enumerate(reqs):
         sub_cu[j + 1] = sub_cu[j] + (cu[i + 1] - cu[i])
-        zs.append(zfull[cu[i]:cu[i + 1]])
     acc, bonus, ceil = oracle.accept_rejection(
-        np.concatenate(zs), sub_cu, ref["w_commit"][reqs], ref["w_verify"][reqs], pu.npi(inp["drafts"])[reqs],
+        z, sub_cu, ref["w_commit"][reqs], ref["w_verify"][reqs], pu.npi(inp["drafts"])[reqs],
         pu.np64(inp["q_rows"][reqs]), pu.np64(inp["u"][reqs]), pu.np64(inp["u_bonus"][reqs]), diag=diag)
     for m in diag["decision_margin"]:
         assert all(x >= 1e-4 for x in m), "accept decision too close to call"
     ga, gb, gc = pu.npi(step.accept)[reqs], pu.npi(step.bonus)[reqs], pu.npi(step.ceiling)[reqs]
     assert np.array_equal(ga, acc) and np.array_equal(gc, ceil)
-    for j in range(len(reqs)):
-        if diag["bonus_margin"][j] >= 1e-6:
-            assert gb[j] == bonus[j], (reqs[j], gb[j], bonus[j])
-    pu.log(f"ok rejection: accepts {ga.tolist()} bonus {gb.tolist()} oracle {bonus.tolist()}")
+    moved = pu.check_bonus(gb, bonus, diag)
+    pu.log(f"ok rejection: {len(reqs)} requests, accepts {ga.tolist()}, bonus moved across a CDF step "
+           f"for {len(moved)}")
+    # the sampled requests' scatter entries against the oracle's accepts
+    ccu, ctok, cslot = pu.npi(step.commit_cu), pu.npi(step.commit_tok), pu.npi(step.commit_slot)
+    r2t, ctx_new, anc = pu.npi(step.req_to_token), pu.npi(step.ctx), pu.npi(step.anchor)
+    drafts = pu.npi(inp["drafts"])
+    for j, i in enumerate(reqs):
+        a = int(acc[j])
+        b = int(gb[j]) if j in moved else int(bonus[j])
+        assert ccu[i + 1] - ccu[i] == a + 1
+        assert ctok[ccu[i]:ccu[i + 1]].tolist() == drafts[i, :a].tolist() + [b]
+        assert cslot[ccu[i]:ccu[i + 1]].tolist() == ref["slot"][cu[i]:cu[i] + a + 1].tolist()
+        assert r2t[i, ctx[i]:ctx[i] + a + 1].tolist() == ref["slot"][cu[i]:cu[i] + a + 1].tolist()
+        assert ctx_new[i] == ctx[i] + a + 1 and anc[i] == b
     # scatter invariants at full size
     a_all = pu.npi(step.accept)
     assert int(step.commit_cu[-1].item()) == int((a_all + 1).sum())
-    M = ref["M"]
     got = np.concatenate([pu.npi(step.commit_slot)[:int((a_all + 1).sum())],
                           pu.npi(step.free_slots)[:int(step.free_count.item())]])
     assert sorted(got.tolist()) == sorted(ref["slot"][:M].tolist())

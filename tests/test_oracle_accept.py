@@ -102,6 +102,18 @@ def test_residual_sample_inverse_cdf():
     assert residual_sample(r, 0.999999)[0] == 4
 
 
+def test_residual_sample_neighbour_across_nearest_boundary():
+    """The token on the far side of the nearest CDF step, skipping tokens of
+    zero weight (the interval of token 3 is [0.25, 0.75))."""
+    r = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    idx, margin, nb = residual_sample(r, 0.26)
+    assert (idx, nb) == (3, 1) and abs(margin - 0.01) < 1e-12
+    idx, margin, nb = residual_sample(r, 0.70)
+    assert (idx, nb) == (3, 4) and abs(margin - 0.05) < 1e-12
+    assert residual_sample(r, 0.01)[2] == 1        # nothing of weight below token 1
+    assert residual_sample(r, 0.99)[2] == 4        # nothing above token 4
+
+
 def test_cap_accept_commits_equal_compact_greedy():
     rng = np.random.default_rng(5)
     B, gamma, V = 40, 6, 7

@@ -147,6 +147,26 @@ def test_zero_theta_keeps_every_positive_survival():
     assert np.array_equal(wc, expect)
 
 
+def test_negative_zero_confidence_is_zero():
+    """-0.0 is a valid confidence equal to 0.0: the windows, K* and E* equal
+    those of the same batch with +0.0, under a cost table where zeros tie
+    with each other (theta flat past the positives) and under a linear one."""
+    rng = np.random.default_rng(11)
+    conf = rng.uniform(0.2, 1.0, size=(7, 5)).astype(np.float32)
+    conf[1, 0] = 0.0
+    conf[4, 2] = 0.0
+    neg = conf.copy()
+    neg[1, 0] = -0.0
+    neg[4, 2] = -0.0
+    assert np.signbit(neg[1, 0]) and not np.signbit(conf[1, 0])
+    bias, alpha, theta = linear_costs(7, 6)
+    for th in (theta, np.zeros_like(theta)):
+        for mode in (oracle.COMPACT, oracle.CAP_ACCEPT):
+            a = schedule(conf, 6, mode, bias, alpha, th)
+            b = schedule(neg, 6, mode, bias, alpha, th)
+            assert all(np.array_equal(x, y) for x, y in zip(a[:2], b[:2])) and a[2:] == b[2:]
+
+
 def test_huge_theta_verifies_anchor_only():
     rng = np.random.default_rng(4)
     conf = rng.uniform(0.5, 1.0, size=(5, 7)).astype(np.float32)
