@@ -55,6 +55,8 @@ extern "C" {
 #define RV_ERR_TIER (-3)          /* tier list not ascending, or too long */
 #define RV_ERR_WORKSPACE (-4)     /* workspace NULL or smaller than needed */
 #define RV_ERR_HIP (-5)           /* a HIP runtime call failed */
+#define RV_ERR_SCRATCH (-6)       /* problem larger than rv_lm_head_accept_noalloc's
+                                     static scratch (RV_NOALLOC_SCRATCH_BYTES) */
 typedef int32_t rv_status;
 
 /* ---- sticky device status codes (rv_device_status) ---------------------- */
@@ -292,6 +294,24 @@ typedef struct {
  * Device errors: BAD_TOKEN for a draft outside [0,V) (it never matches;
  * under rejection it is rejected), BAD_WINDOW. */
 rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream);
+
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): rv_lm_head_accept
+ * with the same arguments and results, but its scratch memory (the slab
+ * partials: 16 bytes per row of B*gamma and 64-column vocabulary slab) is a
+ * static device array of RV_NOALLOC_SCRATCH_BYTES held by the library, one
+ * copy per GPU, until the process ends; the call allocates nothing.
+ * `workspace` is optional here: NULL, or a caller buffer of at least 256
+ * bytes that receives the sticky device status (read it with
+ * rv_device_status); with NULL the status goes to the static array and is
+ * not readable.  Host errors: those of rv_lm_head_accept, RV_ERR_WORKSPACE
+ * for a status buffer under 256 bytes, RV_ERR_SCRATCH when
+ * 256 + 16 * B*gamma * ceil(V/64), rounded up to 256, exceeds
+ * RV_NOALLOC_SCRATCH_BYTES.  Every call on one GPU shares its static array:
+ * calls that overlap on one GPU (other streams, other threads) race, so a
+ * caller serialises them. */
+#define RV_NOALLOC_SCRATCH_BYTES (64u << 20)
+rv_status rv_lm_head_accept_noalloc(const rv_lm_args* a, void* stream);
 
 /* The LM-head weight in MFMA fragment order, made once when the weight is
  * loaded (as a serving system lays out its weights for its kernels), so that

@@ -1180,9 +1180,9 @@ size_t lm_scratch_bytes(int B, int gamma, int V) {
   return align_up(sizeof(float4) * (size_t)B * gamma * n_slabs, 256);
 }
 
-hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
+hipError_t launch_lm(const rv_lm_args& a, void* part_mem, int32_t* status, hipStream_t s) {
   const int n_slabs = (a.V + kSlab - 1) / kSlab;
-  float4* part = reinterpret_cast<float4*>(static_cast<char*>(a.workspace) + kStatusBytes);
+  float4* part = static_cast<float4*>(part_mem);
   const bool rej = (a.rule == RV_REJECTION);
   hipError_t e;
   if (a.dtype == RV_BF16 && a.w_layout == RV_W_TILED) {
@@ -1295,7 +1295,7 @@ hipError_t launch_lm(const rv_lm_args& a, hipStream_t s) {
   ap.accept = a.accept;
   ap.bonus = a.bonus;
   ap.ceiling = a.ceiling;
-  ap.status = status_ptr(a.workspace);
+  ap.status = status;
   ap.B = a.B;
   ap.gamma = a.gamma;
   ap.V = a.V;

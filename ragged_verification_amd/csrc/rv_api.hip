@@ -28,6 +28,23 @@ rv_status hip_status(hipError_t e) { return e == hipSuccess ? RV_OK : RV_ERR_HIP
 
 }  // namespace
 
+rv_status lm_args_check(const rv_lm_args* a) {
+  if (!a || !a->hidden || !a->W || !a->mm || !a->cu || !a->w_commit || !a->w_verify || !a->drafts ||
+      !a->pred || !a->accept || !a->bonus || !a->ceiling)
+    return RV_ERR_INVALID_ARG;
+  if (a->rule != RV_GREEDY && a->rule != RV_REJECTION) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_REJECTION && (!a->q_rows || !a->u || !a->u_bonus || !a->logits)) return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
+  if (a->H < 1 || a->V < 1) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_REJECTION && a->V > kMaxVocabRejection) return RV_ERR_UNSUPPORTED;
+  if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
+  if (a->dtype == RV_BF16 && a->H % 64 != 0) return RV_ERR_UNSUPPORTED;
+  if (a->w_layout != RV_W_ROWS && a->w_layout != RV_W_TILED) return RV_ERR_INVALID_ARG;
+  if (a->w_layout == RV_W_TILED && (a->dtype != RV_BF16 || a->H % 128 != 0)) return RV_ERR_UNSUPPORTED;
+  return RV_OK;
+}
+
 hipError_t launch_clear_status(void* ws, hipStream_t s) {
   hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, status_ptr(ws));
   return hipGetLastError();
@@ -125,22 +142,12 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
 }
 
 rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream) {
-  if (!a || !a->hidden || !a->W || !a->mm || !a->cu || !a->w_commit || !a->w_verify || !a->drafts ||
-      !a->pred || !a->accept || !a->bonus || !a->ceiling)
-    return RV_ERR_INVALID_ARG;
-  if (a->rule != RV_GREEDY && a->rule != RV_REJECTION) return RV_ERR_INVALID_ARG;
-  if (a->rule == RV_REJECTION && (!a->q_rows || !a->u || !a->u_bonus || !a->logits)) return RV_ERR_INVALID_ARG;
-  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
-  if ((long long)a->rows_cap < (long long)a->B * a->gamma) return RV_ERR_INVALID_ARG;
-  if (a->H < 1 || a->V < 1) return RV_ERR_INVALID_ARG;
-  if (a->rule == RV_REJECTION && a->V > kMaxVocabRejection) return RV_ERR_UNSUPPORTED;
-  if (a->dtype != RV_F32 && a->dtype != RV_BF16) return RV_ERR_INVALID_ARG;
-  if (a->dtype == RV_BF16 && a->H % 64 != 0) return RV_ERR_UNSUPPORTED;
-  if (a->w_layout != RV_W_ROWS && a->w_layout != RV_W_TILED) return RV_ERR_INVALID_ARG;
-  if (a->w_layout == RV_W_TILED && (a->dtype != RV_BF16 || a->H % 128 != 0)) return RV_ERR_UNSUPPORTED;
+  const rv_status st = lm_args_check(a);
+  if (st != RV_OK) return st;
   const size_t need = kStatusBytes + lm_scratch_bytes(a->B, a->gamma, a->V);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
-  return hip_status(launch_lm(*a, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_lm(*a, static_cast<char*>(a->workspace) + kStatusBytes, status_ptr(a->workspace),
+                              static_cast<hipStream_t>(stream)));
 }
 
 rv_status rv_lm_tiled_weight_bytes(int32_t V, int32_t H, int32_t dtype, size_t* bytes) {

@@ -101,7 +101,10 @@ struct SchedLaunch;
 hipError_t launch_schedule(const rv_schedule_args& a, hipStream_t s);
 hipError_t launch_pack(const rv_pack_args& a, hipStream_t s);
 hipError_t launch_attn(const rv_attn_args& a, hipStream_t s);
-hipError_t launch_lm(const rv_lm_args& a, hipStream_t s);
+// part: the slab partials (lm_scratch_bytes), status: the sticky status word
+hipError_t launch_lm(const rv_lm_args& a, void* part, int32_t* status, hipStream_t s);
+// host checks of rv_lm_head_accept's arguments other than the workspace
+rv_status lm_args_check(const rv_lm_args* a);
 hipError_t launch_scatter(const rv_scatter_args& a, hipStream_t s);
 hipError_t launch_calibration(const rv_calib_args& a, hipStream_t s);
 hipError_t launch_clear_status(void* ws, hipStream_t s);

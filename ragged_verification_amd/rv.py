@@ -16,8 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librv.so")
 
 RV_OK, RV_ERR_INVALID_ARG, RV_ERR_UNSUPPORTED, RV_ERR_TIER, RV_ERR_WORKSPACE, RV_ERR_HIP = 0, -1, -2, -3, -4, -5
+RV_ERR_SCRATCH = -6
 STATUS_NAMES = {0: "RV_OK", -1: "RV_ERR_INVALID_ARG", -2: "RV_ERR_UNSUPPORTED", -3: "RV_ERR_TIER",
-                -4: "RV_ERR_WORKSPACE", -5: "RV_ERR_HIP"}
+                -4: "RV_ERR_WORKSPACE", -5: "RV_ERR_HIP", -6: "RV_ERR_SCRATCH"}
 DEV_NAMES = {0: "RV_DEV_OK", 1: "RV_DEV_BAD_CONF", 2: "RV_DEV_BAD_COST", 3: "RV_DEV_BAD_WINDOW",
              4: "RV_DEV_TIER_OVERFLOW", 5: "RV_DEV_BAD_PAGE", 6: "RV_DEV_BAD_TOKEN",
              7: "RV_DEV_HIST_OVERFLOW"}
@@ -27,6 +28,7 @@ RV_GREEDY, RV_REJECTION = 0, 1
 RV_F32, RV_BF16 = 0, 1
 RV_W_ROWS, RV_W_TILED = 0, 1
 RV_MAX_GAMMA, RV_MAX_TIERS, RV_MAX_ROWS = 16, 16, 8192
+RV_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _vp, _i32, _f32, _f64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
 
@@ -87,7 +89,8 @@ class CalibArgs(ctypes.Structure):
 STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims, CalibArgs]
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
            "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
-           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model", "rv_calibration"]
+           "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model", "rv_calibration",
+           "rv_lm_head_accept_noalloc"]
 
 _LIB = None
 
@@ -116,7 +119,7 @@ def load(path=LIB_PATH):
     lib.rv_clear_status.argtypes = [_vp, _vp]
     for name, st in (("rv_schedule", ScheduleArgs), ("rv_pack", PackArgs), ("rv_verify_attn", AttnArgs),
                      ("rv_lm_head_accept", LmArgs), ("rv_compact_scatter", ScatterArgs),
-                     ("rv_calibration", CalibArgs)):
+                     ("rv_calibration", CalibArgs), ("rv_lm_head_accept_noalloc", LmArgs)):
         fn = getattr(lib, name)
         fn.restype = _i32
         fn.argtypes = [ctypes.POINTER(st), _vp]
@@ -303,26 +306,44 @@ def rv_lm_tile_weight(W, W_tiled=None, stream=None):
     return W_tiled
 
 
-def rv_lm_head_accept(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
-                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None, W_tiled=None):
-    """W [V][H] gives the vocabulary size; with W_tiled (rv_lm_tile_weight of
-    W) the kernel reads the tiled copy instead."""
+def _lm_args(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling, workspace,
+             logits, q_rows, u, u_bonus, W_tiled):
     rows_cap, H = hidden.shape
     V = W.shape[0]
     B, g1 = drafts.shape
     Wp = _ptr(W, hidden.dtype, "W") if W_tiled is None else _ptr(W_tiled, name="W_tiled")
-    a = LmArgs(hidden=_ptr(hidden, hidden.dtype, "hidden"), W=Wp,
-               mm=_ptr(mm, torch.int32, "mm"), cu=_ptr(cu, torch.int32, "cu"),
-               w_commit=_ptr(w_commit, torch.int32, "w_commit"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
-               drafts=_ptr(drafts, torch.int32, "drafts"), q_rows=_ptr(q_rows, torch.float32, "q_rows"),
-               u=_ptr(u, torch.float32, "u"), u_bonus=_ptr(u_bonus, torch.float32, "u_bonus"),
-               B=B, gamma=g1 + 1, rows_cap=rows_cap, H=H, V=V, dtype=_dtype_code(hidden), rule=rule,
-               w_layout=RV_W_ROWS if W_tiled is None else RV_W_TILED,
-               pred=_ptr(pred, torch.int32, "pred"), accept=_ptr(accept, torch.int32, "accept"),
-               bonus=_ptr(bonus, torch.int32, "bonus"), ceiling=_ptr(ceiling, torch.int32, "ceiling"),
-               logits=_ptr(logits, torch.float32, "logits"),
-               workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    return LmArgs(hidden=_ptr(hidden, hidden.dtype, "hidden"), W=Wp,
+                  mm=_ptr(mm, torch.int32, "mm"), cu=_ptr(cu, torch.int32, "cu"),
+                  w_commit=_ptr(w_commit, torch.int32, "w_commit"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+                  drafts=_ptr(drafts, torch.int32, "drafts"), q_rows=_ptr(q_rows, torch.float32, "q_rows"),
+                  u=_ptr(u, torch.float32, "u"), u_bonus=_ptr(u_bonus, torch.float32, "u_bonus"),
+                  B=B, gamma=g1 + 1, rows_cap=rows_cap, H=H, V=V, dtype=_dtype_code(hidden), rule=rule,
+                  w_layout=RV_W_ROWS if W_tiled is None else RV_W_TILED,
+                  pred=_ptr(pred, torch.int32, "pred"), accept=_ptr(accept, torch.int32, "accept"),
+                  bonus=_ptr(bonus, torch.int32, "bonus"), ceiling=_ptr(ceiling, torch.int32, "ceiling"),
+                  logits=_ptr(logits, torch.float32, "logits"),
+                  workspace=_ptr(workspace, name="workspace"),
+                  workspace_bytes=0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def rv_lm_head_accept(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
+                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None, W_tiled=None):
+    """W [V][H] gives the vocabulary size; with W_tiled (rv_lm_tile_weight of
+    W) the kernel reads the tiled copy instead."""
+    a = _lm_args(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling, workspace,
+                 logits, q_rows, u, u_bonus, W_tiled)
     _check("rv_lm_head_accept", load().rv_lm_head_accept(ctypes.byref(a), _stream(stream)))
+
+
+def rv_lm_head_accept_noalloc(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
+                              status=None, logits=None, q_rows=None, u=None, u_bonus=None, stream=None,
+                              W_tiled=None):
+    """rv_lm_head_accept with the library's static scratch instead of a
+    workspace; ``status`` (optional, at least 256 bytes of device memory)
+    receives the sticky device status."""
+    a = _lm_args(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling, status,
+                 logits, q_rows, u, u_bonus, W_tiled)
+    _check("rv_lm_head_accept_noalloc", load().rv_lm_head_accept_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def rv_compact_scatter(cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, req_to_token, commit_cu,

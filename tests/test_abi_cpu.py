@@ -168,3 +168,22 @@ def test_lm_and_scatter_validation(lib):
     assert lib.rv_compact_scatter(ctypes.byref(s), None) == rv.RV_ERR_WORKSPACE
     s.hist = _fake()             # hist without hist_len
     assert lib.rv_compact_scatter(ctypes.byref(s), None) == rv.RV_ERR_INVALID_ARG
+
+
+def test_lm_noalloc_rejects_beyond_its_scratch(lib):
+    """The no-alloc LM head refuses, before any device work, a problem whose
+    slab partials exceed its static scratch (64 MiB), a status buffer under
+    256 bytes, and whatever rv_lm_head_accept refuses."""
+    a = rv.LmArgs()
+    assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+    for f in ("hidden", "W", "mm", "cu", "w_commit", "w_verify", "drafts", "pred", "accept", "bonus", "ceiling"):
+        setattr(a, f, _fake())
+    a.B, a.gamma, a.rows_cap, a.H, a.dtype, a.rule, a.w_layout = 64, 8, 512, 256, rv.RV_BF16, rv.RV_GREEDY, 0
+    a.V = 1 << 21        # 512 rows x 32768 slabs x 16 bytes: 256 MiB
+    assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_SCRATCH
+    a.B, a.rows_cap, a.V = 256, 2048, 131072 + 64   # 2048 rows x 2049 slabs: 64 MiB + 32 KiB
+    assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_SCRATCH
+    a.workspace, a.workspace_bytes = _fake(), 255
+    assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
+    a.rule = 9
+    assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
