@@ -408,7 +408,9 @@ __device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done
     *s_item = it;
   }
   __syncthreads();
-  return *s_item;
+  // every lane read the same value: tell the compiler, so that the item's
+  // metadata loads and the arithmetic on them stay scalar
+  return __builtin_amdgcn_readfirstlane(*s_item);
 }
 
 // ---- latent (MLA-style) bf16 kernel: LDS DMA ring ---------------------------------
@@ -442,6 +444,24 @@ constexpr int kMlaDmaPerWave = kNK * kMlaChunksPerRow / 256;  // 9 per wave per 
 constexpr int kMlaQT = 64;                                 // query vectors per tile (2 wave pairs x 32)
 
 __device__ inline int swz(int row) { return (row >> 1) & 7; }
+// A per-lane value the compiler must treat as computed here: LDS addresses
+// formed as opaque(base) + constant keep the constant in the instruction's
+// offset field instead of re-adding a scalar base to a lane offset per read.
+__device__ inline uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+// Swizzle of the latent kernels' 1152-byte key rows.  Rows alternate between
+// the two halves of the 64 banks (1152 = 4.5 x 256 bytes), and the XOR with
+// the bit-reversed pair index gives (a) 16 consecutive rows at one chunk:
+// 16 distinct 16-byte bank slots (QK fragment reads), and (b) 4 consecutive
+// rows at an aligned group of 4 chunks: rows r and r+2 in opposite halves of
+// the 8 chunk slots (transposing V^T reads), which (row >> 1) & 7 maps to the
+// same banks.
+__device__ inline int lswz(int row) {
+  const int x = (row >> 1) & 7;
+  return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+}
 
 __device__ inline uint32_t cvt_bf16x2(float lo, float hi) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -597,7 +617,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 
   // DMA chunks: wave wid issues chunks (wid*9 + e)*64 + lane of a tile; chunk
   // c lands at row c/72, physical position c%72 and holds logical chunk
-  // (c%72) ^ swz(row)
+  // (c%72) ^ lswz(row)
   const int cbase = wid * kMlaDmaPerWave * 64 + lane;
   const int last = kv_end - 1;   // keys past the end read this valid row (masked later)
 
@@ -610,7 +630,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   for (int e = 0; e < kMlaDmaPerWave; ++e) {
     const int cidx = cbase + e * 64;
     const int row = cidx / kMlaChunksPerRow;
-    dma_off[e] = (uint32_t)(row * kMlaRowBytes + ((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
+    dma_off[e] = (uint32_t)(row * kMlaRowBytes + ((cidx - row * kMlaChunksPerRow) ^ lswz(row)) * 16);
   }
   struct DmaTile {
     const void* base;   // the tile's first row
@@ -655,7 +675,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       for (int e = 0; e < kMlaDmaPerWave; ++e) {
         const int cidx = cbase + e * 64;
         const int row = cidx / kMlaChunksPerRow;
-        const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ swz(row)) * 16);
+        const uint32_t lg = (uint32_t)(((cidx - row * kMlaChunksPerRow) ^ lswz(row)) * 16);
         dma16(reinterpret_cast<const unsigned char*>(p.k) + (size_t)krow[e] * kMlaRowBytes + lg, lds0 + e * 1024);
       }
     }
@@ -668,7 +688,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   {
     const int r = half * 16 + n16;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) qk_off[kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ swz(r)) * 16;
+    for (int kk = 0; kk < 2; ++kk) qk_off[kk] = r * kMlaRowBytes + ((4 * kk + grp) ^ lswz(r)) * 16;
   }
   // PV (transposing reads): rows kb + n16/4 (kb = 4*grp or 16 + 4*grp), elements
   // 128*wid + 16*mb + 4*(n16 & 3): logical chunk 16*wid + 2*mb + ((n16 & 3) >> 1);
@@ -680,7 +700,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       const int lc = 16 * wid + 2 * mm + ((n16 & 3) >> 1);
-      pv_off[hh][mm] = r * kMlaRowBytes + (lc ^ swz(r)) * 16 + (n16 & 1) * 8;
+      pv_off[hh][mm] = r * kMlaRowBytes + (lc ^ lswz(r)) * 16 + (n16 & 1) * 8;
     }
   }
   // probability exchange: buffer b, block B (0..3), 16 bytes per lane = the
@@ -945,6 +965,405 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
       for (int mb = 0; mb < 8; ++mb)
         *reinterpret_cast<f32x4_t*>(po_ + mb * 16 + grp * 4) = oacc[blk][mb];
     }
+  }
+}
+
+// ---- latent kernel, one workgroup per packed row (all 128 heads) -----------------
+//
+// The 64-vector kernel above needs two workgroups for a 128-head row, so each
+// 32-key tile is DMA'd into LDS twice and its value columns are read twice.
+// Here one workgroup of four waves takes the whole row:
+//  * QK: wave w scores vectors [32w, 32w+32) against all 32 keys of the tile
+//    over the 576 dims with 32x32x16 MFMAs, S^T = K Q^T (K rows straight from
+//    LDS, Q^T in 144 VGPRs); each K fragment feeds one MFMA.
+//  * The 32x32 output layout gives lane l sixteen keys of vector l%32:
+//    keys 8q + 4(l/32) + r (q, r < 4).  The PV MFMA's B operand (P^T, a
+//    16-key step) wants eight keys per lane, so step s takes the keys of
+//    q = 2s, 2s+1: each lane's own probabilities form its B operand with no
+//    lane exchange, provided the V^T operand uses the same key order.  The
+//    wave publishes its 32 vectors' probabilities (32 bytes per lane) for
+//    the other waves.
+//  * PV: wave w accumulates output columns [128w, 128w+128) for all 128
+//    vectors, O^T += V^T P^T: four 32-column blocks x four 32-vector blocks
+//    of 32x32x16 MFMAs (256 accumulators), V^T fragments from the row-major
+//    key rows through transposing LDS reads (keys 16s + 4(l/32) + r and
+//    16s + 8 + 4(l/32) + r of column l%32), each feeding four MFMAs.
+// Per 32-key tile and row the LDS carries 36 KB of DMA, 144 KB of K
+// fragment reads, 32 KB of V^T reads and 40 KB of probability exchange, about
+// a quarter less than two 64-vector workgroups, with half the MFMA
+// instructions.  Pipeline, softmax reference and rerun rule as above.
+// Power-of-two pages of at least 32 keys (a tile lies in one page).
+constexpr int kRowQT = 128;
+constexpr int kRowKRing = 3;          // K fragment registers (read that many minus one MFMAs ahead)
+constexpr int kRowXBytes = 2 * 4 * 2 * 64 * 16;   // probabilities [buffer][vector block][step][lane], 16 B
+constexpr int kRowRedBytes = 4 * 32 * 4;      // per-vector sums [vector block][32]
+constexpr int kRowQrBytes = 4 * 4 * 64 * 16;   // rope query fragments [wave][step][lane], 16 B
+constexpr int kRowLdsBytes = kMlaStages * kMlaStageBytes + kRowXBytes + kRowRedBytes + kPageWin * 4 + kRowQrBytes;
+static_assert(kRowLdsBytes <= 160 * 1024, "latent row kernel LDS");
+
+__device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item, unsigned char* smem) {
+  constexpr int kRing = kMlaStages * kMlaStageBytes;
+  float* red_l = reinterpret_cast<float*>(smem + kRing + kRowXBytes);
+  int* pwin = reinterpret_cast<int*>(smem + kRing + kRowXBytes + kRowRedBytes);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n32 = lane & 31;   // vector (QK) or column (PV) within a 32-block
+  const int hl = lane >> 5;    // lane half: which keys of a step
+
+  const int4 rec = p.items[item];
+  const int i = rec.x, tile = rec.y, sp = rec.z;
+  const int4 info = p.req_info[i];
+  const int ns = info.x;
+  const int row_start = p.cu[i];
+  const int c = p.ctx[i];
+  const int rl = tile / p.n_hb;          // the tile's packed row within the request
+  const int hb = tile % p.n_hb;          // its block of 128 heads
+  const int row = row_start + rl;
+  const int pos = c + rl;                // the row's position: keys 0..pos are visible
+  const int chunk = p.hdr[1];
+  const int kv_begin = win_origin(c, p.window) + sp * chunk;
+  const int kv_end = min(kv_begin + chunk, pos + 1);
+  const int P = p.page_size;
+  const int lim = kv_end - 1;            // last key this item may see
+  const int low = win_low(pos, p.window);
+
+  const int pg0 = kv_begin / P;
+  int npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
+  if (npg > kPageWin) {
+    if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
+    npg = kPageWin;
+  }
+  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
+  for (int x = tid; x < npg; x += 256) {
+    int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
+    if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+    pwin[x] = pg;
+  }
+
+  // query fragments: vector 32*wid + n32, dims 16*ks + 8*hl .. +7; the 512
+  // value dims in registers, the 64 rope dims (steps 32..35) in this wave's
+  // LDS area (each lane reads back only what it wrote)
+  const int head = hb * kRowQT + wid * 32 + n32;
+  const uint32_t qr_lds = (uint32_t)(uintptr_t)smem + kMlaStages * kMlaStageBytes + kRowXBytes + kRowRedBytes +
+                          kPageWin * 4 + (uint32_t)((wid * 4 * 64 + lane) * 16);
+  u32x4_t qf[32];
+  {
+    const bf16_t* qsrc = p.q + ((size_t)row * p.Hq + head) * kMlaD + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) qf[ks] = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 16);
+#pragma unroll
+    for (int ks = 32; ks < 36; ++ks)
+      *(lds_u32x4_t*)(size_t)(qr_lds + (ks - 32) * 1024) = *reinterpret_cast<const u32x4_t*>(qsrc + ks * 16);
+  }
+  auto is_full = [&](int t0) { return t0 + kNK - 1 <= lim && t0 >= low; };
+  wait_vm<0>();
+  __syncthreads();   // page window visible
+
+  const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
+  const uint32_t xbase = smem_lds + kRing;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wid * kMlaDmaPerWave * 1024);
+  const int cbase = wid * kMlaDmaPerWave * 64 + lane;
+  const int last = kv_end - 1;
+  uint32_t dma_off[kMlaDmaPerWave];
+#pragma unroll
+  for (int e = 0; e < kMlaDmaPerWave; ++e) {
+    const int cidx = cbase + e * 64;
+    const int r = cidx / kMlaChunksPerRow;
+    dma_off[e] = (uint32_t)(r * kMlaRowBytes + ((cidx - r * kMlaChunksPerRow) ^ lswz(r)) * 16);
+  }
+  struct DmaTile {
+    const void* base;
+    uint32_t lim;
+    uint32_t lds0;
+  };
+  auto dma_tile = [&](int t, int st, int pg) {
+    const int t0 = kv_begin + t * kNK;
+    DmaTile d;
+    d.base = uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
+                         ((size_t)pg * P + (t0 & (P - 1))) * kMlaRowBytes);
+    d.lim = (uint32_t)(min(last - t0, kNK - 1) * kMlaRowBytes + kMlaRowBytes - 16);
+    d.lds0 = wave_lds + st * kMlaStageBytes;
+    return d;
+  };
+  auto dma_one = [&](const DmaTile& d, int e) { dma16_s(min(dma_off[e], d.lim), d.base, d.lds0 + e * 1024); };
+  auto page_at = [&](int t) { return pwin[((kv_begin + t * kNK) >> p.log2P) - pg0]; };
+  auto issue = [&](int t, int st) {
+    const DmaTile d = dma_tile(t, st, __builtin_amdgcn_readfirstlane(page_at(t)));
+#pragma unroll
+    for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(d, e);
+  };
+
+  // QK fragment offsets: row n32, logical chunk 2*ks + hl; the swizzle
+  // touches the low three chunk bits, so the pattern repeats every 4 ks
+  uint32_t qk_off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qk_off[kk] = n32 * kMlaRowBytes + ((2 * kk + hl) ^ lswz(n32)) * 16;
+  // V^T reads: read `which` of step s covers keys 16s + 8*which + 4*hl + 0..3;
+  // lane r of each 16-lane group addresses row key0 + (r&15)/4 and columns
+  // c0 + 4*(r%4) with c0 = 128*wid + 32*cb + 16*((lane>>4)&1).  The row's
+  // swizzle does not depend on s, and the column chunk's low bits only on cb&1.
+  uint32_t pv_off[2][2];
+#pragma unroll
+  for (int wh = 0; wh < 2; ++wh) {
+    const int r = 8 * wh + 4 * hl + ((lane & 15) >> 2);
+#pragma unroll
+    for (int c1 = 0; c1 < 2; ++c1) {
+      const int lc = 4 * c1 + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);   // low chunk bits
+      pv_off[wh][c1] = r * kMlaRowBytes + ((lc ^ lswz(r)) + 16 * wid) * 16 + (lane & 1) * 8;
+    }
+  }
+  // probability exchange: [buffer][vector block][step][lane], 16 bytes each
+  auto xaddr = [&](int b, int vb, int s2) { return xbase + (uint32_t)((((b * 4 + vb) * 2 + s2) * 64 + lane) * 16); };
+
+  // K fragments (and, for the rope steps, Q fragments) read kRowKRing - 1
+  // MFMAs ahead; the scheduling barrier keeps each read before the MFMA it
+  // precedes (left alone, the compiler sinks it below, leaving one read in
+  // flight)
+  auto qk_tile = [&](uint32_t stg, f32x16_t& sc, auto&& between) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sc[j] = 0.f;
+    u32x4_t fa[kRowKRing], qa[kRowKRing];
+    uint32_t kb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kb[kk] = opaque(stg + qk_off[kk]);
+    const uint32_t qrb = opaque(qr_lds);
+    auto rd = [&](int kn) {
+      fa[kn % kRowKRing] = lds_b128(kb[kn & 3] + (kn >> 2) * 128);
+      if (kn >= 32) qa[kn % kRowKRing] = lds_b128(qrb + (kn - 32) * 1024);
+    };
+#pragma unroll
+    for (int ks = 0; ks < kRowKRing - 1; ++ks) rd(ks);
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) {
+      if (ks + kRowKRing - 1 < 36) rd(ks + kRowKRing - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      sc = mfma32(fa[ks % kRowKRing], ks < 32 ? qf[ks < 32 ? ks : 0] : qa[ks % kRowKRing], sc);
+      between(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto no_op = [](int) {};
+
+  f32x16_t oacc[4][4];   // [32-column block][32-vector block]
+  float m_ref = 0.f, l_part = 0.f, m_seen = -INFINITY, l_all = 0.f;
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[cb][vb][j] = 0.f;
+    l_part = 0.f;
+    m_seen = -INFINITY;
+
+    // scaled scores -> probabilities, in place, for this lane's 16 keys (key
+    // t0 + 8*(j/4) + 4*hl + j%4 of the tile).  A full tile needs no mask and
+    // folds the scale into one fma per key (its largest scaled score is the
+    // largest or the smallest raw score times the scale, by the scale's
+    // sign); an edge tile masks keys outside [low, lim].  The branch is
+    // uniform.
+    auto soft_all = [&](f32x16_t& sc, int t0, bool full) {
+      if (full) {
+        const float mr = -m_ref;
+        float mx = sc[0], mn = sc[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) {
+          mx = fmaxf(mx, sc[j]);
+          mn = fminf(mn, sc[j]);
+        }
+        m_seen = fmaxf(m_seen, (p.scale_log2 >= 0.f ? mx : mn) * p.scale_log2);
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          sc[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], p.scale_log2, mr));
+          sum += sc[j];
+        }
+        l_part += sum;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float v = sc[j] * p.scale_log2;
+          const int k = t0 + 8 * (j >> 2) + 4 * hl + (j & 3);
+          if (k > lim || k < low) v = -INFINITY;
+          m_seen = fmaxf(m_seen, v);
+          v = __builtin_amdgcn_exp2f(v - m_ref);   // exp2(-inf) = 0
+          l_part += v;
+          sc[j] = v;
+        }
+      }
+    };
+    // the PV B operands of steps 0 and 1 from the 16 probabilities
+    auto pack_p = [&](const f32x16_t& sc, u32x4_t (&out)[2]) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        out[s2] = u32x4_t{cvt_bf16x2(sc[8 * s2 + 0], sc[8 * s2 + 1]), cvt_bf16x2(sc[8 * s2 + 2], sc[8 * s2 + 3]),
+                          cvt_bf16x2(sc[8 * s2 + 4], sc[8 * s2 + 5]), cvt_bf16x2(sc[8 * s2 + 6], sc[8 * s2 + 7])};
+    };
+    auto soft = [&](f32x16_t& sc, int t0, bool full, u32x4_t (&out)[2]) {
+      soft_all(sc, t0, full);
+      pack_p(sc, out);
+    };
+
+    if (n_tiles > 0) {
+      issue(0, 0);
+      if (n_tiles > 1) issue(1, 1);
+      if (n_tiles > 1) wait_vm<kMlaDmaPerWave>(); else wait_vm<0>();
+      __syncthreads();
+      f32x16_t sc;
+      qk_tile(smem_lds, sc, no_op);
+      if (pass == 0) {
+        // reference: the max of the first tile's scaled scores (mask ignored)
+        float mx = sc[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sc[j]);
+        mx *= p.scale_log2;
+        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+      }
+      u32x4_t po[2];
+      soft(sc, kv_begin, is_full(kv_begin), po);
+      *(lds_u32x4_t*)(size_t)(xaddr(0, wid, 0)) = po[0];
+      *(lds_u32x4_t*)(size_t)(xaddr(0, wid, 1)) = po[1];
+    }
+
+    int pg_pref = 0;
+    if (n_tiles > 0) pg_pref = page_at(min(2, n_tiles - 1));
+    int st_cur = 0;
+    for (int t = 0; t < n_tiles; ++t) {
+      wait_vm<0>();
+      __syncthreads();
+      const DmaTile dnext =
+          dma_tile(min(t + 2, n_tiles - 1), (t + 2) % kMlaStages, __builtin_amdgcn_readfirstlane(pg_pref));
+      pg_pref = page_at(min(t + 3, n_tiles - 1));
+
+      const uint32_t stg = smem_lds + st_cur * kMlaStageBytes;
+      st_cur = (st_cur == kMlaStages - 1) ? 0 : st_cur + 1;
+      const uint32_t stg_next = smem_lds + st_cur * kMlaStageBytes;
+      const bool more = t + 1 < n_tiles;
+      const int t0n = kv_begin + (t + 1) * kNK;
+      const bool full_n = is_full(t0n);
+
+      f32x16_t sc;
+      // the next tile's DMA, one instruction every fourth QK step (issued
+      // all at once, or during PV, it measured slower)
+      auto spread_dma = [&](int ks) {
+        if ((ks & 3) == 0) dma_one(dnext, ks >> 2);
+      };
+      if (more) {
+        qk_tile(stg_next, sc, spread_dma);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(dnext, e);
+      }
+
+      // O^T[this wave's 128 columns][all vectors] += V^T P^T, step by step;
+      // the next tile's softmax runs between the MFMAs of step 1
+      u32x4_t pn[2];
+      const uint32_t xb = opaque(xaddr(t & 1, 0, 0));
+      uint32_t vbase[2][2];
+#pragma unroll
+      for (int wh = 0; wh < 2; ++wh)
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1) vbase[wh][c1] = opaque(stg + pv_off[wh][c1]);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4_t pb[4];
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) pb[vb] = lds_b128(xb + (vb * 2 + s2) * 1024);
+        auto rd_v = [&](int cb) {
+          const uint32_t c0 = s2 * 16 * kMlaRowBytes + (cb >> 1) * 128;
+          const uint2 lo = lds_tr16(vbase[0][cb & 1] + c0);
+          const uint2 hi = lds_tr16(vbase[1][cb & 1] + c0);
+          return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        };
+        u32x4_t va[2];
+        va[0] = rd_v(0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          if (cb + 1 < 4) va[(cb + 1) & 1] = rd_v(cb + 1);
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb) oacc[cb][vb] = mfma32(va[cb & 1], pb[vb], oacc[cb][vb]);
+          // the next tile's softmax as one block after four MFMAs of step 1
+          // (spread one key per MFMA, or sliced with a branch per slice, it
+          // measured slower: the scheduling barriers and branch boundaries
+          // cost the V^T reads their lead)
+          if (more && s2 == 1 && cb == 0) soft(sc, t0n, full_n, pn);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (more) {
+        *(lds_u32x4_t*)(size_t)(xaddr((t + 1) & 1, wid, 0)) = pn[0];
+        *(lds_u32x4_t*)(size_t)(xaddr((t + 1) & 1, wid, 1)) = pn[1];
+      }
+    }
+
+    wait_vm<0>();
+    // each vector's visible max and sum: the two lane halves hold its keys
+    const float m_all = fmaxf(m_seen, __shfl_xor(m_seen, 32));
+    l_all = l_part + __shfl_xor(l_part, 32);
+    const int need = (pass == 0 && m_all > -INFINITY && (m_all > m_ref + 32.f || m_all < m_ref - 64.f)) ? 1 : 0;
+    if (!__syncthreads_or(need)) break;
+    if (m_all > -INFINITY) m_ref = m_all;
+  }   // pass
+
+  // sums of every vector for the normalisation (block vb from wave vb)
+  if (hl == 0) red_l[wid * 32 + n32] = l_all;
+  if (hl == 0) {
+    if (ns == 1) {
+      if (p.lse) p.lse[(size_t)row * p.Hq + head] = l_all > 0.f ? (m_ref + log2f(l_all)) * kLn2 : -INFINITY;
+    } else {
+      const int slot = info.z + sp * info.w + tile;
+      if (slot >= 0 && slot < p.part_cap) {
+        float* pml = p.part_ml + ((size_t)slot * kRowQT + wid * 32 + n32) * 2;
+        pml[0] = l_all > 0.f ? m_ref : -INFINITY;
+        pml[1] = l_all;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) {
+    const int qv = vb * 32 + n32;
+    const int hd = hb * kRowQT + qv;
+    if (ns == 1) {
+      const float l_tot = red_l[qv];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16_t* dst = p.o + ((size_t)row * p.Hq + hd) * kMlaDv + wid * 128 + 4 * hl;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 pk;
+          pk.x = cvt_bf16x2(oacc[cb][vb][4 * q4 + 0] * inv, oacc[cb][vb][4 * q4 + 1] * inv);
+          pk.y = cvt_bf16x2(oacc[cb][vb][4 * q4 + 2] * inv, oacc[cb][vb][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(dst + 32 * cb + 8 * q4) = pk;
+        }
+    } else {
+      const int slot = info.z + sp * info.w + tile;
+      if (slot < 0 || slot >= p.part_cap) continue;
+      float* po_ = p.part_o + ((size_t)slot * kRowQT + qv) * kMlaDv + wid * 128 + 4 * hl;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4_t*>(po_ + 32 * cb + 8 * q4) =
+              f32x4_t{oacc[cb][vb][4 * q4], oacc[cb][vb][4 * q4 + 1], oacc[cb][vb][4 * q4 + 2],
+                      oacc[cb][vb][4 * q4 + 3]};
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_attn_mla_row(MainParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_item;
+  unsigned done = 0;
+  for (;;) {
+    const int item = next_item(p, &s_item, done);
+    if (item < 0) break;
+    attn_mla_row_item(p, item, smem);
   }
 }
 
@@ -1621,12 +2040,16 @@ __global__ __launch_bounds__(128) void k_attn_f32(F32Params p) {
 }
 
 // ---- host side -----------------------------------------------------------------
-bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnShape* sh, int* nw) {
+// row_tile (latent only): one tile per packed row and block of 128 heads,
+// for the row kernel (Hq a multiple of 128)
+bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnShape* sh, int* nw,
+                bool row_tile = false) {
   if (Hkv <= 0 || Hq % Hkv != 0) return false;
   const int G = Hq / Hkv;
   if (latent) {
     if (!(Dqk == 576 && Dv == 512 && Hkv == 1 && Hq % 64 == 0)) return false;
-    *nw = kMlaQT / 16;   // DMA-ring kernel: 64 query vectors per tile
+    if (row_tile && Hq % kRowQT != 0) return false;
+    *nw = (row_tile ? kRowQT : kMlaQT) / 16;   // 16 query vectors per block
   } else {
     if (!(Dqk == 128 && Dv == 128)) return false;
     if (!(G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return false;
@@ -1641,7 +2064,7 @@ bool pick_shape(int Hq, int Hkv, int Dqk, int Dv, int gamma, bool latent, AttnSh
   sh->RT = QT / sh->NH;
   sh->n_hb = G / sh->NH;
   sh->tpr_max = ((gamma + sh->RT - 1) / sh->RT) * Hkv * sh->n_hb;
-  sh->target = latent ? kTargetItemsLatent : kTargetItemsGqa;
+  sh->target = latent ? (row_tile ? kTargetItemsLatentRow : kTargetItemsLatent) : kTargetItemsGqa;
   return true;
 }
 
@@ -1762,7 +2185,10 @@ size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, in
   int nw;
   const bool latent = (Dqk == 576);
   if (!pick_shape(Hq, Hkv, Dqk, Dv, gamma, latent, &sh, &nw)) return 0;
-  return attn_layout(B, sh, Dv).total;
+  size_t need = attn_layout(B, sh, Dv).total;
+  if (latent && pick_shape(Hq, Hkv, Dqk, Dv, gamma, latent, &sh, &nw, true))
+    need = std::max(need, attn_layout(B, sh, Dv).total);   // the row kernel's plan
+  return need;
 }
 
 hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
@@ -1801,9 +2227,14 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     return hipGetLastError();
   }
 
+  // latent: the row kernel for dense attention over power-of-two pages of at
+  // least 32 keys with a multiple of 128 heads; the 64-vector kernel otherwise
+  const bool pow2_pages = (a.page_size & (a.page_size - 1)) == 0;
+  const bool row_kernel = latent && a.topk_idx == nullptr && pow2_pages && a.page_size >= 32 &&
+                          a.Hq % kRowQT == 0;
   AttnShape sh;
   int nw = 0;
-  if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw)) return hipErrorInvalidValue;
+  if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw, row_kernel)) return hipErrorInvalidValue;
   if (a.B > kPlanMaxB) return hipErrorInvalidValue;   // the plan caches one pair per request in LDS
   const AttnScratch L = attn_layout(a.B, sh, a.Dv);
   char* base = ws + kStatusBytes;
@@ -1882,7 +2313,15 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   mp.topk = a.topk_idx ? a.topk : 0;
   mp.ctr = pp.hdr + kHdrCtr;
 
-  if (latent) {
+  if (row_kernel) {
+    const void* kern = reinterpret_cast<const void*>(k_attn_mla_row);
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kRowLdsBytes);
+    if (e != hipSuccess) return e;
+    int grid = 0;
+    if ((e = persistent_grid(kern, 256, kRowLdsBytes, &grid)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_mla_row, dim3(grid), dim3(256), kRowLdsBytes, s, mp);
+    e = hipGetLastError();
+  } else if (latent) {
     const bool sparse = a.topk_idx != nullptr;
     const bool fast = !sparse && mp.log2P >= 5;   // power-of-two pages of at least 32 keys
     const void* kern = sparse ? reinterpret_cast<const void*>(k_attn_mla<false, true>)

@@ -10,6 +10,7 @@ namespace rv {
 
 constexpr int kStatusBytes = 256;        // status word + padding at workspace start
 constexpr int kTargetItemsLatent = 1024; // latent attention: work items aimed for per launch
+constexpr int kTargetItemsLatentRow = 512;  // latent row kernel (128-head tiles)
 constexpr int kTargetItemsGqa = 512;     // GQA attention: about two items per persistent workgroup
 constexpr size_t kPartBytes = 128u << 20; // split-KV partial outputs held in workspace
 constexpr int kPartSlotsMax = 8192;      // split-KV partial tiles at most

@@ -567,3 +567,18 @@ def test_negative_zero_confidence():
     for mode in ("compact", "cap_accept"):
         step, ref, _ = _full_parity(inp, mode, "bf16")
         assert int(pu.npi(step.w_commit)[17]) == 1
+
+
+def test_mla_negative_scale():
+    """A negative softmax scale (any finite scale is valid): the latent row
+    kernel's largest scaled score then comes from the smallest raw score."""
+    inp = pu.make_inputs("mla_bf16", B=3, V=500, H=256, ctx=("uniform", 60, 700))
+    inp["sm_scale"] = -inp["sm_scale"]
+    _full_parity(inp, "compact", "bf16")
+
+
+def test_mla_256_heads_two_head_blocks():
+    """256 query heads: each packed row is two 128-head tiles of the latent
+    row kernel, one of them on a split key range."""
+    inp = pu.make_inputs("mla_bf16", B=2, Hq=256, V=500, H=256, ctx=("uniform", 1500, 3000))
+    _full_parity(inp, "compact", "bf16")
