@@ -368,6 +368,59 @@ typedef struct {
 } rv_calib_args;
 rv_status rv_calibration(const rv_calib_args* a, void* stream);
 
+/* ---- observability: block-accept estimator -------------------------------- */
+/* DSpark-in-SGLang page, section A2 "the ceiling estimator under truncation":
+ * compact mode hides how many tokens the full block would have accepted; the
+ * estimator recovers that ceiling from the compact run itself, using the
+ * target's token usage and log-probabilities in later steps under the
+ * assumption that the anchor behaves alike with and without truncation, as
+ * an interval on the counterfactual tail.
+ *
+ * Called once per step after rv_lm_head_accept and before rv_compact_scatter
+ * (ctx = the step's anchor positions).  Per request i, with a = accept[i],
+ * w = w_verify[i], rows r0 = cu[i] ..:
+ *  - an open probe (next tail position `pos`) is resolved by the rows k in
+ *    0..a whose predicted position ctx+k+1 equals pos, in order: verdict
+ *    alpha = (pred[r0+k] == tail draft) under greedy, min(1, p(d)/q(d))
+ *    under rejection (p = softmax of logits row r0+k, q = the censored
+ *    step's draft distribution, stored as log q); S *= alpha; E += S; the
+ *    probe closes when its tail is exhausted or S == 0, adding
+ *    (w_censored - 1) + E to `sum`, setting `last` and counting it;
+ *  - a probe whose next position is <= ctx[i] (steps skipped) is dropped;
+ *  - with no probe open and a censored request (w < gamma, a == w - 1), a
+ *    probe opens on drafts d_w .. d_{gamma-1} (positions ctx+w ..) and row
+ *    r0+a resolves its first draft at once.
+ * The open probe's interval is [base + E, base + E + S * left].
+ *
+ * State: caller-owned device memory of rv_estimator_state_bytes(B, gamma)
+ * bytes, zero-filled before the first step (no probe open), structure of
+ * arrays with G = gamma-1: int32 pos[B], left[B], done[B], base[B],
+ * count[B]; float S[B], E[B], last[B]; double sum[B]; int32 tok[B][G];
+ * float lq[B][G] (byte offsets 0, 4B, 8B, 12B, 16B, 20B, 24B, 28B, 32B,
+ * 40B, 40B + 4BG).
+ * Host errors: NULL required pointer (pred for greedy; logits and q_rows for
+ * rejection), bad B/gamma, rows_cap < B*gamma, V < 1, unknown rule, small
+ * workspace.  Device errors: BAD_WINDOW (window or accept out of range: that
+ * request is skipped), BAD_TOKEN (a tail draft outside [0, V) under
+ * rejection: its verdict is 0). */
+typedef struct {
+  const int32_t* cu;         /* [B+1] this step's packing */
+  const int32_t* w_verify;   /* [B] */
+  const int32_t* accept;     /* [B] from rv_lm_head_accept */
+  const int32_t* drafts;     /* [B][gamma-1] this step's drafts */
+  const int32_t* ctx;        /* [B] anchor positions (before the scatter) */
+  const int32_t* pred;       /* [rows_cap] row predictions (greedy) */
+  const float* logits;       /* [rows_cap][V] (rejection) */
+  const float* q_rows;       /* [B][gamma-1][V] draft distributions (rejection) */
+  int32_t B, gamma, rows_cap, V, rule;
+  int32_t _pad0;
+  void* state;               /* in/out, rv_estimator_state_bytes(B, gamma) */
+  void* workspace;           /* status word at its start */
+  size_t workspace_bytes;
+} rv_estimate_args;
+rv_status rv_estimator_state_bytes(int32_t B, int32_t gamma, size_t* bytes);
+rv_status rv_block_accept_estimate(const rv_estimate_args* a, void* stream);
+
 /* ---- cost-table profiling (outside the per-step path) -------------------- */
 /* DSpark-in-SGLang page, section A2 "cost-table profiling and modelling"
  * (with the additive model of section 速读): the step time
@@ -430,7 +483,7 @@ rv_status rv_compact_scatter(const rv_scatter_args* a, void* stream);
 /* ---- ABI self-description ----------------------------------------------- */
 /* Fills out[0] = sizeof(struct), out[1..] = offsetof of each field in
  * declaration order, for struct `which` (0 schedule, 1 pack, 2 attn, 3 lm,
- * 4 scatter, 5 dims, 6 calibration).  Returns the number of values written, or -1 if `cap`
+ * 4 scatter, 5 dims, 6 calibration, 7 estimate).  Returns the number of values written, or -1 if `cap`
  * is too small or `which` unknown.  Host-only; lets a binding verify its
  * struct mirror. */
 int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap);

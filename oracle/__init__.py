@@ -26,6 +26,7 @@ Five stages, one module each:
 ``dense``              fixed-shape padded verify (the static-graph baseline)
 ``cost_fit``           least-squares fit of the step-time model's table
 ``calibration``        per-request confidence statistics and ECE
+``estimator``          block-accept estimator of the ceiling truncation hides
 =====================  ======================================================
 
 Every array argument is a numpy array; bf16 inputs arrive as their exact
@@ -43,6 +44,7 @@ from .scatter import compact_scatter
 from .dense import dense_padded_verify
 from .cost_fit import fit_cost_model, cost_tables
 from .calibration import calibration
+from .estimator import new_state as estimator_state, estimate_update, open_interval
 
 __all__ = [
     "STATIC", "COMPACT", "CAP_ACCEPT", "NO_TRIM", "FIXED_SHIFT",
@@ -51,4 +53,5 @@ __all__ = [
     "GREEDY", "REJECTION", "accept_greedy", "accept_rejection",
     "residual_sample", "compact_scatter", "dense_padded_verify",
     "fit_cost_model", "cost_tables", "calibration",
+    "estimator_state", "estimate_update", "open_interval",
 ]

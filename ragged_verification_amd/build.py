@@ -20,8 +20,9 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "librv.so")
 
 SOURCES = ["rv_api.hip", "k_schedule.hip", "k_pack.hip", "k_attn.hip", "k_lm.hip", "k_scatter.hip",
-           "k_calib.hip", "rv_noalloc.hip"]
-EXTRA = {"k_schedule.hip": ["-ffp-contract=off"], "k_calib.hip": ["-ffp-contract=off"]}
+           "k_calib.hip", "k_estimate.hip", "rv_noalloc.hip"]
+EXTRA = {"k_schedule.hip": ["-ffp-contract=off"], "k_calib.hip": ["-ffp-contract=off"],
+         "k_estimate.hip": ["-ffp-contract=off"]}
 ARCH = "gfx950"
 
 

@@ -176,6 +176,23 @@ rv_status rv_calibration(const rv_calib_args* a, void* stream) {
   return hip_status(launch_calibration(*a, static_cast<hipStream_t>(stream)));
 }
 
+rv_status rv_estimator_state_bytes(int32_t B, int32_t gamma, size_t* bytes) {
+  if (!bytes || !block_ok(B, gamma)) return RV_ERR_INVALID_ARG;
+  *bytes = estimator_state_bytes(B, gamma);
+  return RV_OK;
+}
+
+rv_status rv_block_accept_estimate(const rv_estimate_args* a, void* stream) {
+  if (!a || !a->cu || !a->w_verify || !a->accept || !a->drafts || !a->ctx || !a->state) return RV_ERR_INVALID_ARG;
+  if (a->rule != RV_GREEDY && a->rule != RV_REJECTION) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_GREEDY && !a->pred) return RV_ERR_INVALID_ARG;
+  if (a->rule == RV_REJECTION && (!a->logits || !a->q_rows)) return RV_ERR_INVALID_ARG;
+  if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
+  if ((long long)a->rows_cap < (long long)a->B * a->gamma || a->V < 1) return RV_ERR_INVALID_ARG;
+  if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
+  return hip_status(launch_estimate(*a, static_cast<hipStream_t>(stream)));
+}
+
 rv_status rv_fit_cost_model(const double* bs, const double* M, const double* t, int32_t n, double* coef,
                             double* alpha, int32_t alpha_len, double* theta, int32_t theta_len) {
   if (!bs || !M || !t || !coef || n < 3) return RV_ERR_INVALID_ARG;
@@ -307,6 +324,16 @@ int32_t rv_abi_layout(int32_t which, int64_t* out, int32_t cap) {
                      RV_OFF(S, bin_count), RV_OFF(S, bin_match), RV_OFF(S, bin_conf_fx), RV_OFF(S, ece),
                      RV_OFF(S, req_verified), RV_OFF(S, req_matched), RV_OFF(S, workspace),
                      RV_OFF(S, workspace_bytes)};
+      n = sizeof(t) / sizeof(t[0]);
+      for (int k = 0; k < n; ++k) v[k] = t[k];
+      break;
+    }
+    case 7: {
+      typedef rv_estimate_args S;
+      int64_t t[] = {sizeof(S), RV_OFF(S, cu), RV_OFF(S, w_verify), RV_OFF(S, accept), RV_OFF(S, drafts),
+                     RV_OFF(S, ctx), RV_OFF(S, pred), RV_OFF(S, logits), RV_OFF(S, q_rows), RV_OFF(S, B),
+                     RV_OFF(S, gamma), RV_OFF(S, rows_cap), RV_OFF(S, V), RV_OFF(S, rule), RV_OFF(S, _pad0),
+                     RV_OFF(S, state), RV_OFF(S, workspace), RV_OFF(S, workspace_bytes)};
       n = sizeof(t) / sizeof(t[0]);
       for (int k = 0; k < n; ++k) v[k] = t[k];
       break;

@@ -108,6 +108,8 @@ hipError_t launch_lm(const rv_lm_args& a, void* part, int32_t* status, hipStream
 rv_status lm_args_check(const rv_lm_args* a);
 hipError_t launch_scatter(const rv_scatter_args& a, hipStream_t s);
 hipError_t launch_calibration(const rv_calib_args& a, hipStream_t s);
+hipError_t launch_estimate(const rv_estimate_args& a, hipStream_t s);
+size_t estimator_state_bytes(int B, int gamma);
 hipError_t launch_clear_status(void* ws, hipStream_t s);
 
 // host-side sizing helpers shared by the API layer and the launchers

@@ -184,6 +184,15 @@ class VerifyStep:
                           req_verified=c["req_verified"], req_matched=c["req_matched"], stream=self.stream)
         return c
 
+    def block_accept_estimate(self, state):
+        """One step of the block-accept estimator (rv_block_accept_estimate),
+        between lm() and scatter(): ``state`` is a zero-filled uint8 tensor of
+        rv.rv_estimator_state_bytes(B, gamma) bytes kept across steps."""
+        i = self.inp
+        rv.rv_block_accept_estimate(self.cu, self.w_verify, self.accept, i["drafts"], self.ctx, self.rule, state,
+                                    self.workspace, pred=self.pred if self.rule == rv.RV_GREEDY else None,
+                                    logits=self.logits, q_rows=i.get("q_rows"), stream=self.stream)
+
     # ---- HIP graphs ------------------------------------------------------------
     def capture(self):
         """Record the step into two HIP graphs on a side stream: ``front``

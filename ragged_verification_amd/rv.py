@@ -86,11 +86,17 @@ class CalibArgs(ctypes.Structure):
                 ("workspace", _vp), ("workspace_bytes", _sz)]
 
 
-STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims, CalibArgs]
+class EstimateArgs(ctypes.Structure):
+    _fields_ = [("cu", _vp), ("w_verify", _vp), ("accept", _vp), ("drafts", _vp), ("ctx", _vp), ("pred", _vp),
+                ("logits", _vp), ("q_rows", _vp), ("B", _i32), ("gamma", _i32), ("rows_cap", _i32), ("V", _i32),
+                ("rule", _i32), ("_pad0", _i32), ("state", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+
+
+STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims, CalibArgs, EstimateArgs]
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
            "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
            "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model", "rv_calibration",
-           "rv_lm_head_accept_noalloc"]
+           "rv_lm_head_accept_noalloc", "rv_estimator_state_bytes", "rv_block_accept_estimate"]
 
 _LIB = None
 
@@ -119,10 +125,13 @@ def load(path=LIB_PATH):
     lib.rv_clear_status.argtypes = [_vp, _vp]
     for name, st in (("rv_schedule", ScheduleArgs), ("rv_pack", PackArgs), ("rv_verify_attn", AttnArgs),
                      ("rv_lm_head_accept", LmArgs), ("rv_compact_scatter", ScatterArgs),
-                     ("rv_calibration", CalibArgs), ("rv_lm_head_accept_noalloc", LmArgs)):
+                     ("rv_calibration", CalibArgs), ("rv_lm_head_accept_noalloc", LmArgs),
+                     ("rv_block_accept_estimate", EstimateArgs)):
         fn = getattr(lib, name)
         fn.restype = _i32
         fn.argtypes = [ctypes.POINTER(st), _vp]
+    lib.rv_estimator_state_bytes.restype = _i32
+    lib.rv_estimator_state_bytes.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
     lib.rv_lm_tiled_weight_bytes.restype = _i32
     lib.rv_lm_tiled_weight_bytes.argtypes = [_i32, _i32, _i32, ctypes.POINTER(_sz)]
     lib.rv_lm_tile_weight.restype = _i32
@@ -269,6 +278,39 @@ def rv_calibration(conf, drafts, pred, cu, w_verify, n_bins, bin_count, bin_matc
                   req_matched=_ptr(req_matched, torch.int32, "req_matched"),
                   workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
     _check("rv_calibration", load().rv_calibration(ctypes.byref(a), _stream(stream)))
+
+
+def rv_estimator_state_bytes(B, gamma):
+    n = _sz(0)
+    _check("rv_estimator_state_bytes", load().rv_estimator_state_bytes(B, gamma, ctypes.byref(n)))
+    return n.value
+
+
+def estimator_state_views(state, B, gamma):
+    """Views of the estimator state buffer (uint8 tensor) by field, per the
+    layout rv_block_accept_estimate documents."""
+    G = gamma - 1
+    i32 = lambda off, n: state[off:off + 4 * n].view(torch.int32)
+    f32 = lambda off, n: state[off:off + 4 * n].view(torch.float32)
+    return {"pos": i32(0, B), "left": i32(4 * B, B), "done": i32(8 * B, B), "base": i32(12 * B, B),
+            "count": i32(16 * B, B), "S": f32(20 * B, B), "E": f32(24 * B, B), "last": f32(28 * B, B),
+            "sum": state[32 * B:40 * B].view(torch.float64), "tok": i32(40 * B, B * G).view(B, G),
+            "lq": f32(40 * B + 4 * B * G, B * G).view(B, G)}
+
+
+def rv_block_accept_estimate(cu, w_verify, accept, drafts, ctx, rule, state, workspace, pred=None, logits=None,
+                             q_rows=None, stream=None):
+    B, g1 = drafts.shape
+    rows_cap = pred.numel() if pred is not None else logits.shape[0]
+    V = logits.shape[1] if logits is not None else 1
+    a = EstimateArgs(cu=_ptr(cu, torch.int32, "cu"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+                     accept=_ptr(accept, torch.int32, "accept"), drafts=_ptr(drafts, torch.int32, "drafts"),
+                     ctx=_ptr(ctx, torch.int32, "ctx"), pred=_ptr(pred, torch.int32, "pred"),
+                     logits=_ptr(logits, torch.float32, "logits"), q_rows=_ptr(q_rows, torch.float32, "q_rows"),
+                     B=B, gamma=g1 + 1, rows_cap=rows_cap, V=V, rule=rule, state=_ptr(state, name="state"),
+                     workspace=_ptr(workspace, name="workspace"),
+                     workspace_bytes=workspace.numel() * workspace.element_size())
+    _check("rv_block_accept_estimate", load().rv_block_accept_estimate(ctypes.byref(a), _stream(stream)))
 
 
 def rv_fit_cost_model(bs, M, t, alpha_len=0, theta_len=0):

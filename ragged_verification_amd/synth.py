@@ -202,6 +202,57 @@ def topk_indices(ctx, gamma, K, seed, device="cpu"):
     return out.to(device)
 
 
+def _plant(wl, W, x, conf, targets, gd):
+    """Hidden states whose target argmax at block position k is targets[:, k]
+    (h = x + beta * W[t] / |W[t]|), and drafts d_j equal to targets[:, j-1]
+    with probability conf (or conf ** plant_power), else a uniform other
+    token."""
+    B, gamma = targets.shape
+    V, H = W.shape
+    Wt = W[targets.reshape(-1)].to(torch.float32)
+    unit = Wt / Wt.norm(dim=1, keepdim=True)
+    hidden = (x.reshape(B * gamma, H) + wl.plant_beta * unit).reshape(B, gamma, H).to(W.dtype)
+    coin = torch.rand((B, gamma - 1), generator=gd, device=W.device, dtype=torch.float64)
+    match_p = conf.to(torch.float64)
+    if wl.plant_power != 1.0:   # miscalibrated confidences (observability tests)
+        match_p = match_p ** wl.plant_power
+    correct = coin < match_p
+    other = torch.randint(0, V - 1, (B, gamma - 1), generator=gd, device=W.device, dtype=torch.int64)
+    t_prev = targets[:, :gamma - 1]
+    other = other + (other >= t_prev).to(torch.int64)
+    drafts = torch.where(correct, t_prev, other)
+    return hidden, drafts, correct
+
+
+def target_sequences(wl, B, length, seed):
+    """A fixed target continuation per request (int64 [B, length]): the token
+    the target predicts at every absolute position, for multi-step greedy
+    trajectories in which truncated and full-block verification see the same
+    target (token at position P = seq[i, P])."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return torch.randint(0, wl.V, (B, length), generator=g, dtype=torch.int64)
+
+
+def trajectory_step(wl, W, ctx, seq, seed, device="cpu"):
+    """Greedy step inputs on a target continuation: confidences, drafts
+    d_j (proposals for positions ctx + j, equal to seq with probability conf)
+    and hidden states planted so that block position k predicts
+    seq[i, ctx_i + k + 1].  Returns a dict of conf (f32), drafts (i32),
+    hidden_block and targets [B, gamma]."""
+    B = ctx.numel()
+    gamma = wl.gamma
+    S = _Seeds(seed, device)
+    c = ctx.to("cpu").to(torch.int64)
+    idx = c[:, None] + 1 + torch.arange(gamma)[None, :]
+    targets = torch.gather(seq, 1, idx).to(device)
+    conf = _confidences(wl, B, S.gen("conf"), device)
+    x = torch.randn((B, gamma, wl.H), generator=S.gen("hidden"), device=device, dtype=torch.float32)
+    hidden, drafts, _ = _plant(wl, W, x, conf, targets, S.gen("drafts"))
+    return {"conf": conf.contiguous(), "drafts": drafts.to(torch.int32).contiguous(), "hidden_block": hidden,
+            "targets": targets}
+
+
 def make_inputs(wl, device="cpu", B=None, seed=None):
     """Draw every input of one verify step for workload ``wl``.
 
@@ -255,19 +306,7 @@ def make_inputs(wl, device="cpu", B=None, seed=None):
         conf = _confidences(wl, B, S.gen("conf"), dev)
         targets = torch.randint(0, V, (B, gamma), generator=S.gen("targets"), device=dev,
                                 dtype=torch.int64)
-        Wt = W[targets.reshape(-1)].to(torch.float32)
-        unit = Wt / Wt.norm(dim=1, keepdim=True)
-        hidden = (x.reshape(B * gamma, H) + wl.plant_beta * unit).reshape(B, gamma, H).to(dt)
-        gd = S.gen("drafts")
-        coin = torch.rand((B, gamma - 1), generator=gd, device=dev, dtype=torch.float64)
-        match_p = conf.to(torch.float64)
-        if wl.plant_power != 1.0:   # miscalibrated confidences (observability tests)
-            match_p = match_p ** wl.plant_power
-        correct = coin < match_p
-        other = torch.randint(0, V - 1, (B, gamma - 1), generator=gd, device=dev, dtype=torch.int64)
-        t_prev = targets[:, :gamma - 1]
-        other = other + (other >= t_prev).to(torch.int64)
-        drafts = torch.where(correct, t_prev, other)
+        hidden, drafts, correct = _plant(wl, W, x, conf, targets, S.gen("drafts"))
         out.update(targets=targets, correct=correct)
     else:
         hidden = x.to(dt)
