@@ -225,7 +225,7 @@ def sweep(steps, warmup):
         torch.cuda.empty_cache()
 
 
-def fit_cost(steps, warmup):
+def fit_cost(steps, warmup, out_path=None):
     """Cost-table profiling on this GPU: the mixed-confidence workload at every
     batch size of the sweep, static and compact (the sweep's cost table), gives
     samples (bs, M, five-stage ms); rv_fit_cost_model fits
@@ -273,9 +273,30 @@ def fit_cost(steps, warmup):
         print(json.dumps(out, default=_json_default), flush=True)
         del step, inp
         torch.cuda.empty_cache()
-    print(json.dumps({"fit": {"bias_ms": coef[0], "alpha_ms_per_request": coef[1], "theta_ms_per_row": coef[2],
-                              "samples": len(samples), "rms_residual_ms": float(np.sqrt(np.mean(np.square(resid)))),
-                              "max_abs_residual_ms": float(np.max(np.abs(resid)))}}), flush=True)
+    fit = {"bias_ms": coef[0], "alpha_ms_per_request": coef[1], "theta_ms_per_row": coef[2],
+           "samples": len(samples), "rms_residual_ms": float(np.sqrt(np.mean(np.square(resid)))),
+           "max_abs_residual_ms": float(np.max(np.abs(resid)))}
+    print(json.dumps({"fit": fit}), flush=True)
+    if out_path:
+        # the recorded samples, the fit and the scheduler's tables, for
+        # --cost-table to load
+        with open(out_path, "w") as f:
+            json.dump({"workload": "sweep_gqa", "device": torch.cuda.get_device_name(0),
+                       "samples": [{"bs": b, "M": m, "ms": t} for b, m, t in samples], "fit": fit,
+                       "bias": coef[0], "alpha": alpha, "theta": theta}, f)
+        log(f"cost table written to {out_path}")
+
+
+def load_cost_table(path, inp):
+    """Replace the workload's cost table with one written by --fit-cost."""
+    d = json.load(open(path))
+    B, gamma = inp["B"], inp["gamma"]
+    if len(d["alpha"]) <= B or len(d["theta"]) <= B * gamma:
+        raise SystemExit(f"{path}: tables cover bs < {len(d['alpha'])}, M < {len(d['theta'])}; "
+                         f"this workload needs bs = {B}, M up to {B * gamma}")
+    inp["cost_bias"] = float(d["bias"])
+    inp["cost_alpha"] = torch.tensor(d["alpha"], dtype=torch.float64, device="cuda")
+    inp["cost_theta"] = torch.tensor(d["theta"], dtype=torch.float64, device="cuda")
 
 
 def cpu_baseline(inp, step, n_req=130):
@@ -389,6 +410,10 @@ def main():
                     help="also time each mode replayed from HIP graphs (VerifyStep.capture)")
     ap.add_argument("--fit-cost", action="store_true",
                     help="only run cost-table profiling: fit the step-time model on this GPU and rerun compact with it")
+    ap.add_argument("--cost-table-out", default=None, metavar="PATH",
+                    help="with --fit-cost: write the samples, the fit and the scheduler's tables to PATH (JSON)")
+    ap.add_argument("--cost-table", default=None, metavar="PATH",
+                    help="schedule with a cost table written by --fit-cost --cost-table-out")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the mixed-confidence batch sweep (one JSON line per batch size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -409,12 +434,14 @@ def main():
         sweep(args.steps, args.warmup)
         return
     if args.fit_cost:
-        fit_cost(args.steps, args.warmup)
+        fit_cost(args.steps, args.warmup, args.cost_table_out)
         return
     wl = synth.workload(args.workload)
     t0 = time.time()
     inp = synth.make_inputs(wl, device="cuda")
     torch.cuda.synchronize()
+    if args.cost_table:
+        load_cost_table(args.cost_table, inp)
     log(f"inputs for {wl.name} (B={wl.B}) in {time.time() - t0:.1f}s, "
         f"KV {inp['k_cache'].numel() * 2 / 1e9:.2f} GB, W {inp['W'].numel() * 2 / 1e9:.2f} GB")
 
