@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from ragged_verification_amd import rv, synth  # noqa: E402
-from ragged_verification_amd.pipeline import VerifyStep  # noqa: E402
+from ragged_verification_amd.pipeline import OverlapLoop, VerifyStep  # noqa: E402
 
 METRIC = "packed verify tok/s + accepted tok/s at B=256,γ=8; % of HBM/MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
@@ -299,6 +299,55 @@ def load_cost_table(path, inp):
     inp["cost_theta"] = torch.tensor(d["theta"], dtype=torch.float64, device="cuda")
 
 
+def overlap_bench(steps, warmup, batches=(1, 8, 32, 256)):
+    """Steps per second of a multi-step loop with the scheduler overlapped
+    (OverlapLoop: the next step's schedule on a side stream during this
+    step's attention and LM head) against the same loop in order on one
+    stream, at several batch sizes of the GQA sweep shapes, eager and from one
+    captured graph (which leaves only the device's critical path).  The step
+    inputs cycle through four draws along a target continuation.  One JSON
+    line per batch size."""
+    gamma = 8
+    for B in batches:
+        n = warmup + steps
+        wl = synth.workload("sweep_gqa", B=B, spare_tokens=(n + 2) * gamma, tiers=())
+        inp = synth.make_inputs(wl, device="cuda", B=B)
+        seq = synth.target_sequences(wl, B, int(inp["ctx"].max()) + (n + 2) * gamma + 2, seed=3)
+        draws = [synth.trajectory_step(wl, inp["W"], inp["ctx"], seq, seed=40 + k, device="cuda") for k in range(4)]
+        per_step = [draws[s % 4] for s in range(n)]
+        out = {"workload": "sweep_gqa", "B": B, "steps": steps}
+        for overlap in (False, True):
+            loop = OverlapLoop(inp, per_step, overlap=overlap, hist_cap=(n + 1) * gamma, r2t_extra=(n + 2) * gamma)
+            loop.run(n=warmup)
+            torch.cuda.synchronize()
+            r = {}
+            for how in ("eager", "graph"):
+                if how == "graph":
+                    loop.capture(n=steps)
+                loop.vs.restore()
+                torch.cuda.synchronize()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                t0 = time.perf_counter()
+                a.record()
+                if how == "graph":
+                    loop.replay()
+                else:
+                    loop.run(n=steps)
+                b.record()
+                t_issue = time.perf_counter() - t0
+                torch.cuda.synchronize()
+                assert loop.status() == 0
+                r[how] = {"ms_per_step": a.elapsed_time(b) / steps, "host_issue_ms_per_step": 1e3 * t_issue / steps}
+            out["overlapped" if overlap else "in_order"] = r
+            del loop
+        out["speedup_graph"] = out["in_order"]["graph"]["ms_per_step"] / out["overlapped"]["graph"]["ms_per_step"]
+        out["speedup_eager"] = out["in_order"]["eager"]["ms_per_step"] / out["overlapped"]["eager"]["ms_per_step"]
+        print(json.dumps(out), flush=True)
+        del inp
+        torch.cuda.empty_cache()
+
+
 def cpu_baseline(inp, step, n_req=130):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     schedule and pack for the whole batch, then attention, LM head, accept and
@@ -414,6 +463,9 @@ def main():
                     help="with --fit-cost: write the samples, the fit and the scheduler's tables to PATH (JSON)")
     ap.add_argument("--cost-table", default=None, metavar="PATH",
                     help="schedule with a cost table written by --fit-cost --cost-table-out")
+    ap.add_argument("--overlap", action="store_true",
+                    help="only time the multi-step loop with the scheduler overlapped against in order (batch 1, 8, 32)")
+    ap.add_argument("--overlap-batches", default="1,8,32,256", help="batch sizes for --overlap")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the mixed-confidence batch sweep (one JSON line per batch size)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -435,6 +487,9 @@ def main():
         return
     if args.fit_cost:
         fit_cost(args.steps, args.warmup, args.cost_table_out)
+        return
+    if args.overlap:
+        overlap_bench(args.steps, args.warmup, tuple(int(b) for b in args.overlap_batches.split(",")))
         return
     wl = synth.workload(args.workload)
     t0 = time.time()

@@ -8,14 +8,28 @@
 // scheduler's argmax trades expected accepted tokens against that marginal
 // cost.
 //
-// One workgroup of 1024 threads does the whole batch in LDS (at most 4096
-// candidates): survival products, a bitonic sort of the candidates by
-// (survival desc, request asc, position asc), an int64 fixed-point prefix sum
-// of the ranked survivals, the ratio E(K)/T(K) for every K, and the first
-// arg-max.  Every operation is order independent or sequential per request,
-// so the result is bit-identical to a sequential evaluation: fp64 products in
-// position order, floor(S * 2^40) as int64, exact integer sums, two fp64 adds
-// and one IEEE fp64 divide per K.  Contraction is disabled in this file.
+// One workgroup (1 to 16 waves, at most 4096 candidates):
+//  1. survival products, sequential per request in fp64 (-0.0 made +0.0);
+//  2. a bitonic sort of the survivals alone, descending, 2 to 8 per lane in
+//     registers: strides inside a lane are fmax/fmin pairs, strides up to 63
+//     lanes go through DPP, swizzles or permutes, strides across waves
+//     through LDS (one barrier each).  A single wave sorts up to 64 survivals;
+//     from 65 on the work is spread over at least four waves, one per SIMD;
+//  3. the fixed-point prefix sums of floor(S * 2^40) in ranked order, the
+//     ratio E(K)/T(K) for every K, and the first arg-max K*;
+//  4. the windows: candidates whose survival exceeds the K*-th largest S*
+//     are in; of those equal to it, the first ones in (request, position)
+//     order fill the remaining places (a scan over requests, only when S* is
+//     not unique), which is the order the ranking (S desc, request asc,
+//     position asc) gives equal survivals.
+// Equal survivals have equal fixed-point values, so ranking survivals
+// without candidate ids leaves every E(K) unchanged.  Every operation is
+// order independent or sequential per request, so the result is
+// bit-identical to a sequential evaluation: fp64 products in position order,
+// floor(S * 2^40), exact sums (fp64 adds of integers whose partial sums stay
+// at most 2^53, int64 in the full-block modes), two fp64 adds and one IEEE
+// fp64 divide per K.
+// Contraction is disabled in this file.
 #pragma clang fp contract(off)
 
 #include "rv_common.h"
@@ -23,9 +37,10 @@
 namespace rv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kMaxCand = RV_MAX_SCHED_CANDIDATES;
+constexpr int kMaxCand = RV_MAX_SCHED_CANDIDATES;    // 8 waves x 64 lanes x 8
 constexpr int kShift = 40;
+constexpr double kFix = 1099511627776.0;            // 2^40
+static_assert(kMaxCand == 8 * 64 * 8, "candidate limit is the 8-wave sort");
 
 struct SchedParams {
   const float* conf;
@@ -42,65 +57,182 @@ struct SchedParams {
 
 __device__ inline long long fixed_of(double s) {
   // s in [0,1]: s * 2^40 is exact, floor of a non-negative value is a cast
-  return static_cast<long long>(floor(s * 1099511627776.0));
+  return static_cast<long long>(floor(s * kFix));
 }
 
-// Inclusive scan of one int64 per thread: wave shuffles, then one pass over
-// the 16 wave totals (integer adds, so the order does not matter).  *total
-// gets the workgroup total.  buf holds kThreads / 64 values.
-__device__ long long block_scan_incl(long long v, long long* buf, long long* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// the value lane (lane ^ M) holds, M < 64
+template <int M>
+__device__ inline uint32_t xchg32(uint32_t v) {
+  const int x = static_cast<int>(v);
+  if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);    // quad_perm 1,0,3,2
+  else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); // quad_perm 2,3,0,1
+  else if constexpr (M == 3) return __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true); // quad_perm 3,2,1,0
+  else if constexpr (M == 7) return __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true); // row_half_mirror
+  else if constexpr (M == 15) return __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true); // row_mirror
+  else if constexpr (M < 32) return __builtin_amdgcn_ds_swizzle(x, 0x1F | (M << 10));   // xor within 32
+  else return __builtin_amdgcn_ds_bpermute(static_cast<int>(((threadIdx.x & 63) ^ M) << 2), x);
+}
+template <int M>
+__device__ inline double xchg(double v) {
+  const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = xchg32<M>(static_cast<uint32_t>(b));
+  const uint32_t hi = xchg32<M>(static_cast<uint32_t>(b >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Sort keys are the survivals themselves (S in [0, 1], -0.0 made +0.0, no
+// NaN), padding -1.  One compare-exchange stage of the descending bitonic
+// network over positions p = I * g + j (g = thread, j < I in registers):
+// p meets p ^ m and the lower position keeps the larger key; m = size - 1 is
+// the mirror stage that starts the merge of a size block, a power of two m
+// a half-cleaner.
+template <int W, int I, int m>
+__device__ inline void stage(double (&v)[I], double* xbuf, int& flip) {
+  if constexpr (m < I) {
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const long long u = __shfl_up(v, off);
-    if (lane >= off) v += u;
+    for (int j = 0; j < I; ++j) {
+      const int jj = j ^ m;
+      if (j < jj) {
+        const double a = v[j], b = v[jj];
+        v[j] = fmax(a, b);
+        v[jj] = fmin(a, b);
+      }
+    }
+  } else {
+    constexpr int lgI = (I == 2) ? 1 : (I == 4) ? 2 : (I == 8) ? 3 : 4;
+    constexpr int M = m >> lgI;            // lane distance
+    constexpr int jm = m & (I - 1);        // 0 (half-cleaner) or I-1 (mirror)
+    constexpr int hb = (jm == I - 1) ? (M + 1) >> 1 : M;   // the bit that orders the pair
+    const bool upper = (threadIdx.x & hb) != 0;
+    double o[I];
+    if constexpr (M < 64) {
+#pragma unroll
+      for (int j = 0; j < I; ++j) o[j] = xchg<M>(v[j ^ jm]);
+    } else {
+      // across waves: every lane publishes its keys, one barrier, the partner
+      // lane's keys are read back (two buffers in turn, so the next such stage
+      // may write before the last reader of this one is done)
+      double* b = xbuf + (flip & 1) * (64 * W * I);
+      ++flip;
+      double2* mine = reinterpret_cast<double2*>(b + I * threadIdx.x);
+#pragma unroll
+      for (int j = 0; j < I; j += 2) mine[j / 2] = make_double2(v[j], v[j + 1]);
+      __syncthreads();
+      const double2* part = reinterpret_cast<const double2*>(b + I * (threadIdx.x ^ M));
+#pragma unroll
+      for (int j = 0; j < I; j += 2) {
+        const double2 q = part[(j ^ jm) / 2];
+        if constexpr (jm == 0) {
+          o[j] = q.x;
+          o[j + 1] = q.y;
+        } else {
+          o[j] = q.y;
+          o[j + 1] = q.x;
+        }
+      }
+    }
+    // the lower lane of the pair keeps the larger key, the upper the smaller
+#pragma unroll
+    for (int j = 0; j < I; ++j) v[j] = ((v[j] > o[j]) != upper) ? v[j] : o[j];
   }
-  __syncthreads();   // buf is free
-  if (lane == 63) buf[wv] = v;
+}
+
+template <int W, int I, int ST>
+__device__ inline void cleaners(double (&v)[I], double* xbuf, int& flip) {
+  if constexpr (ST >= 1) {
+    stage<W, I, ST>(v, xbuf, flip);
+    cleaners<W, I, ST / 2>(v, xbuf, flip);
+  }
+}
+
+// sorts the first N positions (N a power of two, uniform) for sizes S.. N
+template <int W, int I, int S>
+__device__ inline void sort_sizes(double (&v)[I], int N, double* xbuf, int& flip) {
+  if constexpr (S <= 64 * W * I) {
+    if (S > N) return;
+    stage<W, I, S - 1>(v, xbuf, flip);
+    cleaners<W, I, S / 4>(v, xbuf, flip);
+    sort_sizes<W, I, S * 2>(v, N, xbuf, flip);
+  }
+}
+
+// Exclusive scan of one value per thread in thread order (butterfly over the
+// wave, then the wave totals); *total gets the sum.  Exact for integers, and
+// for doubles whose partial sums are integers below 2^53.  buf holds W values
+// and must not be read by a scan still in progress (callers alternate).
+template <int M, typename V>
+__device__ inline V xchg_any(V x) {
+  if constexpr (sizeof(V) == 8) {
+    const uint64_t b = static_cast<uint64_t>(__builtin_bit_cast(long long, x));
+    const uint32_t lo = xchg32<M>(static_cast<uint32_t>(b));
+    const uint32_t hi = xchg32<M>(static_cast<uint32_t>(b >> 32));
+    return __builtin_bit_cast(V, static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+  } else {
+    return __builtin_bit_cast(V, xchg32<M>(__builtin_bit_cast(uint32_t, x)));
+  }
+}
+template <int W, typename V>
+__device__ inline V block_scan_excl(V x, V* buf, V* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  V pre = 0, tot = x;
+  auto step = [&](V t, int bit) {
+    if (lane & bit) pre += t;
+    tot += t;
+  };
+  step(xchg_any<1>(tot), 1);
+  step(xchg_any<2>(tot), 2);
+  step(xchg_any<4>(tot), 4);
+  step(xchg_any<8>(tot), 8);
+  step(xchg_any<16>(tot), 16);
+  step(xchg_any<32>(tot), 32);
+  if (lane == 0) buf[wv] = tot;
   __syncthreads();
-  long long before = 0, all = 0;
-  for (int u = 0; u < kThreads / 64; ++u) {
-    const long long x = buf[u];
-    before += u < wv ? x : 0;
-    all += x;
+  V before = 0, all = 0;
+#pragma unroll
+  for (int u = 0; u < W; ++u) {
+    const V y = buf[u];
+    before += u < wv ? y : 0;
+    all += y;
   }
   *total = all;
-  return before + v;
+  return before + pre;
 }
 
-__global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
-  __shared__ uint64_t key[kMaxCand];      // ~bits(S): ascending = S descending
-  __shared__ uint16_t cid[kMaxCand];      // candidate id = i*(gamma-1) + (k-1)
-  __shared__ uint16_t rank_of[kMaxCand];  // sorted position of each candidate
-  __shared__ long long scan_buf[kThreads / 64];
-  __shared__ double red_r[kThreads / 64];
-  __shared__ int red_k[kThreads / 64];
-  __shared__ int bad_cost;
+template <int W, int I>
+__global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
+  constexpr int T = 64 * W;
+  __shared__ __align__(16) double orig[T * I];     // survival of candidate i*(gamma-1) + k-1
+  __shared__ __align__(16) double xbuf[(W > 1) ? 2 * T * I : T * I];
+  __shared__ double scan_d[W];
+  __shared__ long long scan_l[2][W];
+  __shared__ double red_r[W];
+  __shared__ int red_k[W], red_bad[W];
 
-  const int t = threadIdx.x;
+  const int g = threadIdx.x;
+  const int lane = g & 63, wv = g >> 6;
   const int B = p.B, g1 = p.gamma - 1;
   const int n = B * g1;
-  if (t == 0) bad_cost = 0;
+  const bool ranked = (p.mode == RV_COMPACT || p.mode == RV_CAP_ACCEPT);
+  const int R = (B + T - 1) / T;                 // requests per thread, in order
+  const int i0 = g * R, i1 = min(i0 + R, B);
 
-  // The cost-table entries this thread evaluates after the sort (K = j+1
-  // for its ranked slots j, and K = 0 on thread 0), loaded now so that their
-  // latency overlaps the survival products and the sort.
-  const int seg = (n + kThreads - 1) / kThreads;  // <= 4
-  const int j0 = t * seg;
-  constexpr int kSegMax = kMaxCand / kThreads;
-  double th[kSegMax];
+  // cost-table entries for K = I*g+j+1 (and K = 0 on thread 0), loaded first
+  // so that their latency overlaps the survival products and the sort
+  double th[I];
   double alpha_b = 0.0, theta0 = 0.0;
-  if (p.mode == RV_COMPACT || p.mode == RV_CAP_ACCEPT) {
+  if (ranked) {
 #pragma unroll
-    for (int u = 0; u < kSegMax; ++u) th[u] = (u < seg && j0 + u < n) ? p.theta[B + j0 + u + 1] : 0.0;
+    for (int j = 0; j < I; ++j) {
+      const int K = I * g + j + 1;
+      th[j] = K <= n ? p.theta[B + K] : 0.0;
+    }
     alpha_b = p.alpha[B];
-    if (t == 0) theta0 = p.theta[B];
+    if (g == 0) theta0 = p.theta[B];
   }
 
-  // ---- survival products, sequential per request ----------------------------
+  // ---- 1. survival products, sequential per request ----------------------------
   long long local_sum = 0;
-  auto survive = [&](int i) {
-    // all of the request's confidences in flight at once, then the products
+  for (int i = i0; i < i1; ++i) {
     float cv[RV_MAX_GAMMA - 1];
 #pragma unroll
     for (int k = 1; k < RV_MAX_GAMMA; ++k) cv[k - 1] = k <= g1 ? p.conf[i * g1 + (k - 1)] : 0.0f;
@@ -113,150 +245,176 @@ __global__ __launch_bounds__(kThreads) void k_schedule(SchedParams p) {
         set_status(p.status, RV_DEV_BAD_CONF);
         c = 0.0f;
       }
-      // -0.0 is a valid zero; as +0.0 its survival key sorts with the other
-      // zeros (the sort compares bit patterns)
-      if (c == 0.0f) c = 0.0f;
+      if (c == 0.0f) c = 0.0f;   // -0.0 as +0.0: zero survivals compare equal in every form
       S = S * static_cast<double>(c);
-      const int id = i * g1 + (k - 1);
-      if (p.mode == RV_COMPACT || p.mode == RV_CAP_ACCEPT) {
-        key[id] = ~static_cast<uint64_t>(__double_as_longlong(S));
-        cid[id] = static_cast<uint16_t>(id);
-      } else {
-        local_sum += fixed_of(S);
-      }
+      if (ranked) orig[i * g1 + (k - 1)] = S;
+      else local_sum += fixed_of(S);
     }
-  };
-  // the first request of each thread outside any loop, so that its loads
-  // share one round trip with the cost-table loads above (a loop head would
-  // wait for those first)
-  if (t < B) survive(t);
-  for (int i = t + kThreads; i < B; i += kThreads) survive(i);
+  }
   const long long base = static_cast<long long>(B) << kShift;
 
-  if (p.mode == RV_STATIC || p.mode == RV_NO_TRIM) {
+  if (!ranked) {
     long long all = 0;
-    block_scan_incl(local_sum, scan_buf, &all);
-    for (int i = t; i < B; i += kThreads) {
+    block_scan_excl<W, long long>(local_sum, scan_l[0], &all);
+    for (int i = g; i < B; i += T) {
       p.w_commit[i] = p.gamma;
       p.w_verify[i] = p.gamma;
     }
-    if (t == 0) {
+    if (g == 0) {
       p.k_star[0] = n;
-      p.e_star[0] = static_cast<double>(base + all) * (1.0 / 1099511627776.0);
+      p.e_star[0] = static_cast<double>(base + all) * (1.0 / kFix);
     }
     return;
   }
+  __syncthreads();
 
-  // ---- bitonic sort of (key, cid) ascending ---------------------------------
-  int N = 1;
+  // ---- 2. sort the survivals, descending ---------------------------------------
+  int N = I;
   while (N < n) N <<= 1;
-  for (int j = n + t; j < N; j += kThreads) {
-    key[j] = ~0ull;
-    cid[j] = 0xffff;
+  double v[I];
+#pragma unroll
+  for (int j = 0; j < I; j += 2) {
+    const double2 q = reinterpret_cast<const double2*>(orig + I * g)[j / 2];
+    v[j] = I * g + j < n ? q.x : -1.0;
+    v[j + 1] = I * g + j + 1 < n ? q.y : -1.0;
   }
-  __syncthreads();
-  // Thread t compares pairs q = t, t+1024, ...; with stride <= 64 both
-  // elements of every pair lie in the 128-element block 2q/128, which only
-  // the wave of t touches, so such a stage needs only the wave's own LDS
-  // operations to be done before the next; a workgroup barrier follows any
-  // stage that crosses waves and any stage before one that does.
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int q = t; q < N / 2; q += kThreads) {
-        const int lo = 2 * q - (q & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const uint64_t ka = key[lo], kb = key[hi];
-        const uint16_t ia = cid[lo], ib = cid[hi];
-        const bool a_gt_b = (ka > kb) || (ka == kb && ia > ib);
-        if (a_gt_b == up) {
-          key[lo] = kb; key[hi] = ka;
-          cid[lo] = ib; cid[hi] = ia;
-        }
-      }
-      const int next_stride = stride > 1 ? stride >> 1 : size;   // first stride of the next size
-      if (stride >= 128 || (next_stride >= 128 && size < N)) {
-        __syncthreads();
-      } else {
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-      }
-    }
-  }
-  __syncthreads();
+  int flip = 0;
+  sort_sizes<W, I, 2>(v, N, xbuf, flip);
+  // the ranked survivals into the exchange buffer the last cross-wave stage
+  // did not use (every reader of it passed that stage's barrier); published
+  // by the arg-max barrier below
+  double* srt = xbuf + (flip & 1) * (T * I);
+#pragma unroll
+  for (int j = 0; j < I; j += 2) reinterpret_cast<double2*>(srt + I * g)[j / 2] = make_double2(v[j], v[j + 1]);
 
-  // ---- fixed-point prefix sums in ranked order ------------------------------
-  long long run = 0;
-  for (int j = j0; j < j0 + seg && j < n; ++j) {
-    const double S = __longlong_as_double(static_cast<long long>(~key[j]));
-    run += fixed_of(S);
-    rank_of[cid[j]] = static_cast<uint16_t>(j);
+  // ---- 3. fixed-point prefix sums in ranked order, first arg-max ---------------
+  // floor(S * 2^40) as doubles: every partial sum (with the base B * 2^40) is
+  // an integer at most 2^53, so the fp64 adds are exact and equal the int64 sums
+  double f[I];
+  double mine = 0.0;
+#pragma unroll
+  for (int j = 0; j < I; ++j) {
+    f[j] = I * g + j < n ? floor(v[j] * kFix) : 0.0;
+    mine += f[j];
   }
-  long long run_total = 0;
-  const long long incl = block_scan_incl(run, scan_buf, &run_total);
-  long long pre = incl - run;  // exclusive prefix before j0
+  double tot = 0.0;
+  const double pre = block_scan_excl<W, double>(mine, scan_d, &tot);
+  const double based = static_cast<double>(base);
 
-  // ---- ratio for every K, first arg-max -------------------------------------
   const double ba = p.bias + alpha_b;
   double best_r = -1.0;
   int best_k = 0x7fffffff;
   bool bad = false;
-  auto eval = [&](int K, long long nk, double theta) {
-    const double T = ba + theta;
-    if (!(T > 0.0) || !(T < 1e300)) { bad = true; return; }
-    const double r = static_cast<double>(nk) / T;
+  auto eval = [&](int K, double nk, double theta) {
+    const double Tm = ba + theta;
+    if (!(Tm > 0.0) || !(Tm < 1e300)) { bad = true; return; }
+    const double r = nk / Tm;
     if (r > best_r) { best_r = r; best_k = K; }
   };
-  if (t == 0) eval(0, base, theta0);
+  if (g == 0) eval(0, based, theta0);
+  double run = pre;
 #pragma unroll
-  for (int u = 0; u < kSegMax; ++u) {
-    const int j = j0 + u;
-    if (u >= seg || j >= n) break;
-    const double S = __longlong_as_double(static_cast<long long>(~key[j]));
-    pre += fixed_of(S);
-    eval(j + 1, base + pre, th[u]);  // K = j+1 takes the first j+1 ranked candidates
+  for (int j = 0; j < I; ++j) {
+    const int K = I * g + j + 1;
+    run += f[j];
+    if (K <= n) eval(K, based + run, th[j]);   // K takes the first K ranked candidates
   }
-  if (bad) atomicOr(&bad_cost, 1);
-  // first arg-max: the larger ratio, the smaller K on ties (an exact order,
-  // so the shuffle tree gives the sequential answer)
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double rb = __shfl_xor(best_r, off);
-    const int kb = __shfl_xor(best_k, off);
-    if (rb > best_r || (rb == best_r && kb < best_k)) { best_r = rb; best_k = kb; }
-  }
-  if ((t & 63) == 0) {
-    red_r[t >> 6] = best_r;
-    red_k[t >> 6] = best_k;
+  // first arg-max: the largest ratio; of equal ratios the smallest K, which
+  // is the lowest lane holding it (K grows with the lane) and then the first
+  // wave (K grows with the wave)
+  double rmax = best_r;
+  rmax = fmax(rmax, xchg<1>(rmax));
+  rmax = fmax(rmax, xchg<2>(rmax));
+  rmax = fmax(rmax, xchg<4>(rmax));
+  rmax = fmax(rmax, xchg<8>(rmax));
+  rmax = fmax(rmax, xchg<16>(rmax));
+  rmax = fmax(rmax, xchg<32>(rmax));
+  const uint64_t at = __ballot(best_r == rmax);
+  const int first = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(at)));
+  const int kw = __shfl(best_k, first);
+  const bool wave_bad = __ballot(bad) != 0;
+  if (lane == 0) {
+    red_r[wv] = rmax;
+    red_k[wv] = kw;
+    red_bad[wv] = wave_bad ? 1 : 0;
   }
   __syncthreads();
   double rbest = red_r[0];
   int kst = red_k[0];
-  for (int u = 1; u < kThreads / 64; ++u) {
+  int any_bad = red_bad[0];
+#pragma unroll
+  for (int u = 1; u < W; ++u) {
     const double rb = red_r[u];
-    const int kb = red_k[u];
-    if (rb > rbest || (rb == rbest && kb < kst)) { rbest = rb; kst = kb; }
+    if (rb > rbest) { rbest = rb; kst = red_k[u]; }
+    any_bad |= red_bad[u];
   }
-  if (bad_cost) {
+  if (any_bad) {
     kst = 0;
-    if (t == 0) set_status(p.status, RV_DEV_BAD_COST);
+    if (g == 0) set_status(p.status, RV_DEV_BAD_COST);
   }
-  // N_{K*}: the inclusive prefix at position K*-1 (recomputed by its owner)
-  if (t == 0 && kst == 0) p.e_star[0] = static_cast<double>(base) * (1.0 / 1099511627776.0);
-  {
-    long long pre2 = incl - run;
-    for (int j = j0; j < j0 + seg && j < n; ++j) {
-      const double S = __longlong_as_double(static_cast<long long>(~key[j]));
-      pre2 += fixed_of(S);
-      if (j + 1 == kst) p.e_star[0] = static_cast<double>(base + pre2) * (1.0 / 1099511627776.0);
-    }
+  if (g == 0) {
+    p.k_star[0] = kst;
+    if (kst == 0) p.e_star[0] = based * (1.0 / kFix);
   }
-  if (t == 0) p.k_star[0] = kst;
+  // E(K*) from the owner of ranked position K*-1
+  if (kst > 0 && (kst - 1) / I == g) {
+    const int jst = (kst - 1) % I;
+    double e = pre;
+#pragma unroll
+    for (int j = 0; j < I; ++j)
+      if (j <= jst) e += f[j];
+    p.e_star[0] = (based + e) * (1.0 / kFix);
+  }
 
-  // ---- windows ---------------------------------------------------------------
-  for (int i = t; i < B; i += kThreads) {
-    int w = 1;
-    for (int k = 1; k <= g1; ++k) w += (rank_of[i * g1 + (k - 1)] < kst) ? 1 : 0;
+  // ---- 4. windows ----------------------------------------------------------------
+  if (kst == 0) {
+    for (int i = g; i < B; i += T) {
+      p.w_commit[i] = 1;
+      p.w_verify[i] = (p.mode == RV_CAP_ACCEPT) ? p.gamma : 1;
+    }
+    return;
+  }
+  // S*: the K*-th largest survival.  Every survival above it is in; equal
+  // survivals are adjacent in ranked order, so S* is unique when its two
+  // ranked neighbours differ from it, and then the survivals >= S* are
+  // exactly the first K*.
+  const double sstar = srt[kst - 1];
+  const bool unique = (kst < 2 || srt[kst - 2] != sstar) && (kst >= n || srt[kst] != sstar);
+  if (unique) {
+    for (int i = i0; i < i1; ++i) {
+      int w = 1;
+      for (int k = 0; k < g1; ++k) w += orig[i * g1 + k] >= sstar ? 1 : 0;
+      p.w_commit[i] = w;
+      p.w_verify[i] = (p.mode == RV_CAP_ACCEPT) ? p.gamma : w;
+    }
+    return;
+  }
+  // Equal survivals at the boundary: G ranked strictly before S* (binary
+  // search for the first ranked position holding S*), and the remaining
+  // K* - G places go to the candidates equal to S* in (request, position)
+  // order: a scan of their counts over the requests.
+  int lo = 0, hi = kst - 1;     // srt[hi] == S*, srt[i] > S* for i < G
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (srt[mid] > sstar) lo = mid + 1;
+    else hi = mid;
+  }
+  const int r = kst - lo;
+  long long eq_mine = 0;
+  for (int i = i0; i < i1; ++i)
+    for (int k = 0; k < g1; ++k) eq_mine += orig[i * g1 + k] == sstar ? 1 : 0;
+  long long eq_all = 0;
+  int eq_before = static_cast<int>(block_scan_excl<W, long long>(eq_mine, scan_l[1], &eq_all));
+  for (int i = i0; i < i1; ++i) {
+    int gt = 0, eq = 0;
+    for (int k = 0; k < g1; ++k) {
+      const double sv = orig[i * g1 + k];
+      gt += sv > sstar ? 1 : 0;
+      eq += sv == sstar ? 1 : 0;
+    }
+    const int take = min(max(r - eq_before, 0), eq);
+    eq_before += eq;
+    const int w = 1 + gt + take;
     p.w_commit[i] = w;
     p.w_verify[i] = (p.mode == RV_CAP_ACCEPT) ? p.gamma : w;
   }
@@ -278,7 +436,13 @@ hipError_t launch_schedule(const rv_schedule_args& a, hipStream_t s) {
   p.B = a.B;
   p.gamma = a.gamma;
   p.mode = a.mode;
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(kThreads), 0, s, p);
+  // waves x keys per lane: all four SIMDs from 65 candidates on
+  const long long n = (long long)a.B * (a.gamma - 1);
+  if (n <= 64) hipLaunchKernelGGL((k_schedule<1, 8>), dim3(1), dim3(64), 0, s, p);
+  else if (n <= 512) hipLaunchKernelGGL((k_schedule<4, 2>), dim3(1), dim3(256), 0, s, p);
+  else if (n <= 1024) hipLaunchKernelGGL((k_schedule<4, 4>), dim3(1), dim3(256), 0, s, p);
+  else if (n <= 2048) hipLaunchKernelGGL((k_schedule<8, 4>), dim3(1), dim3(512), 0, s, p);
+  else hipLaunchKernelGGL((k_schedule<8, 8>), dim3(1), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -233,3 +233,138 @@ class VerifyStep:
 
     def status(self):
         return rv.rv_device_status(self.workspace, self.stream)
+
+
+class OverlapLoop:
+    """A multi-step verify loop that hides the scheduler behind the forward
+    pass (DSpark-in-SGLang page, §A2 "zero-overhead scheduling" and Fig. 5:
+    the next step's scheduling overlaps the current forward pass on its own
+    stream, cross-iteration order comes from device-side barriers, and no
+    step synchronises with the host).
+
+    Step s runs pack, payload staging, verify attention, LM head + accept
+    and compact scatter on the current stream.  With ``overlap`` the
+    schedule of step s+1 runs on a side stream of the same priority,
+    enqueued after step s's attention so that it overlaps attention and LM
+    head.  Device events order the two streams: pack(s+1) waits for
+    schedule(s+1), and schedule(s+1) waits until step s-1, which used the
+    same one of the two window buffers, has finished with it.  Without
+    ``overlap`` the same work runs in order on one stream.
+
+    Confidence relay: because schedule(s+1) runs while step s is still in
+    flight, it cannot wait for confidences produced alongside step s; step s
+    is scheduled on the confidences of step s-2 (step 0 and 1 on step 0's),
+    the pages' two-step-back relay.  ``steps`` is a list of per-step inputs
+    (``conf``, ``drafts``, ``hidden_block`` on the GPU, shaped as
+    ``make_inputs`` returns them); everything else comes from ``inp``.
+    """
+
+    def __init__(self, inp, steps, mode="compact", overlap=True, **kw):
+        self.vs = VerifyStep(inp, mode=mode, **kw)
+        self.inp, self.steps, self.mode, self.overlap = inp, steps, mode, overlap
+        vs = self.vs
+        dev = vs.w_verify.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.win = [(torch.zeros(vs.B, **i32), torch.zeros(vs.B, **i32), torch.zeros(1, **i32),
+                     torch.zeros(1, dtype=torch.float64, device=dev)) for _ in range(2)]
+        # the side stream's schedule keeps its status word apart
+        self.ws_side = torch.zeros(rv.rv_workspace_size(vs.B, vs.gamma), dtype=torch.uint8, device=dev)
+        self.side = torch.cuda.Stream()
+
+    def relay_conf(self, s):
+        return self.steps[max(s - 2, 0)]["conf"]
+
+    def _schedule(self, s, stream):
+        i, vs = self.inp, self.vs
+        wc, wv, ks, es = self.win[s % 2]
+        rv.rv_schedule(self.relay_conf(s), vs.gamma, self.mode, i["cost_bias"], i["cost_alpha"], i["cost_theta"],
+                       wc, wv, ks, es, self.ws_side, stream)
+
+    def _step_rest(self, s, after_attn=None):
+        """Pack .. scatter of step s on the current stream; ``after_attn``
+        runs between attention and the LM head (where the next schedule is
+        enqueued)."""
+        i, vs = self.inp, self.vs
+        st = self.steps[s]
+        wc, wv, _, _ = self.win[s % 2]
+        drafts = st["drafts"]
+        rv.rv_pack(wv, vs.anchor, drafts, vs.ctx, i["page_table"], i["page_size"], i["num_pages"], vs.tiers,
+                   vs.cu, vs.mm, vs.row_req, vs.row_pos, vs.tok, vs.slot, vs.workspace)
+        req = vs.row_req.long()
+        k = vs.row_pos.long() - vs.ctx[req.clamp(min=0)].long()
+        src = torch.where(req >= 0, req.clamp(min=0) * vs.gamma + k.clamp(0, vs.gamma - 1), torch.zeros_like(req))
+        torch.index_select(vs.q_flat, 0, src, out=vs.q)
+        torch.index_select(st["hidden_block"].reshape(vs.B * vs.gamma, -1), 0, src, out=vs.hidden)
+        rv.rv_verify_attn(vs.q, i["k_cache"], i["v_cache"], i["page_table"], i["page_size"], i["num_pages"], vs.ctx,
+                          vs.cu, vs.mm, vs.gamma, i["sm_scale"], vs.o, vs.lse, vs.workspace)
+        if after_attn is not None:
+            after_attn()
+        rv.rv_lm_head_accept(vs.hidden, i["W"], vs.mm, vs.cu, wc, wv, drafts, vs.rule, vs.pred, vs.accept, vs.bonus,
+                             vs.ceiling, vs.workspace, logits=vs.logits, q_rows=i.get("q_rows"), u=i.get("u"),
+                             u_bonus=i.get("u_bonus"), W_tiled=vs.W_tiled)
+        rv.rv_compact_scatter(vs.cu, wv, vs.accept, vs.bonus, drafts, vs.slot, vs.ctx, vs.anchor, vs.req_to_token,
+                              vs.commit_cu, vs.commit_tok, vs.commit_slot, vs.free_slots, vs.free_count,
+                              vs.workspace, hist=vs.hist, hist_len=vs.hist_len)
+
+    def run(self, n=None, after_step=None):
+        """Run steps 0..n-1 (default: all); ``after_step(s)`` is called after
+        step s is enqueued on the current stream (before its window buffer can
+        be reused), e.g. to copy outputs."""
+        n = len(self.steps) if n is None else n
+        main = torch.cuda.current_stream()
+        if not self.overlap:
+            for s in range(n):
+                self._schedule(s, main)
+                self._step_rest(s)
+                if after_step is not None:
+                    after_step(s)
+            return
+        e_sched = [torch.cuda.Event() for _ in range(n)]
+        e_done = [torch.cuda.Event() for _ in range(n)]
+        self.side.wait_stream(main)            # the inputs are resident before anything reads them
+        self._schedule(0, self.side)
+        e_sched[0].record(self.side)
+        for s in range(n):
+            main.wait_event(e_sched[s])
+
+            def next_schedule(s=s):
+                if s + 1 < n:
+                    if s >= 1:
+                        self.side.wait_event(e_done[s - 1])   # step s-1 is done with this window buffer
+                    self._schedule(s + 1, self.side)
+                    e_sched[s + 1].record(self.side)
+
+            self._step_rest(s, after_attn=next_schedule)
+            if after_step is not None:
+                after_step(s)
+            e_done[s].record(main)
+        main.wait_stream(self.side)
+
+    def capture(self, n=None):
+        """Record steps 0..n-1 (both streams, their event edges included) into
+        one HIP graph; ``replay()`` then runs them with no host work between
+        launches.  The mutated state is restored before capture and must be
+        restored (``self.vs.restore()``) before each replay."""
+        n = len(self.steps) if n is None else n
+        warm = torch.cuda.Stream()
+        warm.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(warm):   # warm-up outside capture: sets kernel attributes once
+            self.run(n=min(n, 2))
+        torch.cuda.current_stream().wait_stream(warm)
+        torch.cuda.synchronize()
+        self.vs.restore()
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, capture_error_mode="thread_local"):
+            self.run(n=n)
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+
+    def window(self, s):
+        """The window buffers step s used (valid until step s+2 is scheduled)."""
+        return self.win[s % 2]
+
+    def status(self):
+        return rv.rv_device_status(self.vs.workspace) or rv.rv_device_status(self.ws_side)
