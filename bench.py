@@ -78,8 +78,53 @@ class StageTimer:
 STAGES = ["schedule", "pack", "attn", "lm_accept", "scatter"]
 
 
-def run_steps(step, n, timer=None):
-    for _ in range(n):
+ROTATE_MIN_BYTES = 1 << 30
+
+
+def heavy_bytes(inp):
+    """Bytes of the inputs a step streams from HBM: the KV caches and the
+    LM-head weight (its tiled copy when the step reads that)."""
+    n = inp["k_cache"].numel() * inp["k_cache"].element_size()
+    if inp.get("v_cache") is not None:
+        n += inp["v_cache"].numel() * inp["v_cache"].element_size()
+    n += inp["W"].numel() * inp["W"].element_size()
+    return n
+
+
+def rotation_inputs(inp, min_bytes=ROTATE_MIN_BYTES):
+    """Input sets for timed steps that rotate through copies of the KV caches
+    and the LM-head weight (everything else shared), enough copies that the
+    rotated bytes reach min_bytes: consecutive steps then cannot be served
+    from the 256 MB last-level cache, as a serving loop's would not be.  One
+    set (no copy) when one copy is already that large."""
+    per = heavy_bytes(inp)
+    n = max(1, -(-min_bytes // per)) if per < min_bytes else 1
+    if n > 1:
+        n = max(n, 2)
+    sets = [inp]
+    for _ in range(n - 1):
+        c = dict(inp)
+        c["k_cache"] = inp["k_cache"].clone()
+        if inp.get("v_cache") is not None:
+            c["v_cache"] = inp["v_cache"].clone()
+        c["W"] = inp["W"].clone()
+        if inp.get("W_tiled") is not None:
+            c["W_tiled"] = inp["W_tiled"].clone()
+        sets.append(c)
+    return sets
+
+
+def use_inputs(step, inp):
+    """Point a built step at another input set of the same shapes."""
+    step.inp = inp
+    if step.W_tiled is not None:
+        step.W_tiled = inp["W_tiled"]
+
+
+def run_steps(step, n, timer=None, sets=None):
+    for s in range(n):
+        if sets is not None and len(sets) > 1:
+            use_inputs(step, sets[s % len(sets)])
         step.restore()
         if timer:
             timer.start("schedule")
@@ -135,12 +180,12 @@ def lm_flops(M, H, V):
     return 2 * M * H * V
 
 
-def measure(step, steps, warmup):
-    run_steps(step, warmup)
+def measure(step, steps, warmup, sets=None):
+    run_steps(step, warmup, sets=sets)
     torch.cuda.synchronize()
     timer = StageTimer(STAGES + ["staging"])
     t0 = time.perf_counter()
-    run_steps(step, steps, timer)
+    run_steps(step, steps, timer, sets=sets)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timer.finish()
@@ -154,27 +199,38 @@ def measure(step, steps, warmup):
                 committed=committed)
 
 
-def measure_graph(step, steps, warmup):
+def measure_graph(step, steps, warmup, sets=None):
     """The same step replayed from its HIP graphs (VerifyStep.capture): front
     (schedule, pack) and back (attention, LM head + accept, scatter) timed
     with HIP events around each replay; staging and state restore between
-    them are not counted, as in the eager timing."""
-    step.capture()
-    for _ in range(warmup):
+    them are not counted, as in the eager timing.  With rotated input sets
+    one graph pair is captured per set and the steps cycle through them."""
+    sets = sets if sets else [step.inp]
+    graphs = []
+    for inp in sets:
+        use_inputs(step, inp)
+        step.capture()
+        graphs.append((step.g_front, step.g_back))
+    for w in range(warmup):
+        use_inputs(step, sets[w % len(sets)])
         step.restore()
-        step.replay()
+        graphs[w % len(sets)][0].replay()
+        step.stage_payload()
+        graphs[w % len(sets)][1].replay()
     torch.cuda.synchronize()
     timer = StageTimer(["front", "staging", "back"])
-    for _ in range(steps):
+    for k in range(steps):
+        g_front, g_back = graphs[k % len(sets)]
+        use_inputs(step, sets[k % len(sets)])
         step.restore()
         timer.start("front")
-        step.g_front.replay()
+        g_front.replay()
         timer.stop("front")
         timer.start("staging")
         step.stage_payload()
         timer.stop("staging")
         timer.start("back")
-        step.g_back.replay()
+        g_back.replay()
         timer.stop("back")
     timer.finish()
     assert step.status() == 0, f"device status {rv.DEV_NAMES.get(step.status())}"
@@ -197,9 +253,13 @@ def sweep(steps, warmup):
         inp = synth.make_inputs(wl, device="cuda", B=B)
         cls = np.arange(B) % 3
         out = {"workload": "sweep_gqa", "B": B}
+        sets = None
         for mode in ("static", "compact", "cap_accept"):
             step = VerifyStep(inp, mode=mode)
-            r = measure(step, steps, warmup)
+            if sets is None:
+                sets = rotation_inputs(inp)
+                out["rotated_copies"] = len(sets)
+            r = measure(step, steps, warmup, sets)
             rec = {"ms_per_step": r["five_stage_ms"], "packed_rows": r["M"], "tier_rows": r["M_pad"],
                    "committed_per_step": r["committed"], "stages_ms": {k: round(v, 4) for k, v in r["per_stage_ms"].items()}}
             wc = step.w_commit.cpu().numpy()
@@ -211,7 +271,7 @@ def sweep(steps, warmup):
                 ceil = step.ceiling.cpu().numpy().astype(np.int64)
                 rec["ceiling_utilisation"] = float((acc + 1).sum() / (ceil + 1).sum())
             if mode == "compact":
-                g = measure_graph(step, steps, warmup)
+                g = measure_graph(step, steps, warmup, sets)
                 rec["graph"] = {"ms_per_step": g["ms_per_step"], "front_ms": round(g["front_ms"], 4),
                                 "back_ms": round(g["back_ms"], 4)}
                 w = step.w_verify.cpu().numpy().astype(np.int64)
@@ -501,9 +561,14 @@ def main():
         f"KV {inp['k_cache'].numel() * 2 / 1e9:.2f} GB, W {inp['W'].numel() * 2 / 1e9:.2f} GB")
 
     results = {}
+    sets = None
     for mode in ["compact"] + ([] if args.no_static else ["static"]):
         step = VerifyStep(inp, mode=mode, window=args.window, topk=args.topk)
-        r = measure(step, args.steps, args.warmup)
+        if sets is None:
+            sets = rotation_inputs(inp)   # after the step made the tiled weight
+            if len(sets) > 1:
+                log(f"rotating {len(sets)} copies of KV and weights ({heavy_bytes(inp) * len(sets) / 1e9:.2f} GB)")
+        r = measure(step, args.steps, args.warmup, sets)
         w = step.w_verify.cpu().numpy().astype(np.int64)
         ctx = inp["ctx"].cpu().numpy().astype(np.int64)
         if args.topk:
@@ -516,7 +581,7 @@ def main():
             r["attn_bytes"] = attn_bytes(ctx, w, wl, window=args.window)
         r["lm_flops"] = lm_flops(r["M"], wl.H, wl.V)
         if args.graph:
-            r["graph"] = measure_graph(step, args.steps, args.warmup)
+            r["graph"] = measure_graph(step, args.steps, args.warmup, sets)
         if wl.rule == "greedy":   # observability, after the timed steps
             cal = step.calibration(10)
             r["calibration"] = {"ece_10_bins": float(cal["ece"].item()),
@@ -566,6 +631,7 @@ def main():
                    "mode": "compact", "B": wl.B, "gamma": wl.gamma, "window": args.window,
                    "topk": args.topk},
         "accepted_tok_s": c["committed"] / t_s,
+        "rotated_input_copies": len(sets),
         "packed_rows": c["M"], "tier_rows": c["M_pad"], "committed_per_step": c["committed"],
         "stages_ms": {k: round(v, 4) for k, v in c["per_stage_ms"].items()},
         "wall_ms_per_step_incl_staging_restore": round(c["wall_ms"], 3),
