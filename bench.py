@@ -79,6 +79,7 @@ STAGES = ["schedule", "pack", "attn", "lm_accept", "scatter"]
 
 
 ROTATE_MIN_BYTES = 1 << 30
+ROTATE_MAX_COPIES = 8
 
 
 def heavy_bytes(inp):
@@ -94,13 +95,12 @@ def heavy_bytes(inp):
 def rotation_inputs(inp, min_bytes=ROTATE_MIN_BYTES):
     """Input sets for timed steps that rotate through copies of the KV caches
     and the LM-head weight (everything else shared), enough copies that the
-    rotated bytes reach min_bytes: consecutive steps then cannot be served
-    from the 256 MB last-level cache, as a serving loop's would not be.  One
-    set (no copy) when one copy is already that large."""
+    rotated bytes reach min_bytes (at most ROTATE_MAX_COPIES sets):
+    consecutive steps then cannot be served from the 256 MB last-level
+    cache, as a serving loop's would not be.  One set (no copy) when one copy
+    is already that large."""
     per = heavy_bytes(inp)
-    n = max(1, -(-min_bytes // per)) if per < min_bytes else 1
-    if n > 1:
-        n = max(n, 2)
+    n = min(max(1, -(-min_bytes // per)), ROTATE_MAX_COPIES) if per < min_bytes else 1
     sets = [inp]
     for _ in range(n - 1):
         c = dict(inp)
@@ -427,6 +427,7 @@ def cpu_baseline(inp, step, n_req=130):
     anchor = inp["anchor"].cpu().numpy().astype(np.int64)
     alpha = inp["cost_alpha"].cpu().numpy()
     theta = inp["cost_theta"].cpu().numpy()
+    n_req = min(n_req, int(inp["B"]))
     reqs = list(range(n_req))
     # host copies of what the sample touches (not timed: data movement)
     pages = sorted({int(p) for r in reqs for p in pt[r] if p >= 0})
@@ -440,6 +441,10 @@ def cpu_baseline(inp, step, n_req=130):
     qb = inp["q_block"][:n_req].float().cpu().numpy()
     hb = inp["hidden_block"][:n_req].float().cpu().numpy()
     W = inp["W"].float().cpu().numpy()
+    if wl.rule == "rejection":
+        q_rows = inp["q_rows"][:n_req].double().cpu().numpy()
+        u_acc = inp["u"][:n_req].double().cpu().numpy()
+        u_bonus = inp["u_bonus"][:n_req].double().cpu().numpy()
 
     t0 = time.perf_counter()
     wc, wv, k_star, e_star = oracle.schedule(conf, gamma, oracle.COMPACT, inp["cost_bias"], alpha, theta)
@@ -453,14 +458,18 @@ def cpu_baseline(inp, step, n_req=130):
     z = oracle.lm_head_logits(x, W)
     pred = oracle.lm_head_pred(z)
     cu_s = np.concatenate([[0], np.cumsum(wv[:n_req])])
-    acc, bonus, ceil = oracle.accept_greedy(pred, cu_s, wc[:n_req], wv[:n_req], drafts[:n_req])
+    if wl.rule == "rejection":
+        acc, bonus, ceil = oracle.accept_rejection(z, cu_s, wc[:n_req], wv[:n_req], drafts[:n_req], q_rows, u_acc,
+                                                   u_bonus)
+    else:
+        acc, bonus, ceil = oracle.accept_greedy(pred, cu_s, wc[:n_req], wv[:n_req], drafts[:n_req])
     r2t = np.full((n_req, int(ctx[:n_req].max()) + gamma), -1)
     oracle.compact_scatter(cu_s, wv[:n_req], acc, bonus, drafts[:n_req], slot[rows], ctx[:n_req],
                            anchor[:n_req], r2t)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
     return {"value": len(rows) / dt, "unit": "tok/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"schedule+pack of all {inp['B']} requests, then attention, LM head, greedy accept "
+            "sample": f"schedule+pack of all {inp['B']} requests, then attention, LM head, {wl.rule} accept "
                       f"and scatter for the {len(rows)} packed rows of the first {n_req} requests "
                       f"(numpy fp64, {dt:.1f} s, host has {cores} cores available)",
             "seconds": dt}

@@ -5,27 +5,39 @@
 // reuses ordinary varlen causal attention (native sparse-MLA on DeepSeek-V4);
 // each backend rebuilds its varlen metadata from the packed layout.
 //
-// Design (gfx950):
-//  * A plan kernel (one workgroup) rebuilds that metadata on the device from
-//    cu[] and ctx[]: it cuts every request into q-tiles (up to 16 query
-//    vectors per wave that share one KV head) and, when the batch alone cannot
-//    fill the chip, splits the key range into chunks (split-KV).  Work items are
-//    ordered request-major so the tiles that read the same KV chunk run
-//    together and share it through L2.
-//  * The main kernel streams each item's keys through LDS in 32-key tiles read
-//    via the page table (register prefetch of the next tile overlaps the MFMA
-//    work of the current one), computes S^T = K Q^T and O^T += V^T P^T with
-//    bf16 16x16x32 MFMAs (fp32 accumulation) and keeps an online base-2
-//    softmax per query vector.  In the S^T orientation each lane owns one
-//    query vector, so the row max needs two cross-lane steps and P^T feeds the
-//    PV MFMA straight from registers; the V^T operand comes from the
-//    row-major value tile through gfx950's transposing LDS reads, so the
-//    latent layout keeps a single copy of each key row in LDS.
-//  * The latent (MLA-style) layout reads one 576-wide row per key and uses its
-//    first 512 entries as the value.
-//  * Split items write fp32 partials (O, running max, normaliser) that a
-//    combine kernel merges.
-//  * fp32 inputs take a plain vector kernel.
+// Design (gfx950).  Every kernel reads keys through the page table and
+// moves them into LDS by direct global->LDS DMA (global_load_lds, 16 bytes
+// per lane) into a ring of stages; scores and outputs use bf16 MFMAs with
+// fp32 accumulation.
+//  * Plans (one workgroup each) rebuild the varlen metadata on the device
+//    from cu[] and ctx[].  k_attn_plan cuts every request into tiles of query
+//    vectors that share one KV head and, when the batch alone cannot fill the
+//    chip, splits the key range into chunks (split-KV), ordered request-major
+//    and per XCD so that the tiles reading one KV chunk share it through L2.
+//    k_attn_plan_bal (GQA) lays every tile's 64-key super-tiles out as one
+//    cost sequence and gives each persistent workgroup an equal contiguous
+//    range of it.
+//  * GQA (k_attn_gqa_bal, persistent): four waves, two query-vector groups x
+//    two key groups, each super-tile's two 32-key halves in a four-stage
+//    ring; S^T = K Q^T and O^T += V^T P^T on 16x16x32 MFMAs with an online
+//    base-2 softmax (each lane owns one query vector; P^T feeds the PV MFMA
+//    from registers; V^T comes from the row-major value rows through
+//    gfx950's transposing LDS reads).  The two key groups merge through LDS
+//    at the end of a range; a range that covers part of a tile writes fp32
+//    partials to its slot.  k_attn_gqa is the same range code over the
+//    chunked plan's work list.
+//  * Latent (MLA-style) layout: one 576-wide row per key, its first 512
+//    entries the value.  k_attn_mla_row takes one packed row with all 128
+//    heads per workgroup (each 32-key tile DMA'd once per row): QK on
+//    32x32x16 MFMAs with the queries' 512 value dims in registers and the 64
+//    rope dims in LDS, probabilities exchanged between the four waves through
+//    LDS, each wave accumulating 128 output columns of all 128 heads; a fixed
+//    softmax reference from the first tile, with one rerun when a later score
+//    leaves its range.  k_attn_mla (64 heads per workgroup) serves other head
+//    counts and page sizes, and the sparse path (per-row key lists).
+//  * k_attn_combine merges split partials (O, max, normaliser); k_attn_pad
+//    writes the rows between the packed count and the tier.
+//  * fp32 inputs take a plain vector kernel (k_attn_f32).
 
 #include <float.h>
 

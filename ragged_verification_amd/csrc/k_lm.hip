@@ -7,21 +7,32 @@
 // block but commits up to the scheduled window and reports the ceiling
 // (DSpark-in-SGLang page, section A2 "verify modes" and "observability").
 //
-// Design (gfx950):
-//  * k_lm_gemm: z = X W^T with bf16 32x32x16 MFMAs (fp32 accumulation), a
-//    128-row x 256-column output tile per workgroup; each of the four waves
-//    owns all 128 rows of a 64-column quarter, so a weight fragment read from
-//    LDS feeds four MFMAs and a hidden-state fragment two.  Both operands
-//    arrive by direct global->LDS DMA into a three-stage ring of 64-wide K
-//    steps whose LDS rows are whole 128-byte lines (chunks XOR-swizzled by
-//    (row >> 1) & 7); the DMA of step k+2 is spread one instruction per two
-//    MFMAs over step k.  Workgroups whose rows lie past the packed total exit
-//    at once, so the work follows the real row count M, not the tier.  The
-//    epilogue goes through an LDS transpose: per 64-column slab each row is
-//    reduced to (max, lowest argmax, sum of exp(z - max)) in 16 bytes, and
-//    the logits are written (row-contiguous float4 runs) only when asked.
-//    The row tiles of one vocabulary tile sit on one XCD, so the weight tile
-//    is fetched from HBM once per XCD.
+// Design (gfx950).  z = X W^T on bf16 32x32x16 MFMAs with fp32
+// accumulation; the epilogue of every GEMM goes through an LDS transpose and
+// reduces each (row, 64-column slab) to (max, lowest argmax, sum of
+// exp(z - max)) in 16 bytes, writing the logits (row-contiguous float4
+// runs) only when asked.  Workgroups past the packed row count M exit at
+// once, so the work follows M, not the tier.
+//  * k_lm_tile_weight (once per weight, model-load work) writes W in MFMA
+//    fragment order: blocks of 32 vocabulary rows, each a run of H/16
+//    fragments of 1 KB, so a wave's B operand for one MFMA is one fully
+//    coalesced 1 KB load straight into registers.
+//  * k_lm_gemm_tiled (the path for more than 256 row slots): 128 rows x 512
+//    (or 256) vocabulary columns per workgroup, each wave 128 x 128 in 256
+//    accumulators; its weight fragments come into an 8-deep register ring
+//    seven 16-wide K sub-steps ahead, the hidden rows through a four-stage
+//    LDS ring (128-byte rows XOR-swizzled by (row >> 1) & 7); the row tiles
+//    of one vocabulary tile are consecutive on one XCD so they share its
+//    weights through L2; MFMAs only for the 32-row blocks that hold packed
+//    rows.
+//  * k_lm_gemm_rows (33 to 256 row slots): all packed rows in one tile
+//    against 128 columns, each wave one 32-column block and every row block,
+//    so each weight byte is loaded by one wave once (16-deep register ring);
+//    above 224 packed rows it switches to two 128-row tiles.
+//  * k_lm_gemm_small (at most 32 row slots): one-wave 32 x 64 tiles streaming
+//    the weight, both operands straight into 16-deep register rings.
+//  * k_lm_gemm: the row-major weight, both operands by DMA into a
+//    three-stage LDS ring (used when no tiled copy is given).
 //  * k_lm_f32: the same partials from fp32 inputs (plain dot products).
 //  * k_accept: one workgroup per request merges the slab partials of its
 //    rows, runs the greedy or rejection scan, and for rejection draws the

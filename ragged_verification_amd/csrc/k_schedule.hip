@@ -216,26 +216,35 @@ __global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
   const int R = (B + T - 1) / T;                 // requests per thread, in order
   const int i0 = g * R, i1 = min(i0 + R, B);
 
-  // cost-table entries for K = I*g+j+1 (and K = 0 on thread 0), loaded first
-  // so that their latency overlaps the survival products and the sort
+  // The first request's confidences, then the cost-table entries for
+  // K = I*g+j+1 and K = 0, all issued before any is used and without
+  // branches (indices clamped into range, the values masked later), so the
+  // two sets of loads share one round trip.
+  auto load_conf = [&](int i, float (&cv)[RV_MAX_GAMMA - 1]) {
+#pragma unroll
+    for (int k = 0; k < RV_MAX_GAMMA - 1; ++k) cv[k] = p.conf[i * g1 + min(k, g1 - 1)];
+  };
+  float cv0[RV_MAX_GAMMA - 1];
+  load_conf(i0 < i1 ? i0 : 0, cv0);
   double th[I];
   double alpha_b = 0.0, theta0 = 0.0;
   if (ranked) {
 #pragma unroll
-    for (int j = 0; j < I; ++j) {
-      const int K = I * g + j + 1;
-      th[j] = K <= n ? p.theta[B + K] : 0.0;
-    }
+    for (int j = 0; j < I; ++j) th[j] = p.theta[B + min(I * g + j + 1, n)];   // B + n < theta_len
     alpha_b = p.alpha[B];
-    if (g == 0) theta0 = p.theta[B];
+    theta0 = p.theta[B];
   }
 
   // ---- 1. survival products, sequential per request ----------------------------
   long long local_sum = 0;
   for (int i = i0; i < i1; ++i) {
     float cv[RV_MAX_GAMMA - 1];
+    if (i == i0) {
 #pragma unroll
-    for (int k = 1; k < RV_MAX_GAMMA; ++k) cv[k - 1] = k <= g1 ? p.conf[i * g1 + (k - 1)] : 0.0f;
+      for (int k = 0; k < RV_MAX_GAMMA - 1; ++k) cv[k] = cv0[k];
+    } else {
+      load_conf(i, cv);
+    }
     double S = 1.0;
 #pragma unroll
     for (int k = 1; k < RV_MAX_GAMMA; ++k) {
@@ -305,19 +314,23 @@ __global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
   double best_r = -1.0;
   int best_k = 0x7fffffff;
   bool bad = false;
-  auto eval = [&](int K, double nk, double theta) {
+  // branch-free, so the divides of the lane's K values overlap
+  auto eval = [&](int K, double nk, double theta, bool valid) {
     const double Tm = ba + theta;
-    if (!(Tm > 0.0) || !(Tm < 1e300)) { bad = true; return; }
-    const double r = nk / Tm;
-    if (r > best_r) { best_r = r; best_k = K; }
+    const bool ok = (Tm > 0.0) && (Tm < 1e300);
+    bad = bad || (valid && !ok);
+    const double r = nk / (ok ? Tm : 1.0);
+    const bool take = valid && ok && r > best_r;
+    best_r = take ? r : best_r;
+    best_k = take ? K : best_k;
   };
-  if (g == 0) eval(0, based, theta0);
+  eval(0, based, theta0, g == 0);
   double run = pre;
 #pragma unroll
   for (int j = 0; j < I; ++j) {
     const int K = I * g + j + 1;
     run += f[j];
-    if (K <= n) eval(K, based + run, th[j]);   // K takes the first K ranked candidates
+    eval(K, based + run, th[j], K <= n);   // K takes the first K ranked candidates
   }
   // first arg-max: the largest ratio; of equal ratios the smallest K, which
   // is the lowest lane holding it (K grows with the lane) and then the first
@@ -380,10 +393,23 @@ __global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
   // exactly the first K*.
   const double sstar = srt[kst - 1];
   const bool unique = (kst < 2 || srt[kst - 2] != sstar) && (kst >= n || srt[kst] != sstar);
+  // a request's survivals, unrolled over the longest block (indices clamped
+  // into the array, positions past the block masked)
+  auto count_req = [&](int i, int& gt, int& eq) {
+    gt = 0;
+    eq = 0;
+#pragma unroll
+    for (int k = 0; k < RV_MAX_GAMMA - 1; ++k) {
+      const double sv = orig[min(i * g1 + k, T * I - 1)];
+      gt += (k < g1 && sv > sstar) ? 1 : 0;
+      eq += (k < g1 && sv == sstar) ? 1 : 0;
+    }
+  };
   if (unique) {
     for (int i = i0; i < i1; ++i) {
-      int w = 1;
-      for (int k = 0; k < g1; ++k) w += orig[i * g1 + k] >= sstar ? 1 : 0;
+      int gt, eq;
+      count_req(i, gt, eq);
+      const int w = 1 + gt + eq;
       p.w_commit[i] = w;
       p.w_verify[i] = (p.mode == RV_CAP_ACCEPT) ? p.gamma : w;
     }
@@ -401,17 +427,16 @@ __global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
   }
   const int r = kst - lo;
   long long eq_mine = 0;
-  for (int i = i0; i < i1; ++i)
-    for (int k = 0; k < g1; ++k) eq_mine += orig[i * g1 + k] == sstar ? 1 : 0;
+  for (int i = i0; i < i1; ++i) {
+    int gt, eq;
+    count_req(i, gt, eq);
+    eq_mine += eq;
+  }
   long long eq_all = 0;
   int eq_before = static_cast<int>(block_scan_excl<W, long long>(eq_mine, scan_l[1], &eq_all));
   for (int i = i0; i < i1; ++i) {
-    int gt = 0, eq = 0;
-    for (int k = 0; k < g1; ++k) {
-      const double sv = orig[i * g1 + k];
-      gt += sv > sstar ? 1 : 0;
-      eq += sv == sstar ? 1 : 0;
-    }
+    int gt, eq;
+    count_req(i, gt, eq);
     const int take = min(max(r - eq_before, 0), eq);
     eq_before += eq;
     const int w = 1 + gt + take;
@@ -419,6 +444,8 @@ __global__ __launch_bounds__(64 * W) void k_schedule(SchedParams p) {
     p.w_verify[i] = (p.mode == RV_CAP_ACCEPT) ? p.gamma : w;
   }
 }
+
+
 
 }  // namespace
 
@@ -438,7 +465,7 @@ hipError_t launch_schedule(const rv_schedule_args& a, hipStream_t s) {
   p.mode = a.mode;
   // waves x keys per lane: all four SIMDs from 65 candidates on
   const long long n = (long long)a.B * (a.gamma - 1);
-  if (n <= 64) hipLaunchKernelGGL((k_schedule<1, 8>), dim3(1), dim3(64), 0, s, p);
+  if (n <= 128) hipLaunchKernelGGL((k_schedule<1, 2>), dim3(1), dim3(64), 0, s, p);
   else if (n <= 512) hipLaunchKernelGGL((k_schedule<4, 2>), dim3(1), dim3(256), 0, s, p);
   else if (n <= 1024) hipLaunchKernelGGL((k_schedule<4, 4>), dim3(1), dim3(256), 0, s, p);
   else if (n <= 2048) hipLaunchKernelGGL((k_schedule<8, 4>), dim3(1), dim3(512), 0, s, p);

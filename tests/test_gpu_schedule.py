@@ -13,9 +13,10 @@ import parity_util as pu
 
 pytestmark = pytest.mark.gpu
 
-# (B, gamma): candidates B * (gamma - 1) around 512, 2048 and 4096
-SHAPES = [(1, 2), (1, 8), (3, 16), (73, 8), (74, 8), (256, 8), (292, 8), (293, 8), (585, 8), (273, 16),
-          (4096, 2), (512, 9)]
+# (B, gamma): candidates B * (gamma - 1) around 64 (one lane per candidate
+# up to there), 512, 2048 and 4096
+SHAPES = [(1, 2), (1, 8), (3, 16), (9, 8), (32, 3), (64, 2), (13, 6), (73, 8), (74, 8), (256, 8), (292, 8),
+          (293, 8), (585, 8), (273, 16), (4096, 2), (512, 9)]
 
 
 def _conf(kind, B, g1, rng):
