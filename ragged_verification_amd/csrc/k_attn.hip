@@ -1297,7 +1297,22 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
         for (int cb = 0; cb < 4; ++cb) {
           if (cb + 1 < 4) va[(cb + 1) & 1] = rd_v(cb + 1);
 #pragma unroll
-          for (int vb = 0; vb < 4; ++vb) oacc[cb][vb] = mfma32(va[cb & 1], pb[vb], oacc[cb][vb]);
+          for (int vb = 0; vb < 4; ++vb) {
+            if (cb == 3 && vb == 3) {
+              // this block's accumulator is pinned to VGPRs: the other 15
+              // (240 AGPRs) leave 16 AGPRs for the scores, so the compiler
+              // no longer parks an output block in VGPRs around every QK
+              // (48 accumulator moves a tile).  Its operands come straight
+              // from LDS loads (waited on by the compiler); the block is
+              // read again only by this MFMA (same accumulator, back to
+              // back) and after the guard that follows the tile loop.
+              asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                           : "+v"(oacc[3][3])
+                           : "v"(va[cb & 1]), "v"(pb[vb]));
+            } else {
+              oacc[cb][vb] = mfma32(va[cb & 1], pb[vb], oacc[cb][vb]);
+            }
+          }
           // the next tile's softmax as one block after four MFMAs of step 1
           // (spread one key per MFMA, or sliced with a branch per slice, it
           // measured slower: the scheduling barriers and branch boundaries
@@ -1311,6 +1326,10 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
         *(lds_u32x4_t*)(size_t)(xaddr((t + 1) & 1, wid, 1)) = pn[1];
       }
     }
+    // the pinned block's last MFMA (32 cycles) completes before anything
+    // else reads or writes its registers: 32 wait states, ordered after it
+    // by the operand
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(oacc[3][3]));
 
     wait_vm<0>();
     // each vector's visible max and sum: the two lane halves hold its keys

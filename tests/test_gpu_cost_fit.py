@@ -5,9 +5,10 @@ the fitted tables drive rv_schedule; the oracle fits the same samples
 (oracle.fit_cost_model) and schedules with its own tables.
 
 The fits agree to 1e-9 relative.  Windows, K* and E* must then be equal bit
-for bit, under a guard that makes the integer decision well posed: the
-oracle's best ratio E/T beats every other K by more than the table
-difference could move it (1e-7 relative)."""
+for bit when the integer decision is well posed (the oracle's best ratio
+E/T beats every other K by more than the table difference could move it,
+1e-7 relative); when measured step times happen to make a near tie, the
+GPU's K* must be one of the near-best K and its E* that K's exact E."""
 
 import numpy as np
 import pytest
@@ -44,22 +45,20 @@ def _step_ms(step, n=5):
     return float(np.median([x.elapsed_time(y) for x, y in ev]))
 
 
-def _ratio_margin(conf, gamma, bias, alpha, theta):
-    """Relative gap between the oracle's best ratio and the best other K."""
+def _ratios(conf, gamma, bias, alpha, theta):
+    """The oracle's ratio E(K)/T(K) for every K, and E(K) in fixed point."""
     B = conf.shape[0]
     S = oracle.survival(conf)
     vals = sorted((S[i, k] for i in range(B) for k in range(1, gamma)), reverse=True)
     q = [int(np.floor(v * 2.0 ** 40)) for v in vals]
     n = B << 40
-    r = []
+    r, e = [], []
     for K in range(len(q) + 1):
         if K:
             n += q[K - 1]
         r.append(float(n) / oracle.step_time(bias, alpha, theta, B, K))
-    r = np.array(r)
-    best = int(np.argmax(r))
-    others = np.delete(r, best)
-    return (r[best] - others.max()) / r[best]
+        e.append(n)
+    return np.array(r), e
 
 
 def test_fitted_cost_table_drives_the_scheduler():
@@ -84,8 +83,11 @@ def test_fitted_cost_table_drives_the_scheduler():
     for B in (8, 24, 48):
         inp = pu.make_inputs("sweep_gqa", B=B, V=64, H=64, ctx=("uniform", 4, 8))
         conf = inp["conf"]
-        margin = _ratio_margin(conf.cpu().numpy(), gamma, bias_o, alpha_o, theta_o)
-        assert margin > 1e-7, f"scheduling decision too close to call at B={B} (margin {margin:.3g})"
+        r, e = _ratios(conf.cpu().numpy(), gamma, bias_o, alpha_o, theta_o)
+        best = int(np.argmax(r))
+        # K whose ratio is within what the 1e-9 table difference could move
+        # (1e-7 relative, with room): the decision among them is not fixed
+        near = [K for K in range(len(r)) if r[K] >= r[best] * (1.0 - 1e-7)]
         i32 = dict(dtype=torch.int32, device="cuda")
         wc, wv, ks = torch.zeros(B, **i32), torch.zeros(B, **i32), torch.zeros(1, **i32)
         es = torch.zeros(1, dtype=torch.float64, device="cuda")
@@ -95,8 +97,15 @@ def test_fitted_cost_table_drives_the_scheduler():
         rv.rv_schedule(conf, gamma, "compact", coef[0], al, th, wc, wv, ks, es, ws)
         torch.cuda.synchronize()
         want = oracle.schedule(conf.cpu().numpy(), gamma, oracle.COMPACT, bias_o, alpha_o, theta_o)
-        assert np.array_equal(pu.npi(wv), want[1]) and int(ks.item()) == want[2], B
-        np.testing.assert_allclose(float(es.item()), want[3], rtol=1e-12)
+        if len(near) == 1:
+            assert np.array_equal(pu.npi(wv), want[1]) and int(ks.item()) == want[2], B
+            np.testing.assert_allclose(float(es.item()), want[3], rtol=1e-12)
+        else:
+            # a near tie: any of the near-best K, with its exact E(K)
+            k_gpu = int(ks.item())
+            assert k_gpu in near, (B, k_gpu, near)
+            assert float(es.item()) == e[k_gpu] / 2.0 ** 40, B
+            pu.log(f"B={B}: near tie among K={near}, GPU chose {k_gpu}")
         pu.log(f"B={B}: K*={want[2]} windows {np.bincount(want[1], minlength=gamma + 1)[1:].tolist()}")
         checked += 1
     assert checked == 3
