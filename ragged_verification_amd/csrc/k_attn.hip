@@ -1160,7 +1160,7 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   auto no_op = [](int) {};
 
   f32x16_t oacc[4][4];   // [32-column block][32-vector block]
-  float m_ref = 0.f, l_part = 0.f, m_seen = -INFINITY, l_all = 0.f;
+  float m_ref = 0.f, l_part = 0.f, m_rel = -INFINITY, l_all = 0.f;
 
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
@@ -1170,29 +1170,30 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[cb][vb][j] = 0.f;
     l_part = 0.f;
-    m_seen = -INFINITY;
+    m_rel = -INFINITY;   // largest visible scaled score less the reference
 
-    // scaled scores -> probabilities, in place, for this lane's 16 keys (key
-    // t0 + 8*(j/4) + 4*hl + j%4 of the tile).  A full tile needs no mask and
-    // folds the scale into one fma per key (its largest scaled score is the
-    // largest or the smallest raw score times the scale, by the scale's
-    // sign); an edge tile masks keys outside [low, lim].  The branch is
-    // uniform.
-    auto soft_all = [&](f32x16_t& sc, int t0, bool full) {
+    // scaled scores -> the PV B operands of steps 0 and 1, for this lane's
+    // 16 keys (key t0 + 8*(j/4) + 4*hl + j%4 of the tile), in registers of
+    // their own (writing them back into the score accumulators would cost a
+    // move each).  A full tile needs no mask: one fma per key forms the
+    // exponent relative to the reference, and the largest exponent is the
+    // tile's largest scaled score less the reference.  An edge tile masks
+    // keys outside [low, lim].  The branch is uniform.
+    auto soft = [&](const f32x16_t& sc, int t0, bool full, u32x4_t (&out)[2]) {
+      float x[16];
       if (full) {
         const float mr = -m_ref;
-        float mx = sc[0], mn = sc[0];
 #pragma unroll
-        for (int j = 1; j < 16; ++j) {
-          mx = fmaxf(mx, sc[j]);
-          mn = fminf(mn, sc[j]);
-        }
-        m_seen = fmaxf(m_seen, (p.scale_log2 >= 0.f ? mx : mn) * p.scale_log2);
+        for (int j = 0; j < 16; ++j) x[j] = __builtin_fmaf(sc[j], p.scale_log2, mr);
+        float mx = x[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, x[j]);
+        m_rel = fmaxf(m_rel, mx);
         float sum = 0.f;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          sc[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[j], p.scale_log2, mr));
-          sum += sc[j];
+          x[j] = __builtin_amdgcn_exp2f(x[j]);
+          sum += x[j];
         }
         l_part += sum;
       } else {
@@ -1201,23 +1202,17 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
           float v = sc[j] * p.scale_log2;
           const int k = t0 + 8 * (j >> 2) + 4 * hl + (j & 3);
           if (k > lim || k < low) v = -INFINITY;
-          m_seen = fmaxf(m_seen, v);
-          v = __builtin_amdgcn_exp2f(v - m_ref);   // exp2(-inf) = 0
+          v -= m_ref;
+          m_rel = fmaxf(m_rel, v);
+          v = __builtin_amdgcn_exp2f(v);   // exp2(-inf) = 0
           l_part += v;
-          sc[j] = v;
+          x[j] = v;
         }
       }
-    };
-    // the PV B operands of steps 0 and 1 from the 16 probabilities
-    auto pack_p = [&](const f32x16_t& sc, u32x4_t (&out)[2]) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
-        out[s2] = u32x4_t{cvt_bf16x2(sc[8 * s2 + 0], sc[8 * s2 + 1]), cvt_bf16x2(sc[8 * s2 + 2], sc[8 * s2 + 3]),
-                          cvt_bf16x2(sc[8 * s2 + 4], sc[8 * s2 + 5]), cvt_bf16x2(sc[8 * s2 + 6], sc[8 * s2 + 7])};
-    };
-    auto soft = [&](f32x16_t& sc, int t0, bool full, u32x4_t (&out)[2]) {
-      soft_all(sc, t0, full);
-      pack_p(sc, out);
+        out[s2] = u32x4_t{cvt_bf16x2(x[8 * s2 + 0], x[8 * s2 + 1]), cvt_bf16x2(x[8 * s2 + 2], x[8 * s2 + 3]),
+                          cvt_bf16x2(x[8 * s2 + 4], x[8 * s2 + 5]), cvt_bf16x2(x[8 * s2 + 6], x[8 * s2 + 7])};
     };
 
     if (n_tiles > 0) {
@@ -1333,6 +1328,7 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
 
     wait_vm<0>();
     // each vector's visible max and sum: the two lane halves hold its keys
+    const float m_seen = m_rel + m_ref;   // -inf when no key was visible
     const float m_all = fmaxf(m_seen, __shfl_xor(m_seen, 32));
     l_all = l_part + __shfl_xor(l_part, 32);
     const int need = (pass == 0 && m_all > -INFINITY && (m_all > m_ref + 32.f || m_all < m_ref - 64.f)) ? 1 : 0;
