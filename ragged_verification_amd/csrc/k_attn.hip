@@ -65,8 +65,11 @@ struct AttnShape {
 
 // Work header written by the plan: [0] items, [1] chunk, [2] partial slots
 // used, [8 + x] / [16 + x] start and length of XCD x's item list, [24 + x]
-// that list's take counter (zeroed by the plan, advanced by the workers).
-constexpr int kHdrXOff = 8, kHdrXLen = 16, kHdrCtr = 24;
+// that list's take counter (zeroed by the plan, advanced by the workers);
+// the shared tail list: start [40], length [41], take counter [24 + 8].
+constexpr int kHdrXOff = 8, kHdrXLen = 16, kHdrCtr = 24, kHdrTOff = 40, kHdrTLen = 41;
+// share of the work (by rank, the shortest chunks) that goes to the tail list
+constexpr int kTailPct = 35;
 // Header of the balanced GQA plan: total super-tiles, super-tiles per
 // virtual worker, virtual workers, tiles, partial slots used.
 constexpr int kBalS = 0, kBalQ = 1, kBalVw = 2, kBalTiles = 3, kBalParts = 4;
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   __shared__ int s_buf[kPlanWaves * 8];
   __shared__ long long s_red[kPlanWaves];
   __shared__ int hist[64];
+  __shared__ int s_rs;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int B = p.B;
@@ -216,8 +220,41 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   }
   __syncthreads();   // the ranked groups are visible to the whole workgroup
 
+  // The ranks from rs on (the shortest chunks, about kTailPct of the work
+  // counted in 32-key tiles) form a shared tail list, which every worker
+  // takes from once its own XCD's list is empty.  The XCD lists are dealt by
+  // group count and a group is one to eight rows, so their work differs;
+  // without a shared tail the last items taken are wherever the fullest list
+  // had got to (on the latent batch workers then ended up to 0.3 ms apart;
+  // a fifth of the work in the tail was not enough, 35% to 70% measured alike).
+  const int segr = ceil_div(n_groups, kPlanThreads);
+  const int r0 = min(t * segr, n_groups), r1 = min(r0 + segr, n_groups);
+  auto group_work = [&](int r) {
+    const int2 g = p.grp[r];
+    const int2 wl = s_wl[g.x];
+    return tiles_of_w(wl.x) * ceil_div(max(min(C, wl.y - g.y * C), 1), kNK);
+  };
+  int wv[1] = {0}, wex[1], wtot[1];
+  for (int r = r0; r < r1; ++r) wv[0] += group_work(r);
+  block_excl_scan<1>(wv, wex, wtot, s_buf);
+  if (t == 0) s_rs = n_groups;
+  __syncthreads();
+  {
+    const int thresh = wtot[0] - (int)((long long)wtot[0] * kTailPct / 100);
+    int run = wex[0];
+    for (int r = r0; r < r1; ++r) {
+      if (run >= thresh) {
+        atomicMin(&s_rs, r);
+        break;
+      }
+      run += group_work(r);
+    }
+  }
+  __syncthreads();
+  const int rs = s_rs;
+
   // items per (cycle, XCD) slot, scanned along the cycles of each XCD
-  const int nc = ceil_div(n_groups, 8);
+  const int nc = ceil_div(rs, 8);
   const int segc = ceil_div(nc, kPlanThreads);
   auto rank_of = [](int c, int x) { return 8 * c + ((c & 1) ? 7 - x : x); };
   int cnt[8], pos[8], xlen[8];
@@ -229,7 +266,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int r = rank_of(c, x);
-      if (r < n_groups) cnt[x] += tiles_of_w(s_wl[p.grp[r].x].x);
+      if (r < rs) cnt[x] += tiles_of_w(s_wl[p.grp[r].x].x);
     }
   }
   block_excl_scan<8>(cnt, pos, xlen, s_buf);
@@ -247,15 +284,28 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int r = rank_of(c, x);
-      if (r >= n_groups) continue;
+      if (r >= rs) continue;
       const int2 g = p.grp[r];
       const int tiles = tiles_of_w(s_wl[g.x].x);
       for (int tl = 0; tl < tiles; ++tl) p.items[pos[x] + tl] = make_int4(g.x, tl, g.y, 0);
       pos[x] += tiles;
     }
   }
+  // the tail list after the XCD lists, in rank order (longest first)
+  int tv[1] = {0}, tex[1], ttot[1];
+  for (int r = max(r0, rs); r < r1; ++r) tv[0] += tiles_of_w(s_wl[p.grp[r].x].x);
+  block_excl_scan<1>(tv, tex, ttot, s_buf);
+  {
+    int q = total + tex[0];
+    for (int r = max(r0, rs); r < r1; ++r) {
+      const int2 g = p.grp[r];
+      const int tiles = tiles_of_w(s_wl[g.x].x);
+      for (int tl = 0; tl < tiles; ++tl) p.items[q + tl] = make_int4(g.x, tl, g.y, 0);
+      q += tiles;
+    }
+  }
   if (t == 0) {
-    p.hdr[0] = total;
+    p.hdr[0] = total + ttot[0];
     p.hdr[1] = C;
     p.hdr[2] = n_parts;
     p.hdr[kHdrSplit] = tot2[2];
@@ -265,6 +315,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
       p.hdr[kHdrXLen + x] = xlen[x];
       p.hdr[kHdrCtr + x] = 0;
     }
+    p.hdr[kHdrTOff] = total;
+    p.hdr[kHdrTLen] = ttot[0];
+    p.hdr[kHdrCtr + 8] = 0;
   }
 }
 
@@ -408,13 +461,15 @@ __device__ inline uint2 lds_tr16(uint32_t addr) {
 __device__ inline int next_item(const MainParams& p, int* s_item, unsigned& done) {
   __syncthreads();   // every thread has read the previous item
   if (threadIdx.x == 0) {
+    // this XCD's list, then the shared tail list (8), then the other XCDs'
     const int x = blockIdx.x & 7;
     int it = -1;
-    for (int probe = 0; probe < 8 && it < 0; ++probe) {
-      const int y = (x + probe) & 7;
+    for (int probe = 0; probe < 9 && it < 0; ++probe) {
+      const int y = probe == 0 ? x : probe == 1 ? 8 : (x + probe - 1) & 7;
       if (done & (1u << y)) continue;
       const int k = atomicAdd(p.ctr + y, 1);
-      if (k < p.hdr[kHdrXLen + y]) it = p.hdr[kHdrXOff + y] + k;
+      const int len = y == 8 ? p.hdr[kHdrTLen] : p.hdr[kHdrXLen + y];
+      if (k < len) it = (y == 8 ? p.hdr[kHdrTOff] : p.hdr[kHdrXOff + y]) + k;
       else done |= 1u << y;
     }
     *s_item = it;
