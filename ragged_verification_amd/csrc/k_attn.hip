@@ -33,8 +33,10 @@
 //    rope dims in LDS, probabilities exchanged between the four waves through
 //    LDS, each wave accumulating 128 output columns of all 128 heads; a fixed
 //    softmax reference from the first tile, with one rerun when a later score
-//    leaves its range.  k_attn_mla (64 heads per workgroup) serves other head
-//    counts and page sizes, and the sparse path (per-row key lists).
+//    leaves its range.  With per-row key lists (sparse) the same kernel runs
+//    over each item's visible list entries, compacted in list order, each
+//    DMA lane reading its slot's row.  k_attn_mla (64 heads per workgroup)
+//    serves other head counts and page sizes.
 //  * k_attn_combine merges split partials (O, max, normaliser); k_attn_pad
 //    writes the rows between the packed count and the tier.
 //  * fp32 inputs take a plain vector kernel (k_attn_f32).
@@ -1067,11 +1069,18 @@ constexpr int kRowRedBytes = 4 * 32 * 4;      // per-vector sums [vector block][
 constexpr int kRowQrBytes = 4 * 4 * 64 * 16;   // rope query fragments [wave][step][lane], 16 B
 constexpr int kRowLdsBytes = kMlaStages * kMlaStageBytes + kRowXBytes + kRowRedBytes + kPageWin * 4 + kRowQrBytes;
 static_assert(kRowLdsBytes <= 160 * 1024, "latent row kernel LDS");
+static_assert(kMaxTopk <= kPageWin && kMaxTopk % 256 == 0, "a key list's slots fit the page-window area");
 
+// SPARSE: the row attends to its key list (topk_idx); the item's slice of
+// the list, less the entries that name no visible position, is compacted in
+// list order into cache rows in the page-window area, and the tile loop runs
+// over those slots as over dense keys, each DMA lane reading its slot's row.
+template <bool SPARSE>
 __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item, unsigned char* smem) {
   constexpr int kRing = kMlaStages * kMlaStageBytes;
   float* red_l = reinterpret_cast<float*>(smem + kRing + kRowXBytes);
   int* pwin = reinterpret_cast<int*>(smem + kRing + kRowXBytes + kRowRedBytes);
+  int* sidx = pwin;   // SPARSE: the compacted slots' cache rows (no page window then)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1090,24 +1099,70 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   const int row = row_start + rl;
   const int pos = c + rl;                // the row's position: keys 0..pos are visible
   const int chunk = p.hdr[1];
-  const int kv_begin = win_origin(c, p.window) + sp * chunk;
-  const int kv_end = min(kv_begin + chunk, pos + 1);
+  // keys [kv_begin, kv_end): positions, or (SPARSE) compacted slots
+  const int kv_begin = SPARSE ? sp * chunk : win_origin(c, p.window) + sp * chunk;
+  int kv_end = SPARSE ? min(kv_begin + chunk, p.topk) : min(kv_begin + chunk, pos + 1);
   const int P = p.page_size;
-  const int lim = kv_end - 1;            // last key this item may see
-  const int low = win_low(pos, p.window);
+  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
 
   const int pg0 = kv_begin / P;
-  int npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
-  if (npg > kPageWin) {
-    if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
-    npg = kPageWin;
+  int npg = 0;
+  if constexpr (SPARSE) {
+    // list entries [kv_begin, kv_end) of this row (at most kMaxTopk, eight
+    // per thread): those naming a position in 0..pos, in list order, as
+    // cache rows; the other entries (-1 pads, later positions) are dropped
+    const int32_t* src = p.topk_idx + (size_t)row * p.topk;
+    int rr[kMaxTopk / 256], cnt[1] = {0};
+#pragma unroll
+    for (int k = 0; k < kMaxTopk / 256; ++k) {
+      const int x = tid * (kMaxTopk / 256) + k;
+      int r = -1;
+      if (x < kv_end - kv_begin) {
+        const int j = src[kv_begin + x];
+        if (j >= 0 && j <= pos) {
+          int pg = (j / P < p.max_pages) ? pt_row[j / P] : -1;
+          if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+          r = pg * P + j % P;
+        }
+      }
+      rr[k] = r;
+      cnt[0] += r >= 0 ? 1 : 0;
+    }
+    // exclusive scan of the counts over the 256 threads (wave scan, then the
+    // four wave totals through LDS)
+    wave_incl_scan<1>(cnt);
+    int* wtot = reinterpret_cast<int*>(red_l);
+    if (lane == 63) wtot[wid] = cnt[0];
+    __syncthreads();
+    int off = cnt[0] - 0, all = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = wtot[u];
+      off += u < wid ? v : 0;
+      all += v;
+    }
+    int own = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk / 256; ++k) own += rr[k] >= 0 ? 1 : 0;
+    off -= own;
+#pragma unroll
+    for (int k = 0; k < kMaxTopk / 256; ++k)
+      if (rr[k] >= 0) sidx[off++] = rr[k];
+    kv_end = kv_begin + all;   // the item's keys are now slots kv_begin .. kv_begin + all - 1
+  } else {
+    npg = kv_end > kv_begin ? (kv_end - 1) / P - pg0 + 1 : 0;
+    if (npg > kPageWin) {
+      if (tid == 0) set_status(p.status, RV_DEV_BAD_PAGE);
+      npg = kPageWin;
+    }
+    for (int x = tid; x < npg; x += 256) {
+      int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
+      if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
+      pwin[x] = pg;
+    }
   }
-  const int* pt_row = p.page_table + (size_t)i * p.max_pages;
-  for (int x = tid; x < npg; x += 256) {
-    int pg = (pg0 + x < p.max_pages) ? pt_row[pg0 + x] : -1;
-    if (pg < 0 || pg >= p.num_pages) { set_status(p.status, RV_DEV_BAD_PAGE); pg = 0; }
-    pwin[x] = pg;
-  }
+  const int lim = kv_end - 1;            // last key (slot) this item may see
+  const int low = SPARSE ? INT32_MIN : win_low(pos, p.window);
 
   // query fragments: vector 32*wid + n32, dims 16*ks + 8*hl .. +7; the 512
   // value dims in registers, the 64 rope dims (steps 32..35) in this wave's
@@ -1126,7 +1181,7 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   }
   auto is_full = [&](int t0) { return t0 + kNK - 1 <= lim && t0 >= low; };
   wait_vm<0>();
-  __syncthreads();   // page window visible
+  __syncthreads();   // page window (SPARSE: compacted slots) visible
 
   const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + kNK - 1) / kNK : 0;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)smem;
@@ -1134,33 +1189,60 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wid * kMlaDmaPerWave * 1024);
   const int cbase = wid * kMlaDmaPerWave * 64 + lane;
   const int last = kv_end - 1;
+  // per DMA instruction e of this lane: its row r of the tile and chunk; the
+  // byte offset r * row + swizzled chunk (SPARSE: r | chunk byte offset << 8)
   uint32_t dma_off[kMlaDmaPerWave];
 #pragma unroll
   for (int e = 0; e < kMlaDmaPerWave; ++e) {
     const int cidx = cbase + e * 64;
     const int r = cidx / kMlaChunksPerRow;
-    dma_off[e] = (uint32_t)(r * kMlaRowBytes + ((cidx - r * kMlaChunksPerRow) ^ lswz(r)) * 16);
+    const uint32_t cb = (uint32_t)(((cidx - r * kMlaChunksPerRow) ^ lswz(r)) * 16);
+    dma_off[e] = SPARSE ? (uint32_t)r | (cb << 8) : (uint32_t)(r * kMlaRowBytes) + cb;
   }
   struct DmaTile {
     const void* base;
     uint32_t lim;
     uint32_t lds0;
+    int t0;
   };
   auto dma_tile = [&](int t, int st, int pg) {
     const int t0 = kv_begin + t * kNK;
     DmaTile d;
-    d.base = uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
-                         ((size_t)pg * P + (t0 & (P - 1))) * kMlaRowBytes);
+    d.base = SPARSE ? p.k
+                    : uniform_ptr(reinterpret_cast<const unsigned char*>(p.k) +
+                                  ((size_t)pg * P + (t0 & (P - 1))) * kMlaRowBytes);
     d.lim = (uint32_t)(min(last - t0, kNK - 1) * kMlaRowBytes + kMlaRowBytes - 16);
     d.lds0 = wave_lds + st * kMlaStageBytes;
+    d.t0 = t0;
     return d;
   };
-  auto dma_one = [&](const DmaTile& d, int e) { dma16_s(min(dma_off[e], d.lim), d.base, d.lds0 + e * 1024); };
-  auto page_at = [&](int t) { return pwin[((kv_begin + t * kNK) >> p.log2P) - pg0]; };
+  // SPARSE: the cache row of the slot that DMA e of tile d reads (slots past
+  // the item's last read the last one: finite data, masked)
+  auto slot_row = [&](const DmaTile& d, int e) {
+    return sidx[min(d.t0 + (int)(dma_off[e] & 255u), last) - kv_begin];
+  };
+  auto dma_row = [&](const DmaTile& d, int e, int krow) {
+    dma16(reinterpret_cast<const unsigned char*>(p.k) + (size_t)krow * kMlaRowBytes + (dma_off[e] >> 8),
+          d.lds0 + e * 1024);
+  };
+  auto dma_one = [&](const DmaTile& d, int e) {
+    if constexpr (SPARSE) dma_row(d, e, slot_row(d, e));
+    else dma16_s(min(dma_off[e], d.lim), d.base, d.lds0 + e * 1024);
+  };
+  auto page_at = [&](int t) { return SPARSE ? 0 : pwin[((kv_begin + t * kNK) >> p.log2P) - pg0]; };
   auto issue = [&](int t, int st) {
     const DmaTile d = dma_tile(t, st, __builtin_amdgcn_readfirstlane(page_at(t)));
+    if constexpr (SPARSE) {
+      // every slot's row first (the LDS reads overlap), then the DMAs
+      int kr[kMlaDmaPerWave];
 #pragma unroll
-    for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(d, e);
+      for (int e = 0; e < kMlaDmaPerWave; ++e) kr[e] = slot_row(d, e);
+#pragma unroll
+      for (int e = 0; e < kMlaDmaPerWave; ++e) dma_row(d, e, kr[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < kMlaDmaPerWave; ++e) dma_one(d, e);
+    }
   };
 
   // QK fragment offsets: row n32, logical chunk 2*ks + hl; the swizzle
@@ -1311,8 +1393,20 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
       f32x16_t sc;
       // the next tile's DMA, one instruction every fourth QK step (issued
       // all at once, or during PV, it measured slower)
+      // SPARSE: each DMA's slot row is read one DMA ahead
+      int kr_next = 0;
+      if constexpr (SPARSE) kr_next = slot_row(dnext, 0);
       auto spread_dma = [&](int ks) {
-        if ((ks & 3) == 0) dma_one(dnext, ks >> 2);
+        if ((ks & 3) == 0) {
+          const int e = ks >> 2;
+          if constexpr (SPARSE) {
+            const int kr = kr_next;
+            if (e + 1 < kMlaDmaPerWave) kr_next = slot_row(dnext, e + 1);
+            dma_row(dnext, e, kr);
+          } else {
+            dma_one(dnext, e);
+          }
+        }
       };
       if (more) {
         qk_tile(stg_next, sc, spread_dma);
@@ -1438,6 +1532,7 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   }
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(256) void k_attn_mla_row(MainParams p) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_item;
@@ -1445,7 +1540,7 @@ __global__ __launch_bounds__(256) void k_attn_mla_row(MainParams p) {
   for (;;) {
     const int item = next_item(p, &s_item, done);
     if (item < 0) break;
-    attn_mla_row_item(p, item, smem);
+    attn_mla_row_item<SPARSE>(p, item, smem);
   }
 }
 
@@ -2309,11 +2404,12 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     return hipGetLastError();
   }
 
-  // latent: the row kernel for dense attention over power-of-two pages of at
-  // least 32 keys with a multiple of 128 heads; the 64-vector kernel otherwise
+  // latent: the row kernel for a multiple of 128 heads, with key lists
+  // (sparse) or dense over power-of-two pages of at least 32 keys; the
+  // 64-vector kernel otherwise
   const bool pow2_pages = (a.page_size & (a.page_size - 1)) == 0;
-  const bool row_kernel = latent && a.topk_idx == nullptr && pow2_pages && a.page_size >= 32 &&
-                          a.Hq % kRowQT == 0;
+  const bool row_kernel = latent && a.Hq % kRowQT == 0 &&
+                          (a.topk_idx != nullptr || (pow2_pages && a.page_size >= 32));
   AttnShape sh;
   int nw = 0;
   if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw, row_kernel)) return hipErrorInvalidValue;
@@ -2396,12 +2492,15 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   mp.ctr = pp.hdr + kHdrCtr;
 
   if (row_kernel) {
-    const void* kern = reinterpret_cast<const void*>(k_attn_mla_row);
+    const bool sparse = a.topk_idx != nullptr;
+    const void* kern = sparse ? reinterpret_cast<const void*>(k_attn_mla_row<true>)
+                              : reinterpret_cast<const void*>(k_attn_mla_row<false>);
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, kRowLdsBytes);
     if (e != hipSuccess) return e;
     int grid = 0;
     if ((e = persistent_grid(kern, 256, kRowLdsBytes, &grid)) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_mla_row, dim3(grid), dim3(256), kRowLdsBytes, s, mp);
+    if (sparse) hipLaunchKernelGGL(k_attn_mla_row<true>, dim3(grid), dim3(256), kRowLdsBytes, s, mp);
+    else hipLaunchKernelGGL(k_attn_mla_row<false>, dim3(grid), dim3(256), kRowLdsBytes, s, mp);
     e = hipGetLastError();
   } else if (latent) {
     const bool sparse = a.topk_idx != nullptr;

@@ -185,6 +185,39 @@ def test_sparse_latent_split_and_empty_rows():
     assert np.all(o[1:M] == 0) and np.all(np.isneginf(step.lse.cpu().numpy()[1:M]))
 
 
+def test_sparse_latent_row_kernel_lists():
+    """128 heads (the one-workgroup-per-row kernel): 2048-entry lists over
+    long contexts (the list split into chunks and merged), with -1 entries,
+    positions past the row and repeated positions scattered through each list
+    (the kernel compacts the visible entries of its chunk in list order; a
+    repeat counts once per entry); then lists with nothing visible."""
+    inp = pu.make_inputs("mla_bf16", B=2, V=500, H=256, ctx=("uniform", 3000, 5000))
+    g = torch.Generator().manual_seed(7)
+    gamma, K = inp["gamma"], 2048
+    ctx = inp["ctx"].cpu()
+    blk = torch.empty((2, gamma, K), dtype=torch.int32)
+    for b in range(2):
+        for k in range(gamma):
+            p_ = int(ctx[b]) + k
+            lst = torch.randint(0, p_ + 1, (K,), generator=g, dtype=torch.int32)
+            u = torch.rand(K, generator=g)
+            lst[u < 0.1] = -1                                   # pads inside the list
+            lst[(u >= 0.1) & (u < 0.2)] = p_ + 1 + (lst[(u >= 0.1) & (u < 0.2)] % 50)   # past the row
+            lst[1::97] = lst[0::97][: lst[1::97].numel()]       # repeats
+            blk[b, k] = lst
+    inp["topk_block"] = blk.to("cuda")
+    _full_parity(inp, "static", "bf16", topk=K)
+    _full_parity(inp, "compact", "bf16", topk=K)
+    inp = pu.make_inputs("mla_bf16", B=2, V=500, H=256, ctx=("uniform", 100, 300))
+    blk = torch.full((2, inp["gamma"], 600), 10**6, dtype=torch.int32, device="cuda")
+    blk[0, 0, 5] = 3   # one visible key for one row
+    inp["topk_block"] = blk
+    step, ref, want = _full_parity(inp, "static", "bf16", topk=600)
+    M = ref["M"]
+    o = step.o.float().cpu().numpy()
+    assert np.all(o[1:M] == 0) and np.all(np.isneginf(step.lse.cpu().numpy()[1:M]))
+
+
 @pytest.mark.parametrize("B", [1, 4])
 def test_lm_few_rows_odd_vocab(B):
     """At most 32 packed rows take the one-wave weight-streaming kernel; with
