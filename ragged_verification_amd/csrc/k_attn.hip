@@ -87,13 +87,13 @@ struct PlanParams {
   const int32_t* cu;
   const int32_t* ctx;
   const int32_t* mm;
-  int4* req_info;        // per request: {n_splits, first group, part_off, tiles}
+  int4* req_info;        // per request: {n_splits, chunk (keys), part_off, tiles}
   int4* items;           // {request, tile, split, 0}, grouped by XCD list
   int2* grp;             // scratch: {request, split} of each group by rank
   int2* split;           // {request, tile} of every tile with split partials
   int32_t* hdr;
   int B, gamma, item_cap, part_cap, target;
-  int n_workers;         // balanced plan: persistent workgroups of the main kernel
+  int n_workers;         // persistent workgroups of the main kernel
   int window;            // sliding window (keys), 0 = full causal
   int topk;              // sparse latent attention: index entries per row (0: dense)
   AttnShape sh;
@@ -121,6 +121,7 @@ constexpr int kPlanMaxB = RV_MAX_ROWS / 2;   // gamma >= 2
 
 __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   __shared__ int2 s_wl[kPlanMaxB];            // per request: window, keys (ctx + window)
+  __shared__ int s_ci[kPlanMaxB];             // per request: its chunk
   __shared__ int s_buf[kPlanWaves * 8];
   __shared__ long long s_red[kPlanWaves];
   __shared__ int hist[64];
@@ -172,6 +173,97 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
     C *= 2;
   }
 
+  // Per-request chunks (req_info.y).  When the work ends on items that are
+  // long next to a worker's share (equal-length requests, e.g. under a
+  // sliding window or with key lists: 815 equal items on 256 workers run 3.2
+  // rounds and most workers idle through the fourth), the requests with the
+  // shortest key ranges get a chunk m times finer, enough of them that about
+  // one finer piece per worker ends the longest-first schedule.  "Long" is
+  // judged at the request that completes the shortest n_workers tiles.
+  for (int i = i0; i < i1; ++i) s_ci[i] = C;
+  {
+    __shared__ int s_cut[3];
+    int lmin = INT32_MAX, lmax = 0;
+    for (int i = i0; i < i1; ++i) {
+      lmin = min(lmin, s_wl[i].y);
+      lmax = max(lmax, s_wl[i].y);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lmin = min(lmin, __shfl_xor(lmin, off));
+      lmax = max(lmax, __shfl_xor(lmax, off));
+    }
+    __syncthreads();   // s_buf is free
+    if (lane == 0) {
+      s_buf[(t >> 6) * 2] = lmin;
+      s_buf[(t >> 6) * 2 + 1] = lmax;
+    }
+    if (t < 64) hist[t] = 0;
+    __syncthreads();
+    for (int u = 0; u < kPlanWaves; ++u) {
+      lmin = min(lmin, s_buf[u * 2]);
+      lmax = max(lmax, s_buf[u * 2 + 1]);
+    }
+    // tiles by key-range length: 64 buckets over [lmin, lmax]
+    const long long span = (long long)lmax - lmin + 1;
+    auto lb = [&](int L) { return (int)(((long long)(L - lmin) * 64) / span); };
+    for (int i = i0; i < i1; ++i) atomicAdd(&hist[lb(s_wl[i].y)], tiles_of_w(s_wl[i].x));
+    __syncthreads();
+    if (t == 0) {
+      const long long share = p.n_workers > 0 ? all_work / p.n_workers : 0;   // tile-keys per worker
+      int m = 1, cum = 0, b = 0;
+      if (share > 0) {
+        while (b < 63 && cum + hist[b] < p.n_workers) cum += hist[b++];
+        const long long lk = min((long long)C, lmin + ((long long)(b + 1) * span + 63) / 64);   // that request's item length, at most
+        if (lk * 8 > share) m = (int)min(8LL, (lk * 8 + share - 1) / share);
+      }
+      int bc = 0;
+      cum = 0;
+      if (m >= 2) {
+        const int need = ceil_div(p.n_workers, m);
+        while (bc < 63 && cum + hist[bc] < need) cum += hist[bc++];
+        cum = need - cum;   // tiles still wanted from bucket bc, in request order
+      }
+      s_cut[0] = m;
+      s_cut[1] = bc;   // buckets below bc: all chosen
+      s_cut[2] = cum;
+    }
+    __syncthreads();
+    const int m = s_cut[0], bcut = s_cut[1], rem = s_cut[2];
+    if (m >= 2) {
+      int in_b[1] = {0}, ex_b[1], tot_b[1];
+      for (int i = i0; i < i1; ++i)
+        if (lb(s_wl[i].y) == bcut) in_b[0] += tiles_of_w(s_wl[i].x);
+      block_excl_scan<1>(in_b, ex_b, tot_b, s_buf);
+      int before = ex_b[0];
+      for (int i = i0; i < i1; ++i) {
+        const int2 wl = s_wl[i];
+        const int b = lb(wl.y);
+        bool pick = b < bcut;
+        if (b == bcut) {
+          pick = before < rem;
+          before += tiles_of_w(wl.x);
+        }
+        if (pick && wl.y > 0) s_ci[i] = max(ceil_div(ceil_div(min(C, wl.y), m), kNK) * kNK, kNK);
+      }
+      // keep the finer chunks only if items and partial slots still fit
+      int cnt[2] = {0, 0}, ex[2], tot[2];
+      for (int i = i0; i < i1; ++i) {
+        const int2 wl = s_wl[i];
+        const int tiles = tiles_of_w(wl.x);
+        const int ns = wl.y > 0 ? ceil_div(wl.y, s_ci[i]) : 1;
+        cnt[0] += ns * tiles;
+        cnt[1] += ns > 1 ? ns * tiles : 0;
+      }
+      block_excl_scan<2>(cnt, ex, tot, s_buf);
+      if (tot[0] > p.item_cap || tot[1] > p.part_cap)
+        for (int i = i0; i < i1; ++i) s_ci[i] = C;
+    }
+    __syncthreads();
+    if (t < 64) hist[t] = 0;
+    __syncthreads();
+  }
+
   // A group is the set of tiles of one request that read one key chunk; its
   // tiles run on one XCD, one after another in that XCD's list, so the chunk
   // is fetched into that XCD's L2 once.  Groups are ranked longest chunk
@@ -181,7 +273,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   int mine[3] = {0, 0, 0}, off2[3], tot2[3];
   for (int i = i0; i < i1; ++i) {
     const int2 wl = s_wl[i];
-    const int ns = wl.y > 0 ? ceil_div(wl.y, C) : 1;
+    const int ns = wl.y > 0 ? ceil_div(wl.y, s_ci[i]) : 1;
     mine[0] += ns;
     mine[1] += ns > 1 ? ns * tiles_of_w(wl.x) : 0;
     mine[2] += ns > 1 ? tiles_of_w(wl.x) : 0;
@@ -189,13 +281,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   block_excl_scan<3>(mine, off2, tot2, s_buf);
   const int n_groups = tot2[0];
   const int n_parts = tot2[1];
-  int grp_off = off2[0], part_off = off2[1], split_off = off2[2];
+  int part_off = off2[1], split_off = off2[2];
   // bucket of a chunk of `len` keys: 0 for a full chunk, up to 63 for the shortest
   auto bucket = [&](int len) { return (int)(((long long)(C - len) * 64) / C); };
   for (int i = i0; i < i1; ++i) {
-    const int L = s_wl[i].y;
-    const int ns = L > 0 ? ceil_div(L, C) : 1;
-    for (int sp = 0; sp < ns; ++sp) atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
+    const int L = s_wl[i].y, ci = s_ci[i];
+    const int ns = L > 0 ? ceil_div(L, ci) : 1;
+    for (int sp = 0; sp < ns; ++sp) atomicAdd(&hist[bucket(max(min(ci, L - sp * ci), 1))], 1);
   }
   __syncthreads();
   if (t < 64) {   // exclusive scan of the 64 bucket counts by wave 0
@@ -208,16 +300,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   for (int i = i0; i < i1; ++i) {
     const int2 wl = s_wl[i];
     const int tiles = tiles_of_w(wl.x);
-    const int L = wl.y;
-    const int ns = L > 0 ? ceil_div(L, C) : 1;
-    p.req_info[i] = make_int4(ns, grp_off, ns > 1 ? part_off : -1, tiles);
+    const int L = wl.y, ci = s_ci[i];
+    const int ns = L > 0 ? ceil_div(L, ci) : 1;
+    p.req_info[i] = make_int4(ns, ci, ns > 1 ? part_off : -1, tiles);
     if (ns > 1)
       for (int tl = 0; tl < tiles; ++tl) p.split[split_off++] = make_int2(i, tl);
     for (int sp = 0; sp < ns; ++sp) {
-      const int rank = atomicAdd(&hist[bucket(max(min(C, L - sp * C), 1))], 1);
+      const int rank = atomicAdd(&hist[bucket(max(min(ci, L - sp * ci), 1))], 1);
       p.grp[rank] = make_int2(i, sp);
     }
-    grp_off += ns;
     part_off += ns > 1 ? ns * tiles : 0;
   }
   __syncthreads();   // the ranked groups are visible to the whole workgroup
@@ -234,7 +325,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   auto group_work = [&](int r) {
     const int2 g = p.grp[r];
     const int2 wl = s_wl[g.x];
-    return tiles_of_w(wl.x) * ceil_div(max(min(C, wl.y - g.y * C), 1), kNK);
+    const int ci = s_ci[g.x];
+    return tiles_of_w(wl.x) * ceil_div(max(min(ci, wl.y - g.y * ci), 1), kNK);
   };
   int wv[1] = {0}, wex[1], wtot[1];
   for (int r = r0; r < r1; ++r) wv[0] += group_work(r);
@@ -618,7 +710,7 @@ __device__ __forceinline__ void attn_mla_item(const MainParams& p, int item, uns
   // SPARSE: keys [kv_begin, kv_end) are index slots of the tile's one row,
   // whose positions lie in 0 .. c + row0
   const int L_tile = SPARSE ? p.topk : c + row0 + rows_here;
-  const int chunk = p.hdr[1];
+  const int chunk = info.y;   // this request's chunk
   const int kv_begin = (SPARSE ? 0 : win_origin(c, p.window)) + sp * chunk;
   const int kv_end = min(kv_begin + chunk, L_tile);
   const int P = p.page_size;
@@ -1098,7 +1190,7 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   const int hb = tile % p.n_hb;          // its block of 128 heads
   const int row = row_start + rl;
   const int pos = c + rl;                // the row's position: keys 0..pos are visible
-  const int chunk = p.hdr[1];
+  const int chunk = info.y;   // this request's chunk
   // keys [kv_begin, kv_end): positions, or (SPARSE) compacted slots
   const int kv_begin = SPARSE ? sp * chunk : win_origin(c, p.window) + sp * chunk;
   int kv_end = SPARSE ? min(kv_begin + chunk, p.topk) : min(kv_begin + chunk, pos + 1);
@@ -1914,7 +2006,7 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const int4 rec = p.items[item];
   const int i = rec.x, tile = rec.y, sp = rec.z;
   const int4 info = p.req_info[i];
-  const int chunk = p.hdr[1];
+  const int chunk = info.y;   // this request's chunk
   const int kv_lo = win_origin(p.ctx[i], p.window) + sp * chunk;
   const int kv_hi = (int)min((long long)kv_lo + chunk, (long long)INT32_MAX);
   const int slot = info.x == 1 ? -1 : (info.z < 0 ? INT32_MAX : info.z + sp * info.w + tile);
@@ -2446,7 +2538,22 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
   pp.item_cap = L.item_cap;
   pp.part_cap = L.part_slots;
   pp.target = sh.target;
-  pp.n_workers = bal_grid;
+  // workers of the main kernel (the chunked plan sizes its finer chunks by
+  // them; 0 for the GQA fallback, which keeps one chunk length)
+  int chunk_workers = 0;
+  if (!bal && latent) {
+    const bool sparse = a.topk_idx != nullptr;
+    const bool fast = !sparse && (a.page_size & (a.page_size - 1)) == 0 && a.page_size >= 32;
+    const void* kern = row_kernel ? (sparse ? reinterpret_cast<const void*>(k_attn_mla_row<true>)
+                                            : reinterpret_cast<const void*>(k_attn_mla_row<false>))
+                       : sparse ? reinterpret_cast<const void*>(k_attn_mla<false, true>)
+                       : fast   ? reinterpret_cast<const void*>(k_attn_mla<true, false>)
+                                : reinterpret_cast<const void*>(k_attn_mla<false, false>);
+    const int lds = row_kernel ? kRowLdsBytes : kMlaLdsBytes;
+    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if ((e = persistent_grid(kern, 256, lds, &chunk_workers)) != hipSuccess) return e;
+  }
+  pp.n_workers = bal ? bal_grid : chunk_workers;
   pp.window = a.window;
   pp.topk = a.topk_idx ? a.topk : 0;
   pp.sh = sh;
