@@ -125,6 +125,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   __shared__ int s_buf[kPlanWaves * 8];
   __shared__ long long s_red[kPlanWaves];
   __shared__ int hist[64];
+  __shared__ int hwork[64];
   __shared__ int s_rs;
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -209,24 +210,32 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
     auto lb = [&](int L) { return (int)(((long long)(L - lmin) * 64) / span); };
     for (int i = i0; i < i1; ++i) atomicAdd(&hist[lb(s_wl[i].y)], tiles_of_w(s_wl[i].x));
     __syncthreads();
-    if (t == 0) {
+    if (t < 64) {   // wave 0: cumulative tiles over the buckets
+      int h[1] = {hist[t]};
+      wave_incl_scan<1>(h);
+      // first bucket whose cumulative count reaches x (63 if none), and the
+      // count before it
+      auto first_reach = [&](int x, int& before) {
+        const unsigned long long hit = __ballot(h[0] >= x);
+        const int b = hit ? __ffsll((long long)hit) - 1 : 63;
+        before = __shfl(h[0], b > 0 ? b - 1 : 0);
+        if (b == 0) before = 0;
+        return b;
+      };
       const long long share = p.n_workers > 0 ? all_work / p.n_workers : 0;   // tile-keys per worker
-      int m = 1, cum = 0, b = 0;
+      int m = 1, bc = 0, before = 0;
       if (share > 0) {
-        while (b < 63 && cum + hist[b] < p.n_workers) cum += hist[b++];
+        const int b = first_reach(p.n_workers, before);
         const long long lk = min((long long)C, lmin + ((long long)(b + 1) * span + 63) / 64);   // that request's item length, at most
         if (lk * 8 > share) m = (int)min(8LL, (lk * 8 + share - 1) / share);
       }
-      int bc = 0;
-      cum = 0;
-      if (m >= 2) {
-        const int need = ceil_div(p.n_workers, m);
-        while (bc < 63 && cum + hist[bc] < need) cum += hist[bc++];
-        cum = need - cum;   // tiles still wanted from bucket bc, in request order
+      const int need = ceil_div(max(p.n_workers, 1), m);
+      if (m >= 2) bc = first_reach(need, before);
+      if (t == 0) {
+        s_cut[0] = m;
+        s_cut[1] = bc;              // buckets below bc: all chosen
+        s_cut[2] = need - before;   // tiles still wanted from bucket bc, in request order
       }
-      s_cut[0] = m;
-      s_cut[1] = bc;   // buckets below bc: all chosen
-      s_cut[2] = cum;
     }
     __syncthreads();
     const int m = s_cut[0], bcut = s_cut[1], rem = s_cut[2];
@@ -284,17 +293,50 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
   int part_off = off2[1], split_off = off2[2];
   // bucket of a chunk of `len` keys: 0 for a full chunk, up to 63 for the shortest
   auto bucket = [&](int len) { return (int)(((long long)(C - len) * 64) / C); };
+  if (t < 64) hwork[t] = 0;
+  __syncthreads();
   for (int i = i0; i < i1; ++i) {
     const int L = s_wl[i].y, ci = s_ci[i];
     const int ns = L > 0 ? ceil_div(L, ci) : 1;
-    for (int sp = 0; sp < ns; ++sp) atomicAdd(&hist[bucket(max(min(ci, L - sp * ci), 1))], 1);
+    const int tiles = tiles_of_w(s_wl[i].x);
+    for (int sp = 0; sp < ns; ++sp) {
+      const int len = max(min(ci, L - sp * ci), 1);
+      atomicAdd(&hist[bucket(len)], 1);
+      atomicAdd(&hwork[bucket(len)], tiles * ceil_div(len, kNK));   // work in 32-key tiles
+    }
   }
   __syncthreads();
-  if (t < 64) {   // exclusive scan of the 64 bucket counts by wave 0
-    int h[1] = {hist[t]};
-    const int own = h[0];
-    wave_incl_scan<1>(h);
-    hist[t] = h[0] - own;
+  // The ranks from rs on (the shortest chunks, from the first bucket at
+  // which about 100 - kTailPct percent of the work, counted in 32-key tiles,
+  // lies before it) form a shared tail list, which every worker takes from
+  // once its own XCD's list is empty.  The XCD lists are dealt by group
+  // count and a group is one to eight rows, so their work differs; without
+  // a shared tail the last items taken are wherever the fullest list had got
+  // to (on the latent batch workers then ended up to 0.3 ms apart; a fifth
+  // of the work in the tail was not enough, 35% to 70% measured alike).
+  if (t < 64) {   // wave 0: exclusive scans of the bucket counts and works
+    int h[2] = {hist[t], hwork[t]};
+    const int own_c = h[0], own_w = h[1];
+    wave_incl_scan<2>(h);
+    hist[t] = h[0] - own_c;
+    const int wall = __shfl(h[1], 63);
+    const int thresh = wall - (int)((long long)wall * kTailPct / 100);
+    // the bucket in which the threshold falls; within it, the groups (of
+    // about equal chunk length) are cut by count in proportion
+    const unsigned long long hit = __ballot(h[1] >= thresh && own_c > 0);
+    const int bt = hit ? __ffsll((long long)hit) - 1 : 63;
+    const int src = bt;
+    const int start_bt = __shfl(h[0] - own_c, src);   // first rank of bucket bt
+    const int cnt_bt = __shfl(own_c, src);
+    const int wex_bt = __shfl(h[1] - own_w, src);
+    const int w_bt = __shfl(own_w, src);
+    if (t == 0) {
+      int r = n_groups;
+      if (hit && w_bt > 0)
+        r = start_bt + (int)min((long long)cnt_bt,
+                                ((long long)(thresh - wex_bt) * cnt_bt + w_bt - 1) / w_bt);
+      s_rs = r;
+    }
   }
   __syncthreads();
   for (int i = i0; i < i1; ++i) {
@@ -312,40 +354,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
     part_off += ns > 1 ? ns * tiles : 0;
   }
   __syncthreads();   // the ranked groups are visible to the whole workgroup
-
-  // The ranks from rs on (the shortest chunks, about kTailPct of the work
-  // counted in 32-key tiles) form a shared tail list, which every worker
-  // takes from once its own XCD's list is empty.  The XCD lists are dealt by
-  // group count and a group is one to eight rows, so their work differs;
-  // without a shared tail the last items taken are wherever the fullest list
-  // had got to (on the latent batch workers then ended up to 0.3 ms apart;
-  // a fifth of the work in the tail was not enough, 35% to 70% measured alike).
+  const int rs = s_rs;
   const int segr = ceil_div(n_groups, kPlanThreads);
   const int r0 = min(t * segr, n_groups), r1 = min(r0 + segr, n_groups);
-  auto group_work = [&](int r) {
-    const int2 g = p.grp[r];
-    const int2 wl = s_wl[g.x];
-    const int ci = s_ci[g.x];
-    return tiles_of_w(wl.x) * ceil_div(max(min(ci, wl.y - g.y * ci), 1), kNK);
-  };
-  int wv[1] = {0}, wex[1], wtot[1];
-  for (int r = r0; r < r1; ++r) wv[0] += group_work(r);
-  block_excl_scan<1>(wv, wex, wtot, s_buf);
-  if (t == 0) s_rs = n_groups;
-  __syncthreads();
-  {
-    const int thresh = wtot[0] - (int)((long long)wtot[0] * kTailPct / 100);
-    int run = wex[0];
-    for (int r = r0; r < r1; ++r) {
-      if (run >= thresh) {
-        atomicMin(&s_rs, r);
-        break;
-      }
-      run += group_work(r);
-    }
-  }
-  __syncthreads();
-  const int rs = s_rs;
 
   // items per (cycle, XCD) slot, scanned along the cycles of each XCD
   const int nc = ceil_div(rs, 8);
