@@ -621,6 +621,17 @@ def main():
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "algorithmic_per_launch": c["attn_bytes"], "launch_ms": attn_ms}
     lm_tflops = c["lm_flops"] / (lm_ms / 1e3) / 1e12
+    # the LM head streams the weight once per launch: below the ridge point
+    # (bf16 peak flops per HBM byte) its bound is HBM, above it the MFMAs
+    lm_bytes = 2 * wl.V * wl.H + 2 * c["M"] * wl.H + 16 * c["M"] * -(-wl.V // 64)
+    if c["lm_flops"] / lm_bytes < PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        lm_gbs = lm_bytes / (lm_ms / 1e3) / 1e9
+        lm_roof = {"bound": "hbm", "achieved": lm_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": lm_gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": lm_bytes, "launch_ms": lm_ms}
+    else:
+        lm_roof = {"bound": "mfma", "achieved": lm_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                   "frac": lm_tflops / PEAK_BF16_TFLOPS, "algorithmic_per_launch": c["lm_flops"],
+                   "launch_ms": lm_ms}
     line = {
         "metric": METRIC,
         "value": c["M"] / t_s,
@@ -644,8 +655,7 @@ def main():
         "packed_rows": c["M"], "tier_rows": c["M_pad"], "committed_per_step": c["committed"],
         "stages_ms": {k: round(v, 4) for k, v in c["per_stage_ms"].items()},
         "wall_ms_per_step_incl_staging_restore": round(c["wall_ms"], 3),
-        "lm_head": {"achieved": lm_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": lm_tflops / PEAK_BF16_TFLOPS, "launch_ms": lm_ms},
+        "lm_head": lm_roof,
         "roofline": roof,
     }
     if "calibration" in c:
