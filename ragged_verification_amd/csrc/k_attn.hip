@@ -439,6 +439,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
 // consecutive partial slots, one per worker in order.
 __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
   __shared__ int2 s_wc[kPlanMaxB];            // per request: window, context
+  __shared__ int2 s_off[kPlanMaxB];           // per request: first tile, first cost unit
   __shared__ int s_buf[kPlanWaves * 8];
   const int t = threadIdx.x;
   const int B = p.B;
@@ -453,7 +454,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
     return ceil_div(L_tile - win_origin(c, p.window), kBalSuper);
   };
 
-  int cnt[2] = {0, 0}, off[2], tot[2];   // tiles, super-tiles
+  // per request: tiles and cost units (super-tiles plus kBalPro per tile)
+  int cnt[2] = {0, 0}, off[2], tot[2];
   for (int i = i0; i < i1; ++i) {
     const int w = p.cu[i + 1] - p.cu[i];
     const int c = p.ctx[i];
@@ -466,47 +468,62 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
   const int n_tiles = tot[0], S = tot[1];
   const int q = max(1, ceil_div(S, max(p.n_workers, 1)));
   const int n_vw = ceil_div(S, q);
-
-  // partial slots: a tile split over k > 1 workers takes k; and the split tiles
-  int parts[2] = {0, 0}, poff[2], ptot[2];
   {
-    int st = off[1];
+    int T = off[0], st = off[1];
     for (int i = i0; i < i1; ++i) {
       const int2 wc = s_wc[i];
       const int n_rb = ceil_div(wc.x, sh.RT);
-      for (int rb = 0; rb < n_rb; ++rb) {
-        const int n = nst(wc.x, wc.y, rb);
-        for (int k = 0; k < per_rb; ++k, st += n + kBalPro) {
-          const int s0 = st + kBalPro;   // cost position of the tile's first super-tile
-          const int kseg = (s0 + n - 1) / q - s0 / q + 1;
-          parts[0] += kseg > 1 ? kseg : 0;
-          parts[1] += kseg > 1 ? 1 : 0;
-        }
-      }
+      s_off[i] = make_int2(T, st);
+      p.req_info[i] = make_int4(n_rb * per_rb, T, 0, 0);
+      T += n_rb * per_rb;
+      for (int rb = 0; rb < n_rb; ++rb) st += per_rb * (nst(wc.x, wc.y, rb) + kBalPro);
     }
+  }
+  __syncthreads();
+
+  // per tile, in parallel (a contiguous run of tiles per thread): its
+  // request (binary search over the requests' first tiles), row block and
+  // cost position; a tile split over k > 1 workers takes k partial slots
+  const int segT = ceil_div(n_tiles, kPlanThreads);
+  const int T0 = min(t * segT, n_tiles), T1 = min(T0 + segT, n_tiles);
+  struct TileAt { int i, n, st; };
+  auto tile_at = [&](int T) {
+    int lo = 0, hi = B - 1;   // last request whose first tile is at or before T
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_off[mid].x <= T) lo = mid; else hi = mid - 1;
+    }
+    const int2 wc = s_wc[lo];
+    const int u = T - s_off[lo].x;
+    const int rb = u / per_rb, k = u % per_rb;
+    int st = s_off[lo].y;
+    for (int r = 0; r < rb; ++r) st += per_rb * (nst(wc.x, wc.y, r) + kBalPro);
+    const int n = nst(wc.x, wc.y, rb);
+    st += k * (n + kBalPro);
+    return TileAt{lo, n, st};
+  };
+  int parts[2] = {0, 0}, poff[2], ptot[2];
+  for (int T = T0; T < T1; ++T) {
+    const TileAt ta = tile_at(T);
+    const int s0 = ta.st + kBalPro;   // cost position of the tile's first super-tile
+    const int kseg = (s0 + ta.n - 1) / q - s0 / q + 1;
+    parts[0] += kseg > 1 ? kseg : 0;
+    parts[1] += kseg > 1 ? 1 : 0;
   }
   block_excl_scan<2>(parts, poff, ptot, s_buf);
 
   int* vw_first = reinterpret_cast<int*>(p.items + n_tiles);
-  int T = off[0], st = off[1], slot = poff[0], split_at = poff[1];
-  for (int i = i0; i < i1; ++i) {
-    const int2 wc = s_wc[i];
-    const int n_rb = ceil_div(wc.x, sh.RT);
-    p.req_info[i] = make_int4(n_rb * per_rb, T, 0, 0);
-    const int T0 = T;
-    for (int rb = 0; rb < n_rb; ++rb) {
-      const int n = nst(wc.x, wc.y, rb);
-      for (int k = 0; k < per_rb; ++k, ++T, st += n + kBalPro) {
-        const int s0 = st + kBalPro;   // cost position of the tile's first super-tile
-        const int v_first = s0 / q, v_last = (s0 + n - 1) / q;
-        const int kseg = v_last - v_first + 1;
-        p.items[T] = make_int4(s0, n, kseg > 1 ? slot : -1, i);
-        slot += kseg > 1 ? kseg : 0;
-        if (kseg > 1) p.split[split_at++] = make_int2(i, T - T0);
-        // workers whose range starts inside this tile
-        for (int v = ceil_div(st, q); v <= v_last; ++v) vw_first[v] = T;
-      }
-    }
+  int slot = poff[0], split_at = poff[1];
+  for (int T = T0; T < T1; ++T) {
+    const TileAt ta = tile_at(T);
+    const int s0 = ta.st + kBalPro;
+    const int v_first = s0 / q, v_last = (s0 + ta.n - 1) / q;
+    const int kseg = v_last - v_first + 1;
+    p.items[T] = make_int4(s0, ta.n, kseg > 1 ? slot : -1, ta.i);
+    slot += kseg > 1 ? kseg : 0;
+    if (kseg > 1) p.split[split_at++] = make_int2(ta.i, T - s_off[ta.i].x);
+    // workers whose range starts inside this tile
+    for (int v = ceil_div(ta.st, q); v <= v_last; ++v) vw_first[v] = T;
   }
   if (t == 0) {
     p.hdr[kBalS] = S;
