@@ -10,6 +10,9 @@
  *   rv_schedule        per-request verify windows from draft confidences
  *   rv_pack            front-pack the windows into a cu_seqlens buffer
  *   rv_verify_attn     varlen causal attention of packed rows, paged KV
+ *   rv_pack_plan, rv_verify_attn_planned
+ *                      the same two stages with the attention plan built in
+ *                      the pack launch
  *   rv_lm_head_accept  target LM head, argmax / min(1,p/q) accept
  *   rv_compact_scatter write committed tokens and KV slots back
  *
@@ -249,6 +252,23 @@ typedef struct {
 } rv_attn_args;
 /* Device errors: BAD_PAGE (the key is read from page 0 instead). */
 rv_status rv_verify_attn(const rv_attn_args* a, void* stream);
+
+/* Stage 2 with the plan of stage 3 in the same launch.  The attention call's
+ * device-side plan (how the packed rows' tiles and key chunks are dealt to
+ * the persistent workgroups; DSpark-in-SGLang page, section A2: each backend
+ * rebuilds its varlen metadata for the packed layout) depends only on cu[],
+ * ctx[] and the call's shape, so one workgroup can pack and then plan.
+ * rv_pack_plan(pack, attn) does what rv_pack(pack) does and leaves in
+ * attn->workspace the plan that rv_verify_attn(attn) would build; attn must
+ * name the pack's cu, mm and ctx arrays and the same B and gamma (otherwise
+ * RV_ERR_INVALID_ARG), and both argument sets are checked as by rv_pack and
+ * rv_verify_attn.  rv_verify_attn_planned(attn) is then stage 3 without its
+ * plan launch: it must follow rv_pack_plan with the same attention arguments
+ * on the same stream, with nothing written to the workspace in between (the
+ * plan is not checked).  For RV_F32 attention, which has no plan,
+ * rv_pack_plan is rv_pack and rv_verify_attn_planned is rv_verify_attn. */
+rv_status rv_pack_plan(const rv_pack_args* pack, const rv_attn_args* attn, void* stream);
+rv_status rv_verify_attn_planned(const rv_attn_args* a, void* stream);
 
 /* ---- stage 4: LM head + accept ------------------------------------------ */
 /* Target LM head over the packed rows (z = W h, fp32 accumulation) and the

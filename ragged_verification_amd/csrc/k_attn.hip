@@ -46,6 +46,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "pack_body.h"
 #include "rv_common.h"
 
 namespace rv {
@@ -119,7 +120,7 @@ constexpr int kPlanThreads = kScanThreads;
 constexpr int kPlanWaves = kScanWaves;
 constexpr int kPlanMaxB = RV_MAX_ROWS / 2;   // gamma >= 2
 
-__global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
+__device__ __forceinline__ void plan_chunked_body(const PlanParams& p) {
   __shared__ int2 s_wl[kPlanMaxB];            // per request: window, keys (ctx + window)
   __shared__ int s_ci[kPlanMaxB];             // per request: its chunk
   __shared__ int s_buf[kPlanWaves * 8];
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) {
 // request}; after the n_tiles entries of items[], the first tile of each
 // virtual worker.  A tile whose super-tiles fall to k > 1 workers owns k
 // consecutive partial slots, one per worker in order.
-__global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
+__device__ __forceinline__ void plan_bal_body(const PlanParams& p) {
   __shared__ int2 s_wc[kPlanMaxB];            // per request: window, context
   __shared__ int2 s_off[kPlanMaxB];           // per request: first tile, first cost unit
   __shared__ int s_buf[kPlanWaves * 8];
@@ -533,6 +534,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) {
     p.hdr[kBalParts] = ptot[0];
     p.hdr[kHdrSplit] = ptot[1];
   }
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_attn_plan(PlanParams p) { plan_chunked_body(p); }
+__global__ __launch_bounds__(kPlanThreads) void k_attn_plan_bal(PlanParams p) { plan_bal_body(p); }
+
+// Stage 2 and stage 3's plan in one launch (one workgroup): the plan reads
+// the cu[] this workgroup has just written.
+template <bool BAL>
+__global__ __launch_bounds__(kPlanThreads) void k_pack_plan(PackParams pk, PlanParams pp) {
+  static_assert(kPlanThreads == kScanThreads, "the pack body's workgroup");
+  pack_body(pk);
+  __syncthreads();   // cu[] and mm[] written by this workgroup are visible to all of it
+  if constexpr (BAL) plan_bal_body(pp);
+  else plan_chunked_body(pp);
 }
 
 // ---- bf16 attention kernels: shared parameters ---------------------------------
@@ -2488,9 +2503,105 @@ size_t attn_scratch_bytes(int B, int gamma, int Hq, int Hkv, int Dqk, int Dv, in
   return need;
 }
 
-hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
+// What the plan and the main kernels of one bf16 attention call share: the
+// kernel choice, the shape, the workspace layout and the plan's parameters.
+struct AttnPrep {
+  bool latent, row_kernel, bal, fast_gqa;
+  int nw, bal_grid;
+  AttnShape sh;
+  AttnScratch L;
+  char* base;
+  PlanParams pp;
+};
+
+hipError_t prep_attn(const rv_attn_args& a, AttnPrep& P) {
   const bool latent = (a.v_cache == nullptr);
   char* ws = static_cast<char*>(a.workspace);
+  hipError_t e;
+  // latent: the row kernel for a multiple of 128 heads, with key lists
+  // (sparse) or dense over power-of-two pages of at least 32 keys; the
+  // 64-vector kernel otherwise
+  const bool pow2_pages = (a.page_size & (a.page_size - 1)) == 0;
+  const bool row_kernel = latent && a.Hq % kRowQT == 0 &&
+                          (a.topk_idx != nullptr || (pow2_pages && a.page_size >= 32));
+  AttnShape sh;
+  int nw = 0;
+  if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw, row_kernel)) return hipErrorInvalidValue;
+  if (a.B > kPlanMaxB) return hipErrorInvalidValue;   // the plan caches one pair per request in LDS
+  const AttnScratch L = attn_layout(a.B, sh, a.Dv);
+  char* base = ws + kStatusBytes;
+
+  // GQA: FAST DMA needs power-of-two pages of 4 .. 2^16 keys and rows under
+  // 2^24 bytes (24-bit in-page offsets).  The balanced schedule applies when
+  // its partial slots (at most workers + tiles) and worker list fit.
+  const int log2P = ((a.page_size & (a.page_size - 1)) == 0) ? __builtin_ctz((unsigned)a.page_size) : -1;
+  const bool fast_gqa = !latent && log2P >= 2 && log2P <= 16 && (long long)a.Hkv * kGqaD * 2 < (1 << 24);
+  int bal_grid = 0;
+  bool bal = false;
+  if (!latent) {
+    if ((e = gqa_bal_grid(nw, fast_gqa, &bal_grid)) != hipSuccess) return e;
+    const long long tiles_max = (long long)a.B * sh.tpr_max;
+    const long long st_max = ((long long)a.max_pages * a.page_size + kBalSuper - 1) / kBalSuper + kBalPro;
+    bal = bal_grid <= 4 * (L.item_cap - tiles_max) && bal_grid + tiles_max <= L.part_slots &&
+          tiles_max * st_max < INT32_MAX;
+  }
+
+  PlanParams& pp = P.pp;
+  pp.cu = a.cu;
+  pp.ctx = a.ctx;
+  pp.mm = a.mm;
+  pp.req_info = reinterpret_cast<int4*>(base + L.req_info);
+  pp.items = reinterpret_cast<int4*>(base + L.items);
+  pp.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
+  pp.grp = reinterpret_cast<int2*>(base + L.grp);
+  pp.split = reinterpret_cast<int2*>(base + L.split);
+  pp.B = a.B;
+  pp.gamma = a.gamma;
+  pp.item_cap = L.item_cap;
+  pp.part_cap = L.part_slots;
+  pp.target = sh.target;
+  // workers of the main kernel (the chunked plan sizes its finer chunks by
+  // them; 0 for the GQA fallback, which keeps one chunk length)
+  int chunk_workers = 0;
+  if (!bal && latent) {
+    const bool sparse = a.topk_idx != nullptr;
+    const bool fast = !sparse && (a.page_size & (a.page_size - 1)) == 0 && a.page_size >= 32;
+    const void* kern = row_kernel ? (sparse ? reinterpret_cast<const void*>(k_attn_mla_row<true>)
+                                            : reinterpret_cast<const void*>(k_attn_mla_row<false>))
+                       : sparse ? reinterpret_cast<const void*>(k_attn_mla<false, true>)
+                       : fast   ? reinterpret_cast<const void*>(k_attn_mla<true, false>)
+                                : reinterpret_cast<const void*>(k_attn_mla<false, false>);
+    const int lds = row_kernel ? kRowLdsBytes : kMlaLdsBytes;
+    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
+    if ((e = persistent_grid(kern, 256, lds, &chunk_workers)) != hipSuccess) return e;
+  }
+  pp.n_workers = bal ? bal_grid : chunk_workers;
+  pp.window = a.window;
+  pp.topk = a.topk_idx ? a.topk : 0;
+  pp.sh = sh;
+  P.latent = latent;
+  P.row_kernel = row_kernel;
+  P.bal = bal;
+  P.fast_gqa = fast_gqa;
+  P.nw = nw;
+  P.bal_grid = bal_grid;
+  P.sh = sh;
+  P.L = L;
+  P.base = base;
+  return hipSuccess;
+}
+
+hipError_t launch_pack_plan(const rv_pack_args& pk, const rv_attn_args& a, hipStream_t s) {
+  if (a.dtype == RV_F32) return launch_pack(pk, s);   // the fp32 kernel has no plan
+  AttnPrep P;
+  hipError_t e = prep_attn(a, P);
+  if (e != hipSuccess) return e;
+  if (P.bal) hipLaunchKernelGGL(k_pack_plan<true>, dim3(1), dim3(kPlanThreads), 0, s, make_pack_params(pk), P.pp);
+  else hipLaunchKernelGGL(k_pack_plan<false>, dim3(1), dim3(kPlanThreads), 0, s, make_pack_params(pk), P.pp);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const rv_attn_args& a, hipStream_t s, bool planned) {
   int32_t* status = status_ptr(a.workspace);
   hipError_t e;
 
@@ -2524,70 +2635,19 @@ hipError_t launch_attn(const rv_attn_args& a, hipStream_t s) {
     return hipGetLastError();
   }
 
-  // latent: the row kernel for a multiple of 128 heads, with key lists
-  // (sparse) or dense over power-of-two pages of at least 32 keys; the
-  // 64-vector kernel otherwise
-  const bool pow2_pages = (a.page_size & (a.page_size - 1)) == 0;
-  const bool row_kernel = latent && a.Hq % kRowQT == 0 &&
-                          (a.topk_idx != nullptr || (pow2_pages && a.page_size >= 32));
-  AttnShape sh;
-  int nw = 0;
-  if (!pick_shape(a.Hq, a.Hkv, a.Dqk, a.Dv, a.gamma, latent, &sh, &nw, row_kernel)) return hipErrorInvalidValue;
-  if (a.B > kPlanMaxB) return hipErrorInvalidValue;   // the plan caches one pair per request in LDS
-  const AttnScratch L = attn_layout(a.B, sh, a.Dv);
-  char* base = ws + kStatusBytes;
-
-  // GQA: FAST DMA needs power-of-two pages of 4 .. 2^16 keys and rows under
-  // 2^24 bytes (24-bit in-page offsets).  The balanced schedule applies when
-  // its partial slots (at most workers + tiles) and worker list fit.
-  const int log2P = ((a.page_size & (a.page_size - 1)) == 0) ? __builtin_ctz((unsigned)a.page_size) : -1;
-  const bool fast_gqa = !latent && log2P >= 2 && log2P <= 16 && (long long)a.Hkv * kGqaD * 2 < (1 << 24);
-  int bal_grid = 0;
-  bool bal = false;
-  if (!latent) {
-    if ((e = gqa_bal_grid(nw, fast_gqa, &bal_grid)) != hipSuccess) return e;
-    const long long tiles_max = (long long)a.B * sh.tpr_max;
-    const long long st_max = ((long long)a.max_pages * a.page_size + kBalSuper - 1) / kBalSuper + kBalPro;
-    bal = bal_grid <= 4 * (L.item_cap - tiles_max) && bal_grid + tiles_max <= L.part_slots &&
-          tiles_max * st_max < INT32_MAX;
+  AttnPrep P;
+  if ((e = prep_attn(a, P)) != hipSuccess) return e;
+  const bool latent = P.latent, row_kernel = P.row_kernel, bal = P.bal, fast_gqa = P.fast_gqa;
+  const int nw = P.nw, bal_grid = P.bal_grid;
+  const AttnShape& sh = P.sh;
+  const AttnScratch& L = P.L;
+  char* base = P.base;
+  const PlanParams& pp = P.pp;
+  if (!planned) {   // else the pack launch built this call's plan (launch_pack_plan)
+    if (bal) hipLaunchKernelGGL(k_attn_plan_bal, dim3(1), dim3(kPlanThreads), 0, s, pp);
+    else hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, pp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-
-  PlanParams pp;
-  pp.cu = a.cu;
-  pp.ctx = a.ctx;
-  pp.mm = a.mm;
-  pp.req_info = reinterpret_cast<int4*>(base + L.req_info);
-  pp.items = reinterpret_cast<int4*>(base + L.items);
-  pp.hdr = reinterpret_cast<int32_t*>(base + L.hdr);
-  pp.grp = reinterpret_cast<int2*>(base + L.grp);
-  pp.split = reinterpret_cast<int2*>(base + L.split);
-  pp.B = a.B;
-  pp.gamma = a.gamma;
-  pp.item_cap = L.item_cap;
-  pp.part_cap = L.part_slots;
-  pp.target = sh.target;
-  // workers of the main kernel (the chunked plan sizes its finer chunks by
-  // them; 0 for the GQA fallback, which keeps one chunk length)
-  int chunk_workers = 0;
-  if (!bal && latent) {
-    const bool sparse = a.topk_idx != nullptr;
-    const bool fast = !sparse && (a.page_size & (a.page_size - 1)) == 0 && a.page_size >= 32;
-    const void* kern = row_kernel ? (sparse ? reinterpret_cast<const void*>(k_attn_mla_row<true>)
-                                            : reinterpret_cast<const void*>(k_attn_mla_row<false>))
-                       : sparse ? reinterpret_cast<const void*>(k_attn_mla<false, true>)
-                       : fast   ? reinterpret_cast<const void*>(k_attn_mla<true, false>)
-                                : reinterpret_cast<const void*>(k_attn_mla<false, false>);
-    const int lds = row_kernel ? kRowLdsBytes : kMlaLdsBytes;
-    if ((e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds)) != hipSuccess) return e;
-    if ((e = persistent_grid(kern, 256, lds, &chunk_workers)) != hipSuccess) return e;
-  }
-  pp.n_workers = bal ? bal_grid : chunk_workers;
-  pp.window = a.window;
-  pp.topk = a.topk_idx ? a.topk : 0;
-  pp.sh = sh;
-  if (bal) hipLaunchKernelGGL(k_attn_plan_bal, dim3(1), dim3(kPlanThreads), 0, s, pp);
-  else hipLaunchKernelGGL(k_attn_plan, dim3(1), dim3(kPlanThreads), 0, s, pp);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
 
   MainParams mp;
   mp.q = static_cast<const bf16_t*>(a.q);

@@ -101,7 +101,11 @@ rv_status rv_schedule(const rv_schedule_args* a, void* stream) {
   return hip_status(launch_schedule(*a, static_cast<hipStream_t>(stream)));
 }
 
-rv_status rv_pack(const rv_pack_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+rv_status pack_args_check(const rv_pack_args* a) {
   if (!a || !a->w_verify || !a->anchor || !a->drafts || !a->ctx || !a->page_table || !a->cu ||
       !a->mm || !a->row_req || !a->row_pos || !a->tok || !a->slot)
     return RV_ERR_INVALID_ARG;
@@ -117,10 +121,10 @@ rv_status rv_pack(const rv_pack_args* a, void* stream) {
     if (a->tiers[a->n_tiers - 1] > a->rows_cap) return RV_ERR_TIER;
   }
   if (!ws_ok(a->workspace, a->workspace_bytes, kStatusBytes)) return RV_ERR_WORKSPACE;
-  return hip_status(launch_pack(*a, static_cast<hipStream_t>(stream)));
+  return RV_OK;
 }
 
-rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
+rv_status attn_args_check(const rv_attn_args* a) {
   if (!a || !a->q || !a->k_cache || !a->page_table || !a->ctx || !a->cu || !a->mm || !a->o)
     return RV_ERR_INVALID_ARG;
   if (!block_ok(a->B, a->gamma)) return RV_ERR_INVALID_ARG;
@@ -138,7 +142,40 @@ rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
   if (a->max_pages > attn_max_pages_limit(a->dtype, latent)) return RV_ERR_UNSUPPORTED;
   const size_t need = kStatusBytes + attn_scratch_bytes(a->B, a->gamma, a->Hq, a->Hkv, a->Dqk, a->Dv, a->dtype);
   if (!ws_ok(a->workspace, a->workspace_bytes, need)) return RV_ERR_WORKSPACE;
+  return RV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rv_status rv_pack(const rv_pack_args* a, void* stream) {
+  const rv_status st = pack_args_check(a);
+  if (st != RV_OK) return st;
+  return hip_status(launch_pack(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_verify_attn(const rv_attn_args* a, void* stream) {
+  const rv_status st = attn_args_check(a);
+  if (st != RV_OK) return st;
   return hip_status(launch_attn(*a, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_pack_plan(const rv_pack_args* pack, const rv_attn_args* attn, void* stream) {
+  rv_status st = pack_args_check(pack);
+  if (st != RV_OK) return st;
+  if ((st = attn_args_check(attn)) != RV_OK) return st;
+  // the plan reads the pack's outputs for the same requests
+  if (attn->cu != pack->cu || attn->mm != pack->mm || attn->ctx != pack->ctx || attn->B != pack->B ||
+      attn->gamma != pack->gamma)
+    return RV_ERR_INVALID_ARG;
+  return hip_status(launch_pack_plan(*pack, *attn, static_cast<hipStream_t>(stream)));
+}
+
+rv_status rv_verify_attn_planned(const rv_attn_args* a, void* stream) {
+  const rv_status st = attn_args_check(a);
+  if (st != RV_OK) return st;
+  return hip_status(launch_attn(*a, static_cast<hipStream_t>(stream), true));
 }
 
 rv_status rv_lm_head_accept(const rv_lm_args* a, void* stream) {

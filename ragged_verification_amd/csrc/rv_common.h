@@ -101,7 +101,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct SchedLaunch;
 hipError_t launch_schedule(const rv_schedule_args& a, hipStream_t s);
 hipError_t launch_pack(const rv_pack_args& a, hipStream_t s);
-hipError_t launch_attn(const rv_attn_args& a, hipStream_t s);
+hipError_t launch_attn(const rv_attn_args& a, hipStream_t s, bool planned = false);
+// stage 2 and the plan of the stage-3 call described by `attn`, in one launch
+hipError_t launch_pack_plan(const rv_pack_args& pack, const rv_attn_args& attn, hipStream_t s);
 // part: the slab partials (lm_scratch_bytes), status: the sticky status word
 hipError_t launch_lm(const rv_lm_args& a, void* part, int32_t* status, hipStream_t s);
 // host checks of rv_lm_head_accept's arguments other than the workspace

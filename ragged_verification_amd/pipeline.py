@@ -20,10 +20,17 @@ from . import rv, synth
 
 class VerifyStep:
     def __init__(self, inp, mode="compact", with_logits=False, rows_cap=None, r2t_extra=64,
-                 hist_cap=64, stream=None, w_layout="tiled", window=0, topk=0):
+                 hist_cap=64, stream=None, w_layout="tiled", window=0, topk=0, fused_plan=True):
         wl = inp["workload"]
         self.inp, self.wl = inp, wl
         self.mode = mode
+        # fused_plan: the pack launch also builds the attention call's plan
+        # (rv_pack_plan); an attention call right after such a pack skips its
+        # own plan launch (rv_verify_attn_planned).  The plan is single use:
+        # the attention kernels advance its work counters, and the LM head's
+        # scratch shares the workspace.
+        self.fused_plan = fused_plan
+        self._plan_ready = False
         dev = inp["conf"].device
         if dev.type != "cuda":
             raise ValueError("VerifyStep needs inputs on the GPU")
@@ -106,15 +113,31 @@ class VerifyStep:
 
     # ---- stages ------------------------------------------------------------------
     def schedule(self):
+        self._plan_ready = False   # this stage may write the workspace
         i = self.inp
         rv.rv_schedule(i["conf"], self.gamma, self.mode, i["cost_bias"], i["cost_alpha"], i["cost_theta"],
                        self.w_commit, self.w_verify, self.k_star, self.e_star, self.workspace, self.stream)
 
-    def pack(self):
+    def _pack_kw(self):
         i = self.inp
-        rv.rv_pack(self.w_verify, self.anchor, i["drafts"], self.ctx, i["page_table"], i["page_size"],
-                   i["num_pages"], self.tiers, self.cu, self.mm, self.row_req, self.row_pos, self.tok,
-                   self.slot, self.workspace, self.stream)
+        return dict(w_verify=self.w_verify, anchor=self.anchor, drafts=i["drafts"], ctx=self.ctx,
+                    page_table=i["page_table"], page_size=i["page_size"], num_pages=i["num_pages"],
+                    tiers=self.tiers, cu=self.cu, mm=self.mm, row_req=self.row_req, row_pos=self.row_pos,
+                    tok=self.tok, slot=self.slot, workspace=self.workspace)
+
+    def _attn_kw(self):
+        i = self.inp
+        return dict(q=self.q, k_cache=i["k_cache"], v_cache=i["v_cache"], page_table=i["page_table"],
+                    page_size=i["page_size"], num_pages=i["num_pages"], ctx=self.ctx, cu=self.cu, mm=self.mm,
+                    gamma=self.gamma, sm_scale=i["sm_scale"], o=self.o, lse=self.lse, workspace=self.workspace,
+                    window=self.window, topk_idx=self.topk_idx)
+
+    def pack(self):
+        if self.fused_plan:
+            rv.rv_pack_plan(self._pack_kw(), self._attn_kw(), self.stream)
+            self._plan_ready = True
+        else:
+            rv.rv_pack(**self._pack_kw(), stream=self.stream)
 
     def stage_payload(self):
         """Gather block-major payload rows into packed order (harness work)."""
@@ -129,12 +152,14 @@ class VerifyStep:
             torch.index_select(self.topk_flat, 0, src, out=self.topk_idx)
 
     def attn(self):
-        i = self.inp
-        rv.rv_verify_attn(self.q, i["k_cache"], i["v_cache"], i["page_table"], i["page_size"], i["num_pages"],
-                          self.ctx, self.cu, self.mm, self.gamma, i["sm_scale"], self.o, self.lse,
-                          self.workspace, self.stream, window=self.window, topk_idx=self.topk_idx)
+        if self._plan_ready:
+            rv.rv_verify_attn_planned(**self._attn_kw(), stream=self.stream)
+        else:
+            rv.rv_verify_attn(**self._attn_kw(), stream=self.stream)
+        self._plan_ready = False
 
     def lm(self):
+        self._plan_ready = False   # this stage may write the workspace
         i = self.inp
         rv.rv_lm_head_accept(self.hidden, i["W"], self.mm, self.cu, self.w_commit, self.w_verify, i["drafts"],
                              self.rule, self.pred, self.accept, self.bonus, self.ceiling, self.workspace,
@@ -142,6 +167,7 @@ class VerifyStep:
                              stream=self.stream, W_tiled=self.W_tiled)
 
     def scatter(self):
+        self._plan_ready = False   # this stage may write the workspace
         i = self.inp
         rv.rv_compact_scatter(self.cu, self.w_verify, self.accept, self.bonus, i["drafts"], self.slot, self.ctx,
                               self.anchor, self.req_to_token, self.commit_cu, self.commit_tok, self.commit_slot,
@@ -166,6 +192,7 @@ class VerifyStep:
 
     # ---- observability -----------------------------------------------------------
     def calibration(self, n_bins=10):
+        self._plan_ready = False   # this stage may write the workspace
         """Confidence calibration of this step's verified drafts (rv_calibration,
         after lm()): returns the device tensors (bin_count, bin_match,
         bin_conf_fx, ece, req_verified, req_matched)."""
@@ -185,6 +212,7 @@ class VerifyStep:
         return c
 
     def block_accept_estimate(self, state):
+        self._plan_ready = False   # this stage may write the workspace
         """One step of the block-accept estimator (rv_block_accept_estimate),
         between lm() and scatter(): ``state`` is a zero-filled uint8 tensor of
         rv.rv_estimator_state_bytes(B, gamma) bytes kept across steps."""

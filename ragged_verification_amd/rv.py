@@ -96,7 +96,8 @@ STRUCTS = [ScheduleArgs, PackArgs, AttnArgs, LmArgs, ScatterArgs, Dims, CalibArg
 EXPORTS = ["rv_version", "rv_workspace_size", "rv_device_status", "rv_clear_status", "rv_schedule",
            "rv_pack", "rv_verify_attn", "rv_lm_head_accept", "rv_compact_scatter", "rv_abi_layout",
            "rv_lm_tiled_weight_bytes", "rv_lm_tile_weight", "rv_fit_cost_model", "rv_calibration",
-           "rv_lm_head_accept_noalloc", "rv_estimator_state_bytes", "rv_block_accept_estimate"]
+           "rv_lm_head_accept_noalloc", "rv_estimator_state_bytes", "rv_block_accept_estimate",
+           "rv_pack_plan", "rv_verify_attn_planned"]
 
 _LIB = None
 
@@ -130,6 +131,10 @@ def load(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = _i32
         fn.argtypes = [ctypes.POINTER(st), _vp]
+    lib.rv_verify_attn_planned.restype = _i32
+    lib.rv_verify_attn_planned.argtypes = [ctypes.POINTER(AttnArgs), _vp]
+    lib.rv_pack_plan.restype = _i32
+    lib.rv_pack_plan.argtypes = [ctypes.POINTER(PackArgs), ctypes.POINTER(AttnArgs), _vp]
     lib.rv_estimator_state_bytes.restype = _i32
     lib.rv_estimator_state_bytes.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
     lib.rv_lm_tiled_weight_bytes.restype = _i32
@@ -230,8 +235,9 @@ def rv_schedule(conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, 
     _check("rv_schedule", load().rv_schedule(ctypes.byref(a), _stream(stream)))
 
 
-def rv_pack(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
-            row_pos, tok, slot, workspace, stream=None):
+def _pack_args(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
+               row_pos, tok, slot, workspace):
+    """PackArgs and the host tier array it points to (keep both alive)."""
     B, g1 = drafts.shape
     tiers = list(tiers or ())
     tarr = (ctypes.c_int32 * max(1, len(tiers)))(*tiers)
@@ -244,11 +250,18 @@ def rv_pack(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tie
                  row_req=_ptr(row_req, torch.int32, "row_req"), row_pos=_ptr(row_pos, torch.int32, "row_pos"),
                  tok=_ptr(tok, torch.int32, "tok"), slot=_ptr(slot, torch.int32, "slot"),
                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    return a, tarr
+
+
+def rv_pack(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
+            row_pos, tok, slot, workspace, stream=None):
+    a, _keep = _pack_args(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
+                          row_pos, tok, slot, workspace)
     _check("rv_pack", load().rv_pack(ctypes.byref(a), _stream(stream)))
 
 
-def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                   o, lse, workspace, stream=None, window=0, topk_idx=None):
+def _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+               o, lse, workspace, window=0, topk_idx=None):
     rows_cap, Hq, Dqk = q.shape
     Hkv = k_cache.shape[2]
     Dv = o.shape[2]
@@ -262,7 +275,30 @@ def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, c
                  topk=0 if topk_idx is None else topk_idx.shape[1], topk_idx=_ptr(topk_idx, torch.int32, "topk_idx"),
                  o=_ptr(o, q.dtype, "o"), lse=_ptr(lse, torch.float32, "lse"),
                  workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
+    return a
+
+
+def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+                   o, lse, workspace, stream=None, window=0, topk_idx=None):
+    a = _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+                   o, lse, workspace, window=window, topk_idx=topk_idx)
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
+
+
+def rv_verify_attn_planned(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+                           o, lse, workspace, stream=None, window=0, topk_idx=None):
+    """Stage 3 after rv_pack_plan (the plan is already in the workspace)."""
+    a = _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
+                   o, lse, workspace, window=window, topk_idx=topk_idx)
+    _check("rv_verify_attn_planned", load().rv_verify_attn_planned(ctypes.byref(a), _stream(stream)))
+
+
+def rv_pack_plan(pack, attn, stream=None):
+    """Stage 2 and the plan of stage 3 in one launch.  ``pack``: the keyword
+    arguments of rv_pack (without stream); ``attn``: those of rv_verify_attn."""
+    pa, _keep = _pack_args(**pack)
+    aa = _attn_args(**attn)
+    _check("rv_pack_plan", load().rv_pack_plan(ctypes.byref(pa), ctypes.byref(aa), _stream(stream)))
 
 
 def rv_calibration(conf, drafts, pred, cu, w_verify, n_bins, bin_count, bin_match, bin_conf_fx, ece, workspace,

@@ -128,6 +128,38 @@ def test_attn_validation(lib):
     assert lib.rv_verify_attn(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
 
 
+def test_pack_plan_validation(lib):
+    """rv_pack_plan checks both argument sets, then that the attention call
+    reads the pack's own cu, mm and ctx for the same B and gamma; the planned
+    attention entry checks its arguments as rv_verify_attn does."""
+    pk = rv.PackArgs()
+    for f in ("w_verify", "anchor", "drafts", "ctx", "page_table", "cu", "mm", "row_req", "row_pos",
+              "tok", "slot"):
+        setattr(pk, f, _fake())
+    pk.B, pk.gamma, pk.max_pages, pk.page_size, pk.num_pages, pk.rows_cap = 2, 8, 4, 64, 8, 16
+    at = rv.AttnArgs()
+    for f in ("q", "k_cache", "page_table", "o"):
+        setattr(at, f, _fake())
+    at.ctx, at.cu, at.mm = pk.ctx, pk.cu, pk.mm
+    at.B, at.gamma, at.rows_cap, at.max_pages, at.page_size, at.num_pages = 2, 8, 16, 4, 64, 8
+    at.Hq, at.Hkv, at.Dqk, at.Dv, at.dtype, at.sm_scale = 128, 1, 576, 512, rv.RV_BF16, 0.04
+    fake_ws = (ctypes.c_uint8 * 16)()
+    big = 1 << 40
+    pk.workspace, pk.workspace_bytes = ctypes.cast(fake_ws, ctypes.c_void_p), big
+    assert lib.rv_pack_plan(ctypes.byref(pk), ctypes.byref(at), None) == rv.RV_ERR_WORKSPACE   # attention's
+    assert lib.rv_verify_attn_planned(ctypes.byref(at), None) == rv.RV_ERR_WORKSPACE
+    at.workspace, at.workspace_bytes = ctypes.cast(fake_ws, ctypes.c_void_p), big
+    at.cu = _fake(7)                      # not the pack's cu
+    assert lib.rv_pack_plan(ctypes.byref(pk), ctypes.byref(at), None) == rv.RV_ERR_INVALID_ARG
+    at.cu, at.B = pk.cu, 1                # another batch
+    assert lib.rv_pack_plan(ctypes.byref(pk), ctypes.byref(at), None) == rv.RV_ERR_INVALID_ARG
+    at.B, pk.rows_cap = 2, 15             # the pack's own check
+    assert lib.rv_pack_plan(ctypes.byref(pk), ctypes.byref(at), None) == rv.RV_ERR_INVALID_ARG
+    pk.rows_cap, at.Hkv = 16, 2           # the attention's own check (latent: one KV head)
+    assert lib.rv_pack_plan(ctypes.byref(pk), ctypes.byref(at), None) == rv.RV_ERR_UNSUPPORTED
+    assert lib.rv_verify_attn_planned(ctypes.byref(at), None) == rv.RV_ERR_UNSUPPORTED
+
+
 def test_tiled_weight_size_and_validation(lib):
     n = ctypes.c_size_t(0)
     # V rounded up to 32 rows, 2 bytes per element

@@ -420,6 +420,33 @@ def _outputs(step):
     return {n: getattr(step, n).clone() for n in names}
 
 
+@pytest.mark.parametrize("wl,kw,step_kw", [
+    ("mla_bf16", dict(B=3, V=1000, H=512, ctx=("uniform", 60, 700)), {}),
+    ("mla_bf16", dict(B=3, V=1000, H=512, ctx=("uniform", 600, 2000)), dict(window=200)),
+    ("mla_bf16", dict(B=2, V=500, H=256, ctx=("uniform", 3000, 5000)), dict(topk=2048)),
+    ("mla_bf16", dict(B=3, Hq=64, V=1000, H=512, ctx=("uniform", 60, 700)), {}),
+    ("gqa_bf16", dict(B=6, V=1000, H=256, ctx=("uniform", 40, 900)), {}),
+    ("tiny_f32", dict(B=4), {}),
+])
+def test_fused_pack_plan_equals_separate_launches(wl, kw, step_kw):
+    """The pack launch that also builds the attention plan (rv_pack_plan +
+    rv_verify_attn_planned) gives every output of the step bit for bit as
+    the separate pack and plan launches do: latent row kernel dense, windowed
+    and with key lists, the 64-head latent kernel, the balanced GQA plan, and
+    the fp32 path (no plan)."""
+    inp = pu.make_inputs(wl, **kw)
+    outs = []
+    for fused in (True, False):
+        step = VerifyStep(inp, mode="compact", with_logits=True, fused_plan=fused, **step_kw)
+        step.run()
+        torch.cuda.synchronize()
+        assert step.status() == 0
+        outs.append(_outputs(step))
+        del step
+    for n in outs[0]:
+        assert torch.equal(outs[0][n], outs[1][n]), n
+
+
 @pytest.mark.parametrize("wl,kw", [("mla_bf16", dict(B=3, V=1000, H=512, ctx=("uniform", 60, 700))),
                                    ("rejection_bf16", dict(B=6, V=3000, H=256,
                                                            ctx=("lognormal", 200, 1.0, 600)))])
