@@ -698,6 +698,7 @@ static_assert(kMlaLdsBytes <= 160 * 1024, "latent kernel LDS");
 
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+typedef __attribute__((address_space(3))) f32x4_t lds_f32x4_t;
 __device__ inline uint2 lds_b64(uint32_t addr) {
   return __builtin_bit_cast(uint2, *(const lds_u32x2_t*)(size_t)addr);
 }
@@ -1356,9 +1357,11 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
   auto slot_row = [&](const DmaTile& d, int e) {
     return sidx[min(d.t0 + (int)(dma_off[e] & 255u), last) - kv_begin];
   };
+  // (the chunk offset is taken through opaque() inside the loop: hoisted,
+  // base + chunk would hold a 64-bit pair per DMA and the kernel would spill)
   auto dma_row = [&](const DmaTile& d, int e, int krow) {
-    dma16(reinterpret_cast<const unsigned char*>(p.k) + (size_t)krow * kMlaRowBytes + (dma_off[e] >> 8),
-          d.lds0 + e * 1024);
+    const uint64_t off = (uint64_t)(uint32_t)krow * kMlaRowBytes + (opaque(dma_off[e]) >> 8);
+    dma16(reinterpret_cast<const unsigned char*>(p.k) + off, d.lds0 + e * 1024);
   };
   auto dma_one = [&](const DmaTile& d, int e) {
     if constexpr (SPARSE) dma_row(d, e, slot_row(d, e));
@@ -1620,49 +1623,80 @@ __device__ __forceinline__ void attn_mla_row_item(const MainParams& p, int item,
     if (m_all > -INFINITY) m_ref = m_all;
   }   // pass
 
+  // No spill reload among the output stores (each would wait for every store
+  // issued before it): the VGPR-held accumulator block is brought back into
+  // registers here, and the lane-dependent values come from an opaque lane
+  // id (formed before the tile loop they would be held across it, spilled).
+  asm volatile("" : "+v"(oacc[3][3]));
+  const int le = (int)opaque((uint32_t)lane);
+  const int n32e = le & 31, hle = le >> 5;
   // sums of every vector for the normalisation (block vb from wave vb)
-  if (hl == 0) red_l[wid * 32 + n32] = l_all;
-  if (hl == 0) {
+  if (hle == 0) red_l[wid * 32 + n32e] = l_all;
+  if (hle == 0) {
     if (ns == 1) {
-      if (p.lse) p.lse[(size_t)row * p.Hq + head] = l_all > 0.f ? (m_ref + log2f(l_all)) * kLn2 : -INFINITY;
+      if (p.lse)
+        p.lse[(size_t)row * p.Hq + hb * kRowQT + wid * 32 + n32e] =
+            l_all > 0.f ? (m_ref + log2f(l_all)) * kLn2 : -INFINITY;
     } else {
       const int slot = info.z + sp * info.w + tile;
       if (slot >= 0 && slot < p.part_cap) {
-        float* pml = p.part_ml + ((size_t)slot * kRowQT + wid * 32 + n32) * 2;
+        float* pml = p.part_ml + ((size_t)slot * kRowQT + wid * 32 + n32e) * 2;
         pml[0] = l_all > 0.f ? m_ref : -INFINITY;
         pml[1] = l_all;
       }
     }
   }
   __syncthreads();
+  if (ns == 1) {
+    // One vector block (32 vectors x 512 columns) at a time through the idle
+    // ring: each wave writes its accumulators into LDS as they are (rows
+    // padded by 16 bytes), then each thread scales 64 columns of one vector
+    // by that vector's 1/sum and writes them as bf16, eight threads to a
+    // 1 KB output row.  (Scaled where they sit, the compiler copies every
+    // block out of the accumulator registers at once and spills them, and
+    // each reload waits for the stores issued before it.)
+    constexpr int kStRow = kMlaDv + 4;   // floats per staged row
+    static_assert(32 * kStRow * 4 <= kRing, "a staged vector block fits the ring");
+    const int sv = tid >> 3, sq = tid & 7;   // read-back: vector, column group
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
-    const int qv = vb * 32 + n32;
-    const int hd = hb * kRowQT + qv;
-    if (ns == 1) {
-      const float l_tot = red_l[qv];
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      bf16_t* dst = p.o + ((size_t)row * p.Hq + hd) * kMlaDv + wid * 128 + 4 * hl;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          uint2 pk;
-          pk.x = cvt_bf16x2(oacc[cb][vb][4 * q4 + 0] * inv, oacc[cb][vb][4 * q4 + 1] * inv);
-          pk.y = cvt_bf16x2(oacc[cb][vb][4 * q4 + 2] * inv, oacc[cb][vb][4 * q4 + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + 32 * cb + 8 * q4) = pk;
-        }
-    } else {
-      const int slot = info.z + sp * info.w + tile;
-      if (slot < 0 || slot >= p.part_cap) continue;
-      float* po_ = p.part_o + ((size_t)slot * kRowQT + qv) * kMlaDv + wid * 128 + 4 * hl;
+    for (int vb = 0; vb < 4; ++vb) {
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4_t*>(po_ + 32 * cb + 8 * q4) =
+          *(lds_f32x4_t*)(size_t)(smem_lds + (uint32_t)(n32e * kStRow + wid * 128 + 32 * cb + 8 * q4 + 4 * hle) * 4) =
               f32x4_t{oacc[cb][vb][4 * q4], oacc[cb][vb][4 * q4 + 1], oacc[cb][vb][4 * q4 + 2],
                       oacc[cb][vb][4 * q4 + 3]};
+      __syncthreads();
+      const float l_tot = red_l[vb * 32 + sv];
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      bf16_t* dst = p.o + ((size_t)row * p.Hq + hb * kRowQT + vb * 32 + sv) * kMlaDv;
+#pragma unroll
+      for (int k = 0; k < kMlaDv / 32; ++k) {
+        const int col = (k * 8 + sq) * 4;
+        const f32x4_t x = *(const lds_f32x4_t*)(size_t)(smem_lds + (uint32_t)(sv * kStRow + col) * 4);
+        uint2 pk;
+        pk.x = cvt_bf16x2(x[0] * inv, x[1] * inv);
+        pk.y = cvt_bf16x2(x[2] * inv, x[3] * inv);
+        *reinterpret_cast<uint2*>(dst + col) = pk;
+      }
+      __syncthreads();   // the block is read before the next one is written
+    }
+  } else {
+    const int slot = info.z + sp * info.w + tile;
+    if (slot >= 0 && slot < p.part_cap) {
+      float* po0 = p.part_o + ((size_t)slot * kRowQT + n32e) * kMlaDv + wid * 128 + 4 * hle;
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        float* po_ = po0 + (size_t)vb * 32 * kMlaDv;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(po_ + 32 * cb + 8 * q4) =
+                f32x4_t{oacc[cb][vb][4 * q4], oacc[cb][vb][4 * q4 + 1], oacc[cb][vb][4 * q4 + 2],
+                        oacc[cb][vb][4 * q4 + 3]};
+      }
     }
   }
 }
