@@ -1760,11 +1760,12 @@ struct GqaCfg {
 };
 
 // Keys [kv_lo, min(kv_hi, the tile's key count)) of tile `tile` of request
-// i.  slot < 0: the range is the tile's whole key range and the normalised
-// output is written; otherwise fp32 partials go to partial slot `slot`.
+// i (context c, packed rows row_start .. row_start + w - 1).  slot < 0: the
+// range is the tile's whole key range and the normalised output is written;
+// otherwise fp32 partials go to partial slot `slot`.
 template <int NV, bool FAST>
-__device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int tile, int kv_lo, int kv_hi,
-                                               int slot, unsigned char* smem) {
+__device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int tile, int c, int row_start, int w,
+                                               int kv_lo, int kv_hi, int slot, unsigned char* smem) {
   using Cfg = GqaCfg<NV>;
   constexpr int NST = Cfg::kStages;
   constexpr int NWV = Cfg::kWaves;
@@ -1782,9 +1783,6 @@ __device__ __forceinline__ void attn_gqa_range(const MainParams& p, int i, int t
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int row_start = p.cu[i];
-  const int w = p.cu[i + 1] - row_start;
-  const int c = p.ctx[i];
   const int rb = tile / (p.Hkv * p.n_hb);
   const int rem = tile % (p.Hkv * p.n_hb);
   const int g = rem / p.n_hb;
@@ -2087,7 +2085,8 @@ __device__ __forceinline__ void attn_gqa_item(const MainParams& p, int item, uns
   const int kv_lo = win_origin(p.ctx[i], p.window) + sp * chunk;
   const int kv_hi = (int)min((long long)kv_lo + chunk, (long long)INT32_MAX);
   const int slot = info.x == 1 ? -1 : (info.z < 0 ? INT32_MAX : info.z + sp * info.w + tile);
-  attn_gqa_range<NV, FAST>(p, i, tile, kv_lo, kv_hi, slot, smem);
+  const int r0 = p.cu[i];
+  attn_gqa_range<NV, FAST>(p, i, tile, p.ctx[i], r0, p.cu[i + 1] - r0, kv_lo, kv_hi, slot, smem);
 }
 
 // Balanced schedule: virtual worker v takes super-tiles [v*q, v*q+q) of the
@@ -2103,20 +2102,36 @@ __global__ __launch_bounds__(64 * GqaCfg<NV>::kWaves) void k_attn_gqa_bal(MainPa
   const int S = p.hdr[kBalS], q = p.hdr[kBalQ], n_vw = p.hdr[kBalVw], n_tiles = p.hdr[kBalTiles];
   const int4* tinfo = p.items;                                          // per tile
   const int* vw_first = reinterpret_cast<const int*>(p.items + n_tiles);
+  const int4 none = make_int4(INT32_MAX, 0, 0, 0);
   for (int vw = blockIdx.x; vw < n_vw; vw += gridDim.x) {
     const int a = vw * q;
     const int b = min(a + q, S);
-    for (int T = vw_first[vw]; T < n_tiles; ++T) {
-      const int4 ti = tinfo[T];   // {first super-tile, super-tiles, first slot or -1, request}
-      if (ti.x >= b) break;
+    // records read at clamped indices and replaced by `none` past the end
+    // (a select between the loaded values, not between addresses)
+    int T = vw_first[vw];
+    int4 ti = tinfo[max(min(T, n_tiles - 1), 0)];   // {first super-tile, super-tiles, first slot or -1, request}
+    if (T >= n_tiles) ti = none;
+    for (; T < n_tiles && ti.x < b; ++T) {
+      // the next tile's record is in flight while this range runs
+      int4 ti_next = tinfo[min(T + 1, n_tiles - 1)];
       const int s0 = max(a, ti.x) - ti.x, s1 = min(b, ti.x + ti.y) - ti.x;
-      if (s1 <= s0) continue;
-      const int i = ti.w;
-      const int tile = T - p.req_info[i].y;
-      const int slot = ti.z < 0 ? -1 : ti.z + (vw - ti.x / q);
-      __syncthreads();   // the previous range's merge and stores are done with the LDS
-      const int org = win_origin(p.ctx[i], p.window);
-      attn_gqa_range<NV, FAST>(p, i, tile, org + s0 * kSuper, org + s1 * kSuper, slot, smem);
+      if (s1 > s0) {
+        // the request's values in one round of loads, ahead of the barrier
+        const int i = ti.w;
+        const int first = p.req_info[i].y, c = p.ctx[i], r0 = p.cu[i], r1 = p.cu[i + 1];
+        const int slot = ti.z < 0 ? -1 : ti.z + (vw - ti.x / q);
+        const int org = win_origin(c, p.window);
+        __syncthreads();   // the previous range's merge and stores are done with the LDS
+        attn_gqa_range<NV, FAST>(p, i, T - first, c, r0, r1 - r0, org + s0 * kSuper, org + s1 * kSuper, slot,
+                                 smem);
+      }
+      // first read of the prefetched record here (the compiler would move it
+      // to scalar registers, and so wait for it, right after the load)
+      asm volatile("" : "+v"(ti_next.x), "+v"(ti_next.y), "+v"(ti_next.z), "+v"(ti_next.w));
+      // (the same record in every lane: uniform again for what follows)
+      ti = T + 1 < n_tiles ? make_int4(__builtin_amdgcn_readfirstlane(ti_next.x), __builtin_amdgcn_readfirstlane(ti_next.y),
+                                       __builtin_amdgcn_readfirstlane(ti_next.z), __builtin_amdgcn_readfirstlane(ti_next.w))
+                           : none;
     }
   }
 }
