@@ -649,25 +649,50 @@ __device__ __forceinline__ void lm_rows_body(const GemmParams& p, unsigned char*
       et[(bm * 32 + (j / 4) * 8 + lh * 4 + (j % 4)) * kRERow + wid * 32 + l32] = acc[bm][j];
   __syncthreads();
   const int rows = min(M, BMB * 32);
-  for (int q = tid; q < rows * (kRBN / kSlab); q += kGemmThreads) {
-    const int row = q / (kRBN / kSlab), sl = q % (kRBN / kSlab);
+  // four lanes per (row, slab), 16 columns each read as float4 runs; the
+  // lanes' (max, lowest argmax, sum of exp) merge through two lane swaps
+  // (one lane scanning 64 columns one float at a time took 8 us of the
+  // 156-row batch's 60)
+  constexpr int kQ = kSlab / 16;
+  const int n_items = rows * (kRBN / kSlab);
+  for (int q0 = 0; q0 < n_items * kQ; q0 += kGemmThreads) {   // uniform trip count
+    const int qq = q0 + tid;
+    const int q = qq / kQ, part = qq % kQ;
+    const bool live = q < n_items;
+    const int row = live ? q / (kRBN / kSlab) : 0, sl = live ? q % (kRBN / kSlab) : 0;
     const int cslab = v0 + sl * kSlab;
-    if (cslab >= p.V) continue;
-    const float* src = et + row * kRERow + sl * kSlab;
+    const int c0 = cslab + part * 16;
+    const float* src = et + row * kRERow + sl * kSlab + part * 16;
+    float z[16];
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(src + i);
+      z[i] = v.x; z[i + 1] = v.y; z[i + 2] = v.z; z[i + 3] = v.w;
+    }
     float best = -INFINITY;
-    int bi = cslab;
-    for (int i = 0; i < kSlab; ++i) {
-      const float z = cslab + i < p.V ? src[i] : -INFINITY;
-      if (z > best) { best = z; bi = cslab + i; }   // strict: lowest index wins ties
+    int bi = c0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (c0 + i >= p.V) z[i] = -INFINITY;
+      if (z[i] > best) { best = z[i]; bi = c0 + i; }   // strict: lowest index wins ties
     }
     float se = 0.f;
     if (p.with_sum && best != -INFINITY) {
-      for (int i = 0; i < kSlab; ++i) {
-        const float z = cslab + i < p.V ? src[i] : -INFINITY;
-        se += (z == -INFINITY) ? 0.f : __expf(z - best);
-      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) se += (z[i] == -INFINITY) ? 0.f : __expf(z[i] - best);
     }
-    p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
+#pragma unroll
+    for (int off = 1; off < kQ; off <<= 1) {
+      const float ob = __shfl_xor(best, off);
+      const int oi = __shfl_xor(bi, off);
+      const float os = __shfl_xor(se, off);
+      const float m = fmaxf(best, ob);
+      if (p.with_sum && m != -INFINITY)
+        se = (best == -INFINITY ? 0.f : se * __expf(best - m)) + (ob == -INFINITY ? 0.f : os * __expf(ob - m));
+      merge_best(best, bi, ob, oi);
+    }
+    if (live && part == 0 && cslab < p.V)
+      p.part[(size_t)row * p.n_slabs + cslab / kSlab] = make_float4(best, __int_as_float(bi), se, 0.f);
   }
   if (p.logits) {
     // row-contiguous float4 runs: 32 lanes per row, eight rows per pass
