@@ -79,10 +79,11 @@ constexpr int kBalS = 0, kBalQ = 1, kBalVw = 2, kBalTiles = 3, kBalParts = 4;
 // Both plans: the number of tiles with split partials (listed in split[]).
 constexpr int kHdrSplit = 6;
 constexpr int kBalSuper = 64;   // keys per super-tile of the GQA kernel (two 32-key sub-tiles)
-// A range's prologue (page window, queries, first DMA) costs about two
-// super-tiles of streaming (3.3 us against 1.43 us per super-tile, measured),
-// so the balanced plan charges each tile that much on top of its super-tiles.
-constexpr int kBalPro = 2;
+// A range's prologue (page window, queries, first DMA) costs about 2.4
+// super-tiles of streaming (3.4-3.6 us against 1.44 us per super-tile,
+// measured), so the balanced plan charges each tile three on top of its
+// super-tiles (two and four measured slower on both GQA batches).
+constexpr int kBalPro = 3;
 
 struct PlanParams {
   const int32_t* cu;
