@@ -9,8 +9,9 @@
 // moves them into LDS by direct global->LDS DMA (global_load_lds, 16 bytes
 // per lane) into a ring of stages; scores and outputs use bf16 MFMAs with
 // fp32 accumulation.
-//  * Plans (one workgroup each) rebuild the varlen metadata on the device
-//    from cu[] and ctx[].  k_attn_plan cuts every request into tiles of query
+//  * Plans (one workgroup each, launched alone or appended to the pack
+//    launch: k_pack_plan) rebuild the varlen metadata on the device from
+//    cu[] and ctx[].  k_attn_plan cuts every request into tiles of query
 //    vectors that share one KV head and, when the batch alone cannot fill the
 //    chip, splits the key range into chunks (split-KV), ordered request-major
 //    and per XCD so that the tiles reading one KV chunk share it through L2.
@@ -37,8 +38,9 @@
 //    over each item's visible list entries, compacted in list order, each
 //    DMA lane reading its slot's row.  k_attn_mla (64 heads per workgroup)
 //    serves other head counts and page sizes.
-//  * k_attn_combine merges split partials (O, max, normaliser); k_attn_pad
-//    writes the rows between the packed count and the tier.
+//  * k_attn_combine merges split partials (O, max, normaliser) and writes
+//    the rows between the packed count and the tier (k_attn_pad does that
+//    for the fp32 kernel).
 //  * fp32 inputs take a plain vector kernel (k_attn_f32).
 
 #include <float.h>
