@@ -23,6 +23,9 @@ class VerifyStep:
                  hist_cap=64, stream=None, w_layout="tiled", window=0, topk=0, fused_plan=True):
         wl = inp["workload"]
         self.inp, self.wl = inp, wl
+        # the stages' C-ABI argument structs, rebuilt only when an input
+        # tensor is replaced (the step's own buffers never are)
+        self._abi = rv.ArgCache()
         self.mode = mode
         # fused_plan: the pack launch also builds the attention call's plan
         # (rv_pack_plan); an attention call right after such a pack skips its
@@ -116,7 +119,8 @@ class VerifyStep:
         self._plan_ready = False   # this stage may write the workspace
         i = self.inp
         rv.rv_schedule(i["conf"], self.gamma, self.mode, i["cost_bias"], i["cost_alpha"], i["cost_theta"],
-                       self.w_commit, self.w_verify, self.k_star, self.e_star, self.workspace, self.stream)
+                       self.w_commit, self.w_verify, self.k_star, self.e_star, self.workspace, self.stream,
+                       cache=self._abi)
 
     def _pack_kw(self):
         i = self.inp
@@ -134,7 +138,7 @@ class VerifyStep:
 
     def pack(self):
         if self.fused_plan:
-            rv.rv_pack_plan(self._pack_kw(), self._attn_kw(), self.stream)
+            rv.rv_pack_plan(self._pack_kw(), self._attn_kw(), self.stream, cache=self._abi)
             self._plan_ready = True
         else:
             rv.rv_pack(**self._pack_kw(), stream=self.stream)
@@ -153,9 +157,9 @@ class VerifyStep:
 
     def attn(self):
         if self._plan_ready:
-            rv.rv_verify_attn_planned(**self._attn_kw(), stream=self.stream)
+            rv.rv_verify_attn_planned(**self._attn_kw(), stream=self.stream, cache=self._abi)
         else:
-            rv.rv_verify_attn(**self._attn_kw(), stream=self.stream)
+            rv.rv_verify_attn(**self._attn_kw(), stream=self.stream, cache=self._abi)
         self._plan_ready = False
 
     def lm(self):
@@ -164,7 +168,7 @@ class VerifyStep:
         rv.rv_lm_head_accept(self.hidden, i["W"], self.mm, self.cu, self.w_commit, self.w_verify, i["drafts"],
                              self.rule, self.pred, self.accept, self.bonus, self.ceiling, self.workspace,
                              logits=self.logits, q_rows=i.get("q_rows"), u=i.get("u"), u_bonus=i.get("u_bonus"),
-                             stream=self.stream, W_tiled=self.W_tiled)
+                             stream=self.stream, W_tiled=self.W_tiled, cache=self._abi)
 
     def scatter(self):
         self._plan_ready = False   # this stage may write the workspace
@@ -172,7 +176,7 @@ class VerifyStep:
         rv.rv_compact_scatter(self.cu, self.w_verify, self.accept, self.bonus, i["drafts"], self.slot, self.ctx,
                               self.anchor, self.req_to_token, self.commit_cu, self.commit_tok, self.commit_slot,
                               self.free_slots, self.free_count, self.workspace, hist=self.hist,
-                              hist_len=self.hist_len, stream=self.stream)
+                              hist_len=self.hist_len, stream=self.stream, cache=self._abi)
 
     def restore(self):
         self.ctx.copy_(self.ctx0)

@@ -164,6 +164,32 @@ def abi_layout(lib, which):
 
 
 # ---- marshalling helpers ------------------------------------------------------
+class ArgCache:
+    """The argument structs of calls a caller repeats on the same buffers
+    (one verify step after another), built once: an entry is reused while
+    every tensor argument is the same object and every other argument has
+    the same value.  Entries hold their arguments, so the tensors stay alive
+    (and their ids unique); tensors must keep their storage (no ``resize_``
+    or ``set_``) while they are cached.  Building a struct validates and
+    converts some 15-30 tensors, about 1 us each on the host."""
+
+    def __init__(self):
+        self._e = {}
+
+    def get(self, name, args, build):
+        key = tuple(id(v) if isinstance(v, torch.Tensor) else v for v in args)
+        e = self._e.get(name)
+        if e is not None and e[0] == key:
+            return e[1]
+        val = build()
+        self._e[name] = (key, val, args)
+        return val
+
+
+def _cached(cache, name, args, build):
+    return build() if cache is None else cache.get(name, args, build)
+
+
 def _ptr(t, dtype=None, name="tensor"):
     if t is None:
         return None
@@ -221,9 +247,16 @@ def rv_clear_status(workspace, stream=None):
 
 
 def rv_schedule(conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, w_verify, k_star,
-                e_star, workspace, stream=None):
+                e_star, workspace, stream=None, cache=None):
+    args = (conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, w_verify, k_star, e_star, workspace)
+    a = _cached(cache, "rv_schedule", args, lambda: _schedule_args(*args))
+    _check("rv_schedule", load().rv_schedule(ctypes.byref(a), _stream(stream)))
+
+
+def _schedule_args(conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, w_verify, k_star, e_star,
+                   workspace):
     B = conf.shape[0]
-    a = ScheduleArgs(conf=_ptr(conf, torch.float32, "conf"), B=B, gamma=gamma,
+    return ScheduleArgs(conf=_ptr(conf, torch.float32, "conf"), B=B, gamma=gamma,
                      mode=MODES[mode] if isinstance(mode, str) else mode,
                      alpha_len=cost_alpha.numel(), theta_len=cost_theta.numel(), cost_bias=float(cost_bias),
                      cost_alpha=_ptr(cost_alpha, torch.float64, "cost_alpha"),
@@ -232,7 +265,6 @@ def rv_schedule(conf, gamma, mode, cost_bias, cost_alpha, cost_theta, w_commit, 
                      w_verify=_ptr(w_verify, torch.int32, "w_verify"),
                      k_star=_ptr(k_star, torch.int32, "k_star"), e_star=_ptr(e_star, torch.float64, "e_star"),
                      workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
-    _check("rv_schedule", load().rv_schedule(ctypes.byref(a), _stream(stream)))
 
 
 def _pack_args(w_verify, anchor, drafts, ctx, page_table, page_size, num_pages, tiers, cu, mm, row_req,
@@ -279,25 +311,28 @@ def _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, m
 
 
 def rv_verify_attn(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                   o, lse, workspace, stream=None, window=0, topk_idx=None):
-    a = _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                   o, lse, workspace, window=window, topk_idx=topk_idx)
+                   o, lse, workspace, stream=None, window=0, topk_idx=None, cache=None):
+    args = (q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale, o, lse, workspace,
+            window, topk_idx)
+    a = _cached(cache, "attn", args, lambda: _attn_args(*args))
     _check("rv_verify_attn", load().rv_verify_attn(ctypes.byref(a), _stream(stream)))
 
 
 def rv_verify_attn_planned(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                           o, lse, workspace, stream=None, window=0, topk_idx=None):
+                           o, lse, workspace, stream=None, window=0, topk_idx=None, cache=None):
     """Stage 3 after rv_pack_plan (the plan is already in the workspace)."""
-    a = _attn_args(q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale,
-                   o, lse, workspace, window=window, topk_idx=topk_idx)
+    args = (q, k_cache, v_cache, page_table, page_size, num_pages, ctx, cu, mm, gamma, sm_scale, o, lse, workspace,
+            window, topk_idx)
+    a = _cached(cache, "attn", args, lambda: _attn_args(*args))
     _check("rv_verify_attn_planned", load().rv_verify_attn_planned(ctypes.byref(a), _stream(stream)))
 
 
-def rv_pack_plan(pack, attn, stream=None):
+def rv_pack_plan(pack, attn, stream=None, cache=None):
     """Stage 2 and the plan of stage 3 in one launch.  ``pack``: the keyword
     arguments of rv_pack (without stream); ``attn``: those of rv_verify_attn."""
-    pa, _keep = _pack_args(**pack)
-    aa = _attn_args(**attn)
+    args = tuple(pack.items()) + tuple(attn.items())
+    pa, _keep, aa = _cached(cache, "pack_plan", tuple(v for _, v in args) + tuple(k for k, _ in args),
+                            lambda: _pack_args(**pack) + (_attn_args(**attn),))
     _check("rv_pack_plan", load().rv_pack_plan(ctypes.byref(pa), ctypes.byref(aa), _stream(stream)))
 
 
@@ -405,11 +440,13 @@ def _lm_args(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, 
 
 
 def rv_lm_head_accept(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling,
-                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None, W_tiled=None):
+                      workspace, logits=None, q_rows=None, u=None, u_bonus=None, stream=None, W_tiled=None,
+                      cache=None):
     """W [V][H] gives the vocabulary size; with W_tiled (rv_lm_tile_weight of
     W) the kernel reads the tiled copy instead."""
-    a = _lm_args(hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling, workspace,
-                 logits, q_rows, u, u_bonus, W_tiled)
+    args = (hidden, W, mm, cu, w_commit, w_verify, drafts, rule, pred, accept, bonus, ceiling, workspace,
+            logits, q_rows, u, u_bonus, W_tiled)
+    a = _cached(cache, "lm", args, lambda: _lm_args(*args))
     _check("rv_lm_head_accept", load().rv_lm_head_accept(ctypes.byref(a), _stream(stream)))
 
 
@@ -426,9 +463,17 @@ def rv_lm_head_accept_noalloc(hidden, W, mm, cu, w_commit, w_verify, drafts, rul
 
 def rv_compact_scatter(cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, req_to_token, commit_cu,
                        commit_tok, commit_slot, free_slots, free_count, workspace, hist=None, hist_len=None,
-                       stream=None):
+                       stream=None, cache=None):
+    args = (cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, req_to_token, commit_cu, commit_tok,
+            commit_slot, free_slots, free_count, workspace, hist, hist_len)
+    a = _cached(cache, "scatter", args, lambda: _scatter_args(*args))
+    _check("rv_compact_scatter", load().rv_compact_scatter(ctypes.byref(a), _stream(stream)))
+
+
+def _scatter_args(cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, req_to_token, commit_cu, commit_tok,
+                  commit_slot, free_slots, free_count, workspace, hist, hist_len):
     B, g1 = drafts.shape
-    a = ScatterArgs(cu=_ptr(cu, torch.int32, "cu"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
+    return ScatterArgs(cu=_ptr(cu, torch.int32, "cu"), w_verify=_ptr(w_verify, torch.int32, "w_verify"),
                     accept=_ptr(accept, torch.int32, "accept"), bonus=_ptr(bonus, torch.int32, "bonus"),
                     drafts=_ptr(drafts, torch.int32, "drafts"), slot=_ptr(slot, torch.int32, "slot"),
                     B=B, gamma=g1 + 1, r2t_stride=req_to_token.shape[1],
@@ -442,4 +487,3 @@ def rv_compact_scatter(cu, w_verify, accept, bonus, drafts, slot, ctx, anchor, r
                     free_slots=_ptr(free_slots, torch.int32, "free_slots"),
                     free_count=_ptr(free_count, torch.int32, "free_count"),
                     workspace=_ptr(workspace, name="workspace"), workspace_bytes=workspace.numel() * workspace.element_size())
-    _check("rv_compact_scatter", load().rv_compact_scatter(ctypes.byref(a), _stream(stream)))

@@ -219,3 +219,36 @@ def test_lm_noalloc_rejects_beyond_its_scratch(lib):
     assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_WORKSPACE
     a.rule = 9
     assert lib.rv_lm_head_accept_noalloc(ctypes.byref(a), None) == rv.RV_ERR_INVALID_ARG
+
+
+def test_arg_cache_reuses_and_rebuilds():
+    """ArgCache hands back the same built structs while the tensor arguments
+    are the same objects and the other arguments the same values, rebuilds
+    on any change, and keeps its tensors alive (so their ids stay theirs)."""
+    import gc
+    import torch
+    from ragged_verification_amd import rv
+    c = rv.ArgCache()
+    built = []
+
+    def build():
+        built.append(object())
+        return built[-1]
+
+    t1, t2 = torch.zeros(4), torch.zeros(4)
+    a = c.get("x", (t1, 3, None), build)
+    assert c.get("x", (t1, 3, None), build) is a and len(built) == 1
+    c.get("x", (t2, 3, None), build)            # another tensor object
+    assert len(built) == 2
+    c.get("x", (t2, 4, None), build)            # another scalar
+    assert len(built) == 3
+    c.get("y", (t2, 4, None), build)            # entries are per call name
+    assert len(built) == 4
+    assert c.get("x", (t2, 4, None), build) is built[2]
+    # the cached entry holds t2: dropping the caller's reference does not let
+    # a new tensor take its id while the entry lives
+    ident = id(t2)
+    del t2
+    gc.collect()
+    fresh = [torch.zeros(4) for _ in range(64)]
+    assert all(id(f) != ident for f in fresh)
