@@ -178,6 +178,25 @@ class VerifyStep:
                               self.free_slots, self.free_count, self.workspace, hist=self.hist,
                               hist_len=self.hist_len, stream=self.stream, cache=self._abi)
 
+    def prime(self):
+        """Build (and cache) the five stages' argument structs for the
+        current inputs without launching anything."""
+        i = self.inp
+        rv.rv_schedule(i["conf"], self.gamma, self.mode, i["cost_bias"], i["cost_alpha"], i["cost_theta"],
+                       self.w_commit, self.w_verify, self.k_star, self.e_star, self.workspace, self.stream,
+                       cache=self._abi, launch=False)
+        if self.fused_plan:
+            rv.rv_pack_plan(self._pack_kw(), self._attn_kw(), self.stream, cache=self._abi, launch=False)
+        rv.rv_verify_attn(**self._attn_kw(), stream=self.stream, cache=self._abi, launch=False)
+        rv.rv_lm_head_accept(self.hidden, i["W"], self.mm, self.cu, self.w_commit, self.w_verify, i["drafts"],
+                             self.rule, self.pred, self.accept, self.bonus, self.ceiling, self.workspace,
+                             logits=self.logits, q_rows=i.get("q_rows"), u=i.get("u"), u_bonus=i.get("u_bonus"),
+                             stream=self.stream, W_tiled=self.W_tiled, cache=self._abi, launch=False)
+        rv.rv_compact_scatter(self.cu, self.w_verify, self.accept, self.bonus, i["drafts"], self.slot, self.ctx,
+                              self.anchor, self.req_to_token, self.commit_cu, self.commit_tok, self.commit_slot,
+                              self.free_slots, self.free_count, self.workspace, hist=self.hist,
+                              hist_len=self.hist_len, stream=self.stream, cache=self._abi, launch=False)
+
     def restore(self):
         self.ctx.copy_(self.ctx0)
         self.anchor.copy_(self.anchor0)

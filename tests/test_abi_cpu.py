@@ -245,6 +245,14 @@ def test_arg_cache_reuses_and_rebuilds():
     c.get("y", (t2, 4, None), build)            # entries are per call name
     assert len(built) == 4
     assert c.get("x", (t2, 4, None), build) is built[2]
+    assert c.get("x", (t1, 3, None), build) is built[0]   # earlier sets are kept too
+    assert c.get("x", (t1, 3, [64, 128]), build) is c.get("x", (t1, 3, [64, 128]), build)
+    small = rv.ArgCache(per_call=2)
+    for n in range(3):
+        small.get("z", (n,), build)
+    n_built = len(built)
+    small.get("z", (0,), build)                  # evicted: rebuilt
+    assert len(built) == n_built + 1
     # the cached entry holds t2: dropping the caller's reference does not let
     # a new tensor take its id while the entry lives
     ident = id(t2)
