@@ -17,6 +17,7 @@ the CPU oracle's rate on a bounded sample of the same workload.
 """
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -49,22 +50,36 @@ def log(msg):
 
 class StageTimer:
     """HIP events on torch's current stream (the stream every call uses);
-    read back once after the timed region has been synchronised."""
+    read back once after the timed region has been synchronised.  The events
+    of ``count`` records per stage are created up front, so the timed region
+    only records them."""
 
-    def __init__(self, names):
+    def __init__(self, names, count=0):
         self.names = names
         self.pairs = {n: [] for n in names}
         self.acc = {n: 0.0 for n in names}
+        self.pool = [torch.cuda.Event(enable_timing=True) for _ in range((len(names) + 1) * count)]
+
+    def _event(self):
+        return self.pool.pop() if self.pool else torch.cuda.Event(enable_timing=True)
 
     def start(self, n):
-        e = torch.cuda.Event(enable_timing=True)
+        e = self._event()
         e.record()
         self.pairs[n].append([e, None])
 
     def stop(self, n):
-        e = torch.cuda.Event(enable_timing=True)
+        e = self._event()
         e.record()
         self.pairs[n][-1][1] = e
+
+    def switch(self, a, b):
+        """Stage a ends where stage b starts: one event for both (a record
+        costs about 4 us of host time, as much as a small stage's work)."""
+        e = self._event()
+        e.record()
+        self.pairs[a][-1][1] = e
+        self.pairs[b].append([e, None])
 
     def collect(self):
         pass
@@ -130,24 +145,19 @@ def run_steps(step, n, timer=None, sets=None):
             timer.start("schedule")
         step.schedule()
         if timer:
-            timer.stop("schedule")
-            timer.start("pack")
+            timer.switch("schedule", "pack")
         step.pack()
         if timer:
-            timer.stop("pack")
-            timer.start("staging")
+            timer.switch("pack", "staging")
         step.stage_payload()
         if timer:
-            timer.stop("staging")
-            timer.start("attn")
+            timer.switch("staging", "attn")
         step.attn()
         if timer:
-            timer.stop("attn")
-            timer.start("lm_accept")
+            timer.switch("attn", "lm_accept")
         step.lm()
         if timer:
-            timer.stop("lm_accept")
-            timer.start("scatter")
+            timer.switch("lm_accept", "scatter")
         step.scatter()
         if timer:
             timer.stop("scatter")
@@ -189,11 +199,16 @@ def measure(step, steps, warmup, sets=None):
             step.prime()
     run_steps(step, warmup, sets=sets)
     torch.cuda.synchronize()
-    timer = StageTimer(STAGES + ["staging"])
-    t0 = time.perf_counter()
-    run_steps(step, steps, timer, sets=sets)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    timer = StageTimer(STAGES + ["staging"], steps)
+    gc.collect()
+    gc.disable()   # no collector pause inside the timed steps
+    try:
+        t0 = time.perf_counter()
+        run_steps(step, steps, timer, sets=sets)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        gc.enable()
     timer.finish()
     assert step.status() == 0, f"device status {rv.DEV_NAMES.get(step.status())}"
     per = {k: v / steps for k, v in timer.acc.items()}
@@ -224,20 +239,23 @@ def measure_graph(step, steps, warmup, sets=None):
         step.stage_payload()
         graphs[w % len(sets)][1].replay()
     torch.cuda.synchronize()
-    timer = StageTimer(["front", "staging", "back"])
-    for k in range(steps):
-        g_front, g_back = graphs[k % len(sets)]
-        use_inputs(step, sets[k % len(sets)])
-        step.restore()
-        timer.start("front")
-        g_front.replay()
-        timer.stop("front")
-        timer.start("staging")
-        step.stage_payload()
-        timer.stop("staging")
-        timer.start("back")
-        g_back.replay()
-        timer.stop("back")
+    timer = StageTimer(["front", "staging", "back"], steps)
+    gc.collect()
+    gc.disable()
+    try:
+        for k in range(steps):
+            g_front, g_back = graphs[k % len(sets)]
+            use_inputs(step, sets[k % len(sets)])
+            step.restore()
+            timer.start("front")
+            g_front.replay()
+            timer.switch("front", "staging")
+            step.stage_payload()
+            timer.switch("staging", "back")
+            g_back.replay()
+            timer.stop("back")
+    finally:
+        gc.enable()
     timer.finish()
     assert step.status() == 0, f"device status {rv.DEV_NAMES.get(step.status())}"
     per = {k: v / steps for k, v in timer.acc.items()}
