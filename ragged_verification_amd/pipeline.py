@@ -40,7 +40,7 @@ class VerifyStep:
         B, gamma = inp["B"], inp["gamma"]
         self.B, self.gamma = B, gamma
         tiers = list(inp["tiers"])
-        self.tiers = tiers
+        self.tiers = tuple(tiers)   # immutable: the argument cache compares it by identity
         self.rows_cap = rows_cap or max([B * gamma] + tiers)
         i32 = dict(dtype=torch.int32, device=dev)
         R = self.rows_cap

@@ -167,21 +167,22 @@ def abi_layout(lib, which):
 class ArgCache:
     """The argument structs of calls a caller repeats on the same buffers
     (one verify step after another), built once: an entry is reused when
-    every tensor argument is the same object and every other argument has
-    the same value.  Up to ``per_call`` argument sets are kept per call (a
-    caller that rotates among a few input copies hits after the first
-    round).  Entries hold their arguments, so the tensors stay alive (and
-    their ids unique); tensors must keep their storage (no ``resize_`` or
-    ``set_``) while they are cached.  Building a struct validates and
-    converts some 15-30 tensors, about 1 us each on the host."""
+    every argument is the very same object as before (compared by identity:
+    equal values in new objects only cost a rebuild).  Up to ``per_call``
+    argument sets are kept per call (a caller that rotates among a few input
+    copies hits after the first round).  Entries hold their arguments, so
+    those objects stay alive and their ids unique.  While cached, tensors
+    must keep their storage (no ``resize_`` or ``set_``) and containers
+    (tiers) must not change in place.  Building a struct validates and
+    converts some 15-30 tensors, about 1 us each on the host; the identity
+    key costs a few tens of nanoseconds per argument."""
 
     def __init__(self, per_call=16):
         self._e = {}
         self._n = per_call
 
     def get(self, name, args, build):
-        key = tuple(id(v) if isinstance(v, torch.Tensor) else (tuple(v) if isinstance(v, list) else v)
-                    for v in args)
+        key = tuple(map(id, args))
         d = self._e.setdefault(name, {})
         e = d.get(key)
         if e is not None:
@@ -341,9 +342,8 @@ def rv_verify_attn_planned(q, k_cache, v_cache, page_table, page_size, num_pages
 def rv_pack_plan(pack, attn, stream=None, cache=None, launch=True):
     """Stage 2 and the plan of stage 3 in one launch.  ``pack``: the keyword
     arguments of rv_pack (without stream); ``attn``: those of rv_verify_attn."""
-    args = tuple(pack.items()) + tuple(attn.items())
-    pa, _keep, aa = _cached(cache, "pack_plan", tuple(v for _, v in args) + tuple(k for k, _ in args),
-                            lambda: _pack_args(**pack) + (_attn_args(**attn),))
+    args = (*pack.keys(), *pack.values(), *attn.keys(), *attn.values())
+    pa, _keep, aa = _cached(cache, "pack_plan", args, lambda: _pack_args(**pack) + (_attn_args(**attn),))
     if not launch:
         return
     _check("rv_pack_plan", load().rv_pack_plan(ctypes.byref(pa), ctypes.byref(aa), _stream(stream)))

@@ -246,7 +246,11 @@ def test_arg_cache_reuses_and_rebuilds():
     assert len(built) == 4
     assert c.get("x", (t2, 4, None), build) is built[2]
     assert c.get("x", (t1, 3, None), build) is built[0]   # earlier sets are kept too
-    assert c.get("x", (t1, 3, [64, 128]), build) is c.get("x", (t1, 3, [64, 128]), build)
+    tiers = (64, 128)
+    assert c.get("x", (t1, 3, tiers), build) is c.get("x", (t1, 3, tiers), build)
+    n_built = len(built)
+    c.get("x", (t1, 3, (64, 256)), build)       # another object: rebuilt
+    assert len(built) == n_built + 1
     small = rv.ArgCache(per_call=2)
     for n in range(3):
         small.get("z", (n,), build)
