@@ -15,6 +15,7 @@ import torch
 
 import oracle
 import parity_util as pu
+from ragged_verification_amd import rv
 from ragged_verification_amd.pipeline import VerifyStep
 
 pytestmark = pytest.mark.gpu
@@ -445,6 +446,43 @@ def test_fused_pack_plan_equals_separate_launches(wl, kw, step_kw):
         del step
     for n in outs[0]:
         assert torch.equal(outs[0][n], outs[1][n]), n
+
+
+def test_cached_argument_structs_equal_fresh_ones():
+    """The binding's argument cache (VerifyStep's default) gives the same
+    outputs bit for bit as building every struct afresh, over several steps
+    in which the inputs switch between two sets (new tensor objects for the
+    KV caches, the weight and the drafts) and back, and the mode changes."""
+    inp = pu.make_inputs("gqa_bf16", B=6, V=1000, H=256, ctx=("uniform", 40, 900))
+    inp["W_tiled"] = rv.rv_lm_tile_weight(inp["W"])
+    inp2 = dict(inp)
+    for k in ("k_cache", "v_cache", "W", "drafts", "conf"):
+        inp2[k] = inp[k].clone()
+    inp2["k_cache"].mul_(0.5)
+    inp2["conf"] = inp2["conf"].flip(0).contiguous()
+    inp2["W_tiled"] = rv.rv_lm_tile_weight(inp2["W"])
+    plan = [(inp, "compact"), (inp2, "compact"), (inp, "compact"), (inp2, "static"), (inp, "compact")]
+    outs = []
+    for cached in (True, False):
+        step = VerifyStep(inp, mode="compact", with_logits=True)
+        assert step.W_tiled is not None
+        if not cached:
+            step._abi = None
+        got = []
+        for src, mode in plan:
+            step.inp = src
+            step.mode = mode
+            step.W_tiled = src["W_tiled"]
+            step.restore()
+            step.run()
+            torch.cuda.synchronize()
+            assert step.status() == 0
+            got.append(_outputs(step))
+        outs.append(got)
+        del step
+    for a, b in zip(*outs):
+        for n in a:
+            assert torch.equal(a[n], b[n]), n
 
 
 @pytest.mark.parametrize("wl,kw", [("mla_bf16", dict(B=3, V=1000, H=512, ctx=("uniform", 60, 700))),
